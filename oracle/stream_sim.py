@@ -1,0 +1,98 @@
+"""Layer-stream schedule and the event log a correct engine must produce.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+What the pages fix (the Soup deep dive, "How layer streaming works", and the
+4 GB-laptop article, "Layer streaming: technical implementation"):
+* the frozen base is cut into per-layer shards kept in (page-locked) host RAM;
+* a few preallocated device layer buffers -- 2 by default, 2 to 8 through
+  ``stream_buffers`` ("Streaming config keys") -- are filled by a separate
+  stream with the next layer while the current one computes;
+* every decoder layer is read twice per SFT step: once for the forward and once
+  for the checkpoint recompute in backward;
+* DPO reads the layer stack more often per step than SFT (1.52x on the 4 GB
+  article, "Computational trade-off"): its reference pass is the same streamed
+  base with the adapters off.
+
+Readings (the pages give no schedule rule): call k of a step uses buffer
+k mod nbuf; at call k the copy stream is kept nbuf-1 layers ahead, i.e. every
+copy j <= k + nbuf - 1 not yet issued is issued; copy j goes to buffer
+j mod nbuf and must wait until the compute of call j - nbuf (the buffer's
+previous user) has finished; call k's compute waits for copy k.  In resident
+mode every shard has its own buffer, all shards are copied once on the first
+call, and call k waits for the copy of its own shard.
+
+The event log is a list of tuples (kind, call, j, layer, buffer, wait):
+  COPY  issued during call ``call``: schedule position j, shard ``layer``,
+        into ``buffer``, after the release of call ``wait`` (-1: no wait)
+  STEP  call ``call`` computes shard ``layer`` from ``buffer`` once copy ``j``
+        is done (``wait`` == j)
+"""
+from __future__ import annotations
+
+COPY = 0
+STEP = 1
+
+
+def sft_schedule(n_layers: int) -> list[int]:
+    """Forward 0..L-1, then backward (recompute + gradient) L-1..0: two reads per layer."""
+    return list(range(n_layers)) + list(range(n_layers - 1, -1, -1))
+
+
+def dpo_schedule(n_layers: int) -> list[int]:
+    """Adapter-off reference forward, then the SFT schedule: three reads per layer."""
+    return list(range(n_layers)) + sft_schedule(n_layers)
+
+
+def simulate(schedule, n_bufs: int, n_shards: int | None = None, resident: bool = False):
+    """Return the event log of one pass over ``schedule`` (see the module header)."""
+    sched = list(schedule)
+    n = len(sched)
+    log = []
+    if resident:
+        shards = n_shards if n_shards is not None else (max(sched) + 1 if sched else 0)
+        for k in range(n):
+            if k == 0:
+                for s in range(shards):
+                    log.append((COPY, 0, s, s, s, -1))
+            s = sched[k]
+            log.append((STEP, k, s, s, s, s))
+        return log
+    issued = 0
+    for k in range(n):
+        while issued < n and issued <= k + n_bufs - 1:
+            j = issued
+            log.append((COPY, k, j, sched[j], j % n_bufs, j - n_bufs if j >= n_bufs else -1))
+            issued += 1
+        log.append((STEP, k, k, sched[k], k % n_bufs, k))
+    return log
+
+
+def copies(log) -> list[tuple]:
+    return [e for e in log if e[0] == COPY]
+
+
+def check_happens_before(log, schedule, n_bufs: int) -> None:
+    """Replay the ring and assert that no buffer is overwritten while a call may still use it.
+
+    A copy into buffer b for position j may start only after the compute of call
+    j - nbuf (the previous user of b) has been released, and that release must
+    come from a call that has already been made when the copy is issued.  Every
+    step must find its own shard in its buffer.
+    """
+    content = {}
+    made = -1
+    for kind, call, j, layer, buf, wait in log:
+        if kind == COPY:
+            prev_user = j - n_bufs
+            if prev_user >= 0:
+                assert wait == prev_user, (j, wait)
+                assert prev_user < call, "release not yet recorded when the copy is issued"
+            else:
+                assert wait == -1
+            content[buf] = (j, layer)
+        else:
+            assert call == made + 1, "calls out of order"
+            made = call
+            assert content.get(buf) == (j, layer), (call, buf, content.get(buf))
+            assert layer == schedule[call]

@@ -1,0 +1,63 @@
+"""Pins for the layer-stream schedule simulator: the read counts the pages print,
+a hand-worked log, and the happens-before invariant for every ring size."""
+import json
+import os
+
+import pytest
+
+from oracle import stream_sim as ss
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")
+
+
+def test_read_counts_match_pages():
+    g = json.load(open(GOLDEN))
+    for L in (1, 3, 24, 32):
+        sft = ss.copies(ss.simulate(ss.sft_schedule(L), 2))
+        dpo = ss.copies(ss.simulate(ss.dpo_schedule(L), 2))
+        assert len(sft) == g["sft_reads_per_layer"]["value"] * L
+        assert len(dpo) == 3 * L
+        # the pages' 1.52x also counts reads outside the layer stack; the stack alone is 1.5x
+        assert abs(len(dpo) / len(sft) - g["dpo_over_sft_stack_reads"]["value"]) <= 0.021
+
+
+def test_hand_worked_log_l3_nbuf2():
+    # schedule [0, 1, 2, 2, 1, 0]; two buffers; copies run one call ahead
+    log = ss.simulate(ss.sft_schedule(3), 2)
+    C, S = ss.COPY, ss.STEP
+    assert log == [
+        (C, 0, 0, 0, 0, -1), (C, 0, 1, 1, 1, -1), (S, 0, 0, 0, 0, 0),
+        (C, 1, 2, 2, 0, 0), (S, 1, 1, 1, 1, 1),
+        (C, 2, 3, 2, 1, 1), (S, 2, 2, 2, 0, 2),
+        (C, 3, 4, 1, 0, 2), (S, 3, 3, 2, 1, 3),
+        (C, 4, 5, 0, 1, 3), (S, 4, 4, 1, 0, 4),
+        (S, 5, 5, 0, 1, 5),
+    ]
+
+
+@pytest.mark.parametrize("nbuf", range(2, 9))
+@pytest.mark.parametrize("L", [1, 2, 5, 32])
+def test_happens_before(nbuf, L):
+    for sched in (ss.sft_schedule(L), ss.dpo_schedule(L)):
+        log = ss.simulate(sched, nbuf)
+        ss.check_happens_before(log, sched, nbuf)
+        # the copy stream never runs more than nbuf - 1 layers ahead of compute
+        for kind, call, j, *_ in log:
+            if kind == ss.COPY:
+                assert j <= call + nbuf - 1
+
+
+def test_happens_before_catches_a_missing_wait():
+    log = ss.simulate(ss.sft_schedule(4), 2)
+    bad = [e if not (e[0] == ss.COPY and e[2] == 3) else (e[0], e[1], e[2], e[3], e[4], -1) for e in log]
+    with pytest.raises(AssertionError):
+        ss.check_happens_before(bad, ss.sft_schedule(4), 2)
+
+
+def test_resident_copies_each_shard_once():
+    sched = ss.sft_schedule(6)
+    log = ss.simulate(sched, 6, n_shards=6, resident=True)
+    cps = ss.copies(log)
+    assert sorted(e[3] for e in cps) == list(range(6))
+    steps = [e for e in log if e[0] == ss.STEP]
+    assert [e[3] for e in steps] == sched and all(e[4] == e[3] for e in steps)
