@@ -1,0 +1,265 @@
+/*
+ * lnf4.h -- C ABI of the streamed NF4 + LoRA linear for AMD Instinct MI355X (gfx950).
+ *
+ * The method.  Layer-streamed LoRA fine-tuning keeps the frozen base model out of
+ * device memory: per-layer shards live in page-locked host RAM and are copied, one
+ * decoder layer at a time, into a few preallocated device buffers by a separate
+ * stream while the current layer computes (Soup deep dive, blog.123qwe.co.kr,
+ * section "Core feature: how layer streaming works"; Soup 4 GB-laptop article,
+ * agentlenshq.com, section "Layer streaming: technical implementation and memory
+ * efficiency").  The frozen weights are 4-bit NF4 ("quantization: 4bit", 4 GB-laptop
+ * article, section "Configuration and training").  Only the low-rank adapters A, B
+ * are trained (20B-RLHF-on-24GB article, agentlenshq.com, section "Low-rank
+ * adaptation via PEFT"); in backward the layer must be on the device again because
+ * the input gradient is W^T applied to the output gradient (Soup deep dive, same
+ * section).
+ *
+ * Conventions for every entry point.
+ *  - All matrices are row-major.  A frozen weight is [out, in] (a PyTorch Linear
+ *    weight).  A is [r, in], B is [out, r].  Activations are [T, features].
+ *  - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *  - Every pointer named "device" is a device address (hipMalloc / torch CUDA
+ *    tensors); "host" pointers are page-locked host memory where stated.
+ *  - Ownership: the caller owns every buffer, workspace and stream.  The library owns
+ *    only the lnf4_stream object and the HIP events inside it.  lora_linear_* and
+ *    nf4_* never allocate device memory.
+ *  - Asynchrony: kernel work is enqueued on the stream argument and returns before it
+ *    runs.  Faults inside kernels surface at a later call or the caller's sync.
+ *  - Determinism: the same inputs and arguments give bitwise identical outputs, run
+ *    to run, and streamed vs resident (no floating-point atomics anywhere).
+ *  - Errors: every call returns LNF4_OK (0) or a negative LNF4_E* code and sets a
+ *    thread-local message readable with lnf4_last_error().  Argument validation runs
+ *    before any HIP call.  No exception crosses the ABI and the library never aborts.
+ *  - Not thread-safe per lnf4_stream object.
+ */
+#ifndef LNF4_H
+#define LNF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t; /* same declaration as the HIP runtime's */
+
+#define LNF4_OK 0
+#define LNF4_EINVAL (-1) /* null pointer, value out of range (r > 64, nbuf outside 2..8, ...) */
+#define LNF4_ESHAPE (-2) /* shape not supported: in % 64 != 0, blocksize != 64, buffer too small */
+#define LNF4_EALIGN (-3) /* device pointer not 16-byte aligned, shard section not 256-byte aligned */
+#define LNF4_EHIP (-4)   /* a HIP runtime call failed; the message names it */
+#define LNF4_ESTATE (-5) /* call out of order, destroyed or finished stream context */
+
+#define LNF4_FMT_NF4 0  /* data = packed codes uint8 [out][in/2], absmax fp32 [out*in/64] */
+#define LNF4_FMT_BF16 1 /* data = bf16 [out][in], absmax unused (un-quantized streaming) */
+
+#define LNF4_MAX_RANK 64
+#define LNF4_MAX_GROUP 8
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* lnf4_last_error(void);
+
+/* Library version string. */
+const char* lnf4_version(void);
+
+/*
+ * The 16-entry NF4 code table, fp32, ascending: T[0] = -1, T[7] = 0, T[15] = +1.
+ * Levels are standard-normal quantiles: 8 positive at probabilities 1/2 + j(d-1/2)/8
+ * (j = 1..8), 7 negative at minus the quantiles of 1/2 + j(d-1/2)/7 (j = 1..7) and 0,
+ * all divided by the quantile of d = ((1 - 1/30) + (1 - 1/32)) / 2.  (The pages name
+ * the format only; this construction is the normal-quantile NF4 reading.)
+ * out: host array of 16 floats.  Runs on the host only.
+ */
+int lnf4_nf4_table(float out[16]);
+
+/*
+ * Decode NF4 to bf16: out[e] = bf16_rne(fp32(T[code(e)] * absmax[e / blocksize])).
+ * The decode is the per-layer dequantization that the Soup deep dive ("how layer
+ * streaming works") measures as the largest streaming-specific cost.
+ *   codes    device, n_elems/2 bytes; byte j holds element 2j (high nibble) and 2j+1 (low)
+ *   absmax   device, n_elems/blocksize fp32
+ *   n_elems  number of elements, a multiple of blocksize (>= 0; 0 is a no-op)
+ *   blocksize must be 64
+ *   out_bf16 device, n_elems bf16
+ * Bitwise equal to the definition for every code and every finite absmax.
+ * Errors: EINVAL (null), ESHAPE (blocksize, n_elems % blocksize), EALIGN (16-byte), EHIP.
+ */
+int nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n_elems, int32_t blocksize,
+                uint16_t* out_bf16, hipStream_t stream);
+
+/*
+ * Quantize fp32 weights to NF4 (set-up, off the hot path: shards are built once).
+ * Blocks of `blocksize` consecutive elements; absmax = max|w| (fp32); code = nearest
+ * level to w/absmax (fp32 division and comparison, ties to the lower index); an
+ * all-zero block gets code 7.  Packing as in nf4_dequant.
+ *   w device fp32 [n_elems]; codes device [n_elems/2]; absmax device [n_elems/blocksize].
+ * Errors: as nf4_dequant.
+ */
+int nf4_quantize(const float* w, int64_t n_elems, int32_t blocksize, uint8_t* codes, float* absmax,
+                 hipStream_t stream);
+
+/* A frozen weight of one projection, as it sits in a device layer buffer. */
+typedef struct lnf4_weight {
+  int32_t fmt;          /* LNF4_FMT_NF4 or LNF4_FMT_BF16 */
+  const void* data;     /* device: NF4 codes uint8 [out][in/2] or bf16 [out][in] */
+  const float* absmax;  /* device: fp32 [out*in/64] for NF4; ignored for BF16 */
+  int64_t out_f, in_f;  /* out >= 1; in a positive multiple of 64 */
+  int32_t blocksize;    /* 64 for NF4 (ignored for BF16) */
+} lnf4_weight;
+
+/*
+ * LoRA linear forward (one projection):
+ *   u = x A^T (fp32, [T, r]);   y = bf16( x W'^T + scale * u B^T )
+ * with W' the decoded weight (NF4 decode fused into the GEMM: W' never exists in
+ * memory) and fp32 accumulation.  The forward is also the backward's recompute.
+ *   W      the frozen weight
+ *   x      device bf16 [T, in]
+ *   T      tokens, >= 0 (0 is a no-op)
+ *   A, B   device bf16 [r, in] and [out, r]; both NULL or r == 0 disables the adapter
+ *          (then y is the frozen base linear exactly: the adapter-off reference pass)
+ *   scale  alpha / r, computed by the caller
+ *   y      device bf16 [T, out]
+ *   u      device fp32 [T, r] written with x A^T; required when the adapter is on
+ * Errors: EINVAL, ESHAPE (in % 64, blocksize), EALIGN, EHIP.
+ */
+int lora_linear_fwd(const lnf4_weight* W, const uint16_t* x, int64_t T, const uint16_t* A,
+                    const uint16_t* B, int32_t r, float scale, uint16_t* y, float* u, hipStream_t stream);
+
+/* Bytes of device workspace lora_linear_bwd needs for these sizes (0 if r == 0 and
+ * the shapes need no split reduction).  Host-only. */
+size_t lora_linear_bwd_workspace(int64_t T, int64_t out_f, int64_t in_f, int32_t r);
+
+/*
+ * LoRA linear backward (one projection), W gets no gradient:
+ *   v  = dy B                                     (fp32 [T, r], in workspace)
+ *   dx = bf16( dy W' + scale * v A )              (+ old dx if accumulate)
+ *   dA = scale * v^T x                            (fp32 [r, in], += old if accumulate)
+ *   dB = scale * dy^T u                           (fp32 [out, r], += old if accumulate)
+ * u is taken from u_saved (the forward's u) or recomputed as x A^T when NULL.
+ *   dx, dA, dB   device outputs; each may be NULL to skip it (dA, dB ignored when the
+ *                adapter is off)
+ *   workspace    device, at least lora_linear_bwd_workspace(T, out, in, r) bytes
+ * Gradient reductions over T use a fixed split and a fixed-order second pass.
+ * Errors: EINVAL, ESHAPE (also workspace too small), EALIGN, EHIP.
+ */
+int lora_linear_bwd(const lnf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t T,
+                    const uint16_t* A, const uint16_t* B, int32_t r, float scale, const float* u_saved,
+                    uint16_t* dx, float* dA, float* dB, int32_t accumulate, void* workspace,
+                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Projections that read the same input (q, k, v read the attention input; gate and
+ * up read the MLP input) run as one grouped launch.  In the forward each projection
+ * writes its own y; in backward the group's input gradient is the sum over its
+ * projections: dx = sum_p ( dy_p W'_p + scale_p v_p A_p ).
+ */
+typedef struct lnf4_proj {
+  lnf4_weight W;
+  const uint16_t* A;   /* device bf16 [r, in] or NULL */
+  const uint16_t* B;   /* device bf16 [out, r] or NULL */
+  int32_t r;           /* 0: adapter off */
+  float scale;
+  uint16_t* y;         /* fwd: device bf16 [T, out] */
+  float* u;            /* fwd: device fp32 [T, r] (written); bwd: saved u or NULL (recompute) */
+  const uint16_t* dy;  /* bwd: device bf16 [T, out] */
+  float* dA;           /* bwd: device fp32 [r, in] or NULL */
+  float* dB;           /* bwd: device fp32 [out, r] or NULL */
+} lnf4_proj;
+
+/* Grouped forward: n (1..8) projections with the same in_f share x. */
+int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
+                   hipStream_t stream);
+
+/* Workspace bytes for lora_group_bwd.  Host-only. */
+size_t lora_group_bwd_workspace(const lnf4_proj* projs, int32_t n, int64_t T);
+
+/* Grouped backward: dx [T, in] = sum over the group (NULL to skip), per-projection dA/dB. */
+int lora_group_bwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, uint16_t* dx,
+                   int32_t accumulate, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Shard layout of one decoder layer: projections in the caller's order (q, k, v, o,
+ * gate, up, down), each as [data][absmax] sections, every section starting on a
+ * 256-byte boundary.  offsets[2p] = data offset, offsets[2p+1] = absmax offset (-1 for
+ * BF16).  total_bytes = shard size.  Host-only.
+ * Errors: EINVAL, ESHAPE (in % 64).
+ */
+int lnf4_shard_layout(int32_t n_proj, const int64_t* out_f, const int64_t* in_f, int32_t fmt,
+                      int64_t* offsets, int64_t* total_bytes);
+
+/* ------------------------------------------------------------------ layer stream */
+typedef struct lnf4_stream lnf4_stream;
+
+#define LNF4_EV_COPY 0      /* a layer copy was issued */
+#define LNF4_EV_STEP 1      /* a call made compute wait for its layer */
+#define LNF4_EV_SLOT_COPY 2 /* a head-slot copy was issued */
+#define LNF4_EV_SLOT_WAIT 3 /* compute was made to wait for the head slot */
+
+typedef struct lnf4_stream_event {
+  int32_t kind;   /* LNF4_EV_* */
+  int32_t call;   /* stream_layer_step call index at which it happened */
+  int32_t j;      /* COPY: schedule position (resident: shard); STEP: copy waited on; SLOT: slot load index */
+  int32_t layer;  /* shard index */
+  int32_t buffer; /* device buffer index (-1 for the slot) */
+  int32_t wait;   /* COPY: call whose release it waited for (-1: none); STEP: copy index;
+                     SLOT_COPY: previous slot load index (-1: none) */
+} lnf4_stream_event;
+
+/*
+ * Create a layer stream over one pass of `schedule` (shard indices, e.g. layers
+ * 0..L-1 then L-1..0 for an SFT step: forward, then recompute + backward).
+ *   host_shards  n_shards page-locked host pointers (one contiguous blob per layer)
+ *   shard_bytes  size of each shard, each <= buf_bytes
+ *   dev_bufs     n_bufs device buffers of buf_bytes each, 256-byte aligned
+ *   n_bufs       ring mode: 2..8 (2 = double buffering).  Resident mode: == n_shards.
+ *   schedule     sched_len shard indices, copied by the library
+ *   resident     0: ring.  1: every shard gets its own buffer and is copied once at the
+ *                first call (the "H2D removed" and bit-exactness reference run)
+ *   copy_stream  the side stream that carries every host-to-device copy
+ *   slot_buf     optional device buffer for the shared embed / lm_head slot (or NULL)
+ *   slot_bytes   its size
+ * Ring rule: call k uses buffer k mod n_bufs; at call k every copy j <= k+n_bufs-1 not
+ * yet issued is issued into buffer j mod n_bufs after the release of call j-n_bufs;
+ * call k's compute waits for copy k.  Errors: EINVAL, ESHAPE, EALIGN, EHIP.
+ */
+int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards,
+                  void* const* dev_bufs, size_t buf_bytes, int32_t n_bufs, const int32_t* schedule,
+                  int32_t sched_len, int32_t resident, hipStream_t copy_stream, void* slot_buf,
+                  size_t slot_bytes, lnf4_stream** out);
+
+/*
+ * Call k of the pass (k = 0, 1, ... in order).  Records the release of call k-1's
+ * buffer on `compute`, issues the copies the ring rule allows, makes `compute` wait
+ * for layer k's copy and returns its device address in *dev_ptr_out.  Every kernel
+ * that reads layer k must be enqueued on `compute` before call k+1.
+ * Errors: ESTATE (k out of order, pass finished, destroyed), EINVAL, EHIP.
+ */
+int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** dev_ptr_out);
+
+/*
+ * Head slot: copy shard `shard` (embed_tokens or the untied lm_head, which share one
+ * device slot: Soup deep dive, "how layer streaming works") into the slot on the copy
+ * stream, after the compute work enqueued so far on `compute` (the previous user of
+ * the slot) has finished.  Does not make compute wait; stream_slot_wait does.
+ */
+int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute);
+int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out);
+
+/* Rewind a finished (or unfinished) pass so the same schedule runs again (next step).
+ * The first copies of the new pass wait for the release of the old pass's buffers. */
+int stream_reset(lnf4_stream* st, hipStream_t compute);
+
+/* Copy up to cap events of the current pass to ev; *n = number copied. */
+int stream_log(const lnf4_stream* st, lnf4_stream_event* ev, int32_t cap, int32_t* n);
+
+/* Bytes copied host-to-device by this context since creation (layers + slot). */
+int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes);
+
+/* Release the context and its events.  NULL is accepted; safe to call once per object. */
+int stream_destroy(lnf4_stream* st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LNF4_H */

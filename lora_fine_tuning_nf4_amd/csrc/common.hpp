@@ -1,0 +1,63 @@
+// Device-side building blocks shared by the lnf4 kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf4_table.hpp"
+
+namespace lnf4 {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// native 4 x 32-bit vector: register arrays of these are split into registers by SROA
+// (arrays of the HIP uint4 wrapper struct can stay in private memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 -> packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+// `lo` lands in bits 0..15 (the lower address), `hi` in bits 16..31.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Decode one dword of NF4 codes (8 elements, element 2b in the high nibble of byte b)
+// with one block scale: out dword q = bf16(T[c_2q]*a) | bf16(T[c_2q+1]*a) << 16.
+// `lut` is the code table in LDS (16 fp32; every lane reads one of 16 words, so the
+// reads broadcast without bank conflicts).  One fp32 product per element, then RNE.
+__device__ __forceinline__ void decode8(uint32_t w, float a, const float* lut, uint32_t out[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t hi = (w >> (8 * b + 4)) & 15u;
+    const uint32_t lo = (w >> (8 * b)) & 15u;
+    const float f0 = lut[hi] * a;
+    const float f1 = lut[lo] * a;
+    out[b] = pack_bf16x2(f0, f1);
+  }
+}
+
+// Same decode, returning fp32 products for element e = 0..7 of the dword.
+__device__ __forceinline__ void decode8_f32(uint32_t w, float a, const float* lut, float out[8]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    out[2 * b] = lut[(w >> (8 * b + 4)) & 15u] * a;
+    out[2 * b + 1] = lut[(w >> (8 * b)) & 15u] * a;
+  }
+}
+
+// Logical block index -> tile index so that the blocks the hardware places on one XCD
+// (block b runs on XCD b % 8) get one contiguous range of tiles: tiles that share an
+// operand then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int per = nb >> 3, rem = nb & 7;
+  const int x = b & 7, i = b >> 3;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+}  // namespace lnf4

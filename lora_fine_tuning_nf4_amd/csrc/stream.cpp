@@ -1,0 +1,282 @@
+// Layer stream: page-locked host shards -> a ring of 2..8 preallocated device layer
+// buffers, copied on a side stream while the current layer computes (the Soup deep
+// dive, "Core feature: how layer streaming works"; the 4 GB-laptop Soup article,
+// "Layer streaming: technical implementation and memory efficiency").
+//
+// Synchronisation uses HIP events only, never host waits:
+//   copy_done[b]  recorded on the copy stream after the copy into buffer b
+//   release[b]    recorded on the compute stream once every kernel of the call that
+//                 used buffer b has been enqueued (at the next call)
+// Call k: record release of call k-1; issue every copy j <= k + nbuf - 1 not yet issued
+// (copy j waits for release[j mod nbuf] of call j - nbuf); compute waits copy_done[k mod
+// nbuf].  Copies are hipMemcpyAsync from pinned memory, carried by the SDMA engines, so
+// they take no compute units.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "abi_internal.hpp"
+#include "lnf4.h"
+
+using namespace lnf4;
+
+struct lnf4_stream {
+  std::vector<const void*> host;
+  std::vector<size_t> bytes;
+  std::vector<void*> bufs;
+  size_t buf_bytes = 0;
+  int nbuf = 0;
+  std::vector<int32_t> sched;
+  bool resident = false;
+  hipStream_t copy = nullptr;
+  void* slot = nullptr;
+  size_t slot_bytes = 0;
+  std::vector<hipEvent_t> copy_done, release;
+  std::vector<char> release_recorded;
+  hipEvent_t slot_release = nullptr, slot_done = nullptr;
+  bool slot_loaded = false;
+  int next_call = 0;
+  int issued = 0;
+  int pass = 0;
+  bool resident_copied = false;
+  int slot_loads = 0;
+  int64_t bytes_copied = 0;
+  std::vector<lnf4_stream_event> log;
+  bool alive = true;
+};
+
+static void log_ev(lnf4_stream* st, int kind, int call, int j, int layer, int buffer, int wait) {
+  lnf4_stream_event e;
+  e.kind = kind;
+  e.call = call;
+  e.j = j;
+  e.layer = layer;
+  e.buffer = buffer;
+  e.wait = wait;
+  st->log.push_back(e);
+}
+
+static void destroy_events(lnf4_stream* st) {
+  for (hipEvent_t e : st->copy_done)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : st->release)
+    if (e) (void)hipEventDestroy(e);
+  if (st->slot_release) (void)hipEventDestroy(st->slot_release);
+  if (st->slot_done) (void)hipEventDestroy(st->slot_done);
+  st->copy_done.clear();
+  st->release.clear();
+  st->slot_release = st->slot_done = nullptr;
+}
+
+static int copy_into(lnf4_stream* st, int buf, int shard) {
+  hipError_t e = hipMemcpyAsync(st->bufs[buf], st->host[shard], st->bytes[shard], hipMemcpyHostToDevice, st->copy);
+  if (e != hipSuccess) return hip_fail(e, "stream: hipMemcpyAsync (host shard -> layer buffer)");
+  e = hipEventRecord(st->copy_done[buf], st->copy);
+  if (e != hipSuccess) return hip_fail(e, "stream: hipEventRecord(copy_done)");
+  st->bytes_copied += (int64_t)st->bytes[shard];
+  return LNF4_OK;
+}
+
+extern "C" {
+
+int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards, void* const* dev_bufs,
+                  size_t buf_bytes, int32_t n_bufs, const int32_t* schedule, int32_t sched_len, int32_t resident,
+                  hipStream_t copy_stream, void* slot_buf, size_t slot_bytes, lnf4_stream** out) {
+  const char* who = "stream_create";
+  if (!out) return fail(LNF4_EINVAL, "%s: out is NULL", who);
+  *out = nullptr;
+  if (!host_shards || !shard_bytes || !dev_bufs || !schedule) return fail(LNF4_EINVAL, "%s: NULL array", who);
+  if (n_shards < 1 || n_shards > (1 << 20)) return fail(LNF4_EINVAL, "%s: n_shards=%d out of range", who, (int)n_shards);
+  if (resident) {
+    if (n_bufs != n_shards) return fail(LNF4_EINVAL, "%s: resident mode needs n_bufs == n_shards (%d != %d)", who, (int)n_bufs, (int)n_shards);
+  } else if (n_bufs < 2 || n_bufs > 8) {
+    return fail(LNF4_EINVAL, "%s: n_bufs=%d outside 2..8", who, (int)n_bufs);
+  }
+  if (sched_len < 1 || sched_len > (1 << 24)) return fail(LNF4_EINVAL, "%s: sched_len=%d out of range", who, (int)sched_len);
+  if (buf_bytes == 0) return fail(LNF4_ESHAPE, "%s: buf_bytes is 0", who);
+  for (int s = 0; s < n_shards; ++s) {
+    if (!host_shards[s]) return fail(LNF4_EINVAL, "%s: host shard %d is NULL", who, s);
+    if (shard_bytes[s] == 0) return fail(LNF4_ESHAPE, "%s: shard %d is empty", who, s);
+    if (shard_bytes[s] > buf_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds buf_bytes %zu", who, s, shard_bytes[s], buf_bytes);
+  }
+  for (int b = 0; b < n_bufs; ++b) {
+    if (!dev_bufs[b]) return fail(LNF4_EINVAL, "%s: device buffer %d is NULL", who, b);
+    if ((uintptr_t)dev_bufs[b] & 255) return fail(LNF4_EALIGN, "%s: device buffer %d not 256-byte aligned", who, b);
+  }
+  for (int k = 0; k < sched_len; ++k)
+    if (schedule[k] < 0 || schedule[k] >= n_shards)
+      return fail(LNF4_EINVAL, "%s: schedule[%d]=%d outside 0..%d", who, k, (int)schedule[k], (int)n_shards - 1);
+  if (slot_buf) {
+    if (slot_bytes == 0) return fail(LNF4_ESHAPE, "%s: slot_bytes is 0", who);
+    if ((uintptr_t)slot_buf & 255) return fail(LNF4_EALIGN, "%s: slot buffer not 256-byte aligned", who);
+  }
+  // host memory must be page-locked, so that copies are true asynchronous DMA
+  for (int s = 0; s < n_shards; ++s) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t e = hipPointerGetAttributes(&attr, host_shards[s]);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(LNF4_EINVAL, "%s: host shard %d is not page-locked host memory", who, s);
+    }
+  }
+  lnf4_stream* st = new (std::nothrow) lnf4_stream();
+  if (!st) return fail(LNF4_EINVAL, "%s: out of host memory", who);
+  st->host.assign(host_shards, host_shards + n_shards);
+  st->bytes.assign(shard_bytes, shard_bytes + n_shards);
+  st->bufs.assign(dev_bufs, dev_bufs + n_bufs);
+  st->buf_bytes = buf_bytes;
+  st->nbuf = n_bufs;
+  st->sched.assign(schedule, schedule + sched_len);
+  st->resident = resident != 0;
+  st->copy = copy_stream;
+  st->slot = slot_buf;
+  st->slot_bytes = slot_bytes;
+  st->copy_done.assign(n_bufs, nullptr);
+  st->release.assign(n_bufs, nullptr);
+  st->release_recorded.assign(n_bufs, 0);
+  for (int b = 0; b < n_bufs; ++b) {
+    hipError_t e = hipEventCreateWithFlags(&st->copy_done[b], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->release[b], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      destroy_events(st);
+      delete st;
+      return hip_fail(e, "stream_create: hipEventCreate");
+    }
+  }
+  if (slot_buf) {
+    hipError_t e = hipEventCreateWithFlags(&st->slot_release, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->slot_done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      destroy_events(st);
+      delete st;
+      return hip_fail(e, "stream_create: hipEventCreate(slot)");
+    }
+  }
+  *out = st;
+  return LNF4_OK;
+}
+
+int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** dev_ptr_out) {
+  const char* who = "stream_layer_step";
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!dev_ptr_out) return fail(LNF4_EINVAL, "%s: dev_ptr_out is NULL", who);
+  const int n = (int)st->sched.size();
+  if (k != st->next_call) return fail(LNF4_ESTATE, "%s: call %d out of order (expected %d)", who, (int)k, st->next_call);
+  if (k >= n) return fail(LNF4_ESTATE, "%s: pass finished (%d calls); call stream_reset", who, n);
+  hipError_t e;
+  int rc;
+  if (st->resident) {
+    if (!st->resident_copied) {
+      for (int s = 0; s < (int)st->host.size(); ++s) {
+        if ((rc = copy_into(st, s, s))) return rc;
+        log_ev(st, LNF4_EV_COPY, k, s, s, s, -1);
+      }
+      st->resident_copied = true;
+    }
+    const int s = st->sched[k];
+    if ((e = hipStreamWaitEvent(compute, st->copy_done[s], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(copy_done)");
+    log_ev(st, LNF4_EV_STEP, k, s, s, s, s);
+    st->next_call = k + 1;
+    *dev_ptr_out = st->bufs[s];
+    return LNF4_OK;
+  }
+  const int nb = st->nbuf;
+  if (k > 0) {
+    const int b = (k - 1) % nb;
+    if ((e = hipEventRecord(st->release[b], compute)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(release)");
+    st->release_recorded[b] = 1;
+  }
+  while (st->issued < n && st->issued <= k + nb - 1) {
+    const int j = st->issued, b = j % nb, layer = st->sched[j];
+    // copy j reuses buffer b after its previous user: call j - nb of this pass, or the
+    // last user of b in the previous pass
+    if (st->release_recorded[b])
+      if ((e = hipStreamWaitEvent(st->copy, st->release[b], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(release)");
+    if ((rc = copy_into(st, b, layer))) return rc;
+    log_ev(st, LNF4_EV_COPY, k, j, layer, b, j >= nb ? j - nb : -1);
+    st->issued = j + 1;
+  }
+  const int b = k % nb;
+  if ((e = hipStreamWaitEvent(compute, st->copy_done[b], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(copy_done)");
+  log_ev(st, LNF4_EV_STEP, k, k, st->sched[k], b, k);
+  st->next_call = k + 1;
+  *dev_ptr_out = st->bufs[b];
+  return LNF4_OK;
+}
+
+int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute) {
+  const char* who = "stream_slot_load";
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
+  if (shard < 0 || shard >= (int)st->host.size()) return fail(LNF4_EINVAL, "%s: shard %d out of range", who, (int)shard);
+  if (st->bytes[shard] > st->slot_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds the slot (%zu)", who, (int)shard, st->bytes[shard], st->slot_bytes);
+  hipError_t e;
+  if ((e = hipEventRecord(st->slot_release, compute)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(slot_release)");
+  if ((e = hipStreamWaitEvent(st->copy, st->slot_release, 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(slot_release)");
+  if ((e = hipMemcpyAsync(st->slot, st->host[shard], st->bytes[shard], hipMemcpyHostToDevice, st->copy)) != hipSuccess)
+    return hip_fail(e, "stream: hipMemcpyAsync (slot)");
+  if ((e = hipEventRecord(st->slot_done, st->copy)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(slot_done)");
+  st->bytes_copied += (int64_t)st->bytes[shard];
+  log_ev(st, LNF4_EV_SLOT_COPY, st->next_call, st->slot_loads, shard, -1, st->slot_loads - 1);
+  st->slot_loads += 1;
+  st->slot_loaded = true;
+  return LNF4_OK;
+}
+
+int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out) {
+  const char* who = "stream_slot_wait";
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
+  if (!st->slot_loaded) return fail(LNF4_ESTATE, "%s: no slot load issued", who);
+  hipError_t e = hipStreamWaitEvent(compute, st->slot_done, 0);
+  if (e != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(slot_done)");
+  log_ev(st, LNF4_EV_SLOT_WAIT, st->next_call, st->slot_loads - 1, -1, -1, st->slot_loads - 1);
+  if (slot_ptr_out) *slot_ptr_out = st->slot;
+  return LNF4_OK;
+}
+
+int stream_reset(lnf4_stream* st, hipStream_t compute) {
+  const char* who = "stream_reset";
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!st->resident && st->next_call > 0) {
+    // release the last call's buffer; earlier buffers were released by later calls
+    const int b = (st->next_call - 1) % st->nbuf;
+    hipError_t e = hipEventRecord(st->release[b], compute);
+    if (e != hipSuccess) return hip_fail(e, "stream: hipEventRecord(release at reset)");
+    st->release_recorded[b] = 1;
+  }
+  st->next_call = 0;
+  st->issued = 0;
+  st->pass += 1;
+  st->log.clear();
+  return LNF4_OK;
+}
+
+int stream_log(const lnf4_stream* st, lnf4_stream_event* ev, int32_t cap, int32_t* n) {
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "stream_log: stream context is NULL or destroyed");
+  if (!n) return fail(LNF4_EINVAL, "stream_log: n is NULL");
+  if (cap < 0 || (cap > 0 && !ev)) return fail(LNF4_EINVAL, "stream_log: bad buffer");
+  const int m = (int)st->log.size() < cap ? (int)st->log.size() : cap;
+  for (int i = 0; i < m; ++i) ev[i] = st->log[i];
+  *n = m;
+  return LNF4_OK;
+}
+
+int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes) {
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "stream_bytes_copied: stream context is NULL or destroyed");
+  if (!bytes) return fail(LNF4_EINVAL, "stream_bytes_copied: bytes is NULL");
+  *bytes = st->bytes_copied;
+  return LNF4_OK;
+}
+
+int stream_destroy(lnf4_stream* st) {
+  if (!st) return LNF4_OK;
+  destroy_events(st);
+  delete st;
+  return LNF4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the header
+declares, its NF4 table equals the oracle's bit for bit, and argument validation rejects
+bad calls with the documented codes before touching the GPU."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from lora_fine_tuning_nf4_amd import lnf4
+from oracle import nf4 as onf4
+
+
+@pytest.fixture(scope="module")
+def L():
+    return lnf4.lib()
+
+
+def test_exports_every_header_symbol(L):
+    names = lnf4.header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_table_matches_oracle_bitwise(L):
+    lib_tab = np.array(lnf4.lnf4_nf4_table(), np.float32)
+    assert np.array_equal(lib_tab.view(np.uint32), onf4.nf4_table().view(np.uint32))
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-NULL address that is never dereferenced
+
+
+def test_dequant_validation(L):
+    assert L.nf4_dequant(FAKE, FAKE, 64, 32, FAKE, None) == lnf4.LNF4_ESHAPE
+    assert L.nf4_dequant(FAKE, FAKE, 63, 64, FAKE, None) == lnf4.LNF4_ESHAPE
+    assert L.nf4_dequant(None, FAKE, 64, 64, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.nf4_dequant(FAKE + 1, FAKE, 64, 64, FAKE, None) == lnf4.LNF4_EALIGN
+    assert L.nf4_dequant(None, None, 0, 64, None, None) == lnf4.LNF4_OK  # empty is a no-op
+    assert "blocksize" in lnf4.lnf4_last_error() or lnf4.lnf4_last_error() != ""
+
+
+def _weight(fmt=0, data=FAKE, absmax=FAKE, out_f=128, in_f=128, bs=64):
+    return lnf4.lnf4_weight(fmt, data, absmax, out_f, in_f, bs)
+
+
+def test_fwd_validation(L):
+    fwd = L.lora_linear_fwd
+    W = _weight()
+    assert fwd(None, FAKE, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_EINVAL
+    assert fwd(ctypes.byref(_weight(in_f=100)), FAKE, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_ESHAPE
+    assert fwd(ctypes.byref(_weight(bs=32)), FAKE, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_ESHAPE
+    assert fwd(ctypes.byref(_weight(fmt=7)), FAKE, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_EINVAL
+    assert fwd(ctypes.byref(_weight(absmax=None)), FAKE, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_EINVAL
+    assert fwd(ctypes.byref(_weight(data=FAKE + 2)), FAKE, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_EALIGN
+    assert fwd(ctypes.byref(W), FAKE, 4, FAKE, FAKE, 65, 1.0, FAKE, FAKE, None) == lnf4.LNF4_EINVAL   # r > 64
+    assert fwd(ctypes.byref(W), FAKE, 4, FAKE, None, 8, 1.0, FAKE, FAKE, None) == lnf4.LNF4_EINVAL   # one of A, B
+    assert fwd(ctypes.byref(W), FAKE, 4, FAKE, FAKE, 8, 1.0, FAKE, None, None) == lnf4.LNF4_EINVAL   # u missing
+    assert fwd(ctypes.byref(W), None, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_EINVAL   # x missing
+    assert fwd(ctypes.byref(W), FAKE + 8, 4, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_EALIGN
+    assert fwd(ctypes.byref(W), FAKE, -1, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_EINVAL
+    # T = 0 is a no-op that never touches the device
+    assert fwd(ctypes.byref(W), None, 0, None, None, 0, 0.0, None, None, None) == lnf4.LNF4_OK
+
+
+def test_bwd_validation_and_workspace(L):
+    W = _weight(out_f=100)
+    bwd = L.lora_linear_bwd
+    # out_f must be a multiple of 8 in backward
+    assert bwd(ctypes.byref(W), FAKE, FAKE, 4, None, None, 0, 0.0, None, FAKE, None, None, 0, None, 0, None) \
+        == lnf4.LNF4_ESHAPE
+    W = _weight()
+    ws = lnf4.lora_linear_bwd_workspace(256, 128, 128, 8)
+    assert ws > 0 and ws % 256 == 0
+    assert lnf4.lora_linear_bwd_workspace(256, 128, 128, 0) == 0
+    # workspace too small
+    assert bwd(ctypes.byref(W), FAKE, FAKE, 256, FAKE, FAKE, 8, 1.0, None, FAKE, FAKE, FAKE, 0, FAKE, ws - 256,
+               None) == lnf4.LNF4_ESHAPE
+    assert bwd(ctypes.byref(W), FAKE, FAKE, 256, FAKE, FAKE, 8, 1.0, None, FAKE, FAKE, FAKE, 0, None, ws,
+               None) == lnf4.LNF4_EINVAL
+    assert bwd(ctypes.byref(W), FAKE, None, 256, None, None, 0, 0.0, None, FAKE, None, None, 0, None, 0,
+               None) == lnf4.LNF4_EINVAL  # dy missing
+
+
+def test_group_validation(L):
+    p = lnf4.make_proj(_weight(), y=FAKE)
+    q = lnf4.make_proj(_weight(in_f=256), y=FAKE)
+    arr = (lnf4.lnf4_proj * 2)(p, q)
+    assert L.lora_group_fwd(arr, 2, FAKE, 4, 1, None) == lnf4.LNF4_ESHAPE   # different in_f
+    assert L.lora_group_fwd(arr, 9, FAKE, 4, 1, None) == lnf4.LNF4_EINVAL
+    assert L.lora_group_fwd(arr, 0, FAKE, 4, 1, None) == lnf4.LNF4_EINVAL
+
+
+def test_shard_layout():
+    outs = [896, 128, 128, 896, 4864, 4864, 896]
+    ins = [896, 896, 896, 896, 896, 896, 4864]
+    offs, total = lnf4.lnf4_shard_layout(outs, ins, lnf4.FMT_NF4)
+    assert all(o % 256 == 0 for o in offs)
+    P = sum(o * i for o, i in zip(outs, ins))
+    assert P == 14_909_440
+    # codes (P/2) + absmax (P/64 * 4), each section padded to 256 bytes
+    assert P // 2 + P // 16 <= total <= P // 2 + P // 16 + 256 * 14
+    for p in range(7):
+        n = outs[p] * ins[p]
+        assert offs[2 * p + 1] - offs[2 * p] >= n // 2
+    offs, total = lnf4.lnf4_shard_layout(outs, ins, lnf4.FMT_BF16)
+    assert offs[1] == -1 and total >= 2 * P
+    with pytest.raises(lnf4.LNF4Error):
+        lnf4.lnf4_shard_layout([16], [100], lnf4.FMT_NF4)
+
+
+def test_stream_validation(L):
+    out = ctypes.c_void_p()
+    hs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    sb = (ctypes.c_size_t * 2)(1024, 1024)
+    db = (ctypes.c_void_p * 9)(*([FAKE] * 9))
+    sc = (ctypes.c_int32 * 4)(0, 1, 1, 0)
+    args = lambda nb, sched=sc, sl=4, bb=4096, res=0: L.stream_create(hs, sb, 2, db, bb, nb, sched, sl, res, None,
+                                                                      None, 0, ctypes.byref(out))
+    assert args(9) == lnf4.LNF4_EINVAL           # more than 8 buffers
+    assert args(1) == lnf4.LNF4_EINVAL           # fewer than 2
+    assert args(2, bb=512) == lnf4.LNF4_ESHAPE   # shard larger than a buffer
+    bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
+    assert args(2, sched=bad) == lnf4.LNF4_EINVAL  # schedule names a missing shard
+    assert args(3, res=1) == lnf4.LNF4_EINVAL    # resident needs one buffer per shard
+    db2 = (ctypes.c_void_p * 2)(FAKE + 16, FAKE)
+    assert L.stream_create(hs, sb, 2, db2, 4096, 2, sc, 4, 0, None, None, 0, ctypes.byref(out)) == lnf4.LNF4_EALIGN
+    p = ctypes.c_void_p()
+    assert L.stream_layer_step(None, 0, None, ctypes.byref(p)) == lnf4.LNF4_ESTATE
+    assert L.stream_destroy(None) == lnf4.LNF4_OK
