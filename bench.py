@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Train tokens/s of the layer-streamed NF4 + LoRA stack on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the embed slot copy, the
+forward of every layer (fused NF4 decode + MFMA GEMMs + rank-r LoRA terms, streamed
+from pinned host shards through 2 device layer buffers), the lm_head slot copy, and the
+backward of every layer in reverse (second read of the layer, forward recompute, input
+gradients, adapter gradients).  Default workload: the Llama-3.1-8B-shaped stack (32
+layers of q, k, v, o, gate, up, down NF4 projections, LoRA r=8 alpha=32 on q and v,
+batch 1 x seq 2048), synthetic seeded weights and activations already resident in device
+memory / pinned host memory when the timed region starts.
+
+Prints one JSON line.  Everything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(wl, group, kind):
+    """Algorithmic flops of one grouped GEMM launch (2 M N K)."""
+    T = wl.tokens
+    outs = [wl.shapes[p][0] for p in group]
+    in_f = wl.shapes[group[0]][1]
+    return 2.0 * T * sum(outs) * in_f
+
+
+def cpu_baseline(wl, seed: int, layers: int):
+    """The oracle, as it stands, on one layer of the workload (timed on the host cores)."""
+    import numpy as np
+    import synthgen
+    from oracle import layer as olayer
+    from oracle import nf4 as onf4
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    T = wl.tokens
+    codes, absmax = {}, {}
+    for p in synthgen.PROJ_ORDER:
+        o, i = wl.shapes[p]
+        codes[p], absmax[p] = onf4.quantize(synthgen.weight_f32(o, i, seed, "cpu", p))
+    xs = {gi: onf4.bf16_bits_to_f64(synthgen.act_bits(T, wl.shapes[g[0]][1], seed, "cpu-x", gi))
+          for gi, g in enumerate(synthgen.GROUPS)}
+    dys = {p: onf4.bf16_bits_to_f64(synthgen.act_bits(T, wl.shapes[p][0], seed, "cpu-dy", p))
+           for p in synthgen.PROJ_ORDER}
+    ad = {}
+    for p in wl.adapted:
+        o, i = wl.shapes[p]
+        ad[p] = (onf4.bf16_bits_to_f64(synthgen.adapter_a_bits(wl.rank, i, seed, "cpu", p)),
+                 onf4.bf16_bits_to_f64(synthgen.adapter_b_bits(o, wl.rank, seed, "cpu", p)), wl.scale)
+    t0 = time.perf_counter()
+    Wd = {p: onf4.decode_f64(codes[p], absmax[p]) for p in synthgen.PROJ_ORDER}
+    t1 = time.perf_counter()
+    olayer.layer_step(Wd, ad, xs, dys, dpo="ref" in wl.passes)
+    t2 = time.perf_counter()
+    t_layer = 2.0 * (t1 - t0) + (t2 - t1)      # two reads (decodes) per layer per step
+    return {
+        "value": T / (layers * t_layer),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one {wl.name} layer at T={T}: NF4 decode of the 7 projections ({t1 - t0:.2f} s, counted twice: "
+                   f"one decode per read) + oracle layer step fwd/recompute/bwd ({t2 - t1:.2f} s); "
+                   f"stack step = {layers} x layer"),
+        "seconds_per_layer_step": t_layer,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--nbuf", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (testing)")
+    ap.add_argument("--no-resident", action="store_true", help="skip the H2D-removed reference run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU only: the streamed NF4+LoRA path runs on a single MI355X "
+               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); multi-GPU data parallelism is not built")
+        log(msg)
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import synthgen
+    from lora_fine_tuning_nf4_amd import lnf4
+    from lora_fine_tuning_nf4_amd.stack import GROUPS, StreamedStack
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    lnf4.lib()  # fail loudly if the HIP library is missing
+    wl = synthgen.WORKLOADS[args.workload]
+    L = args.layers if args.layers is not None else wl.layers
+    torch.cuda.set_device(0)
+
+    t_setup = time.perf_counter()
+    stack = StreamedStack(wl, n_bufs=args.nbuf, seed=args.seed, layers=L)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s: {L} layers x {stack.shard_bytes / 1e6:.1f} MB shards, "
+        f"nbuf={args.nbuf}, T={stack.T}")
+
+    for _ in range(args.warmup):
+        stack.step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K streamed steps, with HIP events around every grouped GEMM call
+    keys = [("fwd", gi, True) for gi in range(len(GROUPS))] + [("bwd", gi, True) for gi in range(len(GROUPS))]
+    if stack.dpo:
+        keys += [("fwd", gi, False) for gi in range(len(GROUPS))]
+    stack.timers = {k: ([], []) for k in keys}
+    b0 = stack.bytes_copied()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        stack.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    b1 = stack.bytes_copied()
+    timers = stack.timers
+    stack.timers = None
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    tokens = stack.T
+    value = tokens / (ms_per_step / 1000.0)
+
+    # per-call GEMM times (ms)
+    call_ms = {}
+    for k, (st, en) in timers.items():
+        ts = [a.elapsed_time(b) for a, b in zip(st, en)]
+        call_ms[k] = ts
+    gemm_time_ms = sum(sum(v) for v in call_ms.values()) / args.steps
+    gemm_flops_step = 0.0
+    for (kind, gi, _on), ts in call_ms.items():
+        gemm_flops_step += gemm_flops(wl, GROUPS[gi], kind) * len(ts) / args.steps
+    # dominant kernel: the gate|up forward GEMM (the largest single launch of the step)
+    dom = call_ms[("fwd", 2, True)]
+    dom_ms = sum(dom) / len(dom)
+    dom_flops = gemm_flops(wl, GROUPS[2], "fwd")
+    achieved = dom_flops / (dom_ms / 1000.0) / 1e12
+    dx_dom = call_ms[("bwd", 2, True)]
+    dx_ms = sum(dx_dom) / len(dx_dom)
+
+    breakdown = {f"{k[0]}_{'+'.join(GROUPS[k[1]])}{'' if k[2] else '_adapters_off'}_ms":
+                 round(sum(v) / len(v), 4) for k, v in call_ms.items() if v}
+
+    result = {
+        "metric": "train tokens/s, 8B-shape NF4+LoRA layer fwd+bwd (streamed stack step)",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights quantized to NF4 on the device, N(0,1) bf16 activations)",
+        "config": {"workload": wl.name, "layers": L, "tokens_per_step": tokens, "global_batch": 1,
+                   "seq_len": tokens, "lora": {"r": wl.rank, "alpha": wl.alpha, "targets": list(wl.adapted)},
+                   "weights": wl.fmt, "stream_buffers": args.nbuf,
+                   "head_slot": bool(stack.slot is not None), "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": "k_fwd<NF4,BM=256> gate|up forward: M=2048 N=28672 K=4096 (fused NF4 decode)",
+            "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4),
+            "launches_timed": len(dom),
+        },
+        "gemm": {
+            "tflops_all_grouped_gemms": round(gemm_flops_step / (gemm_time_ms / 1000.0) / 1e12, 2),
+            "frac_of_peak_all_gemms": round(gemm_flops_step / (gemm_time_ms / 1000.0) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "gemm_ms_per_step": round(gemm_time_ms, 3),
+            "dx_gate_up_ms": round(dx_ms, 4),
+            "dx_gate_up_tflops": round(gemm_flops(wl, GROUPS[2], "bwd") / (dx_ms / 1000) / 1e12, 2),
+            "per_call_avg_ms": breakdown,
+        },
+        "h2d": {
+            "bytes_per_step": (b1 - b0) // args.steps,
+            "avg_GBps_over_step": round((b1 - b0) / args.steps / (ms_per_step / 1000.0) / 1e9, 2),
+        },
+    }
+
+    if not args.no_resident:
+        for _ in range(max(1, args.warmup)):
+            stack.step(resident=True)
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        for _ in range(args.steps):
+            stack.step(resident=True)
+        torch.cuda.synchronize()
+        r_ms = (time.perf_counter() - r0) * 1000.0 / args.steps
+        result["resident_h2d_removed"] = {
+            "ms_per_step": round(r_ms, 3), "tokens_per_s": round(tokens / (r_ms / 1000.0), 2),
+            "exposed_copy_ms_per_step": round(ms_per_step - r_ms, 3),
+        }
+
+    # copy-only rate of the link (the same copies, no compute)
+    hb = stack.host[0]
+    db = stack.bufs[0]
+    cs = stack.copy
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        e0.record(cs)
+        for _ in range(8):
+            db.copy_(hb, non_blocking=True)
+        e1.record(cs)
+    torch.cuda.synchronize()
+    result["h2d"]["copy_only_GBps"] = round(8 * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
+
+    stack.close()
+    del stack
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on one layer ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args.seed, L)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -99,15 +99,24 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
   for (int s = 0; s < n_shards; ++s) {
     if (!host_shards[s]) return fail(LNF4_EINVAL, "%s: host shard %d is NULL", who, s);
     if (shard_bytes[s] == 0) return fail(LNF4_ESHAPE, "%s: shard %d is empty", who, s);
-    if (shard_bytes[s] > buf_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds buf_bytes %zu", who, s, shard_bytes[s], buf_bytes);
   }
   for (int b = 0; b < n_bufs; ++b) {
     if (!dev_bufs[b]) return fail(LNF4_EINVAL, "%s: device buffer %d is NULL", who, b);
     if ((uintptr_t)dev_bufs[b] & 255) return fail(LNF4_EALIGN, "%s: device buffer %d not 256-byte aligned", who, b);
   }
-  for (int k = 0; k < sched_len; ++k)
+  for (int k = 0; k < sched_len; ++k) {
     if (schedule[k] < 0 || schedule[k] >= n_shards)
       return fail(LNF4_EINVAL, "%s: schedule[%d]=%d outside 0..%d", who, k, (int)schedule[k], (int)n_shards - 1);
+    // a shard that goes through the layer buffers must fit one (slot-only shards are
+    // checked against the slot when they are loaded)
+    if (shard_bytes[schedule[k]] > buf_bytes)
+      return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds buf_bytes %zu", who, (int)schedule[k],
+                  shard_bytes[schedule[k]], buf_bytes);
+  }
+  if (resident)
+    for (int s = 0; s < n_shards; ++s)
+      if (shard_bytes[s] > buf_bytes)
+        return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds buf_bytes %zu", who, s, shard_bytes[s], buf_bytes);
   if (slot_buf) {
     if (slot_bytes == 0) return fail(LNF4_ESHAPE, "%s: slot_bytes is 0", who);
     if ((uintptr_t)slot_buf & 255) return fail(LNF4_EALIGN, "%s: slot buffer not 256-byte aligned", who);
