@@ -1,0 +1,97 @@
+"""Parity at the full Llama-3.1-8B layer shapes, in the launch configuration the benchmark
+times (grouped q|k|v and gate|up calls, T = 2048), on sampled outputs the oracle computes
+one by one: whole rows of y and dx, whole columns of dA, whole rows of dB."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import synthgen  # noqa: E402
+from lora_fine_tuning_nf4_amd import lnf4  # noqa: E402
+from oracle import nf4 as onf4  # noqa: E402
+from helpers import bf16_f64, check_tol, dev_f32, dev_u16, dev_u8, host_f32, host_u16  # noqa: E402
+
+WL = synthgen.WORKLOADS["llama8b"]
+T = WL.tokens
+ROWS = [0, 1, 777, 1500, T - 1]
+
+
+def _group(names, seed=0):
+    in_f = WL.shapes[names[0]][1]
+    x = synthgen.act_bits(T, in_f, seed, "full-x", *names)
+    P = {}
+    for p in names:
+        o, i = WL.shapes[p]
+        codes, absmax = onf4.quantize(synthgen.weight_f32(o, i, seed, "full", p))
+        on = p in WL.adapted
+        P[p] = dict(codes=codes, absmax=absmax, on=on, o=o,
+                    A=synthgen.adapter_a_bits(WL.rank, i, seed, "full", p) if on else None,
+                    B=synthgen.adapter_b_bits(o, WL.rank, seed, "full", p) if on else None,
+                    dy=synthgen.act_bits(T, o, seed, "full-dy", p))
+    return x, P
+
+
+def _dev(names, x, P):
+    dev = {"x": dev_u16(x)}
+    projs = []
+    for p in names:
+        d = P[p]
+        o, i = WL.shapes[p]
+        d["dcodes"], d["dabsmax"] = dev_u8(d["codes"]), dev_f32(d["absmax"])
+        d["y"] = torch.empty((T, o), dtype=torch.int16, device="cuda")
+        d["ddy"] = dev_u16(d["dy"])
+        if d["on"]:
+            d["dA_in"], d["dB_in"] = dev_u16(d["A"]), dev_u16(d["B"])
+            d["u"] = torch.empty((T, WL.rank), dtype=torch.float32, device="cuda")
+            d["dA"] = torch.empty((WL.rank, i), dtype=torch.float32, device="cuda")
+            d["dB"] = torch.empty((o, WL.rank), dtype=torch.float32, device="cuda")
+        W = lnf4.make_weight(lnf4.FMT_NF4, d["dcodes"], d["dabsmax"], o, i, 64)
+        projs.append(lnf4.make_proj(W, A=d.get("dA_in"), B=d.get("dB_in"), r=WL.rank if d["on"] else 0,
+                                    scale=WL.scale if d["on"] else 0.0, y=d["y"], u=d.get("u"), dy=d["ddy"],
+                                    dA=d.get("dA"), dB=d.get("dB")))
+    return dev, projs
+
+
+@pytest.mark.parametrize("names", [("q", "k", "v"), ("gate", "up")], ids=["qkv", "gate_up"])
+def test_full_size_group_sampled(names):
+    x, P = _group(names)
+    dev, projs = _dev(names, x, P)
+    in_f = WL.shapes[names[0]][1]
+    lnf4.lora_group_fwd(projs, dev["x"], T, 1)
+    dx = torch.empty((T, in_f), dtype=torch.int16, device="cuda")
+    ws_bytes = lnf4.lora_group_bwd_workspace(projs, T)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    lnf4.lora_group_bwd(projs, dev["x"], T, dx, 0, ws, ws_bytes)
+    torch.cuda.synchronize()
+
+    xs = bf16_f64(x[ROWS])
+    dx_ref = np.zeros((len(ROWS), in_f))
+    xf = None
+    for p in names:
+        d = P[p]
+        Wd = onf4.decode_f64(d["codes"], d["absmax"])
+        y_ref = xs @ Wd.T
+        dyr = bf16_f64(d["dy"][ROWS])
+        dx_ref += dyr @ Wd
+        if d["on"]:
+            A, B = bf16_f64(d["A"]), bf16_f64(d["B"])
+            y_ref += WL.scale * (xs @ A.T) @ B.T
+            dx_ref += WL.scale * (dyr @ B) @ A
+            # adapter gradients need the whole batch: sampled columns of dA, rows of dB
+            if xf is None:
+                xf = bf16_f64(x)
+            dyf = bf16_f64(d["dy"])
+            v = dyf @ B
+            u = xf @ A.T
+            cols = [0, 5, in_f // 2, in_f - 1]
+            check_tol(host_f32(d["dA"])[:, cols], WL.scale * v.T @ xf[:, cols], f"dA {p}")
+            orow = [0, 3, d["o"] // 2, d["o"] - 1]
+            check_tol(host_f32(d["dB"])[orow], WL.scale * dyf[:, orow].T @ u, f"dB {p}")
+            check_tol(host_f32(d["u"])[ROWS], xs @ A.T, f"u {p}")
+        check_tol(bf16_f64(host_u16(d["y"])[ROWS]), y_ref, f"y {p}")
+        del Wd
+    check_tol(bf16_f64(host_u16(dx)[ROWS]), dx_ref, "dx")

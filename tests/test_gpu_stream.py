@@ -1,0 +1,173 @@
+"""GPU checks of the layer stream and of a streamed stack step.
+
+* the engine's event log equals the oracle's schedule simulator (ring sizes 2..8, SFT and
+  DPO schedules, resident mode) and every step's buffer holds its layer's shard bytes;
+* a streamed pass gives bitwise the same outputs and gradients as a resident pass
+  (the pages hold the streamed-vs-resident logit difference at 0.0);
+* a small streamed stack step matches the oracle layer step for every layer.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import synthgen  # noqa: E402
+from lora_fine_tuning_nf4_amd import lnf4  # noqa: E402
+from lora_fine_tuning_nf4_amd.stack import StreamedStack  # noqa: E402
+from oracle import layer as olayer  # noqa: E402
+from oracle import nf4 as onf4  # noqa: E402
+from oracle import stream_sim as ss  # noqa: E402
+from helpers import bf16_f64, check_tol  # noqa: E402
+
+
+def _pinned_shards(n, nbytes, seed=0):
+    rs = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        h.copy_(torch.from_numpy(rs.integers(0, 256, nbytes, dtype=np.uint8)))
+        out.append(h)
+    return out
+
+
+@pytest.mark.parametrize("nbuf", [2, 3, 8])
+@pytest.mark.parametrize("mode", ["sft", "dpo"])
+def test_stream_log_and_buffers_match_simulator(nbuf, mode):
+    L, nbytes = 5, 4096 + 512
+    shards = _pinned_shards(L, nbytes, seed=nbuf)
+    bufs = [torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sched = ss.sft_schedule(L) if mode == "sft" else ss.dpo_schedule(L)
+    copy = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    st = lnf4.stream_create(shards, [nbytes] * L, bufs, nbytes + 256, sched, 0, copy)
+    try:
+        for step in range(2):  # two passes: the second starts behind the first pass's releases
+            for k in range(len(sched)):
+                p = lnf4.stream_layer_step(st, k, comp)
+                j = [i for i, b in enumerate(bufs) if b.data_ptr() == p]
+                assert j == [k % nbuf]
+                got = bufs[j[0]][:nbytes].cpu()   # reads on the compute stream, after the wait
+                assert torch.equal(got, shards[sched[k]]), (step, k)
+            assert lnf4.stream_log(st) == ss.simulate(sched, nbuf)
+            lnf4.stream_reset(st, comp)
+        with pytest.raises(lnf4.LNF4Error):
+            lnf4.stream_layer_step(st, 1, comp)   # out of order
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st)
+
+
+def test_resident_log_matches_simulator():
+    L, nbytes = 4, 2048
+    shards = _pinned_shards(L, nbytes, seed=7)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    sched = ss.sft_schedule(L)
+    comp = torch.cuda.current_stream()
+    st = lnf4.stream_create(shards, [nbytes] * L, bufs, nbytes, sched, 1, torch.cuda.Stream())
+    try:
+        for k in range(len(sched)):
+            p = lnf4.stream_layer_step(st, k, comp)
+            assert p == bufs[sched[k]].data_ptr()
+        assert lnf4.stream_log(st) == ss.simulate(sched, L, n_shards=L, resident=True)
+        assert lnf4.stream_bytes_copied(st) == L * nbytes
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st)
+
+
+def test_rejects_unpinned_host_memory():
+    h = torch.empty(1024, dtype=torch.uint8)  # pageable
+    b = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lnf4.LNF4Error) as ei:
+        lnf4.stream_create([h, h], [1024, 1024], [b, b], 1024, [0, 1], 0, torch.cuda.Stream())
+    assert ei.value.code == lnf4.LNF4_EINVAL
+
+
+def _small_workload(fmt="nf4", adapted=("q", "v"), rank=8):
+    shapes = synthgen._decoder_shapes(256, 4, 2, 64, 512)  # q 256x256, k/v 128x256, gate/up 512x256, down 256x512
+    return synthgen.Workload(f"small_{fmt}", 200, shapes, rank, 2.0 * rank, adapted, layers=3, fmt=fmt,
+                             vocab=320, hidden=256)
+
+
+def _snapshot(stack):
+    torch.cuda.synchronize()
+    out = {"y": {p: t.view(torch.int16).cpu().numpy().copy() for p, t in stack.y.items()},
+           "dx": [t.view(torch.int16).cpu().numpy().copy() for t in stack.dx], "grads": []}
+    for ls in stack.layers:
+        out["grads"].append({p: (ls.dA[p].cpu().numpy().copy(), ls.dB[p].cpu().numpy().copy()) for p in ls.dA})
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "bf16"])
+def test_streamed_equals_resident_bitwise(fmt):
+    wl = _small_workload(fmt)
+    stack = StreamedStack(wl, n_bufs=2, seed=3)
+    try:
+        stack.step()
+        a = _snapshot(stack)
+        stack.step(resident=True)
+        b = _snapshot(stack)
+        stack.step()
+        c = _snapshot(stack)
+    finally:
+        stack.close()
+    for snap in (b, c):
+        for p in a["y"]:
+            assert np.array_equal(a["y"][p], snap["y"][p]), p
+        for g in range(len(a["dx"])):
+            assert np.array_equal(a["dx"][g], snap["dx"][g]), g
+        for l, gr in enumerate(a["grads"]):
+            for p in gr:
+                assert np.array_equal(gr[p][0], snap["grads"][l][p][0])
+                assert np.array_equal(gr[p][1], snap["grads"][l][p][1])
+
+
+def _host_weights(stack, layer):
+    """Decoded weights of one layer, read back from its pinned host shard with the oracle."""
+    wl = stack.wl
+    blob = stack.host[layer].numpy()
+    W = {}
+    for pi, p in enumerate(synthgen.PROJ_ORDER):
+        o, i = wl.shapes[p]
+        d0, a0 = stack.offsets[2 * pi], stack.offsets[2 * pi + 1]
+        if stack.fmt == lnf4.FMT_NF4:
+            codes = blob[d0:d0 + o * i // 2].reshape(o, i // 2)
+            absmax = blob[a0:a0 + o * i // 16].view(np.float32)
+            W[p] = onf4.decode_f64(codes, absmax)
+        else:
+            W[p] = bf16_f64(blob[d0:d0 + o * i * 2].view(np.uint16).reshape(o, i))
+    return W
+
+
+@pytest.mark.parametrize("dpo", [False, True])
+def test_stack_step_matches_oracle(dpo):
+    wl = _small_workload("nf4", adapted=("q", "k", "v", "o", "gate", "up", "down"), rank=4)
+    stack = StreamedStack(wl, n_bufs=2, seed=5, dpo=dpo)
+    try:
+        stack.step()
+        torch.cuda.synchronize()
+        # the shared output buffers hold the last layer processed: layer 0 (backward ends there)
+        for layer in range(stack.L):
+            ls = stack.layers[layer]
+            W = _host_weights(stack, layer)
+            ad = {p: (bf16_f64(ls.A[p].view(torch.int16).cpu().numpy().view(np.uint16)),
+                      bf16_f64(ls.B[p].view(torch.int16).cpu().numpy().view(np.uint16)), wl.scale) for p in ls.A}
+            xs = {gi: bf16_f64(x.view(torch.int16).cpu().numpy().view(np.uint16)) for gi, x in enumerate(ls.x)}
+            dys = {p: bf16_f64(d.view(torch.int16).cpu().numpy().view(np.uint16)) for p, d in ls.dy.items()}
+            ref = olayer.layer_step(W, ad, xs, dys, dpo=dpo)
+            for p in ls.A:
+                check_tol(ls.dA[p].cpu().numpy(), ref["grads"][p][0], f"L{layer} dA {p}")
+                check_tol(ls.dB[p].cpu().numpy(), ref["grads"][p][1], f"L{layer} dB {p}")
+            if layer == 0:
+                for p, t in stack.y.items():
+                    check_tol(bf16_f64(t.view(torch.int16).cpu().numpy().view(np.uint16)), ref["recompute"][p],
+                              f"y {p}")
+                for gi, t in enumerate(stack.dx):
+                    check_tol(bf16_f64(t.view(torch.int16).cpu().numpy().view(np.uint16)), ref["dx"][gi],
+                              f"dx group {gi}")
+    finally:
+        stack.close()
