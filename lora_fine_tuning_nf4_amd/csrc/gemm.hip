@@ -44,8 +44,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// position of 16-byte chunk c of activation-tile row `row` (8 chunks per 128-byte row)
-__device__ __forceinline__ int act_pos(int row, int c) { return row * BK + ((c ^ (row & 7)) << 3); }
+// Activation tiles are [rows][64] bf16 (128-byte rows of eight 16-byte chunks).  Chunk c
+// of row `row` sits at slot c ^ swz(row): with 64 LDS banks (256 bytes), the 16 lanes
+// served together read rows r..r+15 at one logical chunk, and the even and the odd rows
+// each cover 8 distinct slots, so a 16-byte-per-lane read is conflict free.
+__device__ __forceinline__ int act_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int act_pos(int row, int c) { return row * BK + ((c ^ act_swz(row)) << 3); }
 // position of chunk c of decoded-weight row `n` in the dx kernel's transposed W tile
 __device__ __forceinline__ int wt_pos(int n, int c) { return n * BK + ((c ^ ((n ^ (n >> 3)) & 7)) << 3); }
 
@@ -131,17 +135,32 @@ constexpr int epi_bytes() { return (2 * BM + BN) * LNF4_EPI_RANK * 2; }
 template <int FMT, int BM>
 __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
   constexpr int MI = BM / 32;
-  constexpr int XL = BM * BK / 8 / NTHR;  // 16-byte chunks per thread per activation tile
-  constexpr int XS_BYTES = 2 * BM * BK * 2;
-  constexpr int SMEM = XS_BYTES > epi_bytes<BM>() ? XS_BYTES : epi_bytes<BM>();
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  __shared__ float lut[16];
-  uint16_t* xs0 = (uint16_t*)smem;
+  constexpr int NM = 2 * MI;                       // MFMAs per 16-wide K step
+  // One ring stage: the activation tile [BM][64] bf16, then the weight tile of the 256
+  // columns (NF4: 32 code bytes + one fp32 absmax per column; bf16: 128 bytes per column).
+  constexpr int X_BYTES = BM * BK * 2;
+  constexpr int W_BYTES = FMT == 0 ? BN * 32 : BN * 128;
+  constexpr int A_BYTES = FMT == 0 ? BN * 4 : 0;
+  // Three distinct LDS objects, one per ring stage: the compiler then knows which
+  // direct-to-LDS loads each LDS read can alias and never waits for the loads still
+  // streaming into the other stages.  The LoRA staging (before the K loop) spreads over
+  // the three (hi, lo, adapter rows), so each stage holds at least a 64-rank slab.
+  constexpr int STAGE_RAW = X_BYTES + W_BYTES + A_BYTES;
+  constexpr int EPI_SLAB = BN * LNF4_EPI_RANK * 2;
+  constexpr int STAGE = STAGE_RAW > EPI_SLAB ? STAGE_RAW : EPI_SLAB;
+  static_assert(3 * STAGE + 64 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+  // byte-pair code table: entry b = (T[b >> 4], T[b & 15]), the fp32 levels of the two
+  // codes one byte holds (high nibble first)
+  __shared__ __attribute__((aligned(16))) float2 lut2[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  if (tid < 16) lut[tid] = c_gemm_table[tid];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);  // NTHR == 256
 
   const int nb = args.n_tiles_m * args.n_tiles_n;
   const int tile = xcd_remap(blockIdx.x, nb);
@@ -156,40 +175,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
   const int m0 = tm * BM;
   const int nloc0 = (tn - P.tile_n0) * BN;
   const int nk = K / BK;
-
-  // B-operand rows: columns n = nloc0 + 64*wave + 32*j + l32 (clamped; results discarded)
-  const uint8_t* wrow[2];
-  const float* arow[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int n = nloc0 + 64 * wave + 32 * j + l32;
-    n = n < out_f ? n : out_f - 1;
-    if (FMT == 0) {
-      wrow[j] = (const uint8_t*)P.w + (size_t)n * (K / 2) + 16 * h;
-      arow[j] = P.absmax + (size_t)n * (K / 64);
-    } else {
-      wrow[j] = (const uint8_t*)P.w + (size_t)n * K * 2 + 64 * h;
-      arow[j] = nullptr;
-    }
-  }
-  // activation tile rows (clamped; rows >= M only feed discarded outputs)
-  const int xc = tid & 7;
-  const uint16_t* xbase = args.x + (size_t)m0 * K;
-  uint32_t xoff[XL];
-#pragma unroll
-  for (int q = 0; q < XL; ++q) {
-    const int rr = q * 32 + (tid >> 3);
-    const int lr = (m0 + rr < M) ? rr : (M - 1 - m0);
-    xoff[q] = (uint32_t)lr * (uint32_t)K + (uint32_t)(xc * 8);
-  }
-
-  constexpr int WL = (FMT == 0) ? 1 : 4;  // 16-byte loads per B column per K-step
-  u32x4 xr[XL];
-  u32x4 wr[2][WL];
-  float ar[2] = {0.f, 0.f};
+  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;   // this lane's two tile columns
 
   // ---- accumulators start at the rank-r LoRA term s * u[m, :] . B[n, :]
-  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;
   floatx16 acc[MI][2];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -199,9 +187,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   if (P.u != nullptr && P.r > 0) {
     const int r = P.r, RP = (r + 15) & ~15;
-    uint16_t* Uh = (uint16_t*)smem;
-    uint16_t* Ul = Uh + BM * RP;
-    uint16_t* V = Ul + BM * RP;
+    uint16_t* Uh = (uint16_t*)sm0;
+    uint16_t* Ul = (uint16_t*)sm1;
+    uint16_t* V = (uint16_t*)sm2;
     for (int idx = tid; idx < BM * RP; idx += NTHR) {
       const int mm = idx / RP, kk = idx - mm * RP, gm = m0 + mm;
       const float uv = (gm < M && kk < r) ? P.scale * P.u[(size_t)gm * r + kk] : 0.0f;
@@ -216,76 +204,235 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
     __syncthreads();
   }
 
-#define LNF4_LOAD_X(kb_)                                                         \
-  _Pragma("unroll") for (int q = 0; q < XL; ++q) xr[q] = *(const u32x4*)(xbase + xoff[q] + (kb_)*BK);
-#define LNF4_STORE_X(buf_)                                                       \
-  _Pragma("unroll") for (int q = 0; q < XL; ++q)                                   \
-    *(u32x4*)&xs0[(buf_)*BM * BK + act_pos(q * 32 + (tid >> 3), xc)] = xr[q];
-#define LNF4_LOAD_W(kb_, dst, adst)                                              \
-  _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                  \
-    if (FMT == 0) {                                                              \
-      dst[j][0] = *(const u32x4*)(wrow[j] + (kb_) * (BK / 2));                   \
-      adst[j] = arow[j][(kb_)];                                                  \
-    } else {                                                                     \
-      _Pragma("unroll") for (int s = 0; s < 4; ++s)                              \
-        dst[j][s] = *(const u32x4*)(wrow[j] + (kb_) * BK * 2 + 16 * s);          \
-      adst[j] = 0.f;                                                             \
-    }                                                                            \
+  // ---- global -> LDS operand streams (no register staging, two K-blocks ahead).
+  // Every direct load of a wave writes 64 consecutive 16-byte (or 4-byte) LDS slots, lane L
+  // to slot L, so each lane picks the global source that belongs in its slot.
+  //  * activation: load q of wave w fills tile rows (w*XQ+q)*8 .. +7; lane L holds row
+  //    (w*XQ+q)*8 + L/8, slot L%8 = logical chunk (L%8) ^ swz(row).  Rows >= M read row
+  //    M-1 (their outputs are discarded).
+  //  * NF4 codes: per column 32 bytes (K-block of 64 codes); wave w loads its 64 columns
+  //    in 2 loads, lane L -> column 64w + 32q + L/2, half L%2.  absmax: one dword load per
+  //    wave, lane L -> column 64w + L.
+  //  * bf16 weights: per column 128 bytes (8 chunks, swizzled like the activation rows);
+  //    wave w loads its 64 columns in 8 loads.
+  //  Columns >= out_f read column out_f-1 (outputs discarded).
+  constexpr int XQ = X_BYTES / 1024 / 4;
+  constexpr int WQ = FMT == 0 ? 2 : 8;
+  constexpr int NLD = XQ + WQ + (FMT == 0 ? 1 : 0);  // vector-memory ops per wave per K-block
+  const uint16_t* xbase = args.x + (size_t)m0 * K;
+  uint32_t xoff[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int row = (wave * XQ + q) * 8 + (lane >> 3);
+    const int lr = (m0 + row < M) ? row : (M - 1 - m0);
+    xoff[q] = (uint32_t)lr * (uint32_t)K + (uint32_t)(((lane & 7) ^ act_swz(row)) * 8);
   }
+  const uint8_t* wsrc[WQ];
+  const float* asrc = nullptr;
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    if (FMT == 0) {
+      int n = nloc0 + 64 * wave + 32 * q + (lane >> 1);
+      n = n < out_f ? n : out_f - 1;
+      wsrc[q] = (const uint8_t*)P.w + (size_t)n * (K / 2) + 16 * (lane & 1);
+    } else {
+      const int col = 8 * q + (lane >> 3);  // column within the wave's 64
+      int n = nloc0 + 64 * wave + col;
+      n = n < out_f ? n : out_f - 1;
+      wsrc[q] = (const uint8_t*)P.w + (size_t)n * K * 2 + (((lane & 7) ^ act_swz(col)) * 16);
+    }
+  }
+  if (FMT == 0) {
+    int n = nloc0 + 64 * wave + lane;
+    n = n < out_f ? n : out_f - 1;
+    asrc = P.absmax + (size_t)n * (K / 64);
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr;
 
-  LNF4_LOAD_X(0);
-  LNF4_LOAD_W(0, wr, ar);
-  LNF4_STORE_X(0);
+#define LNF4_ISSUE(kb_, SM_)                                                                    \
+  {                                                                                             \
+    uint8_t* sx_ = SM_;                                                                         \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q) __builtin_amdgcn_global_load_lds(             \
+        (const void*)(xbase + xoff[q] + (kb_) * BK), (lds_ptr)(sx_ + (wave_u * XQ + q) * 1024), 16, 0, 0); \
+    _Pragma("unroll") for (int q = 0; q < WQ; ++q) __builtin_amdgcn_global_load_lds(             \
+        (const void*)(wsrc[q] + (kb_) * (FMT == 0 ? 32 : 128)),                                 \
+        (lds_ptr)(sx_ + X_BYTES + (wave_u * WQ + q) * 1024), 16, 0, 0);                         \
+    if (FMT == 0)                                                                               \
+      __builtin_amdgcn_global_load_lds((const void*)(asrc + (kb_)),                             \
+                                       (lds_ptr)(sx_ + X_BYTES + W_BYTES + wave_u * 256), 4, 0, 0); \
+  }
+  // wait until at most n vector-memory ops of this wave are outstanding (gfx9 s_waitcnt
+  // encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait")
+#define LNF4_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+  // ... and every LDS access of this wave completed (lgkmcnt 0)
+#define LNF4_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+
+  // NF4 B fragment (8 consecutive K of one column) for MFMA step s: table-read phase
+  // (nibble -> LDS table -> fp32 level) and finish phase (one fp32 product by the block's
+  // absmax, RNE pack to bf16), so the table reads go out early in a step and are consumed
+  // at its end.
+#define LNF4_LUT8(lv, cw_)                                                         \
+  {                                                                                \
+    const uint32_t c_ = (cw_);                                                     \
+    _Pragma("unroll") for (int b_ = 0; b_ < 4; ++b_) {                             \
+      const float2 p_ = lut2[(c_ >> (8 * b_)) & 255u];                             \
+      lv[2 * b_] = p_.x;                                                           \
+      lv[2 * b_ + 1] = p_.y;                                                       \
+    }                                                                              \
+  }
+#define LNF4_FIN8(dst, lv, a_)                                                     \
+  dst = as_bf16x8(pack_bf16x2(lv[0] * (a_), lv[1] * (a_)), pack_bf16x2(lv[2] * (a_), lv[3] * (a_)), \
+                  pack_bf16x2(lv[4] * (a_), lv[5] * (a_)), pack_bf16x2(lv[6] * (a_), lv[7] * (a_)));
+
+  // per-lane operand reads from a stage
+#define LNF4_READ_CODES(SM_, c0, c1, s0, s1)                                     \
+  {                                                                              \
+    c0 = *(const u32x4*)((SM_) + X_BYTES + nc0 * 32 + 16 * h);                   \
+    c1 = *(const u32x4*)((SM_) + X_BYTES + nc1 * 32 + 16 * h);                   \
+    s0 = ((const float*)((SM_) + X_BYTES + W_BYTES))[nc0];                       \
+    s1 = ((const float*)((SM_) + X_BYTES + W_BYTES))[nc1];                       \
+  }
+  // bf16 weights: chunk 4h+s of a column
+#define LNF4_READ_BW(SM_, s_, col_) \
+  (*(const bf16x8*)((SM_) + X_BYTES + (col_) * 128 + (((4 * h + (s_)) ^ act_swz(col_)) * 16)))
+#define LNF4_XS(SM_) ((const uint16_t*)(SM_))
+
+  // prologue: blocks 0 and 1 in flight; block 0 visible
+  LNF4_ISSUE(0, sm0);
+  LNF4_ISSUE((nk > 1 ? 1 : 0), sm1);
+  LNF4_WAIT_VM(NLD);
   __syncthreads();
 
-  for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    // Prefetch the next K-block (the last iteration re-reads its own block: no branch,
-    // so the loads stay ahead of the MFMA work instead of being merged with the stores).
-    const int kn = kb + 1 < nk ? kb + 1 : kb;
-    u32x4 wn[2][WL];
-    float an[2];
-    LNF4_LOAD_X(kn);
-    LNF4_LOAD_W(kn, wn, an);
-    const uint16_t* xt = xs0 + cur * BM * BK;
+  bf16x8 ac[MI], an_[MI];
+  bf16x8 bc0, bc1, bn0, bn1;
+  u32x4 cw0, cw1;      // code words of the current block (NF4)
+  float sa0 = 0.f, sa1 = 0.f;
+  if (FMT == 0) {
+    LNF4_READ_CODES(sm0, cw0, cw1, sa0, sa1);
+    float l0[8], l1[8];
+    LNF4_LUT8(l0, cw0[0]);
+    LNF4_LUT8(l1, cw1[0]);
+    LNF4_FIN8(bc0, l0, sa0);
+    LNF4_FIN8(bc1, l1, sa1);
+  } else {
+    bc0 = LNF4_READ_BW(sm0, 0, nc0);
+    bc1 = LNF4_READ_BW(sm0, 0, nc1);
+  }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8 b0, b1;
-      if (FMT == 0) {
-        const uint32_t c0 = wr[0][0][s];
-        const uint32_t c1 = wr[1][0][s];
-        uint32_t o[4];
-        decode8(c0, ar[0], lut, o);
-        b0 = as_bf16x8(o[0], o[1], o[2], o[3]);
-        decode8(c1, ar[1], lut, o);
-        b1 = as_bf16x8(o[0], o[1], o[2], o[3]);
-      } else {
-        b0 = __builtin_bit_cast(bf16x8, wr[0][s]);
-        b1 = __builtin_bit_cast(bf16x8, wr[1][s]);
-      }
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const bf16x8 a = *(const bf16x8*)&xt[act_pos(32 * i + l32, 4 * h + s)];
-        acc[i][0] = mfma32(a, b0, acc[i][0]);
-        acc[i][1] = mfma32(a, b1, acc[i][1]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // the other buffer was last read before the previous barrier: safe to overwrite
-    LNF4_STORE_X(cur ^ 1);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int s = 0; s < WL; ++s) wr[j][s] = wn[j][s];
-      ar[j] = an[j];
-    }
-    __syncthreads();
+  for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(32 * i + l32, 4 * h)];
+
+  // One K-block on stage SC; SN holds the next block, SP receives the block two ahead.
+  // The loop is unrolled three times with the stages rotated, so every LDS access names
+  // its stage statically.
+#define LNF4_FWD_BLOCK(SC, SN, SP)                                                             \
+  {                                                                                            \
+    LNF4_ISSUE((kb + 2 < nk ? kb + 2 : nk - 1), SP); /* the tail re-reads the last block */    \
+    u32x4 nw0, nw1;                                                                            \
+    float ns0 = 0.f, ns1 = 0.f;                                                                \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 3) {                                                                            \
+        /* block kb+1 (issued one block ago) must be in LDS for every wave, and every wave */  \
+        /* must be done with stage SC before block kb+3 is issued into it */                   \
+        /* (a bare s_barrier: a fenced __syncthreads would also wait for the loads of */     \
+        /* block kb+2, which are meant to stay in flight) */                                   \
+        LNF4_WAIT_VM_LGKM0(NLD);                                                               \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
+      float l0[8], l1[8];                                                                      \
+      if (FMT == 0) {                                                                          \
+        if (s < 3) {                                                                           \
+          LNF4_LUT8(l0, cw0[s + 1 < 4 ? s + 1 : 0]);                                           \
+          LNF4_LUT8(l1, cw1[s + 1 < 4 ? s + 1 : 0]);                                           \
+        } else {                                                                               \
+          LNF4_READ_CODES(SN, nw0, nw1, ns0, ns1);                                             \
+          LNF4_LUT8(l0, nw0[0]);                                                               \
+          LNF4_LUT8(l1, nw1[0]);                                                               \
+        }                                                                                      \
+      } else {                                                                                 \
+        if (s < 3) {                                                                           \
+          bn0 = LNF4_READ_BW(SC, s + 1, nc0);                                                  \
+          bn1 = LNF4_READ_BW(SC, s + 1, nc1);                                                  \
+        } else {                                                                               \
+          bn0 = LNF4_READ_BW(SN, 0, nc0);                                                      \
+          bn1 = LNF4_READ_BW(SN, 0, nc1);                                                      \
+        }                                                                                      \
+      }                                                                                        \
+      if (s < 3) {                                                                             \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
+            *(const bf16x8*)&LNF4_XS(SC)[act_pos(32 * i + l32, 4 * h + s + 1)];                \
+      } else {                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
+            *(const bf16x8*)&LNF4_XS(SN)[act_pos(32 * i + l32, 4 * h)];                        \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
+        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
+        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+      }                                                                                        \
+      if (FMT == 0) {                                                                          \
+        LNF4_FIN8(bn0, l0, (s < 3 ? sa0 : ns0));                                               \
+        LNF4_FIN8(bn1, l1, (s < 3 ? sa1 : ns1));                                               \
+        /* issue order: table addresses and reads first, A-fragment reads, then the */         \
+        /* products and packs, spread between the MFMAs */                                     \
+        _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                        \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                   \
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                                   \
+        }                                                                                      \
+        _Pragma("unroll") for (int g = 4; g < NM - NM / 4; ++g) {                              \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+          __builtin_amdgcn_sched_group_barrier(0x100, (MI + (NM - NM / 4 - 4) - 1) / (NM - NM / 4 - 4), 0); \
+        }                                                                                      \
+        _Pragma("unroll") for (int g = NM - NM / 4; g < NM; ++g) {                             \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+          __builtin_amdgcn_sched_group_barrier(0x002, (24 + NM / 4 - 1) / (NM / 4), 0);        \
+        }                                                                                      \
+      } else {                                                                                 \
+        _Pragma("unroll") for (int g = 0; g < NM; ++g) {                                       \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
+        }                                                                                      \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) ac[i] = an_[i];                           \
+      bc0 = bn0;                                                                               \
+      bc1 = bn1;                                                                               \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    if (FMT == 0) {                                                                            \
+      cw0 = nw0;                                                                               \
+      cw1 = nw1;                                                                               \
+      sa0 = ns0;                                                                               \
+      sa1 = ns1;                                                                               \
+    }                                                                                          \
   }
 
-#undef LNF4_LOAD_X
-#undef LNF4_STORE_X
-#undef LNF4_LOAD_W
+  // unrolled twice over (six blocks per trip): the compiler drops the per-stage
+  // knowledge of in-flight loads at the loop head and drains them there once per trip
+  for (int kb = 0;;) {
+    LNF4_FWD_BLOCK(sm0, sm1, sm2);
+    if (++kb == nk) break;
+    LNF4_FWD_BLOCK(sm1, sm2, sm0);
+    if (++kb == nk) break;
+    LNF4_FWD_BLOCK(sm2, sm0, sm1);
+    if (++kb == nk) break;
+    LNF4_FWD_BLOCK(sm0, sm1, sm2);
+    if (++kb == nk) break;
+    LNF4_FWD_BLOCK(sm1, sm2, sm0);
+    if (++kb == nk) break;
+    LNF4_FWD_BLOCK(sm2, sm0, sm1);
+    if (++kb == nk) break;
+  }
+#undef LNF4_FWD_BLOCK
+#undef LNF4_READ_CODES
+#undef LNF4_READ_BW
+#undef LNF4_XS
+#undef LNF4_ISSUE
+#undef LNF4_WAIT_VM
+#undef LNF4_WAIT_VM_LGKM0
+#undef LNF4_LUT8
+#undef LNF4_FIN8
+
   // ---- store bf16
   const int n0g = nloc0 + nc0, n1g = nloc0 + nc1;
 #pragma unroll
@@ -536,15 +683,15 @@ static int pick_bm(int M, int tiles_n_256) {
 hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   FwdArgs a = a0;
   if (a.M <= 0 || a.n_tiles_n <= 0) return hipSuccess;
-  const int bm = pick_bm(a.M, a.n_tiles_n);
+  // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
+  const int bm = fmt == 0 ? pick_bm(a.M, a.n_tiles_n) : 128;
   a.n_tiles_m = (a.M + bm - 1) / bm;
   const dim3 grid(a.n_tiles_m * a.n_tiles_n), block(NTHR);
   if (fmt == 0) {
     if (bm == 256) hipLaunchKernelGGL((k_fwd<0, 256>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_fwd<0, 128>), grid, block, 0, s, a);
   } else {
-    if (bm == 256) hipLaunchKernelGGL((k_fwd<1, 256>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_fwd<1, 128>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_fwd<1, 128>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -14,7 +14,7 @@ import re
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblnf4.so")
+LIB_PATH = os.environ.get("LNF4_LIB") or os.path.join(_HERE, "liblnf4.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "lnf4.h")
 
 LNF4_OK = 0
