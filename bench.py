@@ -25,6 +25,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+CSRC = os.path.join(ROOT, "lora_fine_tuning_nf4_amd", "csrc")
+# sources the forward GEMM kernel is compiled from: a counter summary taken on other sources
+# no longer describes the kernel that runs
+FWD_KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp", "nf4_table.hpp")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fwd_nf4_gate_up_llama8b_T2048.traffic.txt")
+CAL_ELEMS = 64 << 20        # float32 elements of the calibration copy (256 MiB read + 256 MiB written)
 
 
 def log(*a):
@@ -37,6 +43,47 @@ def gemm_flops(wl, group, kind):
     outs = [wl.shapes[p][0] for p in group]
     in_f = wl.shapes[group[0]][1]
     return 2.0 * T * sum(outs) * in_f
+
+
+def fwd_bytes(wl, group):
+    """Algorithmic HBM bytes of one grouped NF4 forward launch: x read once, codes and absmax
+    read once, y written once (bf16), plus the adapters' B and u when adapted."""
+    T = wl.tokens
+    in_f = wl.shapes[group[0]][1]
+    b = 2 * T * in_f
+    for p in group:
+        o = wl.shapes[p][0]
+        b += o * in_f // 2 + 4 * (o * in_f // 64) + 2 * T * o
+        if p in wl.adapted:
+            b += 2 * o * wl.rank + 4 * T * wl.rank
+    return b
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in FWD_KERNEL_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate|up forward kernel, from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary; None when that summary is missing or was taken on
+    other kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_PROFILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None, "stale (kernel sources changed since the counters were taken)"
+        return int(float(kv["traffic_bytes_per_launch"])), os.path.relpath(TRAFFIC_PROFILE, ROOT)
+    except (OSError, KeyError, ValueError):
+        return None, "no counter summary"
 
 
 def cpu_baseline(wl, seed: int, layers: int):
@@ -163,6 +210,7 @@ def main():
     dx_dom = call_ms[("bwd", 2, True)]
     dx_ms = sum(dx_dom) / len(dx_dom)
 
+    traffic, traffic_src = measured_traffic()
     breakdown = {f"{k[0]}_{'+'.join(GROUPS[k[1]])}{'' if k[2] else '_adapters_off'}_ms":
                  round(sum(v) / len(v), 4) for k, v in call_ms.items() if v}
 
@@ -185,7 +233,8 @@ def main():
                    "head_slot": bool(stack.slot is not None), "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "traffic_source": traffic_src,
+            "algorithmic_bytes_per_launch": fwd_bytes(wl, GROUPS[2]),
             "kernel": "k_fwd<NF4,BM=256> gate|up forward: M=2048 N=28672 K=4096 (fused NF4 decode)",
             "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4),
             "launches_timed": len(dom),
@@ -231,6 +280,16 @@ def main():
         e1.record(cs)
     torch.cuda.synchronize()
     result["h2d"]["copy_only_GBps"] = round(8 * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
+
+    # a plain device copy of known size, the reference point that scales rocprofv3's
+    # FETCH_SIZE / WRITE_SIZE counters to bytes in a counter run of this same command
+    ca = torch.ones(CAL_ELEMS, dtype=torch.float32, device="cuda")
+    cb = torch.empty_like(ca)
+    torch.neg(ca, out=cb)
+    torch.cuda.synchronize()
+    result["pmc_calibration"] = {"kernel": "torch neg, float32 elementwise", "bytes_read": 4 * CAL_ELEMS,
+                                 "bytes_written": 4 * CAL_ELEMS}
+    del ca, cb
 
     stack.close()
     del stack

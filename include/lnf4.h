@@ -171,7 +171,9 @@ typedef struct lnf4_proj {
 int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
                    hipStream_t stream);
 
-/* Workspace bytes for lora_group_bwd.  Host-only. */
+/* Workspace bytes for lora_group_bwd with these projs and T: which gradients are asked
+ * for (dA, dB non-NULL) and whether u is saved decide the buffers, so query with the
+ * same descriptors as the call.  Host-only. */
 size_t lora_group_bwd_workspace(const lnf4_proj* projs, int32_t n, int64_t T);
 
 /* Grouped backward: dx [T, in] = sum over the group (NULL to skip), per-projection dA/dB. */
@@ -244,6 +246,22 @@ int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** de
  * the slot) has finished.  Does not make compute wait; stream_slot_wait does.
  */
 int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute);
+
+/*
+ * The same copy issued in n_parts pieces (part = 0, 1, ..., n_parts-1, in order, on
+ * successive calls), so a large slot shard can trickle over the copy stream between
+ * layer copies instead of holding it for one long transfer.  Part p copies bytes
+ * [p*c, min((p+1)*c, size)) with c = ceil(size/n_parts) rounded up to 4 KiB.  Part 0
+ * waits for the work enqueued so far on `compute` (the slot's previous user); the load
+ * counts as issued after the last part, and only then may stream_slot_wait be called.
+ * Each part logs one SLOT_COPY event with buffer = -1 - part.
+ * Errors: EINVAL (no slot, shard or part out of range, n_parts outside 1..1024),
+ * ESHAPE (shard larger than the slot), ESTATE (part out of order, destroyed), EHIP.
+ */
+int stream_slot_load_part(lnf4_stream* st, int32_t shard, int32_t part, int32_t n_parts, hipStream_t compute);
+
+/* Make `compute` wait for the last complete slot load; *slot_ptr_out = the slot.
+ * Errors: EINVAL (no slot), ESTATE (no complete load issued, destroyed), EHIP. */
 int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out);
 
 /* Rewind a finished (or unfinished) pass so the same schedule runs again (next step).

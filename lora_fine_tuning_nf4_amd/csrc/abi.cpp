@@ -107,13 +107,35 @@ int group_fwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
   a.M = (int)T;
   a.K = K;
   a.n_proj = n;
+  // u_p = x A_p^T for every adapted projection: they share x, so one job per run of
+  // projections whose ranks sum to at most 64
+  {
+    RankArgs ra;
+    std::memset(&ra, 0, sizeof ra);
+    ra.T = (int)T;
+    for (int p = 0; p < n; ++p) {
+      if (!on[p]) continue;
+      const lnf4_proj& P = projs[p];
+      RankJob* J = ra.n_jobs > 0 ? &ra.job[ra.n_jobs - 1] : nullptr;
+      if (!J || J->R + P.r > LNF4_MAX_RANK || J->n == kMaxGroup) {
+        J = &ra.job[ra.n_jobs++];
+        J->src = x;
+        J->K = K;
+        J->layout = 0;
+      }
+      J->W[J->n] = P.A;
+      J->dst[J->n] = P.u;
+      J->r[J->n] = P.r;
+      J->dst_stride[J->n] = P.r;
+      J->n += 1;
+      J->R += P.r;
+    }
+    hipError_t e = launch_rank_proj(ra, s);
+    if (e != hipSuccess) return hip_fail(e, "u = x A^T launch");
+  }
   int tiles = 0;
   for (int p = 0; p < n; ++p) {
     const lnf4_proj& P = projs[p];
-    if (on[p]) {
-      hipError_t e = launch_xa(x, P.A, (int)T, K, P.r, P.u, s);
-      if (e != hipSuccess) return hip_fail(e, "u = x A^T launch");
-    }
     FwdProj& q = a.p[p];
     q.w = P.W.data;
     q.absmax = P.W.absmax;
@@ -133,31 +155,99 @@ int group_fwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
 }
 
 // --------------------------------------------------------------------------- group bwd
+// Workspace of one grouped backward call.  The adapted projections are cut into runs
+// whose ranks sum to at most 64 ("chunks"); a chunk's v = dy B columns sit side by side
+// in one fp32 [T][R_chunk] array, so the dA of the whole chunk is one reduction against x.
 struct BwdPlan {
-  size_t v_off[LNF4_MAX_GROUP];
-  size_t u_off[LNF4_MAX_GROUP];
-  size_t part_off;
+  int n_chunks;
+  int chunk_of[LNF4_MAX_GROUP];   // chunk of projection p (-1: adapter off)
+  int v_col[LNF4_MAX_GROUP];      // first column of p's v in its chunk
+  int chunk_R[LNF4_MAX_GROUP];
+  size_t v_off[LNF4_MAX_GROUP];   // per chunk
+  size_t pa_off[LNF4_MAX_GROUP];  // per chunk: dA partials (-1: no dA asked in the chunk)
+  size_t u_off[LNF4_MAX_GROUP];   // per projection: recomputed u (-1: saved or not needed)
+  size_t pb_off[LNF4_MAX_GROUP];  // per projection: dB partials (-1: no dB)
   size_t total;
 };
 
 static void plan_bwd(const lnf4_proj* projs, int32_t n, int64_t T, const int* on, BwdPlan& pl) {
-  size_t off = 0, part = 0;
+  const size_t none = (size_t)-1;
+  pl.n_chunks = 0;
+  for (int p = 0; p < LNF4_MAX_GROUP; ++p) {
+    pl.chunk_of[p] = -1;
+    pl.v_col[p] = 0;
+    pl.chunk_R[p] = 0;
+    pl.v_off[p] = pl.pa_off[p] = pl.u_off[p] = pl.pb_off[p] = none;
+  }
+  int members[LNF4_MAX_GROUP] = {0};
   for (int p = 0; p < n; ++p) {
-    pl.v_off[p] = pl.u_off[p] = (size_t)-1;
     if (!on[p]) continue;
-    const size_t tr = round256((size_t)T * projs[p].r * sizeof(float));
-    pl.v_off[p] = off;
-    off += tr;
+    const int r = projs[p].r;
+    if (pl.n_chunks == 0 || pl.chunk_R[pl.n_chunks - 1] + r > LNF4_MAX_RANK) pl.n_chunks += 1;
+    const int c = pl.n_chunks - 1;
+    pl.chunk_of[p] = c;
+    pl.v_col[p] = pl.chunk_R[c];
+    pl.chunk_R[c] += r;
+    members[c] += 1;
+  }
+  size_t off = 0;
+  const int in_f = n > 0 ? (int)projs[0].W.in_f : 0;
+  for (int c = 0; c < pl.n_chunks; ++c) {
+    pl.v_off[c] = off;
+    off += round256((size_t)T * pl.chunk_R[c] * sizeof(float));
+    bool any_dA = false;
+    for (int p = 0; p < n; ++p) any_dA = any_dA || (pl.chunk_of[p] == c && projs[p].dA);
+    if (any_dA) {
+      pl.pa_off[c] = off;
+      off += round256(grad_partial_bytes((int32_t)T, in_f, pl.chunk_R[c]));
+    }
+  }
+  for (int p = 0; p < n; ++p) {
+    if (!on[p] || !projs[p].dB) continue;
     if (!projs[p].u) {
       pl.u_off[p] = off;
-      off += tr;
+      off += round256((size_t)T * projs[p].r * sizeof(float));
     }
-    const size_t c = (size_t)(projs[p].W.in_f > projs[p].W.out_f ? projs[p].W.in_f : projs[p].W.out_f);
-    const size_t g = round256(grad_workspace_bytes((int32_t)T, (int32_t)c, projs[p].r));
-    if (g > part) part = g;
+    pl.pb_off[p] = off;
+    off += round256(grad_partial_bytes((int32_t)T, (int32_t)projs[p].W.out_f, projs[p].r));
   }
-  pl.part_off = off;
-  pl.total = off + part;
+  pl.total = off;
+}
+
+// launch a list of rank jobs in batches of kMaxJobs
+// launch a list of rank jobs: one launch per layout, in batches of kMaxJobs
+static hipError_t launch_rank_jobs(const RankJob* jobs, int nj, int T, hipStream_t s) {
+  for (int layout = 0; layout < 2; ++layout) {
+    RankArgs ra;
+    std::memset(&ra, 0, sizeof ra);
+    ra.T = T;
+    for (int j = 0; j < nj; ++j) {
+      if (jobs[j].layout != layout) continue;
+      ra.job[ra.n_jobs++] = jobs[j];
+      if (ra.n_jobs == kMaxJobs) {
+        hipError_t e = launch_rank_proj(ra, s);
+        if (e != hipSuccess) return e;
+        ra.n_jobs = 0;
+      }
+    }
+    hipError_t e = launch_rank_proj(ra, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static hipError_t launch_grad_jobs(const GradJob* jobs, int nj, int T, int accumulate, hipStream_t s) {
+  for (int j0 = 0; j0 < nj; j0 += kMaxJobs) {
+    GradArgs ga;
+    std::memset(&ga, 0, sizeof ga);
+    ga.T = T;
+    ga.accumulate = accumulate ? 1 : 0;
+    ga.n_jobs = nj - j0 < kMaxJobs ? nj - j0 : kMaxJobs;
+    for (int j = 0; j < ga.n_jobs; ++j) ga.job[j] = jobs[j0 + j];
+    hipError_t e = launch_rank_grad(ga, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 static int bwd_adapter_flags(const lnf4_proj* projs, int32_t n, int* on, const char* who) {
@@ -240,23 +330,60 @@ int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
     return LNF4_OK;
   }
   const int N = (int)projs[0].W.in_f;
-  float* v[LNF4_MAX_GROUP];
+  const bool any_dA = [&] {
+    for (int p = 0; p < n; ++p)
+      if (on[p] && projs[p].dA) return true;
+    return false;
+  }();
+  // v = dy B per adapted projection (into its chunk's columns), and u = x A^T where dB
+  // needs it and it was not saved
+  const float* v[LNF4_MAX_GROUP];
   const float* u[LNF4_MAX_GROUP];
+  RankJob jobs[2 * LNF4_MAX_GROUP];
+  int nj = 0;
   for (int p = 0; p < n; ++p) {
     const lnf4_proj& P = projs[p];
-    v[p] = nullptr;
-    u[p] = nullptr;
+    v[p] = u[p] = nullptr;
     if (!on[p]) continue;
-    v[p] = (float*)(wsb + pl.v_off[p]);
-    if ((e = launch_dyb(P.dy, P.B, (int)T, (int)P.W.out_f, P.r, v[p], s)) != hipSuccess) return hip_fail(e, "v = dy B launch");
-    if (P.u) {
-      u[p] = P.u;
-    } else if (P.dB) {
-      float* uw = (float*)(wsb + pl.u_off[p]);
-      if ((e = launch_xa(x, P.A, (int)T, N, P.r, uw, s)) != hipSuccess) return hip_fail(e, "u recompute launch");
-      u[p] = uw;
+    const int c = pl.chunk_of[p];
+    float* vp = (float*)(wsb + pl.v_off[c]) + pl.v_col[p];
+    v[p] = vp;
+    if (dx || any_dA) {
+      RankJob& J = jobs[nj++];
+      std::memset(&J, 0, sizeof J);
+      J.src = P.dy;
+      J.K = (int)P.W.out_f;
+      J.layout = 1;
+      J.n = 1;
+      J.R = P.r;
+      J.W[0] = P.B;
+      J.r[0] = P.r;
+      J.dst[0] = vp;
+      J.dst_stride[0] = pl.chunk_R[c];
+    }
+    if (P.dB) u[p] = P.u ? P.u : (const float*)(wsb + pl.u_off[p]);
+  }
+  {
+    RankJob* J = nullptr;
+    for (int p = 0; p < n; ++p) {
+      const lnf4_proj& P = projs[p];
+      if (!on[p] || !P.dB || P.u) continue;
+      if (!J || J->R + P.r > LNF4_MAX_RANK) {
+        J = &jobs[nj++];
+        std::memset(J, 0, sizeof *J);
+        J->src = x;
+        J->K = N;
+        J->layout = 0;
+      }
+      J->W[J->n] = P.A;
+      J->dst[J->n] = (float*)(wsb + pl.u_off[p]);
+      J->r[J->n] = P.r;
+      J->dst_stride[J->n] = P.r;
+      J->n += 1;
+      J->R += P.r;
     }
   }
+  if ((e = launch_rank_jobs(jobs, nj, (int)T, s)) != hipSuccess) return hip_fail(e, "v = dy B / u = x A^T launch");
   if (dx) {
     DxArgs a;
     std::memset(&a, 0, sizeof a);
@@ -273,6 +400,7 @@ int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
       q.absmax = P.W.absmax;
       q.dy = P.dy;
       q.v = on[p] ? v[p] : nullptr;
+      q.v_stride = on[p] ? pl.chunk_R[pl.chunk_of[p]] : 0;
       q.A = on[p] ? P.A : nullptr;
       q.out_f = (int)P.W.out_f;
       q.r = on[p] ? P.r : 0;
@@ -283,16 +411,46 @@ int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
     a.total_kb = kb;
     if ((e = launch_dx(a, projs[0].W.fmt, s)) != hipSuccess) return hip_fail(e, "fused dx GEMM launch");
   }
-  float* part = (float*)(wsb + pl.part_off);
+  // adapter gradients: dA of each chunk against x, dB of each projection against its dy
+  GradJob gj[2 * LNF4_MAX_GROUP];
+  int ng = 0;
+  for (int c = 0; c < pl.n_chunks; ++c) {
+    if (pl.pa_off[c] == (size_t)-1) continue;
+    GradJob& G = gj[ng++];
+    std::memset(&G, 0, sizeof G);
+    G.Q = x;
+    G.C = N;
+    G.P = (const float*)(wsb + pl.v_off[c]);
+    G.pstride = pl.chunk_R[c];
+    G.R = pl.chunk_R[c];
+    G.transpose = 1;
+    G.part = (float*)(wsb + pl.pa_off[c]);
+    for (int p = 0; p < n; ++p) {
+      if (pl.chunk_of[p] != c) continue;
+      G.G[G.n] = projs[p].dA;  // may be NULL: that weight's dA is skipped
+      G.r[G.n] = projs[p].r;
+      G.scale[G.n] = projs[p].scale;
+      G.n += 1;
+    }
+  }
   for (int p = 0; p < n; ++p) {
     const lnf4_proj& P = projs[p];
-    if (!on[p]) continue;
-    if (P.dA && (e = launch_grad(v[p], x, (int)T, N, P.r, P.scale, 1, accumulate, P.dA, part, s)) != hipSuccess)
-      return hip_fail(e, "dA launch");
-    if (P.dB && (e = launch_grad(u[p], P.dy, (int)T, (int)P.W.out_f, P.r, P.scale, 0, accumulate, P.dB, part, s)) !=
-                    hipSuccess)
-      return hip_fail(e, "dB launch");
+    if (!on[p] || !P.dB) continue;
+    GradJob& G = gj[ng++];
+    std::memset(&G, 0, sizeof G);
+    G.Q = P.dy;
+    G.C = (int)P.W.out_f;
+    G.P = u[p];
+    G.pstride = P.r;
+    G.R = P.r;
+    G.transpose = 0;
+    G.part = (float*)(wsb + pl.pb_off[p]);
+    G.n = 1;
+    G.G[0] = P.dB;
+    G.r[0] = P.r;
+    G.scale[0] = P.scale;
   }
+  if ((e = launch_grad_jobs(gj, ng, (int)T, accumulate, s)) != hipSuccess) return hip_fail(e, "dA / dB launch");
   return LNF4_OK;
 }
 
@@ -358,9 +516,11 @@ size_t lora_linear_bwd_workspace(int64_t T, int64_t out_f, int64_t in_f, int32_t
   p.W.out_f = out_f;
   p.W.in_f = in_f;
   p.r = r;
-  // worst case: adapter on and u recomputed
+  // worst case: adapter on, both gradients asked for and u recomputed
   p.A = (const uint16_t*)16;
   p.B = (const uint16_t*)16;
+  p.dA = (float*)16;
+  p.dB = (float*)16;
   return group_bwd_ws(&p, 1, T);
 }
 

@@ -32,6 +32,7 @@ __constant__ float c_gemm_table[16] = LNF4_TABLE_INIT;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int NTHR = 256;
+constexpr int kGroupM = 4;   // row-tiles per group of the tile order (tile_coords)
 // largest rank (summed over a group in backward) the fused epilogue stages in LDS
 #define LNF4_EPI_RANK 64
 
@@ -88,6 +89,7 @@ __device__ __forceinline__ DxProj select_dx(const DxArgs& a, int idx) {
   LNF4_SEL(P, a.p, idx, r);
   LNF4_SEL(P, a.p, idx, scale);
   LNF4_SEL(P, a.p, idx, kb0);
+  LNF4_SEL(P, a.p, idx, v_stride);
   return P;
 }
 
@@ -162,9 +164,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);  // NTHR == 256
 
-  const int nb = args.n_tiles_m * args.n_tiles_n;
-  const int tile = xcd_remap(blockIdx.x, nb);
-  const int tm = tile % args.n_tiles_m, tn = tile / args.n_tiles_m;
+  int tm, tn;
+  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
   int pi = 0;
 #pragma unroll
   for (int q = 1; q < kMaxGroup; ++q)
@@ -470,9 +471,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx(const DxArgs args) {
   const int l32 = lane & 31, h = lane >> 5;
   if (tid < 16) lut[tid] = c_gemm_table[tid];
 
-  const int nb = args.n_tiles_m * args.n_tiles_n;
-  const int tile = xcd_remap(blockIdx.x, nb);
-  const int tm = tile % args.n_tiles_m, tn = tile / args.n_tiles_m;
+  int tm, tn;
+  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
   const int M = args.M, N = args.N;
   const int m0 = tm * BM, n0 = tn * BN;
 
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx(const DxArgs args) {
       const int r = P.r;
       for (int idx = tid; idx < BM * r; idx += NTHR) {
         const int mm = idx / r, kk = idx - mm * r, gm = m0 + mm;
-        if (gm < M) split_bf16(P.scale * P.v[(size_t)gm * r + kk], Uh[mm * RP + off + kk], Ul[mm * RP + off + kk]);
+        if (gm < M) split_bf16(P.scale * P.v[(size_t)gm * P.v_stride + kk], Uh[mm * RP + off + kk], Ul[mm * RP + off + kk]);
       }
       for (int idx = tid; idx < BN * r; idx += NTHR) {
         const int kk = idx / BN, nn = idx - kk * BN, n = n0 + nn;

@@ -39,12 +39,13 @@ struct DxProj {
   const void* w;        // NF4 codes [out][in/2] or bf16 [out][in]
   const float* absmax;
   const uint16_t* dy;   // [T][out]
-  const float* v;       // [T][r] fp32 or null
+  const float* v;       // [T][v_stride] fp32 (this projection's r columns) or null
   const uint16_t* A;    // [r][in] bf16
   int32_t out_f;        // K extent of this projection (multiple of 8)
   int32_t r;
   float scale;
   int32_t kb0;          // first 64-wide K-block of this projection in the group's K space
+  int32_t v_stride;
 };
 struct DxArgs {
   uint16_t* dx;
@@ -68,19 +69,48 @@ hipError_t launch_nf4_quantize(const float* w, int64_t n_elems, uint8_t* codes, 
                                hipStream_t s);
 
 // ---------------------------------------------------------------- skinny LoRA products
-// u[T][r] = x[T][in] A[r][in]^T            (fp32 out)
-hipError_t launch_xa(const uint16_t* x, const uint16_t* A, int32_t T, int32_t in_f, int32_t r, float* u,
-                     hipStream_t s);
-// v[T][r] = dy[T][out] B[out][r]           (fp32 out)
-hipError_t launch_dyb(const uint16_t* dy, const uint16_t* B, int32_t T, int32_t out_f, int32_t r, float* v,
-                      hipStream_t s);
-// G = scale * P^T Q over T with P [T][r] fp32 and Q [T][C] bf16:
-//   transpose_out = 1: G is [r][C] (dA with P = v, Q = x)
-//   transpose_out = 0: G is [C][r] (dB with P = u, Q = dy)
-// Deterministic: fixed split over T into partials (workspace), fixed-order reduce.
+constexpr int kMaxJobs = 8;
+// One activation matrix src [T][K] bf16 times the weights of one job, ranks concatenated
+// (R = sum r_p <= 64):
+//   layout 0: W_p = A_p [r_p][K]  ->  dst_p[t][k] = sum_i src[t][i] A_p[k][i]      (u)
+//   layout 1: W_p = B_p [K][r_p]  ->  dst_p[t][k] = sum_i src[t][i] B_p[i][k]      (v; n == 1)
+// dst_p is fp32 with row stride dst_stride[p].
+struct RankJob {
+  const uint16_t* src;
+  const uint16_t* W[kMaxGroup];
+  float* dst[kMaxGroup];
+  int32_t r[kMaxGroup];
+  int32_t dst_stride[kMaxGroup];
+  int32_t n, K, layout, R;
+};
+struct RankArgs {
+  int32_t T;
+  int32_t n_jobs;
+  RankJob job[kMaxJobs];
+};
+hipError_t launch_rank_proj(const RankArgs& a, hipStream_t s);
+
+// Gradients reduced over T: for the weights of a job (ranks concatenated in P),
+//   G_p = scale_p * sum_t Q[t][c] P[t][off_p + k]
+// written [r_p][C] (transpose = 1: dA with Q = x, P = v) or [C][r_p] (transpose = 0: dB
+// with Q = dy_p, P = u_p); G_p == null skips that weight.  part: the job's workspace of
+// grad_partial_bytes(T, C, R) bytes.  Deterministic: fixed splits, fixed-order sums.
+struct GradJob {
+  const uint16_t* Q;
+  const float* P;
+  float* part;
+  float* G[kMaxGroup];
+  int32_t r[kMaxGroup];
+  float scale[kMaxGroup];
+  int32_t n, C, R, pstride, transpose;
+};
+struct GradArgs {
+  int32_t T, nsplit, tchunk, accumulate, n_jobs;
+  GradJob job[kMaxJobs];
+};
+size_t grad_partial_bytes(int32_t T, int32_t C, int32_t R);
+hipError_t launch_rank_grad(const GradArgs& a, hipStream_t s);
+
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
-size_t grad_workspace_bytes(int32_t T, int32_t C, int32_t r);
-hipError_t launch_grad(const float* P, const uint16_t* Q, int32_t T, int32_t C, int32_t r, float scale,
-                       int32_t transpose_out, int32_t accumulate, float* G, float* partial, hipStream_t s);
 
 }  // namespace lnf4

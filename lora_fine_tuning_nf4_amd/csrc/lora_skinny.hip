@@ -5,192 +5,255 @@
 //   dA = s v^T x  [r, in]  (reduction over T)
 //   dB = s dy^T u [out, r] (reduction over T)
 //
-// u and v: one wavefront owns a few rows; its 64 lanes split the long dimension into
-// 8-element chunks (16-byte loads), accumulate rows x rank partial sums, and finish with
-// a butterfly reduce-scatter across the wave: at each xor-shuffle step a lane keeps half
-// of its values and sends the other half, so 32 values need 16+8+4+2+1 shuffles plus one
-// final pairwise add instead of 32 full reductions, and each lane ends up owning one
-// finished value.  Results are fp32.
+// u and v (k_rank_proj): one launch serves several jobs (blockIdx.y).  A job is one
+// activation matrix src [T, K] and the weights that multiply it; weights that share src
+// (q and v both read x) are one job with their ranks concatenated (R = sum r_p <= 64), so
+// src is read from HBM once.  A workgroup owns RB rows of src and all of K: its 8 waves
+// take interleaved 512-wide K slices (lane = 8 consecutive K, one 16-byte load), each
+// lane accumulates RB x RMAX partial dot products, a butterfly reduce-scatter across the
+// wave leaves each lane NV/64 finished slice totals, and the 8 waves' totals are added in
+// a fixed order through LDS.  Results are fp32 and deterministic.
 //
-// dA and dB: each lane owns COLS columns and all r ranks; a workgroup covers a fixed slice
-// of T; partial sums go to a workspace and a second kernel adds the slices in a fixed
-// order (deterministic, no atomics).
+// dA and dB (k_rank_grad): a job is Q [T, C] bf16 times P [T, R] fp32 reduced over T, for
+// the weights whose ranks are concatenated in P (dA of every adapted projection of a
+// group shares Q = x; each dB has its own Q = dy_p).  Each lane owns CPL columns and all
+// R ranks; P rows are wave-uniform (scalar loads).  The 4 waves of a workgroup split the
+// workgroup's T range and add through LDS in a fixed order; workgroups along T write
+// partials that k_rank_grad_reduce adds in a fixed order (no atomics).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace lnf4 {
 
+// Butterfly reduce-scatter of NV (64 or 128) per-lane values over the 64 lanes of a wave:
+// at each xor step a lane keeps one half of its values and adds the partner's copy of
+// that half, so NV values need NV/2 + NV/4 + ... + NV/64 shuffles.  On return
+// v[j] (j < NV/64) is the wave total of value index lane * (NV/64) + j.
 template <int NV>
-__device__ __forceinline__ float wave_reduce_scatter(float (&v)[NV], int lane) {
-  // returns the total of value index (NV == 64 ? lane : lane >> 1)
+__device__ __forceinline__ void wave_reduce_scatter(float (&v)[NV], int lane) {
+  static_assert(NV == 64 || NV == 128, "NV");  // one or two finished values per lane
 #pragma unroll
-  for (int w = NV / 2, mask = 32; w >= 1; w >>= 1, mask >>= 1) {
-    const bool up = (lane & mask) != 0;
+  for (int st = 0; st < 6; ++st) {  // a counted loop, so it unrolls and v stays in registers
+    const int mask = 32 >> st, w = NV >> (st + 1);
+    const uint32_t m = (lane & mask) != 0 ? 0xffffffffu : 0u;
 #pragma unroll
     for (int i = 0; i < w; ++i) {
-      const float send = up ? v[i] : v[i + w];
-      const float keep = up ? v[i + w] : v[i];
+      // choose by bit masks: a select between two array elements would be folded into a
+      // lane-dependent index, which sends the whole array to scratch memory
+      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + w]);
+      const float send = __uint_as_float((a & m) | (b & ~m));
+      const float keep = __uint_as_float((b & m) | (a & ~m));
       v[i] = keep + __shfl_xor(send, mask, 64);
     }
   }
-  float t = v[0];
-  if (NV == 32) t += __shfl_xor(t, 1, 64);
-  return t;
 }
 
-__device__ __forceinline__ void unpack8(const uint4& q, float f[8]) {
-  f[0] = bf16_lo(q.x); f[1] = bf16_hi(q.x);
-  f[2] = bf16_lo(q.y); f[3] = bf16_hi(q.y);
-  f[4] = bf16_lo(q.z); f[5] = bf16_hi(q.z);
-  f[6] = bf16_lo(q.w); f[7] = bf16_hi(q.w);
+// projection that owns concatenated rank kk (ranks r[0], r[1], ... laid end to end);
+// off = its first concatenated rank
+__device__ __forceinline__ int rank_owner(const int32_t* r, int n, int kk, int& off) {
+  int p = 0;
+  off = 0;
+  while (p + 1 < n && kk >= off + r[p]) {
+    off += r[p];
+    ++p;
+  }
+  return p;
 }
 
-// ---------------------------------------------------------------- u = x A^T
-// RMAX: rank capacity (r <= RMAX); RPW rows per wave, RPW * RMAX in {32, 64}.
-template <int RMAX, int RPW>
-__global__ __launch_bounds__(256) void k_xa(const uint16_t* __restrict__ x, const uint16_t* __restrict__ A,
-                                            int T, int in_f, int r, float* __restrict__ u) {
-  constexpr int NV = RPW * RMAX;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * 4 + wave) * RPW;
-  if (t0 >= T) return;  // whole wave exits together
+__device__ __forceinline__ void unpack8(const u32x4& q, float f[8]) {
+  f[0] = bf16_lo(q[0]); f[1] = bf16_hi(q[0]);
+  f[2] = bf16_lo(q[1]); f[3] = bf16_hi(q[1]);
+  f[4] = bf16_lo(q[2]); f[5] = bf16_hi(q[2]);
+  f[6] = bf16_lo(q[3]); f[7] = bf16_hi(q[3]);
+}
+
+// ==================================================================== u = x A^T, v = dy B
+// RMAX: rank capacity of the job (R <= RMAX); RB rows of src per workgroup.
+template <int RMAX>
+struct RankCfg {
+  static constexpr int RB = 64 / RMAX;
+  static constexpr int NV = RB * RMAX;  // per-lane accumulators
+};
+
+template <int RMAX, int LAYOUT>
+__global__ __launch_bounds__(512) void k_rank_proj(const RankArgs args) {
+  constexpr int RB = RankCfg<RMAX>::RB, NV = RankCfg<RMAX>::NV;
+  __shared__ float part[8][NV];
+  __shared__ const uint16_t* wrow[RMAX];   // layout 0: row pointer of each concatenated rank
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const RankJob& J = args.job[blockIdx.y];
+  const int T = args.T, K = J.K, R = J.R, n = J.n;
+  const int t0 = blockIdx.x * RB;
+  if (t0 >= T) return;  // whole workgroup
+  if (LAYOUT == 0 && tid < RMAX) {
+    int off;
+    const int p = rank_owner(J.r, n, tid, off);
+    wrow[tid] = (tid < R) ? J.W[p] + (size_t)(tid - off) * K : nullptr;
+  }
+  __syncthreads();
+
   float acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-  const int nch = in_f / 8;
-  for (int c = lane; c < nch; c += 64) {
-    float xf[RPW][8];
+  const int nch = K / 8;
+  for (int c = 64 * wave + lane; c - lane < nch; c += 512) {  // wave-uniform trip count
+    const bool ok = c < nch;
+    const int cc = ok ? c : 0;
+    u32x4 xq[RB];
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
+    for (int rr = 0; rr < RB; ++rr) {
       const int t = (t0 + rr < T) ? t0 + rr : T - 1;
-      unpack8(*(const uint4*)(x + (size_t)t * in_f + 8 * c), xf[rr]);
+      xq[rr] = *(const u32x4*)(J.src + (size_t)t * K + 8 * cc);
+      if (!ok) xq[rr] = u32x4{0, 0, 0, 0};
     }
+    if (LAYOUT == 0) {
+      float xf[RB][8];
 #pragma unroll
-    for (int k = 0; k < RMAX; ++k) {
-      if (k < r) {
-        float af[8];
-        unpack8(*(const uint4*)(A + (size_t)k * in_f + 8 * c), af);
+      for (int rr = 0; rr < RB; ++rr) unpack8(xq[rr], xf[rr]);
 #pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-          float s = acc[rr * RMAX + k];
+      for (int k = 0; k < RMAX; ++k) {
+        if (k < R) {
+          float wf[8];
+          unpack8(*(const u32x4*)(wrow[k] + 8 * cc), wf);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s += xf[rr][e] * af[e];
-          acc[rr * RMAX + k] = s;
+          for (int rr = 0; rr < RB; ++rr) {
+            float s = acc[rr * RMAX + k];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += xf[rr][e] * wf[e];
+            acc[rr * RMAX + k] = s;
+          }
+        }
+      }
+    } else {
+      // B [K][r]: the lane's 8 rows are 8r contiguous bf16 (16r bytes); eight ranks of one
+      // row at a time
+      const uint16_t* bp = J.W[0] + (size_t)(8 * cc) * R;
+      const bool vec = R == RMAX && ((uintptr_t)J.W[0] & 15) == 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int k8 = 0; k8 < RMAX / 8; ++k8) {
+          if (8 * k8 < R) {
+            if (RMAX >= 32) __builtin_amdgcn_sched_barrier(0);  // bound the B rows in flight
+            float wf[8];
+            if (vec) {
+              unpack8(*(const u32x4*)(bp + e * RMAX + 8 * k8), wf);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) wf[j] = (8 * k8 + j < R) ? bf16_to_f32(bp[e * R + 8 * k8 + j]) : 0.f;
+            }
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+              const uint32_t wd = xq[rr][e >> 1];
+              const float xe = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) acc[rr * RMAX + 8 * k8 + j] += xe * wf[j];
+            }
+          }
         }
       }
     }
   }
-  const float tot = wave_reduce_scatter<NV>(acc, lane);
-  const int idx = (NV == 64) ? lane : (lane >> 1);
-  const int rr = idx / RMAX, k = idx % RMAX;
-  const bool writer = (NV == 64) || ((lane & 1) == 0);
-  if (writer && k < r && t0 + rr < T) u[(size_t)(t0 + rr) * r + k] = tot;
-}
-
-// ---------------------------------------------------------------- v = dy B
-template <int RMAX, int RPW>
-__global__ __launch_bounds__(256) void k_dyb(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ B,
-                                             int T, int out_f, int r, float* __restrict__ v) {
-  constexpr int NV = RPW * RMAX;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * 4 + wave) * RPW;
-  if (t0 >= T) return;
-  float acc[NV];
+  wave_reduce_scatter<NV>(acc, lane);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-  const int nch = out_f / 8;
-  const bool fast = (r == RMAX);
-  for (int c = lane; c < nch; c += 64) {
-    float df[RPW][8];
+  for (int j = 0; j < NV / 64; ++j) part[wave][lane * (NV / 64) + j] = acc[j];
+  __syncthreads();
+  if (tid < NV) {
+    float s = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int t = (t0 + rr < T) ? t0 + rr : T - 1;
-      unpack8(*(const uint4*)(dy + (size_t)t * out_f + 8 * c), df[rr]);
-    }
-    // rows 8c .. 8c+7 of B, each r bf16
-    const uint16_t* bp = B + (size_t)(8 * c) * r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float bf[RMAX];
-      if (fast) {
-#pragma unroll
-        for (int k8 = 0; k8 < RMAX / 8; ++k8) unpack8(*(const uint4*)(bp + e * RMAX + 8 * k8), bf + 8 * k8);
-      } else {
-#pragma unroll
-        for (int k = 0; k < RMAX; ++k) bf[k] = (k < r) ? bf16_to_f32(bp[e * r + k]) : 0.f;
-      }
-#pragma unroll
-      for (int rr = 0; rr < RPW; ++rr)
-#pragma unroll
-        for (int k = 0; k < RMAX; ++k) acc[rr * RMAX + k] += df[rr][e] * bf[k];
+    for (int w = 0; w < 8; ++w) s += part[w][tid];
+    const int rr = tid / RMAX, kk = tid % RMAX, t = t0 + rr;
+    if (kk < R && t < T) {
+      int off;
+      const int p = rank_owner(J.r, n, kk, off);
+      J.dst[p][(size_t)t * J.dst_stride[p] + (kk - off)] = s;
     }
   }
-  const float tot = wave_reduce_scatter<NV>(acc, lane);
-  const int idx = (NV == 64) ? lane : (lane >> 1);
-  const int rr = idx / RMAX, k = idx % RMAX;
-  const bool writer = (NV == 64) || ((lane & 1) == 0);
-  if (writer && k < r && t0 + rr < T) v[(size_t)(t0 + rr) * r + k] = tot;
 }
 
-// ---------------------------------------------------------------- dA / dB partials
-static inline int grad_nsplit(int T) {
-  int ns = (T + 63) / 64;
-  return ns < 1 ? 1 : (ns > 32 ? 32 : ns);
-}
+// ==================================================================== dA, dB partials
+template <int RMAX>
+struct GradCfg {
+  static constexpr int CPL = RMAX <= 32 ? 2 : 1;  // columns per lane
+  static constexpr int COLS = 64 * CPL;          // columns per workgroup
+};
 
-template <int RMAX, int COLS>
-__global__ __launch_bounds__(64) void k_grad_partial(const float* __restrict__ P, const uint16_t* __restrict__ Q,
-                                                     int T, int C, int r, int tchunk, float* __restrict__ part) {
-  const int lane = threadIdx.x;
-  const int c0 = (blockIdx.x * 64 + lane) * COLS;
+template <int RMAX>
+__global__ __launch_bounds__(256) void k_rank_grad(const GradArgs args) {
+  constexpr int CPL = GradCfg<RMAX>::CPL, COLS = GradCfg<RMAX>::COLS;
+  constexpr int NVAL = CPL * RMAX;
+  __shared__ float red[4][64 * NVAL];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const GradJob& J = args.job[blockIdx.z];
+  const int T = args.T, C = J.C, R = J.R;
+  const int cb = blockIdx.x * COLS;
+  if (cb >= C) return;  // whole workgroup (jobs have different widths)
   const int split = blockIdx.y;
-  const int tb = split * tchunk;
-  const int te = (tb + tchunk < T) ? tb + tchunk : T;
-  float acc[COLS][RMAX];
+  const int tb = split * args.tchunk;
+  const int te = tb + args.tchunk < T ? tb + args.tchunk : T;
+  // this wave's rows: a quarter of the workgroup's range
+  const int q4 = (te - tb + 3) / 4;
+  const int wb = tb + wave * q4;
+  const int we = wb + q4 < te ? wb + q4 : te;
+  const int c0 = cb + lane * CPL;
+  const bool ok = c0 < C;  // C is even when CPL == 2
+  const int cc = ok ? c0 : 0;
+
+  float acc[CPL][RMAX];
 #pragma unroll
-  for (int e = 0; e < COLS; ++e)
+  for (int e = 0; e < CPL; ++e)
 #pragma unroll
     for (int k = 0; k < RMAX; ++k) acc[e][k] = 0.f;
-  const bool ok = c0 < C;
-  const int cc = ok ? c0 : 0;
-  for (int t = tb; t < te; ++t) {
-    float q[COLS];
-    if (COLS == 2) {
-      const uint32_t w = *(const uint32_t*)(Q + (size_t)t * C + cc);
+  for (int t = wb; t < we; ++t) {
+    float q[CPL];
+    if (CPL == 2) {
+      const uint32_t w = *(const uint32_t*)(J.Q + (size_t)t * C + cc);
       q[0] = bf16_lo(w);
-      q[COLS - 1] = bf16_hi(w);
+      q[CPL - 1] = bf16_hi(w);
     } else {
-      q[0] = bf16_to_f32(Q[(size_t)t * C + cc]);
+      q[0] = bf16_to_f32(J.Q[(size_t)t * C + cc]);
     }
-    const float* pr = P + (size_t)t * r;
+    const float* pr = J.P + (size_t)t * J.pstride;  // wave-uniform row
 #pragma unroll
     for (int k = 0; k < RMAX; ++k) {
-      const float pk = (k < r) ? pr[k] : 0.f;
+      const float pk = (k < R) ? pr[k] : 0.f;
 #pragma unroll
-      for (int e = 0; e < COLS; ++e) acc[e][k] += pk * q[e];
+      for (int e = 0; e < CPL; ++e) acc[e][k] += pk * q[e];
     }
   }
-  if (!ok) return;
-  float* dst = part + ((size_t)split * C + c0) * r;
 #pragma unroll
-  for (int e = 0; e < COLS; ++e)
+  for (int e = 0; e < CPL; ++e)
 #pragma unroll
-    for (int k = 0; k < RMAX; ++k)
-      if (k < r) dst[e * r + k] = acc[e][k];
+    for (int k = 0; k < RMAX; ++k) red[wave][lane * NVAL + e * RMAX + k] = acc[e][k];
+  __syncthreads();
+  // fixed-order sum of the 4 waves; partial layout [split][c][R]
+  float* dst = J.part + (size_t)split * C * R;
+  for (int i = tid; i < 64 * NVAL; i += 256) {
+    const float s = red[0][i] + red[1][i] + red[2][i] + red[3][i];
+    const int l = i / NVAL, e = (i % NVAL) / RMAX, k = i % RMAX;
+    const int c = cb + l * CPL + e;
+    if (c < C && k < R) dst[(size_t)c * R + k] = s;
+  }
 }
 
-__global__ __launch_bounds__(256) void k_grad_reduce(const float* __restrict__ part, int nsplit, int C, int r,
-                                                     float scale, int transpose_out, int accumulate,
-                                                     float* __restrict__ G) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over C * r in [c][k] order
-  const int64_t n = (int64_t)C * r;
+// G_p = s_p * sum over splits, written [r_p][C] (transpose) or [C][r_p]; one thread per
+// (job, c, k) of the concatenated ranks
+__global__ __launch_bounds__(256) void k_rank_grad_reduce(const GradArgs args) {
+  const GradJob& J = args.job[blockIdx.y];
+  const int64_t n = (int64_t)J.C * J.R;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   float s = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) s += part[(size_t)sp * n + idx];
-  s *= scale;
-  const int c = (int)(idx / r), k = (int)(idx % r);
-  const size_t o = transpose_out ? (size_t)k * C + c : (size_t)idx;
-  G[o] = accumulate ? G[o] + s : s;
+  for (int sp = 0; sp < args.nsplit; ++sp) s += J.part[(size_t)sp * n + idx];
+  const int c = (int)(idx / J.R), kk = (int)(idx % J.R);
+  int off;
+  const int p = rank_owner(J.r, J.n, kk, off);
+  float* G = J.G[p];
+  if (G == nullptr) return;  // this weight's gradient was not asked for
+  const int k = kk - off, r = J.r[p];
+  s *= J.scale[p];
+  const size_t o = J.transpose ? (size_t)k * J.C + c : (size_t)c * r + k;
+  G[o] = args.accumulate ? G[o] + s : s;
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
@@ -198,7 +261,9 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
   if (i < n) p[i] = 0.f;
 }
 
-// ---------------------------------------------------------------- launchers
+// ==================================================================== launchers
+static int rank_cap(int R) { return R <= 8 ? 8 : R <= 16 ? 16 : R <= 32 ? 32 : 64; }
+
 // Zero-fill with a kernel rather than a memset node, so the call is safe to capture.
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -206,61 +271,83 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_xa(const uint16_t* x, const uint16_t* A, int32_t T, int32_t in_f, int32_t r, float* u,
-                     hipStream_t s) {
-  if (T <= 0 || r <= 0) return hipSuccess;
-  const dim3 blk(256);
-  if (r <= 8) hipLaunchKernelGGL((k_xa<8, 4>), dim3((T + 15) / 16), blk, 0, s, x, A, T, in_f, r, u);
-  else if (r <= 16) hipLaunchKernelGGL((k_xa<16, 2>), dim3((T + 7) / 8), blk, 0, s, x, A, T, in_f, r, u);
-  else if (r <= 32) hipLaunchKernelGGL((k_xa<32, 1>), dim3((T + 3) / 4), blk, 0, s, x, A, T, in_f, r, u);
-  else hipLaunchKernelGGL((k_xa<64, 1>), dim3((T + 3) / 4), blk, 0, s, x, A, T, in_f, r, u);
-  return hipGetLastError();
-}
-
-hipError_t launch_dyb(const uint16_t* dy, const uint16_t* B, int32_t T, int32_t out_f, int32_t r, float* v,
-                      hipStream_t s) {
-  if (T <= 0 || r <= 0) return hipSuccess;
-  const dim3 blk(256);
-  if (r <= 8) hipLaunchKernelGGL((k_dyb<8, 4>), dim3((T + 15) / 16), blk, 0, s, dy, B, T, out_f, r, v);
-  else if (r <= 16) hipLaunchKernelGGL((k_dyb<16, 2>), dim3((T + 7) / 8), blk, 0, s, dy, B, T, out_f, r, v);
-  else if (r <= 32) hipLaunchKernelGGL((k_dyb<32, 1>), dim3((T + 3) / 4), blk, 0, s, dy, B, T, out_f, r, v);
-  else hipLaunchKernelGGL((k_dyb<64, 1>), dim3((T + 3) / 4), blk, 0, s, dy, B, T, out_f, r, v);
-  return hipGetLastError();
-}
-
-size_t grad_workspace_bytes(int32_t T, int32_t C, int32_t r) {
-  if (T <= 0 || r <= 0 || C <= 0) return 0;
-  return (size_t)grad_nsplit(T) * (size_t)C * (size_t)r * sizeof(float);
-}
-
-hipError_t launch_grad(const float* P, const uint16_t* Q, int32_t T, int32_t C, int32_t r, float scale,
-                       int32_t transpose_out, int32_t accumulate, float* G, float* partial, hipStream_t s) {
-  if (r <= 0 || C <= 0) return hipSuccess;
-  if (T <= 0) {
-    // empty reduction: the gradient is zero (or unchanged when accumulating)
-    if (!accumulate) return launch_fill_zero(G, (int64_t)C * r, s);
-    return hipSuccess;
+template <int LAYOUT>
+static hipError_t launch_rank_layout(const RankArgs& a, int rmax, hipStream_t s) {
+  const dim3 blk(512);
+  switch (rmax) {
+    case 8:
+      hipLaunchKernelGGL((k_rank_proj<8, LAYOUT>), dim3((a.T + RankCfg<8>::RB - 1) / RankCfg<8>::RB, a.n_jobs), blk,
+                         0, s, a);
+      break;
+    case 16:
+      hipLaunchKernelGGL((k_rank_proj<16, LAYOUT>), dim3((a.T + RankCfg<16>::RB - 1) / RankCfg<16>::RB, a.n_jobs),
+                         blk, 0, s, a);
+      break;
+    case 32:
+      hipLaunchKernelGGL((k_rank_proj<32, LAYOUT>), dim3((a.T + RankCfg<32>::RB - 1) / RankCfg<32>::RB, a.n_jobs),
+                         blk, 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((k_rank_proj<64, LAYOUT>), dim3((a.T + RankCfg<64>::RB - 1) / RankCfg<64>::RB, a.n_jobs),
+                         blk, 0, s, a);
+      break;
   }
-  const int ns = grad_nsplit(T);
-  const int tchunk = (T + ns - 1) / ns;
-  if (r <= 8) {
-    const dim3 grid((C + 127) / 128, ns);
-    hipLaunchKernelGGL((k_grad_partial<8, 2>), grid, dim3(64), 0, s, P, Q, T, C, r, tchunk, partial);
-  } else if (r <= 16) {
-    const dim3 grid((C + 127) / 128, ns);
-    hipLaunchKernelGGL((k_grad_partial<16, 2>), grid, dim3(64), 0, s, P, Q, T, C, r, tchunk, partial);
-  } else if (r <= 32) {
-    const dim3 grid((C + 63) / 64, ns);
-    hipLaunchKernelGGL((k_grad_partial<32, 1>), grid, dim3(64), 0, s, P, Q, T, C, r, tchunk, partial);
-  } else {
-    const dim3 grid((C + 63) / 64, ns);
-    hipLaunchKernelGGL((k_grad_partial<64, 1>), grid, dim3(64), 0, s, P, Q, T, C, r, tchunk, partial);
+  return hipGetLastError();
+}
+
+// every job of one launch must have the same layout
+hipError_t launch_rank_proj(const RankArgs& a, hipStream_t s) {
+  if (a.T <= 0 || a.n_jobs <= 0) return hipSuccess;
+  int rmax = 8;
+  for (int j = 0; j < a.n_jobs; ++j) rmax = rank_cap(a.job[j].R) > rmax ? rank_cap(a.job[j].R) : rmax;
+  return a.job[0].layout == 0 ? launch_rank_layout<0>(a, rmax, s) : launch_rank_layout<1>(a, rmax, s);
+}
+
+int grad_nsplit(int T) {
+  int ns = T / 128;
+  return ns < 1 ? 1 : (ns > 8 ? 8 : ns);
+}
+
+size_t grad_partial_bytes(int32_t T, int32_t C, int32_t R) {
+  if (T <= 0 || R <= 0 || C <= 0) return 0;
+  return (size_t)grad_nsplit(T) * (size_t)C * (size_t)R * sizeof(float);
+}
+
+hipError_t launch_rank_grad(const GradArgs& a0, hipStream_t s) {
+  if (a0.T <= 0 || a0.n_jobs <= 0) return hipSuccess;
+  GradArgs a = a0;
+  a.nsplit = grad_nsplit(a.T);
+  a.tchunk = (a.T + a.nsplit - 1) / a.nsplit;
+  int rmax = 8, cmax = 0;
+  int64_t nmax = 0;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    rmax = rank_cap(a.job[j].R) > rmax ? rank_cap(a.job[j].R) : rmax;
+    cmax = a.job[j].C > cmax ? a.job[j].C : cmax;
+    const int64_t n = (int64_t)a.job[j].C * a.job[j].R;
+    nmax = n > nmax ? n : nmax;
+  }
+  const dim3 blk(256);
+  switch (rmax) {
+    case 8:
+      hipLaunchKernelGGL(k_rank_grad<8>, dim3((cmax + GradCfg<8>::COLS - 1) / GradCfg<8>::COLS, a.nsplit, a.n_jobs),
+                         blk, 0, s, a);
+      break;
+    case 16:
+      hipLaunchKernelGGL(k_rank_grad<16>, dim3((cmax + GradCfg<16>::COLS - 1) / GradCfg<16>::COLS, a.nsplit, a.n_jobs),
+                         blk, 0, s, a);
+      break;
+    case 32:
+      hipLaunchKernelGGL(k_rank_grad<32>, dim3((cmax + GradCfg<32>::COLS - 1) / GradCfg<32>::COLS, a.nsplit, a.n_jobs),
+                         blk, 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL(k_rank_grad<64>, dim3((cmax + GradCfg<64>::COLS - 1) / GradCfg<64>::COLS, a.nsplit, a.n_jobs),
+                         blk, 0, s, a);
+      break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)C * r;
-  hipLaunchKernelGGL(k_grad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, partial, ns, C, r, scale,
-                     transpose_out, accumulate, G);
+  hipLaunchKernelGGL(k_rank_grad_reduce, dim3((unsigned)((nmax + 255) / 256), a.n_jobs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

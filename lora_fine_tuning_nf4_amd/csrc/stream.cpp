@@ -37,6 +37,9 @@ struct lnf4_stream {
   std::vector<char> release_recorded;
   hipEvent_t slot_release = nullptr, slot_done = nullptr;
   bool slot_loaded = false;
+  int slot_part_next = 0;    // next part of a load issued in parts (0: none under way)
+  int slot_part_n = 0;
+  int slot_part_shard = -1;
   int next_call = 0;
   int issued = 0;
   int pass = 0;
@@ -222,6 +225,7 @@ int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute) {
   if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
   if (shard < 0 || shard >= (int)st->host.size()) return fail(LNF4_EINVAL, "%s: shard %d out of range", who, (int)shard);
   if (st->bytes[shard] > st->slot_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds the slot (%zu)", who, (int)shard, st->bytes[shard], st->slot_bytes);
+  if (st->slot_part_next != 0) return fail(LNF4_ESTATE, "%s: a part-wise slot load is under way", who);
   hipError_t e;
   if ((e = hipEventRecord(st->slot_release, compute)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(slot_release)");
   if ((e = hipStreamWaitEvent(st->copy, st->slot_release, 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(slot_release)");
@@ -235,11 +239,56 @@ int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute) {
   return LNF4_OK;
 }
 
+int stream_slot_load_part(lnf4_stream* st, int32_t shard, int32_t part, int32_t n_parts, hipStream_t compute) {
+  const char* who = "stream_slot_load_part";
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
+  if (shard < 0 || shard >= (int)st->host.size()) return fail(LNF4_EINVAL, "%s: shard %d out of range", who, (int)shard);
+  if (n_parts < 1 || n_parts > 1024 || part < 0 || part >= n_parts)
+    return fail(LNF4_EINVAL, "%s: part %d of %d out of range (1 <= n_parts <= 1024)", who, (int)part, (int)n_parts);
+  if (st->bytes[shard] > st->slot_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds the slot (%zu)", who, (int)shard, st->bytes[shard], st->slot_bytes);
+  if (part != st->slot_part_next || (part > 0 && (shard != st->slot_part_shard || n_parts != st->slot_part_n)))
+    return fail(LNF4_ESTATE, "%s: expected part %d of the load under way, got part %d of %d (shard %d)", who,
+                st->slot_part_next, (int)part, (int)n_parts, (int)shard);
+  // part p covers bytes [p*chunk, min((p+1)*chunk, size)), chunk rounded up to 4 KiB
+  const size_t size = st->bytes[shard];
+  const size_t chunk = ((size + (size_t)n_parts - 1) / (size_t)n_parts + 4095) & ~(size_t)4095;
+  const size_t b0 = (size_t)part * chunk < size ? (size_t)part * chunk : size;
+  const size_t b1 = b0 + chunk < size ? b0 + chunk : size;
+  hipError_t e;
+  if (part == 0) {
+    // the slot's previous user is the compute work enqueued so far
+    if ((e = hipEventRecord(st->slot_release, compute)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(slot_release)");
+    if ((e = hipStreamWaitEvent(st->copy, st->slot_release, 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(slot_release)");
+    st->slot_loaded = false;  // a wait now would see a half-written slot
+  }
+  if (b1 > b0) {
+    if ((e = hipMemcpyAsync((uint8_t*)st->slot + b0, (const uint8_t*)st->host[shard] + b0, b1 - b0,
+                            hipMemcpyHostToDevice, st->copy)) != hipSuccess)
+      return hip_fail(e, "stream: hipMemcpyAsync (slot part)");
+  }
+  st->bytes_copied += (int64_t)(b1 - b0);
+  log_ev(st, LNF4_EV_SLOT_COPY, st->next_call, st->slot_loads, shard, -1 - part, part == 0 ? st->slot_loads - 1 : -1);
+  if (part + 1 < n_parts) {
+    st->slot_part_next = part + 1;
+    st->slot_part_n = n_parts;
+    st->slot_part_shard = shard;
+    return LNF4_OK;
+  }
+  if ((e = hipEventRecord(st->slot_done, st->copy)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(slot_done)");
+  st->slot_part_next = 0;
+  st->slot_part_n = 0;
+  st->slot_part_shard = -1;
+  st->slot_loads += 1;
+  st->slot_loaded = true;
+  return LNF4_OK;
+}
+
 int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out) {
   const char* who = "stream_slot_wait";
   if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
-  if (!st->slot_loaded) return fail(LNF4_ESTATE, "%s: no slot load issued", who);
+  if (!st->slot_loaded) return fail(LNF4_ESTATE, "%s: no complete slot load issued", who);
   hipError_t e = hipStreamWaitEvent(compute, st->slot_done, 0);
   if (e != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(slot_done)");
   log_ev(st, LNF4_EV_SLOT_WAIT, st->next_call, st->slot_loads - 1, -1, -1, st->slot_loads - 1);

@@ -81,6 +81,7 @@ def _declare(L):
                                 POINTER(c_int32), i32, i32, vp, vp, sz, POINTER(c_void_p)]),
         "stream_layer_step": (i32, [vp, i32, vp, POINTER(c_void_p)]),
         "stream_slot_load": (i32, [vp, i32, vp]),
+        "stream_slot_load_part": (i32, [vp, i32, i32, i32, vp]),
         "stream_slot_wait": (i32, [vp, vp, POINTER(c_void_p)]),
         "stream_reset": (i32, [vp, vp]),
         "stream_log": (i32, [vp, POINTER(lnf4_stream_event), i32, POINTER(c_int32)]),
@@ -239,6 +240,10 @@ def stream_layer_step(st, k: int, compute=None) -> int:
 
 def stream_slot_load(st, shard: int, compute=None):
     _check(lib().stream_slot_load(st, shard, _stream(compute)))
+
+
+def stream_slot_load_part(st, shard: int, part: int, n_parts: int, compute=None):
+    _check(lib().stream_slot_load_part(st, shard, part, n_parts, _stream(compute)))
 
 
 def stream_slot_wait(st, compute=None) -> int:

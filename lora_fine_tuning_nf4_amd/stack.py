@@ -126,6 +126,7 @@ class StreamedStack:
         self.st = lnf4.stream_create(shards, sizes, self.bufs, self.shard_bytes, sched, 0, self.copy, self.slot,
                                      slot_bytes)
         self.timers = None
+        self._embed_in_slot = False   # the next step's embed_tokens was loaded during the last backward
         self.st_res = None
         self.res_bufs = None
 
@@ -206,8 +207,10 @@ class StreamedStack:
         st = self.enable_resident() if resident else self.st
         slot = self.slot is not None and not resident
         if slot:
-            lnf4.stream_slot_load(st, self.head_ids[0], self.compute)   # embed_tokens
+            if not self._embed_in_slot:   # first step: nothing trickled in yet
+                lnf4.stream_slot_load(st, self.head_ids[0], self.compute)   # embed_tokens
             lnf4.stream_slot_wait(st, self.compute)
+            self._embed_in_slot = False
         n_fwd = 2 * L if self.dpo else L
         for k, layer in enumerate(self.schedule):
             base = lnf4.stream_layer_step(st, k, self.compute)
@@ -220,11 +223,17 @@ class StreamedStack:
                     lnf4.stream_slot_load(st, self.head_ids[1], self.compute)
                     lnf4.stream_slot_wait(st, self.compute)
             else:
+                if slot:
+                    # the backward is compute-bound: the next step's embed_tokens trickles into
+                    # the slot in one piece per layer, between the layer copies
+                    lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L, self.compute)
                 for gi in range(len(GROUPS)):          # recompute from the checkpointed inputs
                     self._group_fwd(layer, gi, base, adapters=True)
                 for gi in reversed(range(len(GROUPS))):
                     self._group_bwd(layer, gi, base)
         lnf4.stream_reset(st, self.compute)
+        if slot:
+            self._embed_in_slot = True
 
     def log(self):
         return lnf4.stream_log(self.st)

@@ -130,4 +130,7 @@ def test_stream_validation(L):
     assert L.stream_create(hs, sb, 2, db2, 4096, 2, sc, 4, 0, None, None, 0, ctypes.byref(out)) == lnf4.LNF4_EALIGN
     p = ctypes.c_void_p()
     assert L.stream_layer_step(None, 0, None, ctypes.byref(p)) == lnf4.LNF4_ESTATE
+    assert L.stream_slot_load_part(None, 0, 0, 4, None) == lnf4.LNF4_ESTATE
+    assert L.stream_slot_load(None, 0, None) == lnf4.LNF4_ESTATE
+    assert L.stream_slot_wait(None, None, ctypes.byref(p)) == lnf4.LNF4_ESTATE
     assert L.stream_destroy(None) == lnf4.LNF4_OK

@@ -171,3 +171,34 @@ def test_stack_step_matches_oracle(dpo):
                               f"dx group {gi}")
     finally:
         stack.close()
+
+
+@pytest.mark.parametrize("n_parts", [1, 3, 7])
+def test_slot_load_in_parts(n_parts):
+    L, nbytes, slot_bytes = 3, 4096, 3 * 4096 + 100
+    shards = _pinned_shards(L, nbytes, seed=11)
+    head = _pinned_shards(1, slot_bytes - 100, seed=12)[0]
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    slot = torch.zeros(slot_bytes, dtype=torch.uint8, device="cuda")
+    comp = torch.cuda.current_stream()
+    st = lnf4.stream_create(shards + [head], [nbytes] * L + [head.numel()], bufs, nbytes, [0, 1, 2], 0,
+                            torch.cuda.Stream(), slot, slot_bytes)
+    try:
+        b0 = lnf4.stream_bytes_copied(st)
+        for part in range(n_parts):
+            if part > 0:
+                with pytest.raises(lnf4.LNF4Error) as ei:   # the load is not complete yet
+                    lnf4.stream_slot_wait(st, comp)
+                assert ei.value.code == lnf4.LNF4_ESTATE
+            with pytest.raises(lnf4.LNF4Error):              # parts go in order
+                lnf4.stream_slot_load_part(st, L, part + 1, n_parts, comp)
+            lnf4.stream_slot_load_part(st, L, part, n_parts, comp)
+        p = lnf4.stream_slot_wait(st, comp)
+        assert p == slot.data_ptr()
+        assert torch.equal(slot[:head.numel()].cpu(), head)
+        assert lnf4.stream_bytes_copied(st) - b0 == head.numel()
+        ev = [e for e in lnf4.stream_log(st) if e[0] == lnf4.EV_SLOT_COPY]
+        assert [e[4] for e in ev] == [-1 - q for q in range(n_parts)]
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st)
