@@ -36,6 +36,10 @@ constexpr int kGroupM = 4;   // row-tiles per group of the tile order (tile_coor
 // largest rank (summed over a group in backward) the fused epilogue stages in LDS
 #define LNF4_EPI_RANK 64
 
+// 16-byte-segment swizzle of a 128-byte code row (consecutive row pairs share it, so 16
+// consecutive rows cover all 64 banks in a transposing read)
+__device__ __forceinline__ int wswz(int row) { return (row >> 1) & 7; }
+
 __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -670,6 +674,336 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx(const DxArgs args) {
 }
 
 // =====================================================================================
+// Input gradient, NF4 weights: direct-to-LDS ring with transposing code reads
+// =====================================================================================
+// dx [T][N] = sum over the group's K space (the projections' out rows) of dy . W'.
+// The MFMA B operand needs 8 consecutive K (= 8 weight rows) of one column per lane, but
+// the codes hold each row's columns contiguously.  The code tile [64 rows][256 cols] goes
+// to LDS row-major by direct loads and is read back with ds_read_b64_tr_b4: in each group
+// of 16 lanes, lane j names one 8-byte run (16 codes of one row) and lane i receives the
+// i-th code of each of the 16 runs, i.e. 16 consecutive rows of one column.  With the
+// high-nibble-first packing, code position i of a run is column i ^ 1, so lane l32 holds
+// column l32 ^ 1 of its 32-column group; the accumulator columns follow that order.
+// Each decoded value uses its own row's absmax (one fp32 product, one RNE, as in the
+// forward).  absmax arrives as one 64-row column per wave ([wave][row], 4-byte loads).
+template <int BM>
+__global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
+  constexpr int MI = BM / 32;
+  constexpr int NM = 2 * MI;
+  constexpr int X_BYTES = BM * BK * 2;     // dy tile [BM][64] bf16
+  constexpr int W_BYTES = BK * BN / 2;     // codes [64][128 B]
+  constexpr int A_BYTES = 4 * BK * 4;      // absmax [4 waves][64 rows] fp32
+  constexpr int STAGE_RAW = X_BYTES + W_BYTES + A_BYTES;
+  constexpr int SLAB_U = BM * LNF4_EPI_RANK * 2, SLAB_V = BN * LNF4_EPI_RANK * 2;
+  constexpr int SLAB = SLAB_U > SLAB_V ? SLAB_U : SLAB_V;
+  constexpr int STAGE = STAGE_RAW > SLAB ? STAGE_RAW : SLAB;
+  static_assert(3 * STAGE + 2048 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+  // byte-pair code table in transposed order: a byte of a transposed read holds rows 2b
+  // (low nibble) and 2b+1 (high nibble) of one column
+  __shared__ __attribute__((aligned(16))) float2 lut2[256];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  lut2[tid] = make_float2(c_gemm_table[tid & 15], c_gemm_table[tid >> 4]);  // NTHR == 256
+
+  int tm, tn;
+  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  const int M = args.M, N = args.N;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkb = args.total_kb;
+  // this lane's two accumulator columns within the tile (see the header comment)
+  const int nc0 = 64 * wave + (l32 ^ 1), nc1 = nc0 + 32;
+
+  // ---- accumulators start at the rank-R LoRA term (ranks of the group concatenated)
+  floatx16 acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  int R = 0;
+  for (int pi = 0; pi < args.n_proj; ++pi) {
+    const DxProj P = select_dx(args, pi);
+    if (P.v != nullptr && P.r > 0) R += P.r;
+  }
+  if (R > 0) {
+    const int RP = (R + 15) & ~15;
+    uint16_t* Uh = (uint16_t*)sm0;
+    uint16_t* Ul = (uint16_t*)sm1;
+    uint16_t* V = (uint16_t*)sm2;
+    for (int idx = tid; idx < BM * RP; idx += NTHR) Uh[idx] = Ul[idx] = 0;
+    for (int idx = tid; idx < BN * RP; idx += NTHR) V[idx] = 0;
+    __syncthreads();
+    int off = 0;
+    for (int pi = 0; pi < args.n_proj; ++pi) {
+      const DxProj P = select_dx(args, pi);
+      if (P.v == nullptr || P.r <= 0) continue;
+      const int r = P.r;
+      for (int idx = tid; idx < BM * r; idx += NTHR) {
+        const int mm = idx / r, kk = idx - mm * r, gm = m0 + mm;
+        if (gm < M) split_bf16(P.scale * P.v[(size_t)gm * P.v_stride + kk], Uh[mm * RP + off + kk], Ul[mm * RP + off + kk]);
+      }
+      for (int idx = tid; idx < BN * r; idx += NTHR) {
+        const int kk = idx / BN, nn = idx - kk * BN, n = n0 + nn;
+        if (n < N) V[nn * RP + off + kk] = P.A[(size_t)kk * N + n];
+      }
+      off += r;
+    }
+    __syncthreads();
+    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+    __syncthreads();
+  }
+
+  // ---- direct global -> LDS loads of one K-block (64 rows of one projection)
+  //  * dy: load q of wave w fills tile rows (w*XQ+q)*8 .. +7 (as the forward's x)
+  //  * codes: load q of wave w fills weight rows 16w+8q .. +7; lane L -> row 16w+8q+L/8,
+  //    16-byte slot L%8 holding logical segment (L%8) ^ wswz(row)
+  //  * absmax: one 4-byte load per wave, lane L -> row L of the wave's 64-column block
+  //  Rows past the projection's out_f and columns past N read clamped addresses; their
+  //  weights are zeroed by the decode (rows) or their outputs dropped (columns).
+  constexpr int XQ = X_BYTES / 1024 / 4;
+  constexpr int NLD = XQ + 3;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int halfN = N / 2, nblk = N / 64;
+  const int cbyte_max = halfN - 16;
+  const int ablk = (n0 / 64 + wave) < nblk ? n0 / 64 + wave : nblk - 1;
+
+#define LNF4_DXQ_PROJ(kb_, P_)                                                   \
+  int pi_ = 0;                                                                   \
+  _Pragma("unroll") for (int q = 1; q < kMaxGroup; ++q) if (q < args.n_proj && (kb_) >= args.p[q].kb0) pi_ = q; \
+  pi_ = __builtin_amdgcn_readfirstlane(pi_);                                     \
+  const DxProj& P_ = args.p[pi_];
+
+#define LNF4_DXQ_ISSUE(kb_, SM_)                                                                 \
+  {                                                                                              \
+    LNF4_DXQ_PROJ(kb_, Pi_)                                                                      \
+    const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q) {                                             \
+      const int row = (wave * XQ + q) * 8 + (lane >> 3);                                        \
+      const int gr = m0 + row < M ? m0 + row : M - 1;                                            \
+      const int oc = k0_ + 8 * ((lane & 7) ^ act_swz(row));                                      \
+      const int o = oc < Kp_ - 8 ? oc : Kp_ - 8;                                                 \
+      __builtin_amdgcn_global_load_lds((const void*)(Pi_.dy + (size_t)gr * Kp_ + o),             \
+                                       (lds_ptr)((SM_) + (wave_u * XQ + q) * 1024), 16, 0, 0);   \
+    }                                                                                            \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                              \
+      const int row = 16 * wave + 8 * q + (lane >> 3);                                           \
+      const int gk = k0_ + row < Kp_ ? k0_ + row : Kp_ - 1;                                      \
+      const int cb = n0 / 2 + 16 * ((lane & 7) ^ wswz(row));                                     \
+      const int cbc = cb < cbyte_max ? cb : cbyte_max;                                           \
+      __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)Pi_.w + (size_t)gk * halfN + cbc), \
+                                       (lds_ptr)((SM_) + X_BYTES + (wave_u * 2 + q) * 1024), 16, 0, 0); \
+    }                                                                                            \
+    {                                                                                            \
+      const int gk = k0_ + lane < Kp_ ? k0_ + lane : Kp_ - 1;                                    \
+      __builtin_amdgcn_global_load_lds((const void*)(Pi_.absmax + (size_t)gk * nblk + ablk),     \
+                                       (lds_ptr)((SM_) + X_BYTES + W_BYTES + wave_u * 256), 4, 0, 0); \
+    }                                                                                            \
+  }
+#define LNF4_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define LNF4_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  // transposed code reads of one stage: cw[s] = 8 codes (rows 32h+8s .. +7) of the column
+  const int trow0 = 32 * h + (lane & 15), trow1 = trow0 + 16;
+  const int tpart = 8 * ((lane >> 4) & 1);
+  const int toff00 = trow0 * 128 + 16 * ((2 * wave + 0) ^ wswz(trow0)) + tpart;
+  const int toff01 = trow1 * 128 + 16 * ((2 * wave + 0) ^ wswz(trow1)) + tpart;
+  const int toff10 = trow0 * 128 + 16 * ((2 * wave + 1) ^ wswz(trow0)) + tpart;
+  const int toff11 = trow1 * 128 + 16 * ((2 * wave + 1) ^ wswz(trow1)) + tpart;
+#define LNF4_TR4(SM_, off_) \
+  __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i_t*)((SM_) + X_BYTES + (off_)))
+#define LNF4_DXQ_CODES(SM_, c0_, c1_)                              \
+  {                                                                \
+    const v2i_t a_ = LNF4_TR4(SM_, toff00), b_ = LNF4_TR4(SM_, toff01); \
+    const v2i_t c_ = LNF4_TR4(SM_, toff10), d_ = LNF4_TR4(SM_, toff11); \
+    c0_ = u32x4{(uint32_t)a_.x, (uint32_t)a_.y, (uint32_t)b_.x, (uint32_t)b_.y}; \
+    c1_ = u32x4{(uint32_t)c_.x, (uint32_t)c_.y, (uint32_t)d_.x, (uint32_t)d_.y}; \
+  }
+  // absmax of rows 32h+8s .. +7 of this wave's column block
+#define LNF4_DXQ_SCALES(SM_, s_, a_)                                                              \
+  {                                                                                              \
+    const float* ap_ = (const float*)((SM_) + X_BYTES + W_BYTES + wave * 256) + 32 * h + 8 * (s_); \
+    const floatx4 lo_ = *(const floatx4*)ap_, hi_ = *(const floatx4*)(ap_ + 4);                  \
+    a_[0] = lo_[0]; a_[1] = lo_[1]; a_[2] = lo_[2]; a_[3] = lo_[3];                             \
+    a_[4] = hi_[0]; a_[5] = hi_[1]; a_[6] = hi_[2]; a_[7] = hi_[3];                             \
+  }
+#define LNF4_LUT8X(lv, cw_)                                                        \
+  {                                                                                \
+    const uint32_t c_ = (cw_);                                                     \
+    _Pragma("unroll") for (int b_ = 0; b_ < 4; ++b_) {                             \
+      const float2 p_ = lut2[(c_ >> (8 * b_)) & 255u];                             \
+      lv[2 * b_] = p_.x;                                                           \
+      lv[2 * b_ + 1] = p_.y;                                                       \
+    }                                                                              \
+  }
+#define LNF4_FIN8X(dst, lv, a_)                                                    \
+  dst = as_bf16x8(pack_bf16x2(lv[0] * a_[0], lv[1] * a_[1]), pack_bf16x2(lv[2] * a_[2], lv[3] * a_[3]), \
+                  pack_bf16x2(lv[4] * a_[4], lv[5] * a_[5]), pack_bf16x2(lv[6] * a_[6], lv[7] * a_[7]));
+  // rows of step s past the projection's out_f decode to zero (out_f is a multiple of 8,
+  // so the 8 rows of a step are all in or all out)
+#define LNF4_DXQ_MASK(a_, k0_, Kp_, s_)                                             \
+  {                                                                                \
+    const bool in_ = (k0_) + 32 * h + 8 * (s_) < (Kp_);                            \
+    _Pragma("unroll") for (int e_ = 0; e_ < 8; ++e_) a_[e_] = in_ ? a_[e_] : 0.0f; \
+  }
+#define LNF4_XS(SM_) ((const uint16_t*)(SM_))
+
+  // prologue: blocks 0 and 1 in flight; block 0 visible
+  LNF4_DXQ_ISSUE(0, sm0);
+  LNF4_DXQ_ISSUE((nkb > 1 ? 1 : 0), sm1);
+  LNF4_WAIT_VM(NLD);
+  __syncthreads();
+
+  int kc0, kcp;  // K offset within its projection and that projection's out_f, current block
+  {
+    LNF4_DXQ_PROJ(0, P0_)
+    kc0 = (0 - P0_.kb0) * BK;
+    kcp = P0_.out_f;
+  }
+  bf16x8 ac[MI], an_[MI];
+  bf16x8 bc0, bc1, bn0, bn1;
+  u32x4 cw0, cw1;
+  {
+    LNF4_DXQ_CODES(sm0, cw0, cw1);
+    float l0[8], l1[8], a[8];
+    LNF4_LUT8X(l0, cw0[0]);
+    LNF4_LUT8X(l1, cw1[0]);
+    LNF4_DXQ_SCALES(sm0, 0, a);
+    LNF4_DXQ_MASK(a, kc0, kcp, 0);
+    LNF4_FIN8X(bc0, l0, a);
+    LNF4_FIN8X(bc1, l1, a);
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(32 * i + l32, 4 * h)];
+
+#define LNF4_DXQ_BLOCK(SC, SN, SP)                                                             \
+  {                                                                                            \
+    LNF4_DXQ_ISSUE((kb + 2 < nkb ? kb + 2 : nkb - 1), SP);                                     \
+    int kn0, knp; /* the next block's K offset and out_f */                                    \
+    {                                                                                          \
+      const int kbn_ = kb + 1 < nkb ? kb + 1 : kb;                                             \
+      LNF4_DXQ_PROJ(kbn_, Pn_)                                                                 \
+      kn0 = (kbn_ - Pn_.kb0) * BK;                                                             \
+      knp = Pn_.out_f;                                                                         \
+    }                                                                                          \
+    u32x4 nw0, nw1;                                                                            \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 3) {                                                                            \
+        LNF4_WAIT_VM_LGKM0(NLD);                                                               \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
+      float l0[8], l1[8], a[8];                                                                \
+      if (s < 3) {                                                                             \
+        LNF4_LUT8X(l0, cw0[s + 1 < 4 ? s + 1 : 0]);                                            \
+        LNF4_LUT8X(l1, cw1[s + 1 < 4 ? s + 1 : 0]);                                            \
+        LNF4_DXQ_SCALES(SC, (s + 1 < 4 ? s + 1 : 0), a);                                       \
+      } else {                                                                                 \
+        LNF4_DXQ_CODES(SN, nw0, nw1);                                                          \
+        LNF4_LUT8X(l0, nw0[0]);                                                                \
+        LNF4_LUT8X(l1, nw1[0]);                                                                \
+        LNF4_DXQ_SCALES(SN, 0, a);                                                             \
+      }                                                                                        \
+      if (s < 3) {                                                                             \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
+            *(const bf16x8*)&LNF4_XS(SC)[act_pos(32 * i + l32, 4 * h + s + 1)];                \
+      } else {                                                                                 \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
+            *(const bf16x8*)&LNF4_XS(SN)[act_pos(32 * i + l32, 4 * h)];                        \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
+        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
+        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+      }                                                                                        \
+      if (s < 3) {                                                                             \
+        LNF4_DXQ_MASK(a, kc0, kcp, s + 1);                                                     \
+      } else {                                                                                 \
+        LNF4_DXQ_MASK(a, kn0, knp, 0);                                                         \
+      }                                                                                        \
+      LNF4_FIN8X(bn0, l0, a);                                                                  \
+      LNF4_FIN8X(bn1, l1, a);                                                                  \
+      _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                          \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                                     \
+      }                                                                                        \
+      _Pragma("unroll") for (int g = 4; g < NM - NM / 4; ++g) {                                \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, (MI + (NM - NM / 4 - 4) - 1) / (NM - NM / 4 - 4), 0); \
+      }                                                                                        \
+      _Pragma("unroll") for (int g = NM - NM / 4; g < NM; ++g) {                               \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x002, (32 + NM / 4 - 1) / (NM / 4), 0);          \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) ac[i] = an_[i];                           \
+      bc0 = bn0;                                                                               \
+      bc1 = bn1;                                                                               \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    cw0 = nw0;                                                                                 \
+    cw1 = nw1;                                                                                 \
+    kc0 = kn0;                                                                                 \
+    kcp = knp;                                                                                 \
+  }
+
+  for (int kb = 0;;) {
+    LNF4_DXQ_BLOCK(sm0, sm1, sm2);
+    if (++kb == nkb) break;
+    LNF4_DXQ_BLOCK(sm1, sm2, sm0);
+    if (++kb == nkb) break;
+    LNF4_DXQ_BLOCK(sm2, sm0, sm1);
+    if (++kb == nkb) break;
+    LNF4_DXQ_BLOCK(sm0, sm1, sm2);
+    if (++kb == nkb) break;
+    LNF4_DXQ_BLOCK(sm1, sm2, sm0);
+    if (++kb == nkb) break;
+    LNF4_DXQ_BLOCK(sm2, sm0, sm1);
+    if (++kb == nkb) break;
+  }
+#undef LNF4_DXQ_BLOCK
+#undef LNF4_DXQ_PROJ
+#undef LNF4_DXQ_ISSUE
+#undef LNF4_WAIT_VM
+#undef LNF4_WAIT_VM_LGKM0
+#undef LNF4_TR4
+#undef LNF4_DXQ_CODES
+#undef LNF4_DXQ_SCALES
+#undef LNF4_LUT8X
+#undef LNF4_FIN8X
+#undef LNF4_DXQ_MASK
+#undef LNF4_XS
+
+  // ---- store bf16 (optionally accumulating into the existing dx)
+  const int n0g = n0 + nc0, n1g = n0 + nc1;
+  const bool c0ok = n0g < N, c1ok = n1g < N;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      if (gm >= M) continue;
+      uint16_t* dr = args.dx + (size_t)gm * N;
+      float v0 = acc[i][0][q], v1 = acc[i][1][q];
+      if (args.accumulate) {
+        if (c0ok) v0 += bf16_to_f32(dr[n0g]);
+        if (c1ok) v1 += bf16_to_f32(dr[n1g]);
+      }
+      if (c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
+      if (c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
+    }
+  }
+}
+
+// =====================================================================================
 // Launchers
 // =====================================================================================
 static int pick_bm(int M, int tiles_n_256) {
@@ -704,8 +1038,8 @@ hipError_t launch_dx(const DxArgs& a0, int fmt, hipStream_t s) {
   a.n_tiles_m = (a.M + bm - 1) / bm;
   const dim3 grid(a.n_tiles_m * a.n_tiles_n), block(NTHR);
   if (fmt == 0) {
-    if (bm == 256) hipLaunchKernelGGL((k_dx<0, 256>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_dx<0, 128>), grid, block, 0, s, a);
+    if (bm == 256) hipLaunchKernelGGL((k_dxq<256>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dxq<128>), grid, block, 0, s, a);
   } else {
     if (bm == 256) hipLaunchKernelGGL((k_dx<1, 256>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_dx<1, 128>), grid, block, 0, s, a);
