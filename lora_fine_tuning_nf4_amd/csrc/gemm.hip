@@ -33,8 +33,30 @@ constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int NTHR = 256;
 constexpr int kGroupM = 4;   // row-tiles per group of the tile order (tile_coords)
+
 // largest rank (summed over a group in backward) the fused epilogue stages in LDS
 #define LNF4_EPI_RANK 64
+
+// Raw buffer resource over [p, p + bytes) for the direct-to-LDS buffer loads: a 32-bit
+// per-lane offset plus a wave-uniform offset address the data with no per-lane 64-bit
+// arithmetic, and a load whose per-lane offset reaches past `bytes` returns zeros.
+// (dword 3 = 0x00020000: the untyped 32-bit format of gfx9-class buffer descriptors)
+// The host pass of hipcc only parses kernel bodies; it has no buffer-resource type, and a
+// kernel it cannot parse gets no launch stub, so it sees an inert stand-in.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+#define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_, (lds_ptr)(lds_), size_, voff_, soff_, 0, 0)
+#else
+typedef const void* rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* p, int64_t) { return p; }
+#define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) ((void)0)
+#endif
 
 // 16-byte-segment swizzle of a 128-byte code row (consecutive row pairs share it, so 16
 // consecutive rows cover all 64 banks in a transposing read)
@@ -108,13 +130,14 @@ __device__ __forceinline__ DxProj select_dx(const DxArgs& a, int idx) {
 // with zeros), writing straight into the accumulators.
 template <int MI>
 __device__ __forceinline__ void rank_update(floatx16 (&acc)[MI][2], const uint16_t* Uh, const uint16_t* Ul,
-                                            const uint16_t* V, int RP, int l32, int h, int nc0, int nc1) {
+                                            const uint16_t* V, int RP, int l32, int h, int nc0, int nc1,
+                                            int row0 = 0) {
   for (int ks = 0; ks < RP; ks += 16) {
     const bf16x8 b0 = *(const bf16x8*)&V[nc0 * RP + ks + 8 * h];
     const bf16x8 b1 = *(const bf16x8*)&V[nc1 * RP + ks + 8 * h];
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int row = 32 * i + l32;
+      const int row = row0 + 32 * i + l32;
       const bf16x8 ah = *(const bf16x8*)&Uh[row * RP + ks + 8 * h];
       const bf16x8 al = *(const bf16x8*)&Ul[row * RP + ks + 8 * h];
       acc[i][0] = mfma32(ah, b0, acc[i][0]);
@@ -138,9 +161,14 @@ constexpr int epi_bytes() { return (2 * BM + BN) * LNF4_EPI_RANK * 2; }
 // =====================================================================================
 // Forward
 // =====================================================================================
-template <int FMT, int BM>
-__global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
-  constexpr int MI = BM / 32;
+// NW = 4: each wave owns 64 columns x all BM rows (one wave per SIMD).  NW = 8: two waves
+// per column group, each on half of the rows (two waves per SIMD: more latency hiding,
+// each code decoded by both waves of its column group).
+template <int FMT, int BM, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
+  constexpr int NT = 64 * NW;
+  constexpr int WM = NW / 4;          // waves sharing a column group
+  constexpr int MI = BM / 32 / WM;    // 32-row MFMA tiles per wave
   constexpr int NM = 2 * MI;                       // MFMAs per 16-wide K step
   // One ring stage: the activation tile [BM][64] bf16, then the weight tile of the 256
   // columns (NF4: 32 code bytes + one fp32 absmax per column; bf16: 128 bytes per column).
@@ -159,17 +187,23 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
   // byte-pair code table: entry b = (T[b >> 4], T[b & 15]), the fp32 levels of the two
-  // codes one byte holds (high nibble first)
-  __shared__ __attribute__((aligned(16))) float2 lut2[256];
+  // codes one byte holds (high nibble first).  The large alignment places it at LDS
+  // address 0, so an entry's address is just byte << 3: one byte-select shift per lookup.
+  __shared__ __attribute__((aligned(2048))) float2 lut2[256];
+  __shared__ float lut1[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);  // NTHR == 256
+  if (tid < 256) lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);
+  if (tid < 16) lut1[tid] = c_gemm_table[tid];
+  const int wn = wave & 3;                 // column group
+  const int rbase = (wave >> 2) * (BM / WM);  // first tile row of this wave
 
   int tm, tn;
   tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  tn += args.tn_base;
   int pi = 0;
 #pragma unroll
   for (int q = 1; q < kMaxGroup; ++q)
@@ -180,7 +214,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
   const int m0 = tm * BM;
   const int nloc0 = (tn - P.tile_n0) * BN;
   const int nk = K / BK;
-  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;   // this lane's two tile columns
+  const int nc0 = 64 * wn + l32, nc1 = nc0 + 32;   // this lane's two tile columns
 
   // ---- accumulators start at the rank-r LoRA term s * u[m, :] . B[n, :]
   floatx16 acc[MI][2];
@@ -195,17 +229,17 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
     uint16_t* Uh = (uint16_t*)sm0;
     uint16_t* Ul = (uint16_t*)sm1;
     uint16_t* V = (uint16_t*)sm2;
-    for (int idx = tid; idx < BM * RP; idx += NTHR) {
+    for (int idx = tid; idx < BM * RP; idx += NT) {
       const int mm = idx / RP, kk = idx - mm * RP, gm = m0 + mm;
       const float uv = (gm < M && kk < r) ? P.scale * P.u[(size_t)gm * r + kk] : 0.0f;
       split_bf16(uv, Uh[idx], Ul[idx]);
     }
-    for (int idx = tid; idx < BN * RP; idx += NTHR) {
+    for (int idx = tid; idx < BN * RP; idx += NT) {
       const int nn = idx / RP, kk = idx - nn * RP, n = nloc0 + nn;
       V[idx] = (n < out_f && kk < r) ? P.B[(size_t)n * r + kk] : (uint16_t)0;
     }
     __syncthreads();
-    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1, rbase);
     __syncthreads();
   }
 
@@ -221,50 +255,57 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
   //  * bf16 weights: per column 128 bytes (8 chunks, swizzled like the activation rows);
   //    wave w loads its 64 columns in 8 loads.
   //  Columns >= out_f read column out_f-1 (outputs discarded).
-  constexpr int XQ = X_BYTES / 1024 / 4;
-  constexpr int WQ = FMT == 0 ? 2 : 8;
+  constexpr int XQ = X_BYTES / 1024 / NW;
+  constexpr int WQ = (FMT == 0 ? 8 : 32) / NW;
   constexpr int NLD = XQ + WQ + (FMT == 0 ? 1 : 0);  // vector-memory ops per wave per K-block
-  const uint16_t* xbase = args.x + (size_t)m0 * K;
+  // Buffer loads: one resource per operand (scalar registers), a constant 32-bit per-lane
+  // byte offset per load, and the K-block advance as the wave-uniform offset, so no
+  // per-lane address arithmetic remains in the K loop.
+  const rsrc_t xrs = make_rsrc(args.x + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
   uint32_t xoff[XQ];
 #pragma unroll
   for (int q = 0; q < XQ; ++q) {
     const int row = (wave * XQ + q) * 8 + (lane >> 3);
     const int lr = (m0 + row < M) ? row : (M - 1 - m0);
-    xoff[q] = (uint32_t)lr * (uint32_t)K + (uint32_t)(((lane & 7) ^ act_swz(row)) * 8);
+    xoff[q] = 2u * ((uint32_t)lr * (uint32_t)K + (uint32_t)(((lane & 7) ^ act_swz(row)) * 8));
   }
-  const uint8_t* wsrc[WQ];
-  const float* asrc = nullptr;
+  const rsrc_t wrs =
+      make_rsrc(P.w, FMT == 0 ? (int64_t)out_f * K / 2 : (int64_t)out_f * K * 2);
+  uint32_t woff[WQ];
 #pragma unroll
   for (int q = 0; q < WQ; ++q) {
+    const int g = wave * WQ + q;  // 1 KB load index within the tile
     if (FMT == 0) {
-      int n = nloc0 + 64 * wave + 32 * q + (lane >> 1);
+      int n = nloc0 + 32 * g + (lane >> 1);
       n = n < out_f ? n : out_f - 1;
-      wsrc[q] = (const uint8_t*)P.w + (size_t)n * (K / 2) + 16 * (lane & 1);
+      woff[q] = (uint32_t)n * (uint32_t)(K / 2) + 16u * (lane & 1);
     } else {
-      const int col = 8 * q + (lane >> 3);  // column within the wave's 64
-      int n = nloc0 + 64 * wave + col;
+      const int col = 8 * g + (lane >> 3);
+      int n = nloc0 + col;
       n = n < out_f ? n : out_f - 1;
-      wsrc[q] = (const uint8_t*)P.w + (size_t)n * K * 2 + (((lane & 7) ^ act_swz(col)) * 16);
+      woff[q] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ act_swz(col)) * 16);
     }
   }
+  // absmax: wave w loads columns (256/NW)*w + lane (lanes past 256/NW stay idle)
+  constexpr int ACOL = 256 / NW;
+  const rsrc_t ars = make_rsrc(P.absmax, FMT == 0 ? (int64_t)out_f * (K / 64) * 4 : 0);
+  uint32_t aoff = 0;
   if (FMT == 0) {
-    int n = nloc0 + 64 * wave + lane;
+    int n = nloc0 + ACOL * wave + (lane & (ACOL - 1));
     n = n < out_f ? n : out_f - 1;
-    asrc = P.absmax + (size_t)n * (K / 64);
+    aoff = 4u * (uint32_t)n * (uint32_t)(K / 64);
   }
-  typedef __attribute__((address_space(3))) void* lds_ptr;
 
 #define LNF4_ISSUE(kb_, SM_)                                                                    \
   {                                                                                             \
     uint8_t* sx_ = SM_;                                                                         \
-    _Pragma("unroll") for (int q = 0; q < XQ; ++q) __builtin_amdgcn_global_load_lds(             \
-        (const void*)(xbase + xoff[q] + (kb_) * BK), (lds_ptr)(sx_ + (wave_u * XQ + q) * 1024), 16, 0, 0); \
-    _Pragma("unroll") for (int q = 0; q < WQ; ++q) __builtin_amdgcn_global_load_lds(             \
-        (const void*)(wsrc[q] + (kb_) * (FMT == 0 ? 32 : 128)),                                 \
-        (lds_ptr)(sx_ + X_BYTES + (wave_u * WQ + q) * 1024), 16, 0, 0);                         \
-    if (FMT == 0)                                                                               \
-      __builtin_amdgcn_global_load_lds((const void*)(asrc + (kb_)),                             \
-                                       (lds_ptr)(sx_ + X_BYTES + W_BYTES + wave_u * 256), 4, 0, 0); \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                              \
+        LNF4_BUF_LDS(xrs, sx_ + (wave_u * XQ + q) * 1024, 16, xoff[q], (kb_) * (BK * 2));       \
+    _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                              \
+        LNF4_BUF_LDS(wrs, sx_ + X_BYTES + (wave_u * WQ + q) * 1024, 16, woff[q],                \
+                     (kb_) * (FMT == 0 ? 32 : 128));                                            \
+    if (FMT == 0 && (NW == 4 || lane < ACOL))                                                   \
+      LNF4_BUF_LDS(ars, sx_ + X_BYTES + W_BYTES + wave_u * (4 * ACOL), 4, aoff, (kb_) * 4);     \
   }
   // wait until at most n vector-memory ops of this wave are outstanding (gfx9 s_waitcnt
   // encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait")
@@ -276,6 +317,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
   // (nibble -> LDS table -> fp32 level) and finish phase (one fp32 product by the block's
   // absmax, RNE pack to bf16), so the table reads go out early in a step and are consumed
   // at its end.
+#ifdef LNF4_NIBBLE_LUT
+#define LNF4_LUT8(lv, cw_)                                                         \
+  {                                                                                \
+    const uint32_t c_ = (cw_);                                                     \
+    _Pragma("unroll") for (int b_ = 0; b_ < 4; ++b_) {                             \
+      lv[2 * b_] = lut1[(c_ >> (8 * b_ + 4)) & 15u];                               \
+      lv[2 * b_ + 1] = lut1[(c_ >> (8 * b_)) & 15u];                               \
+    }                                                                              \
+  }
+#else
 #define LNF4_LUT8(lv, cw_)                                                         \
   {                                                                                \
     const uint32_t c_ = (cw_);                                                     \
@@ -285,6 +336,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
       lv[2 * b_ + 1] = p_.y;                                                       \
     }                                                                              \
   }
+#endif
 #define LNF4_FIN8(dst, lv, a_)                                                     \
   dst = as_bf16x8(pack_bf16x2(lv[0] * (a_), lv[1] * (a_)), pack_bf16x2(lv[2] * (a_), lv[3] * (a_)), \
                   pack_bf16x2(lv[4] * (a_), lv[5] * (a_)), pack_bf16x2(lv[6] * (a_), lv[7] * (a_)));
@@ -324,18 +376,25 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
     bc1 = LNF4_READ_BW(sm0, 0, nc1);
   }
 #pragma unroll
-  for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(32 * i + l32, 4 * h)];
+  for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(rbase + 32 * i + l32, 4 * h)];
 
   // One K-block on stage SC; SN holds the next block, SP receives the block two ahead.
   // The loop is unrolled three times with the stages rotated, so every LDS access names
   // its stage statically.
 #define LNF4_FWD_BLOCK(SC, SN, SP)                                                             \
   {                                                                                            \
-    LNF4_ISSUE((kb + 2 < nk ? kb + 2 : nk - 1), SP); /* the tail re-reads the last block */    \
     u32x4 nw0, nw1;                                                                            \
     float ns0 = 0.f, ns1 = 0.f;                                                                \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
       __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 1) {                                                                            \
+        /* block kb+2 goes into stage SP, which no wave reads any more.  Issued after step */  \
+        /* 0's LDS reads: at the loop head the compiler cannot tell which stage an */         \
+        /* in-flight load targets and drains them all before the first LDS read, and */       \
+        /* that first read now only waits for block kb+1, issued a block ago */               \
+        LNF4_ISSUE((kb + 2 < nk ? kb + 2 : nk - 1), SP); /* the tail re-reads the last block */ \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
       if (s == 3) {                                                                            \
         /* block kb+1 (issued one block ago) must be in LDS for every wave, and every wave */  \
         /* must be done with stage SC before block kb+3 is issued into it */                   \
@@ -366,10 +425,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
       }                                                                                        \
       if (s < 3) {                                                                             \
         _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
-            *(const bf16x8*)&LNF4_XS(SC)[act_pos(32 * i + l32, 4 * h + s + 1)];                \
+            *(const bf16x8*)&LNF4_XS(SC)[act_pos(rbase + 32 * i + l32, 4 * h + s + 1)];        \
       } else {                                                                                 \
         _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
-            *(const bf16x8*)&LNF4_XS(SN)[act_pos(32 * i + l32, 4 * h)];                        \
+            *(const bf16x8*)&LNF4_XS(SN)[act_pos(rbase + 32 * i + l32, 4 * h)];                \
       }                                                                                        \
       _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
         acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
@@ -445,7 +504,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd(const FwdArgs args) {
     __builtin_amdgcn_sched_barrier(0);  // bound the accumulator reads that are live at once
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int row = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      const int row = rbase + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
       const int gm = m0 + row;
       if (gm >= M) continue;
       const float v0 = acc[i][0][q], v1 = acc[i][1][q];
@@ -702,14 +761,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
   // byte-pair code table in transposed order: a byte of a transposed read holds rows 2b
-  // (low nibble) and 2b+1 (high nibble) of one column
-  __shared__ __attribute__((aligned(16))) float2 lut2[256];
+  // (low nibble) and 2b+1 (high nibble) of one column; at LDS address 0 (see k_fwd)
+  __shared__ __attribute__((aligned(2048))) float2 lut2[256];
+  __shared__ float lut1[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   lut2[tid] = make_float2(c_gemm_table[tid & 15], c_gemm_table[tid >> 4]);  // NTHR == 256
+  if (tid < 16) lut1[tid] = c_gemm_table[tid];
 
   int tm, tn;
   tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
@@ -769,7 +830,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   //  weights are zeroed by the decode (rows) or their outputs dropped (columns).
   constexpr int XQ = X_BYTES / 1024 / 4;
   constexpr int NLD = XQ + 3;
-  typedef __attribute__((address_space(3))) void* lds_ptr;
   const int halfN = N / 2, nblk = N / 64;
   const int cbyte_max = halfN - 16;
   const int ablk = (n0 / 64 + wave) < nblk ? n0 / 64 + wave : nblk - 1;
@@ -780,31 +840,39 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   pi_ = __builtin_amdgcn_readfirstlane(pi_);                                     \
   const DxProj& P_ = args.p[pi_];
 
+  // per-lane constant parts of the buffer-load offsets (see k_fwd); the projection and the
+  // K offset go into each block's resources, whose ranges end at the projection's last
+  // row, so rows past out_f load as zeros: zero absmax, hence zero weights
+  uint32_t dyr2[XQ], dyc[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int row = (wave * XQ + q) * 8 + (lane >> 3);
+    dyr2[q] = 2u * (uint32_t)(m0 + row < M ? m0 + row : M - 1);
+    dyc[q] = 16u * (uint32_t)((lane & 7) ^ act_swz(row));
+  }
+  uint32_t cwoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * wave + 8 * q + (lane >> 3);
+    const int cb = n0 / 2 + 16 * ((lane & 7) ^ wswz(row));
+    cwoff[q] = (uint32_t)row * (uint32_t)halfN + (uint32_t)(cb < cbyte_max ? cb : cbyte_max);
+  }
+  const uint32_t caoff = 4u * ((uint32_t)lane * (uint32_t)nblk + (uint32_t)ablk);
+
 #define LNF4_DXQ_ISSUE(kb_, SM_)                                                                 \
   {                                                                                              \
     LNF4_DXQ_PROJ(kb_, Pi_)                                                                      \
     const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
-    _Pragma("unroll") for (int q = 0; q < XQ; ++q) {                                             \
-      const int row = (wave * XQ + q) * 8 + (lane >> 3);                                        \
-      const int gr = m0 + row < M ? m0 + row : M - 1;                                            \
-      const int oc = k0_ + 8 * ((lane & 7) ^ act_swz(row));                                      \
-      const int o = oc < Kp_ - 8 ? oc : Kp_ - 8;                                                 \
-      __builtin_amdgcn_global_load_lds((const void*)(Pi_.dy + (size_t)gr * Kp_ + o),             \
-                                       (lds_ptr)((SM_) + (wave_u * XQ + q) * 1024), 16, 0, 0);   \
-    }                                                                                            \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                              \
-      const int row = 16 * wave + 8 * q + (lane >> 3);                                           \
-      const int gk = k0_ + row < Kp_ ? k0_ + row : Kp_ - 1;                                      \
-      const int cb = n0 / 2 + 16 * ((lane & 7) ^ wswz(row));                                     \
-      const int cbc = cb < cbyte_max ? cb : cbyte_max;                                           \
-      __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)Pi_.w + (size_t)gk * halfN + cbc), \
-                                       (lds_ptr)((SM_) + X_BYTES + (wave_u * 2 + q) * 1024), 16, 0, 0); \
-    }                                                                                            \
-    {                                                                                            \
-      const int gk = k0_ + lane < Kp_ ? k0_ + lane : Kp_ - 1;                                    \
-      __builtin_amdgcn_global_load_lds((const void*)(Pi_.absmax + (size_t)gk * nblk + ablk),     \
-                                       (lds_ptr)((SM_) + X_BYTES + W_BYTES + wave_u * 256), 4, 0, 0); \
-    }                                                                                            \
+    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, ((int64_t)M * Kp_ - k0_) * 2);    \
+    const rsrc_t wrs_ =                                                          \
+        make_rsrc((const uint8_t*)Pi_.w + (size_t)k0_ * halfN, (int64_t)(Kp_ - k0_) * halfN);    \
+    const rsrc_t ars_ =                                                          \
+        make_rsrc(Pi_.absmax + (size_t)k0_ * nblk, (int64_t)(Kp_ - k0_) * nblk * 4);             \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                               \
+        LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + q) * 1024, 16, dyr2[q] * (uint32_t)Kp_ + dyc[q], 0); \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                                \
+        LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * 2 + q) * 1024, 16, cwoff[q], 0);          \
+    LNF4_BUF_LDS(ars_, (SM_) + X_BYTES + W_BYTES + wave_u * 256, 4, caoff, 0);                    \
   }
 #define LNF4_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define LNF4_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
@@ -834,6 +902,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     a_[0] = lo_[0]; a_[1] = lo_[1]; a_[2] = lo_[2]; a_[3] = lo_[3];                             \
     a_[4] = hi_[0]; a_[5] = hi_[1]; a_[6] = hi_[2]; a_[7] = hi_[3];                             \
   }
+#ifdef LNF4_NIBBLE_LUT
+#define LNF4_LUT8X(lv, cw_)                                                        \
+  {                                                                                \
+    const uint32_t c_ = (cw_);                                                     \
+    _Pragma("unroll") for (int b_ = 0; b_ < 4; ++b_) {                             \
+      lv[2 * b_] = lut1[(c_ >> (8 * b_)) & 15u];                                   \
+      lv[2 * b_ + 1] = lut1[(c_ >> (8 * b_ + 4)) & 15u];                           \
+    }                                                                              \
+  }
+#else
 #define LNF4_LUT8X(lv, cw_)                                                        \
   {                                                                                \
     const uint32_t c_ = (cw_);                                                     \
@@ -843,16 +921,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       lv[2 * b_ + 1] = p_.y;                                                       \
     }                                                                              \
   }
+#endif
 #define LNF4_FIN8X(dst, lv, a_)                                                    \
   dst = as_bf16x8(pack_bf16x2(lv[0] * a_[0], lv[1] * a_[1]), pack_bf16x2(lv[2] * a_[2], lv[3] * a_[3]), \
                   pack_bf16x2(lv[4] * a_[4], lv[5] * a_[5]), pack_bf16x2(lv[6] * a_[6], lv[7] * a_[7]));
-  // rows of step s past the projection's out_f decode to zero (out_f is a multiple of 8,
-  // so the 8 rows of a step are all in or all out)
-#define LNF4_DXQ_MASK(a_, k0_, Kp_, s_)                                             \
-  {                                                                                \
-    const bool in_ = (k0_) + 32 * h + 8 * (s_) < (Kp_);                            \
-    _Pragma("unroll") for (int e_ = 0; e_ < 8; ++e_) a_[e_] = in_ ? a_[e_] : 0.0f; \
-  }
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))
 
   // prologue: blocks 0 and 1 in flight; block 0 visible
@@ -861,12 +933,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   LNF4_WAIT_VM(NLD);
   __syncthreads();
 
-  int kc0, kcp;  // K offset within its projection and that projection's out_f, current block
-  {
-    LNF4_DXQ_PROJ(0, P0_)
-    kc0 = (0 - P0_.kb0) * BK;
-    kcp = P0_.out_f;
-  }
   bf16x8 ac[MI], an_[MI];
   bf16x8 bc0, bc1, bn0, bn1;
   u32x4 cw0, cw1;
@@ -876,7 +942,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     LNF4_LUT8X(l0, cw0[0]);
     LNF4_LUT8X(l1, cw1[0]);
     LNF4_DXQ_SCALES(sm0, 0, a);
-    LNF4_DXQ_MASK(a, kc0, kcp, 0);
     LNF4_FIN8X(bc0, l0, a);
     LNF4_FIN8X(bc1, l1, a);
   }
@@ -885,17 +950,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 
 #define LNF4_DXQ_BLOCK(SC, SN, SP)                                                             \
   {                                                                                            \
-    LNF4_DXQ_ISSUE((kb + 2 < nkb ? kb + 2 : nkb - 1), SP);                                     \
-    int kn0, knp; /* the next block's K offset and out_f */                                    \
-    {                                                                                          \
-      const int kbn_ = kb + 1 < nkb ? kb + 1 : kb;                                             \
-      LNF4_DXQ_PROJ(kbn_, Pn_)                                                                 \
-      kn0 = (kbn_ - Pn_.kb0) * BK;                                                             \
-      knp = Pn_.out_f;                                                                         \
-    }                                                                                          \
     u32x4 nw0, nw1;                                                                            \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
       __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 1) { /* after step 0's LDS reads, as in k_fwd */                                \
+        LNF4_DXQ_ISSUE((kb + 2 < nkb ? kb + 2 : nkb - 1), SP);                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
       if (s == 3) {                                                                            \
         LNF4_WAIT_VM_LGKM0(NLD);                                                               \
         __builtin_amdgcn_s_barrier();                                                          \
@@ -923,11 +984,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
         acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
         acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
       }                                                                                        \
-      if (s < 3) {                                                                             \
-        LNF4_DXQ_MASK(a, kc0, kcp, s + 1);                                                     \
-      } else {                                                                                 \
-        LNF4_DXQ_MASK(a, kn0, knp, 0);                                                         \
-      }                                                                                        \
       LNF4_FIN8X(bn0, l0, a);                                                                  \
       LNF4_FIN8X(bn1, l1, a);                                                                  \
       _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                          \
@@ -950,8 +1006,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     __builtin_amdgcn_sched_barrier(0);                                                         \
     cw0 = nw0;                                                                                 \
     cw1 = nw1;                                                                                 \
-    kc0 = kn0;                                                                                 \
-    kcp = knp;                                                                                 \
   }
 
   for (int kb = 0;;) {
@@ -978,7 +1032,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #undef LNF4_DXQ_SCALES
 #undef LNF4_LUT8X
 #undef LNF4_FIN8X
-#undef LNF4_DXQ_MASK
 #undef LNF4_XS
 
   // ---- store bf16 (optionally accumulating into the existing dx)
@@ -1014,19 +1067,56 @@ static int pick_bm(int M, int tiles_n_256) {
   return 128;
 }
 
+static int n_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+           prop.multiProcessorCount > 0) ? prop.multiProcessorCount : 256;
+  }
+  return cus;
+}
+
 hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   FwdArgs a = a0;
   if (a.M <= 0 || a.n_tiles_n <= 0) return hipSuccess;
-  // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
-  const int bm = fmt == 0 ? pick_bm(a.M, a.n_tiles_n) : 128;
-  a.n_tiles_m = (a.M + bm - 1) / bm;
-  const dim3 grid(a.n_tiles_m * a.n_tiles_n), block(NTHR);
-  if (fmt == 0) {
-    if (bm == 256) hipLaunchKernelGGL((k_fwd<0, 256>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_fwd<0, 128>), grid, block, 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_fwd<1, 128>), grid, block, 0, s, a);
+  a.tn_base = 0;
+  if (fmt != 0) {
+    // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
+    a.n_tiles_m = (a.M + 127) / 128;
+    hipLaunchKernelGGL((k_fwd<1, 128, 4>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
+    return hipGetLastError();
   }
+  const int cus = n_cus();
+  const int tn_all = a.n_tiles_n;
+  const int tm256 = (a.M + 255) / 256;
+  const int t256 = tm256 * tn_all;
+  if (pick_bm(a.M, tn_all) == 128) {
+    a.n_tiles_m = (a.M + 127) / 128;
+    hipLaunchKernelGGL((k_fwd<0, 128, 4>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+  }
+  if (t256 <= cus) {
+    // one partial wave of tiles: two waves per SIMD hide more latency per tile
+    a.n_tiles_m = tm256;
+    hipLaunchKernelGGL((k_fwd<0, 256, 8>), dim3(t256), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
+  // Whole waves of 256-row tiles; the column tiles of a trailing partial wave run as
+  // 128-row tiles (twice as many, half the work each), which fill the last wave instead
+  // of leaving part of the chip idle.
+  int nn256 = tn_all;
+  if (t256 % cus != 0) nn256 = ((t256 / cus) * cus) / tm256;
+  a.n_tiles_m = tm256;
+  a.n_tiles_n = nn256;
+  hipLaunchKernelGGL((k_fwd<0, 256, 4>), dim3(tm256 * nn256), dim3(NTHR), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nn256 == tn_all) return e;
+  a.tn_base = nn256;
+  a.n_tiles_n = tn_all - nn256;
+  a.n_tiles_m = (a.M + 127) / 128;
+  hipLaunchKernelGGL((k_fwd<0, 128, 4>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@ struct FwdArgs {
   int32_t M;            // T
   int32_t K;            // in
   int32_t n_proj;
-  int32_t n_tiles_n;    // total N-tiles over the group
+  int32_t n_tiles_n;    // N-tiles covered by this launch
   int32_t n_tiles_m;
+  int32_t tn_base;      // first N-tile of this launch in the group's tile space
   FwdProj p[kMaxGroup];
 };
 
