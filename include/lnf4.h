@@ -30,6 +30,9 @@
  *  - Errors: every call returns LNF4_OK (0) or a negative LNF4_E* code and sets a
  *    thread-local message readable with lnf4_last_error().  Argument validation runs
  *    before any HIP call.  No exception crosses the ABI and the library never aborts.
+ *  - Size limits: every weight matrix and every activation matrix passed to the GEMM
+ *    entry points must span at most 2^31-1 bytes (ESHAPE otherwise); the kernels
+ *    address each one through a 31-bit buffer range.
  *  - Not thread-safe per lnf4_stream object.
  */
 #ifndef LNF4_H

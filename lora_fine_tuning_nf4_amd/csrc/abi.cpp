@@ -46,6 +46,9 @@ static int check_weight(const lnf4_weight* W, const char* who) {
   if (W->out_f < 1 || W->out_f > (1 << 24)) return fail(LNF4_ESHAPE, "%s: out_f=%lld out of range", who, (long long)W->out_f);
   if (W->in_f < 64 || W->in_f > (1 << 24) || W->in_f % 64 != 0)
     return fail(LNF4_ESHAPE, "%s: in_f=%lld must be a positive multiple of 64", who, (long long)W->in_f);
+  // the kernels address each matrix through a buffer resource with a 31-bit byte range
+  const int64_t wbytes = W->fmt == LNF4_FMT_NF4 ? W->out_f * W->in_f / 2 : W->out_f * W->in_f * 2;
+  if (wbytes > (int64_t)INT32_MAX) return fail(LNF4_ESHAPE, "%s: weight of %lld bytes exceeds 2^31-1", who, (long long)wbytes);
   if (W->fmt == LNF4_FMT_NF4) {
     if (W->blocksize != 64) return fail(LNF4_ESHAPE, "%s: blocksize=%d (only 64 is supported)", who, (int)W->blocksize);
     if (!W->absmax) return fail(LNF4_EINVAL, "%s: absmax is NULL for an NF4 weight", who);
@@ -56,6 +59,13 @@ static int check_weight(const lnf4_weight* W, const char* who) {
 
 static int check_tokens(int64_t T, const char* who) {
   if (T < 0 || T > (int64_t)INT32_MAX / 2) return fail(LNF4_EINVAL, "%s: T=%lld out of range", who, (long long)T);
+  return LNF4_OK;
+}
+
+// an activation [T, features] bf16 must fit a 31-bit byte range
+static int check_activation(int64_t T, int64_t features, const char* what, const char* who) {
+  if (T * features * 2 > (int64_t)INT32_MAX)
+    return fail(LNF4_ESHAPE, "%s: %s of %lld x %lld bf16 exceeds 2^31-1 bytes", who, what, (long long)T, (long long)features);
   return LNF4_OK;
 }
 
@@ -85,6 +95,7 @@ int group_fwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
     if ((rc = check_weight(&P.W, who))) return rc;
     if (P.W.in_f != projs[0].W.in_f) return fail(LNF4_ESHAPE, "%s: projection %d has a different in_f", who, p);
     if (P.W.fmt != projs[0].W.fmt) return fail(LNF4_EINVAL, "%s: projection %d has a different format", who, p);
+    if ((rc = check_activation(T, P.W.in_f, "x", who)) || (rc = check_activation(T, P.W.out_f, "y", who))) return rc;
     if ((rc = adapter_state(P.A, P.B, P.r, who)) < 0) return rc;
     on[p] = enabled ? rc : 0;
     if (T > 0) {
@@ -286,6 +297,7 @@ int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
     if (P.W.in_f != projs[0].W.in_f) return fail(LNF4_ESHAPE, "%s: projection %d has a different in_f", who, p);
     if (P.W.fmt != projs[0].W.fmt) return fail(LNF4_EINVAL, "%s: projection %d has a different format", who, p);
     if (P.W.out_f % 8 != 0) return fail(LNF4_ESHAPE, "%s: out_f=%lld must be a multiple of 8 in backward", who, (long long)P.W.out_f);
+    if ((rc = check_activation(T, P.W.in_f, "x", who)) || (rc = check_activation(T, P.W.out_f, "dy", who))) return rc;
     if (on[p] && (P.dA || P.dB)) need_dy = true;
     if (on[p] && (P.dA || (P.dB && !P.u))) need_x = true;
     if (on[p] && P.dA && !aligned(P.dA, 4)) return fail(LNF4_EALIGN, "%s: dA not 4-byte aligned", who);

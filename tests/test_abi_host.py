@@ -134,3 +134,12 @@ def test_stream_validation(L):
     assert L.stream_slot_load(None, 0, None) == lnf4.LNF4_ESTATE
     assert L.stream_slot_wait(None, None, ctypes.byref(p)) == lnf4.LNF4_ESTATE
     assert L.stream_destroy(None) == lnf4.LNF4_OK
+
+
+def test_size_limits(L):
+    # a weight or activation beyond 2^31-1 bytes is rejected before any HIP call
+    big = lnf4.make_weight(lnf4.FMT_BF16, FAKE, None, 1 << 16, 1 << 15, 64)  # 2^32 bytes of bf16
+    assert L.lora_linear_fwd(ctypes.byref(big), FAKE, 16, None, None, 0, 0.0, FAKE, None, None) == lnf4.LNF4_ESHAPE
+    w = lnf4.make_weight(lnf4.FMT_NF4, FAKE, FAKE, 1024, 1 << 20, 64)       # codes 2^29 bytes: fine
+    assert L.lora_linear_fwd(ctypes.byref(w), FAKE, 1 << 11, None, None, 0, 0.0, FAKE, None, None) \
+        == lnf4.LNF4_ESHAPE                                                 # x: 2^11 x 2^20 bf16 = 2^32 bytes
