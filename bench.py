@@ -235,7 +235,7 @@ def main():
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "traffic_source": traffic_src,
             "algorithmic_bytes_per_launch": fwd_bytes(wl, GROUPS[2]),
-            "kernel": "k_fwd<NF4,BM=256> gate|up forward: M=2048 N=28672 K=4096 (fused NF4 decode)",
+            "kernel": "k_fwd<NF4,BM=256,4 waves> gate|up forward: M=2048 N=28672 K=4096 (fused NF4 decode), one launch",
             "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4),
             "launches_timed": len(dom),
         },
@@ -280,6 +280,47 @@ def main():
         e1.record(cs)
     torch.cuda.synchronize()
     result["h2d"]["copy_only_GBps"] = round(8 * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
+    # every shard once (host placement can differ between shards)
+    rates = []
+    for h in stack.host:
+        with torch.cuda.stream(cs):
+            e0.record(cs)
+            db[:h.numel()].copy_(h, non_blocking=True)
+            e1.record(cs)
+        torch.cuda.synchronize()
+        rates.append(h.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9)
+    result["h2d"]["per_shard_GBps"] = {"min": round(min(rates), 2), "mean": round(sum(rates) / len(rates), 2),
+                                       "max": round(max(rates), 2)}
+    if stack.slot is not None:
+        head = {}
+        for name, sid in zip(("embed", "lm_head"), stack.head_ids):
+            h = stack.all_shards[sid]
+            with torch.cuda.stream(cs):
+                e0.record(cs)
+                stack.slot[:h.numel()].copy_(h, non_blocking=True)
+                e1.record(cs)
+            torch.cuda.synchronize()
+            head[name + "_GBps"] = round(h.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
+        h = stack.all_shards[stack.head_ids[0]]
+        part = (h.numel() + L - 1) // L
+        with torch.cuda.stream(cs):
+            e0.record(cs)
+            for q in range(L):
+                stack.slot[q * part:min((q + 1) * part, h.numel())].copy_(h[q * part:min((q + 1) * part, h.numel())],
+                                                                           non_blocking=True)
+            e1.record(cs)
+        torch.cuda.synchronize()
+        head[f"embed_in_{L}_parts_GBps"] = round(h.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
+        result["h2d"]["head_slot"] = head
+    # the stream schedule alone: the same copies, waits and slot loads with no GEMMs
+    for _ in range(2):
+        stack.step(compute=False)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    for _ in range(args.steps):
+        stack.step(compute=False)
+    torch.cuda.synchronize()
+    result["h2d"]["schedule_only_ms_per_step"] = round((time.perf_counter() - c0) * 1000.0 / args.steps, 3)
 
     # a plain device copy of known size, the reference point that scales rocprofv3's
     # FETCH_SIZE / WRITE_SIZE counters to bytes in a counter run of this same command

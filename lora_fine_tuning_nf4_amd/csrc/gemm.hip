@@ -1103,20 +1103,8 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
     hipLaunchKernelGGL((k_fwd<0, 256, 8>), dim3(t256), dim3(512), 0, s, a);
     return hipGetLastError();
   }
-  // Whole waves of 256-row tiles; the column tiles of a trailing partial wave run as
-  // 128-row tiles (twice as many, half the work each), which fill the last wave instead
-  // of leaving part of the chip idle.
-  int nn256 = tn_all;
-  if (t256 % cus != 0) nn256 = ((t256 / cus) * cus) / tm256;
   a.n_tiles_m = tm256;
-  a.n_tiles_n = nn256;
-  hipLaunchKernelGGL((k_fwd<0, 256, 4>), dim3(tm256 * nn256), dim3(NTHR), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nn256 == tn_all) return e;
-  a.tn_base = nn256;
-  a.n_tiles_n = tn_all - nn256;
-  a.n_tiles_m = (a.M + 127) / 128;
-  hipLaunchKernelGGL((k_fwd<0, 128, 4>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL((k_fwd<0, 256, 4>), dim3(t256), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

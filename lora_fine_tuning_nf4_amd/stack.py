@@ -200,9 +200,11 @@ class StreamedStack:
             tm[key][1].append(torch.cuda.Event(enable_timing=True))
             tm[key][1][-1].record(self.compute)
 
-    def step(self, resident: bool = False):
+    def step(self, resident: bool = False, compute: bool = True):
         """One training step over the whole stack (all calls asynchronous on the compute stream).
-        resident=True runs the same step from the resident context (no layer copies)."""
+        resident=True runs the same step from the resident context (no layer copies).
+        compute=False issues the same stream calls (copies, waits, slot loads) without the
+        GEMM calls: the time of the stream schedule alone."""
         L = self.L
         st = self.enable_resident() if resident else self.st
         slot = self.slot is not None and not resident
@@ -216,7 +218,7 @@ class StreamedStack:
             base = lnf4.stream_layer_step(st, k, self.compute)
             if k < n_fwd:
                 ref_pass = self.dpo and k < L
-                for gi in range(len(GROUPS)):
+                for gi in range(len(GROUPS) if compute else 0):
                     self._group_fwd(layer, gi, base, adapters=not ref_pass)
                 if k == n_fwd - 1 and slot:
                     # the untied lm_head takes the slot for the loss at the forward/backward turn
@@ -227,9 +229,9 @@ class StreamedStack:
                     # the backward is compute-bound: the next step's embed_tokens trickles into
                     # the slot in one piece per layer, between the layer copies
                     lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L, self.compute)
-                for gi in range(len(GROUPS)):          # recompute from the checkpointed inputs
+                for gi in range(len(GROUPS) if compute else 0):   # recompute from the checkpointed inputs
                     self._group_fwd(layer, gi, base, adapters=True)
-                for gi in reversed(range(len(GROUPS))):
+                for gi in reversed(range(len(GROUPS) if compute else 0)):
                     self._group_bwd(layer, gi, base)
         lnf4.stream_reset(st, self.compute)
         if slot:
