@@ -130,6 +130,123 @@ def cpu_baseline(wl, seed: int, layers: int):
     }
 
 
+def dequant_share(wl, seed: int, reps: int = 10):
+    """Fused NF4 GEMMs against the unfused path (nf4_dequant of the layer to bf16, then the
+    same GEMMs on bf16 weights) for one resident layer step (forward + recompute + backward)."""
+    import torch
+    import synthgen
+    from lora_fine_tuning_nf4_amd import lnf4
+    from lora_fine_tuning_nf4_amd.stack import GROUPS
+
+    T = wl.tokens
+    dev = "cuda"
+    groups = []
+    for g in GROUPS:
+        in_f = wl.shapes[g[0]][1]
+        x = synthgen.device_normal((T, in_f), 1.0, seed, "ds-x", *g, dtype=torch.bfloat16)
+        ent = {"x": x, "dx": torch.empty(T, in_f, dtype=torch.bfloat16, device=dev), "p": []}
+        for p in g:
+            o, i = wl.shapes[p]
+            w = synthgen.device_normal((o, i), 0.02, seed, "ds-w", p)
+            codes = torch.empty(o * i // 2, dtype=torch.uint8, device=dev)
+            am = torch.empty(o * i // 64, dtype=torch.float32, device=dev)
+            lnf4.nf4_quantize(w, o * i, 64, codes, am)
+            del w
+            on = p in wl.adapted
+            d = {"codes": codes, "am": am, "o": o, "i": i, "on": on,
+                 "wbf": torch.empty(o * i, dtype=torch.bfloat16, device=dev),
+                 "y": torch.empty(T, o, dtype=torch.bfloat16, device=dev),
+                 "dy": synthgen.device_normal((T, o), 1.0, seed, "ds-dy", p, dtype=torch.bfloat16)}
+            if on:
+                d["A"] = synthgen.device_uniform((wl.rank, i), 1.0 / i ** 0.5, seed, "ds-A", p, dtype=torch.bfloat16)
+                d["B"] = synthgen.device_normal((o, wl.rank), 0.01, seed, "ds-B", p, dtype=torch.bfloat16)
+                d["u"] = torch.empty(T, wl.rank, device=dev)
+                d["dA"] = torch.empty(wl.rank, i, device=dev)
+                d["dB"] = torch.empty(o, wl.rank, device=dev)
+            ent["p"].append(d)
+        groups.append(ent)
+
+    def projs(ent, fmt):
+        out = []
+        for d in ent["p"]:
+            W = (lnf4.make_weight(lnf4.FMT_NF4, d["codes"], d["am"], d["o"], d["i"]) if fmt == lnf4.FMT_NF4
+                 else lnf4.make_weight(lnf4.FMT_BF16, d["wbf"], None, d["o"], d["i"]))
+            on = d["on"]
+            out.append(lnf4.make_proj(W, A=d.get("A"), B=d.get("B"), r=wl.rank if on else 0,
+                                      scale=wl.scale if on else 0.0, y=d["y"], u=d.get("u"), dy=d["dy"],
+                                      dA=d.get("dA"), dB=d.get("dB")))
+        return out
+
+    ws_bytes = max(lnf4.lora_group_bwd_workspace(projs(e, lnf4.FMT_NF4), T) for e in groups)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def gemms(fmt):
+        for e in groups:                      # forward
+            lnf4.lora_group_fwd(projs(e, fmt), e["x"], T, 1)
+        for e in groups:                      # recompute
+            lnf4.lora_group_fwd(projs(e, fmt), e["x"], T, 1)
+        for e in reversed(groups):            # backward
+            lnf4.lora_group_bwd(projs(e, fmt), e["x"], T, e["dx"], 0, ws, ws_bytes)
+
+    def dequant():
+        for e in groups:
+            for d in e["p"]:
+                lnf4.nf4_dequant(d["codes"], d["am"], d["o"] * d["i"], 64, d["wbf"])
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    fused = timed(lambda: gemms(lnf4.FMT_NF4))
+    dq = timed(dequant)
+    bf = timed(lambda: gemms(lnf4.FMT_BF16))
+    # the unfused path decodes the layer once per read: twice per layer step
+    unfused = 2 * dq + bf
+    return {"layer_step_fused_ms": round(fused, 4), "dequant_layer_ms": round(dq, 4),
+            "layer_step_bf16_gemms_ms": round(bf, 4), "layer_step_unfused_ms": round(unfused, 4),
+            "dequant_share_of_unfused": round(2 * dq / unfused, 4),
+            "fused_speedup_over_unfused": round(unfused / fused, 3),
+            "dequant_GBps": round(sum(d["o"] * d["i"] for e in groups for d in e["p"]) * 2.5625 / (dq / 1000) / 1e9, 1)}
+
+
+def t_sweep(wl, seed: int, nbuf: int, steps: int, tokens=(2048, 4096, 8192)):
+    """Streamed and resident stack step at several batch sizes (where copy stops dominating)."""
+    import torch
+    from lora_fine_tuning_nf4_amd.stack import StreamedStack
+
+    out = []
+    for T in tokens:
+        stack = StreamedStack(wl, n_bufs=nbuf, seed=seed, tokens=T)
+        try:
+            res = {}
+            for mode in ("streamed", "resident"):
+                for _ in range(2):
+                    stack.step(resident=(mode == "resident"))
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    stack.step(resident=(mode == "resident"))
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) * 1000.0 / steps
+                res[mode] = {"ms_per_step": round(ms, 2), "tokens_per_s": round(T / (ms / 1000.0), 1)}
+        finally:
+            stack.close()
+            del stack
+            torch.cuda.empty_cache()
+        out.append({"tokens": T, **res, "exposed_copy_ms": round(res["streamed"]["ms_per_step"] -
+                                                                  res["resident"]["ms_per_step"], 2)})
+        log(f"T={T}: {out[-1]}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +258,8 @@ def main():
     ap.add_argument("--no-resident", action="store_true", help="skip the H2D-removed reference run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--study", action="store_true",
+                    help="also measure the dequant share (fused vs dequant + bf16 GEMMs) and a T sweep")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -174,11 +293,11 @@ def main():
         stack.step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K streamed steps, with HIP events around every grouped GEMM call
-    keys = [("fwd", gi, True) for gi in range(len(GROUPS))] + [("bwd", gi, True) for gi in range(len(GROUPS))]
-    if stack.dpo:
-        keys += [("fwd", gi, False) for gi in range(len(GROUPS))]
-    stack.timers = {k: ([], []) for k in keys}
+    # ---- timed region: K streamed steps; HIP events on the compute stream (where the
+    # kernels run) around every launch of the dominant kernel only, so the events cost the
+    # step next to nothing
+    dom_key = ("fwd", 2, True)
+    stack.timers = {dom_key: ([], [])}
     b0 = stack.bytes_copied()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -187,23 +306,34 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     b1 = stack.bytes_copied()
-    timers = stack.timers
+    dom_timer = stack.timers[dom_key]
     stack.timers = None
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     tokens = stack.T
     value = tokens / (ms_per_step / 1000.0)
 
-    # per-call GEMM times (ms)
+    # per-call GEMM times (ms) for the breakdown: extra steps after the timed region with
+    # events around every grouped call
+    keys = [("fwd", gi, True) for gi in range(len(GROUPS))] + [("bwd", gi, True) for gi in range(len(GROUPS))]
+    if stack.dpo:
+        keys += [("fwd", gi, False) for gi in range(len(GROUPS))]
+    n_bd = max(1, min(2, args.steps))
+    stack.timers = {k: ([], []) for k in keys}
+    for _ in range(n_bd):
+        stack.step()
+    torch.cuda.synchronize()
+    timers = stack.timers
+    stack.timers = None
     call_ms = {}
     for k, (st, en) in timers.items():
-        ts = [a.elapsed_time(b) for a, b in zip(st, en)]
-        call_ms[k] = ts
-    gemm_time_ms = sum(sum(v) for v in call_ms.values()) / args.steps
+        call_ms[k] = [a.elapsed_time(b) for a, b in zip(st, en)]
+    gemm_time_ms = sum(sum(v) for v in call_ms.values()) / n_bd
     gemm_flops_step = 0.0
     for (kind, gi, _on), ts in call_ms.items():
-        gemm_flops_step += gemm_flops(wl, GROUPS[gi], kind) * len(ts) / args.steps
-    # dominant kernel: the gate|up forward GEMM (the largest single launch of the step)
-    dom = call_ms[("fwd", 2, True)]
+        gemm_flops_step += gemm_flops(wl, GROUPS[gi], kind) * len(ts) / n_bd
+    # dominant kernel: the gate|up forward GEMM (the largest single launch of the step),
+    # timed inside the timed region
+    dom = [a.elapsed_time(b) for a, b in zip(*dom_timer)]
     dom_ms = sum(dom) / len(dom)
     dom_flops = gemm_flops(wl, GROUPS[2], "fwd")
     achieved = dom_flops / (dom_ms / 1000.0) / 1e12
@@ -335,6 +465,13 @@ def main():
     stack.close()
     del stack
     torch.cuda.empty_cache()
+
+    if args.study:
+        log("study: dequant share ...")
+        result["study"] = {"dequant_share": dequant_share(wl, args.seed)}
+        torch.cuda.empty_cache()
+        log("study: T sweep ...")
+        result["study"]["t_sweep"] = t_sweep(wl, args.seed, args.nbuf, max(2, args.steps // 2))
 
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on one layer ...")

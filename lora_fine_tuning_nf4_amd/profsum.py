@@ -60,10 +60,12 @@ def trace(trace_dir: str, bench_json: str, command: str) -> str:
     out.append(f"dominant launch: {DOM_NAME} with grid {DOM_GRID} (gate|up forward, M=2048 N=28672 K=4096)")
     out.append(f"  dispatches in the trace: {len(dom)}")
     if bench is not None and dom:
+        # the bench's warm-up steps come first, then its timed steps
         n = int(bench["roofline"]["launches_timed"])
-        timed = [d for _, d in dom[-n:]]
+        skip = int(bench["warmup"]) * (n // int(bench["steps"]))
+        timed = [d for _, d in dom[skip:skip + n]]
         avg = sum(timed) / len(timed) / 1e6
-        out.append(f"  timed-region dispatches (last {n}): avg {avg:.4f} ms, "
+        out.append(f"  timed-region dispatches (#{skip}..#{skip + n - 1}): avg {avg:.4f} ms, "
                    f"min {min(timed) / 1e6:.4f} ms, max {max(timed) / 1e6:.4f} ms")
         out.append(f"  bench.py HIP-event average in the same run: {bench['roofline']['avg_launch_ms']:.4f} ms "
                    f"(ratio {bench['roofline']['avg_launch_ms'] / avg:.3f})")
