@@ -21,4 +21,5 @@ nf4         code table, bf16 rounding, quantize / pack / decode
 lora        LoRA linear forward and backward (plain matrix definitions)
 stream_sim  the layer-stream schedule and its event log
 layer       one decoder layer's projections composed into a layer step
+head        embedding gather, token cross-entropy, sequence sums, sigmoid DPO
 """
