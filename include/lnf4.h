@@ -193,6 +193,75 @@ int lora_group_bwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
 int lnf4_shard_layout(int32_t n_proj, const int64_t* out_f, const int64_t* in_f, int32_t fmt,
                       int64_t* offsets, int64_t* total_bytes);
 
+/* ------------------------------------------------------------------ output side
+ * The vocab-sized embed_tokens and the untied lm_head take turns in one device slot
+ * of the layer stream (Soup deep dive, "Core feature: how layer streaming works"): the
+ * embedding lookup reads the slot at the start of a step, and the output head plus its
+ * loss read it at the forward/backward turn, optionally a chunk of tokens at a time
+ * (the stream_loss_chunk key, same article, "Streaming config keys").  The lm_head
+ * GEMMs themselves are lora_linear_fwd / lora_linear_bwd with a BF16 weight [V, H]
+ * pointing into the slot and the adapter off.
+ */
+
+/*
+ * Embedding lookup: out[t][:] = table[ids[t]][:] (bf16 rows copied bitwise).
+ *   table   device bf16 [vocab, hidden] (the slot holding embed_tokens), 16-byte aligned
+ *   hidden  a positive multiple of 8
+ *   ids     device int32 [T]; an id outside [0, vocab) yields a zero row (device ids
+ *           cannot be checked by the host)
+ *   out     device bf16 [T, hidden], 16-byte aligned
+ * Errors: EINVAL (T, NULL), ESHAPE (vocab, hidden), EALIGN, EHIP.
+ */
+int lnf4_embed_gather(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* ids, int64_t T,
+                      uint16_t* out, hipStream_t stream);
+
+/*
+ * Token cross-entropy on bf16 logits [T, V] from the output head:
+ *   lse_t        = log sum_j exp(l[t][j])                          (fp32)
+ *   logp[t]      = l[t][label_t] - lse_t
+ *   dlogits[t][j] = bf16( g_t * (exp(l[t][j] - lse_t) - [j == label_t]) )
+ *   g_t          = grad_scale * (seq_scale ? seq_scale[t / rows_per_scale] : 1)
+ * so grad_scale = 1/T gives the gradient of the mean token loss, and a per-sequence
+ * seq_scale carries a sequence-level objective (the preference loss) back to tokens.
+ * A label outside [0, V) marks an ignored token: logp 0 and a zero gradient row.
+ *   logits   device bf16 [T, V], V a positive multiple of 8, 16-byte aligned
+ *   labels   device int32 [T]
+ *   seq_scale device fp32 [ceil(T / rows_per_scale)] or NULL
+ *   logp     device fp32 [T] or NULL;  dlogits device bf16 [T, V] or NULL (one of the
+ *            two is required).  dlogits may alias logits (each row is read in full
+ *            before it is overwritten by the same workgroup).
+ * Every reduction has a fixed order: bitwise reproducible.
+ * Errors: EINVAL (T, NULL, rows_per_scale < 1, non-finite grad_scale), ESHAPE (V), EALIGN, EHIP.
+ */
+int lnf4_cross_entropy(const uint16_t* logits, int64_t T, int64_t vocab, const int32_t* labels, float grad_scale,
+                       const float* seq_scale, int64_t rows_per_scale, float* logp, uint16_t* dlogits,
+                       hipStream_t stream);
+
+/*
+ * Per-sequence sums of token values (log-probs): sums[i] = sum_{j < seq_len} x[i*seq_len + j],
+ * fp32 in a fixed order.  x device fp32 [n_seq * seq_len]; sums device fp32 [n_seq].
+ * Errors: EINVAL, EALIGN, EHIP.
+ */
+int lnf4_sequence_sums(const float* x, int32_t n_seq, int64_t seq_len, float* sums, hipStream_t stream);
+
+/*
+ * Sigmoid preference loss over n_pairs pairs of sequence log-prob sums, ordered
+ * (chosen_0, rejected_0, chosen_1, ...).  The reference sums come from the same
+ * streamed base with the adapters off (Soup 4 GB article, "Memory-free reference
+ * model"; 20B-RLHF article, step 3).  The pages name the preference step but give no
+ * formula; the reading taken is the standard sigmoid form with temperature beta:
+ *   m_p  = beta * ((pol[2p] - ref[2p]) - (pol[2p+1] - ref[2p+1]))
+ *   loss = mean_p log(1 + exp(-m_p))
+ *   coef[2p] = -beta * sigmoid(-m_p) / P,  coef[2p+1] = +beta * sigmoid(-m_p) / P
+ * coef is dloss / dpol, and a token's loss is minus its log-prob, so passing coef as
+ * seq_scale to lnf4_cross_entropy with grad_scale = -1 and rows_per_scale = sequence
+ * length gives the gradient of the preference loss with respect to the policy logits.
+ *   pol_sums, ref_sums device fp32 [2 n_pairs]; loss device fp32 [1]; coef device fp32 [2 n_pairs]
+ * Errors: EINVAL (n_pairs outside 1..2^20, beta not finite or <= 0, NULL), EALIGN, EHIP.
+ */
+int lnf4_dpo_loss(const float* pol_sums, const float* ref_sums, int32_t n_pairs, float beta, float* loss, float* coef,
+                  hipStream_t stream);
+
 /* ------------------------------------------------------------------ layer stream */
 typedef struct lnf4_stream lnf4_stream;
 

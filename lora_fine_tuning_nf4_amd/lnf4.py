@@ -77,6 +77,10 @@ def _declare(L):
         "lora_group_bwd": (i32, [POINTER(lnf4_proj), i32, vp, i64, vp, i32, vp, sz, vp]),
         "lnf4_shard_layout": (i32, [i32, POINTER(c_int64), POINTER(c_int64), i32, POINTER(c_int64),
                                     POINTER(c_int64)]),
+        "lnf4_embed_gather": (i32, [vp, i64, i64, vp, i64, vp, vp]),
+        "lnf4_cross_entropy": (i32, [vp, i64, i64, vp, f32, vp, i64, vp, vp, vp]),
+        "lnf4_sequence_sums": (i32, [vp, i32, i64, vp, vp]),
+        "lnf4_dpo_loss": (i32, [vp, vp, i32, f32, vp, vp, vp]),
         "stream_create": (i32, [POINTER(c_void_p), POINTER(c_size_t), i32, POINTER(c_void_p), sz, i32,
                                 POINTER(c_int32), i32, i32, vp, vp, sz, POINTER(c_void_p)]),
         "stream_layer_step": (i32, [vp, i32, vp, POINTER(c_void_p)]),
@@ -215,6 +219,26 @@ def lnf4_shard_layout(out_f, in_f, fmt: int):
     total = c_int64()
     _check(lib().lnf4_shard_layout(n, o, i, fmt, offs, ctypes.byref(total)))
     return [offs[k] for k in range(2 * n)], total.value
+
+
+# ------------------------------------------------------------------ output side
+def lnf4_embed_gather(table, vocab: int, hidden: int, ids, T: int, out, stream=None):
+    _check(lib().lnf4_embed_gather(_ptr(table), vocab, hidden, _ptr(ids), T, _ptr(out), _stream(stream)))
+
+
+def lnf4_cross_entropy(logits, T: int, vocab: int, labels, grad_scale: float, seq_scale, rows_per_scale: int, logp,
+                       dlogits, stream=None):
+    _check(lib().lnf4_cross_entropy(_ptr(logits), T, vocab, _ptr(labels), grad_scale, _ptr(seq_scale),
+                                    rows_per_scale, _ptr(logp), _ptr(dlogits), _stream(stream)))
+
+
+def lnf4_sequence_sums(x, n_seq: int, seq_len: int, sums, stream=None):
+    _check(lib().lnf4_sequence_sums(_ptr(x), n_seq, seq_len, _ptr(sums), _stream(stream)))
+
+
+def lnf4_dpo_loss(pol_sums, ref_sums, n_pairs: int, beta: float, loss, coef, stream=None):
+    _check(lib().lnf4_dpo_loss(_ptr(pol_sums), _ptr(ref_sums), n_pairs, beta, _ptr(loss), _ptr(coef),
+                               _stream(stream)))
 
 
 # ------------------------------------------------------------------ layer stream

@@ -11,6 +11,7 @@ used here; these synthetic stand-ins have the checkpoints' layer shapes):
   adapter B         ~ N(0, 0.01)            bf16
   activations x     ~ N(0, 1)               bf16
   output grads dy   ~ N(0, 1)               bf16
+  token ids         ~ U{0, ..., vocab-1}    int32 (inputs and labels)
 Every tensor has its own stream, keyed by (seed, workload, layer, name).
 """
 from __future__ import annotations
@@ -113,6 +114,11 @@ def act_bits(rows: int, cols: int, seed: int, *keys) -> np.ndarray:
     return to_bf16_bits(normal_f32((rows, cols), 1.0, seed, "act", *keys))
 
 
+def token_ids(n: int, vocab: int, seed: int, *keys) -> np.ndarray:
+    """n uniform random token ids in [0, vocab), int32."""
+    return rng(seed, "ids", *keys).integers(0, vocab, size=n).astype(np.int32)
+
+
 # ------------------------------------------------------------------ device draws
 def device_normal(shape, std: float, seed: int, *keys, dtype=None, device="cuda"):
     """torch normal draws made on the device (large workloads), keyed like the host draws."""
@@ -131,3 +137,12 @@ def device_uniform(shape, bound: float, seed: int, *keys, dtype=None, device="cu
     g.manual_seed(int.from_bytes(h[:8], "little") & ((1 << 63) - 1))
     t = (torch.rand(shape, generator=g, device=device, dtype=torch.float32) * 2.0 - 1.0) * bound
     return t if dtype is None else t.to(dtype)
+
+
+def device_token_ids(n: int, vocab: int, seed: int, *keys, device="cuda"):
+    """n uniform random token ids in [0, vocab) drawn on the device, int32."""
+    import torch
+    h = hashlib.sha256(repr((int(seed),) + tuple(str(k) for k in keys)).encode()).digest()
+    g = torch.Generator(device=device)
+    g.manual_seed(int.from_bytes(h[:8], "little") & ((1 << 63) - 1))
+    return torch.randint(0, vocab, (n,), generator=g, device=device, dtype=torch.int64).to(torch.int32)

@@ -143,3 +143,31 @@ def test_size_limits(L):
     w = lnf4.make_weight(lnf4.FMT_NF4, FAKE, FAKE, 1024, 1 << 20, 64)       # codes 2^29 bytes: fine
     assert L.lora_linear_fwd(ctypes.byref(w), FAKE, 1 << 11, None, None, 0, 0.0, FAKE, None, None) \
         == lnf4.LNF4_ESHAPE                                                 # x: 2^11 x 2^20 bf16 = 2^32 bytes
+
+
+def test_output_side_validation(L):
+    # embedding gather
+    assert L.lnf4_embed_gather(FAKE, 100, 12, FAKE, 4, FAKE, None) == lnf4.LNF4_ESHAPE    # hidden % 8
+    assert L.lnf4_embed_gather(FAKE, 0, 16, FAKE, 4, FAKE, None) == lnf4.LNF4_ESHAPE      # empty vocab
+    assert L.lnf4_embed_gather(None, 100, 16, FAKE, 4, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.lnf4_embed_gather(FAKE + 2, 100, 16, FAKE, 4, FAKE, None) == lnf4.LNF4_EALIGN
+    assert L.lnf4_embed_gather(FAKE, 100, 16, FAKE, -1, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.lnf4_embed_gather(None, 100, 16, None, 0, None, None) == lnf4.LNF4_OK        # T = 0: no-op
+    # cross-entropy
+    ce = L.lnf4_cross_entropy
+    assert ce(FAKE, 4, 100, FAKE, 1.0, None, 1, FAKE, FAKE, None) == lnf4.LNF4_ESHAPE     # V % 8
+    assert ce(FAKE, 4, 96, FAKE, 1.0, None, 1, None, None, None) == lnf4.LNF4_EINVAL      # nothing asked for
+    assert ce(FAKE, 4, 96, None, 1.0, None, 1, FAKE, None, None) == lnf4.LNF4_EINVAL      # labels missing
+    assert ce(FAKE, 4, 96, FAKE, 1.0, FAKE, 0, FAKE, None, None) == lnf4.LNF4_EINVAL      # rows_per_scale
+    assert ce(FAKE, 4, 96, FAKE, float("nan"), None, 1, FAKE, None, None) == lnf4.LNF4_EINVAL
+    assert ce(FAKE + 8, 4, 96, FAKE, 1.0, None, 1, FAKE, None, None) == lnf4.LNF4_EALIGN
+    assert ce(FAKE, 4, 96, FAKE, 1.0, None, 1, None, FAKE + 2, None) == lnf4.LNF4_EALIGN
+    assert ce(None, 0, 96, None, 1.0, None, 1, None, None, None) == lnf4.LNF4_OK
+    # sequence sums and the preference loss
+    assert L.lnf4_sequence_sums(FAKE, 2, 0, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.lnf4_sequence_sums(FAKE, -1, 8, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.lnf4_sequence_sums(None, 0, 8, None, None) == lnf4.LNF4_OK
+    assert L.lnf4_dpo_loss(FAKE, FAKE, 0, 0.1, FAKE, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.lnf4_dpo_loss(FAKE, FAKE, 2, 0.0, FAKE, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.lnf4_dpo_loss(FAKE, None, 2, 0.1, FAKE, FAKE, None) == lnf4.LNF4_EINVAL
+    assert L.lnf4_dpo_loss(FAKE, FAKE, 2, 0.1, FAKE + 1, FAKE, None) == lnf4.LNF4_EALIGN
