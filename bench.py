@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Train tokens/s of the layer-streamed NF4 + LoRA stack on one MI355X.
 
-One step = one pass of the whole hot path over one batch: the embed slot copy, the
-forward of every layer (fused NF4 decode + MFMA GEMMs + rank-r LoRA terms, streamed
-from pinned host shards through 2 device layer buffers), the lm_head slot copy, and the
-backward of every layer in reverse (second read of the layer, forward recompute, input
-gradients, adapter gradients).  Default workload: the Llama-3.1-8B-shaped stack (32
+One step = one pass of the whole hot path over one batch: the embed slot copy and the
+embedding lookup, the forward of every layer (fused NF4 decode + MFMA GEMMs + rank-r
+LoRA terms, streamed from pinned host shards through 2 device layer buffers), the
+lm_head slot copy, the untied lm_head GEMM, token cross-entropy and lm_head input
+gradient, and the backward of every layer in reverse (second read of the layer, forward
+recompute, input gradients, adapter gradients).  Default workload: the Llama-3.1-8B-shaped stack (32
 layers of q, k, v, o, gate, up, down NF4 projections, LoRA r=8 alpha=32 on q and v,
 batch 1 x seq 2048), synthetic seeded weights and activations already resident in device
 memory / pinned host memory when the timed region starts.
@@ -57,6 +58,24 @@ def fwd_bytes(wl, group):
         if p in wl.adapted:
             b += 2 * o * wl.rank + 4 * T * wl.rank
     return b
+
+
+def head_summary(wl, stack, head_ms):
+    """Time of the output side at the forward/backward turn (lm_head GEMMs + cross-entropy
+    [+ sequence sums and DPO loss]) and the rate of its two GEMMs."""
+    if not stack.head:
+        return None
+    T, V, H = stack.T, wl.vocab, wl.hidden
+    n_chunks = -(-T // stack.chunk)
+    out = {"loss_chunk_tokens": stack.chunk, "chunks": n_chunks}
+    for part, ms in head_ms.items():
+        gemms = 2 if part in ("sft", "pol") else 1                # logits, and dh where there is a gradient
+        if part == "pol" and n_chunks > 1:
+            gemms += 1                                            # logits again for the gradient pass
+        flops = gemms * 2.0 * T * V * H
+        out[f"{part}_ms"] = round(ms, 4)
+        out[f"{part}_gemm_tflops_incl_loss"] = round(flops / (ms / 1000.0) / 1e12, 2)
+    return out
 
 
 def kernel_source_hash() -> str:
@@ -258,6 +277,8 @@ def main():
     ap.add_argument("--no-resident", action="store_true", help="skip the H2D-removed reference run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--loss-chunk", type=int, default=None,
+                    help="tokens per chunk of the output head and its loss (default: all tokens at once)")
     ap.add_argument("--study", action="store_true",
                     help="also measure the dequant share (fused vs dequant + bf16 GEMMs) and a T sweep")
     args = ap.parse_args()
@@ -284,7 +305,7 @@ def main():
     torch.cuda.set_device(0)
 
     t_setup = time.perf_counter()
-    stack = StreamedStack(wl, n_bufs=args.nbuf, seed=args.seed, layers=L)
+    stack = StreamedStack(wl, n_bufs=args.nbuf, seed=args.seed, layers=L, loss_chunk=args.loss_chunk)
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s: {L} layers x {stack.shard_bytes / 1e6:.1f} MB shards, "
         f"nbuf={args.nbuf}, T={stack.T}")
@@ -317,6 +338,8 @@ def main():
     keys = [("fwd", gi, True) for gi in range(len(GROUPS))] + [("bwd", gi, True) for gi in range(len(GROUPS))]
     if stack.dpo:
         keys += [("fwd", gi, False) for gi in range(len(GROUPS))]
+    head_keys = ([("head", "ref"), ("head", "pol")] if stack.dpo else [("head", "sft")]) if stack.head else []
+    keys += head_keys
     n_bd = max(1, min(2, args.steps))
     stack.timers = {k: ([], []) for k in keys}
     for _ in range(n_bd):
@@ -324,9 +347,13 @@ def main():
     torch.cuda.synchronize()
     timers = stack.timers
     stack.timers = None
-    call_ms = {}
+    call_ms, head_ms = {}, {}
     for k, (st, en) in timers.items():
-        call_ms[k] = [a.elapsed_time(b) for a, b in zip(st, en)]
+        ms = [a.elapsed_time(b) for a, b in zip(st, en)]
+        if k[0] == "head":
+            head_ms[k[1]] = sum(ms) / max(1, len(ms))
+        else:
+            call_ms[k] = ms
     gemm_time_ms = sum(sum(v) for v in call_ms.values()) / n_bd
     gemm_flops_step = 0.0
     for (kind, gi, _on), ts in call_ms.items():
@@ -341,6 +368,8 @@ def main():
     dx_ms = sum(dx_dom) / len(dx_dom)
 
     traffic, traffic_src = measured_traffic()
+    if (wl.name, stack.T, L) != ("llama8b", 2048, 32):
+        traffic, traffic_src = None, "counters were taken on the llama8b T=2048 gate|up launch only"
     breakdown = {f"{k[0]}_{'+'.join(GROUPS[k[1]])}{'' if k[2] else '_adapters_off'}_ms":
                  round(sum(v) / len(v), 4) for k, v in call_ms.items() if v}
 
@@ -360,12 +389,14 @@ def main():
         "config": {"workload": wl.name, "layers": L, "tokens_per_step": tokens, "global_batch": 1,
                    "seq_len": tokens, "lora": {"r": wl.rank, "alpha": wl.alpha, "targets": list(wl.adapted)},
                    "weights": wl.fmt, "stream_buffers": args.nbuf,
-                   "head_slot": bool(stack.slot is not None), "parallelism": "single GPU"},
+                   "head_slot": bool(stack.slot is not None), "loss_chunk": stack.chunk if stack.head else None,
+                   "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "traffic_source": traffic_src,
             "algorithmic_bytes_per_launch": fwd_bytes(wl, GROUPS[2]),
-            "kernel": "k_fwd<NF4,BM=256,4 waves> gate|up forward: M=2048 N=28672 K=4096 (fused NF4 decode), one launch",
+            "kernel": (f"k_fwd<NF4,BM=256,4 waves> gate|up forward: M={stack.T} N={sum(wl.shapes[p][0] for p in GROUPS[2])} "
+                       f"K={wl.shapes[GROUPS[2][0]][1]} (fused NF4 decode), one launch"),
             "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4),
             "launches_timed": len(dom),
         },
@@ -377,6 +408,7 @@ def main():
             "dx_gate_up_tflops": round(gemm_flops(wl, GROUPS[2], "bwd") / (dx_ms / 1000) / 1e12, 2),
             "per_call_avg_ms": breakdown,
         },
+        "head": head_summary(wl, stack, head_ms),
         "h2d": {
             "bytes_per_step": (b1 - b0) // args.steps,
             "avg_GBps_over_step": round((b1 - b0) / args.steps / (ms_per_step / 1000.0) / 1e9, 2),

@@ -8,10 +8,19 @@ gradients and adapter gradients are formed; a DPO step first runs the same strea
 with the adapters off (4 GB-laptop Soup article, "Memory-free reference model").  The
 vocab-sized embed_tokens and untied lm_head share one device slot.
 
-Only the linear projections are on this path: the attention core, norms, activations and
-the loss head between them are not, so every projection group reads its own synthetic
-checkpointed input and every projection its own synthetic output gradient.  All work is
-enqueued by C ABI calls; this module only lays out memory and orders the calls.
+The output side runs where the slot schedule puts it: the embedding lookup of the step's
+token ids at the start (embed_tokens in the slot), and at the forward/backward turn the
+untied lm_head (a bf16 [vocab, hidden] GEMM), the token cross-entropy and the lm_head's
+input gradient, optionally a chunk of tokens at a time (the ``stream_loss_chunk`` key of
+the Soup deep dive, "Streaming config keys").  A DPO step takes log-prob sums over each
+sequence in the reference pass and the policy pass and turns the sigmoid preference loss
+into per-sequence gradient scales of the policy's cross-entropy.
+
+The attention core, norms and activations between the projections are not on this path,
+so every projection group reads its own synthetic checkpointed input, every projection
+its own synthetic output gradient, and the lm_head a synthetic final hidden state (one
+for the policy pass, one for the reference pass).  All work is enqueued by C ABI calls;
+this module only lays out memory and orders the calls.
 """
 from __future__ import annotations
 
@@ -48,7 +57,7 @@ class LayerState:
 class StreamedStack:
     def __init__(self, wl: synthgen.Workload, n_bufs: int = 2, seed: int = 0,
                  layers: int | None = None, tokens: int | None = None, head_slot: bool = True,
-                 dpo: bool | None = None, device: str = "cuda"):
+                 dpo: bool | None = None, loss_chunk: int | None = None, device: str = "cuda"):
         self.wl = wl
         self.L = layers if layers is not None else wl.layers
         self.T = tokens if tokens is not None else wl.tokens
@@ -93,6 +102,7 @@ class StreamedStack:
                 sizes.append(nbytes)
             self.slot = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.all_shards = shards
+        self._init_output_side(loss_chunk)
 
         # ---- per-layer adapters, checkpointed inputs, output gradients, gradients
         r = wl.rank
@@ -130,6 +140,42 @@ class StreamedStack:
         self.st_res = None
         self.res_bufs = None
 
+    def _init_output_side(self, loss_chunk):
+        """Token ids, labels, the synthetic final hidden states, and the head's logits,
+        log-prob and gradient buffers (nothing when the workload has no head slot)."""
+        self.head = self.slot is not None
+        if not self.head:
+            return
+        wl, T, dev, seed = self.wl, self.T, self.dev, self.seed
+        V, H = wl.vocab, wl.hidden
+        bf16, f32 = torch.bfloat16, torch.float32
+        self.ids = synthgen.device_token_ids(T, V, seed, "ids")
+        self.labels = synthgen.device_token_ids(T, V, seed, "labels")
+        self.h0 = torch.empty((T, H), dtype=bf16, device=dev)                  # embedding rows
+        self.h_last = synthgen.device_normal((T, H), 1.0, seed, "h_last", dtype=bf16)
+        self.logp = torch.empty(T, dtype=f32, device=dev)
+        self.dh = torch.empty((T, H), dtype=bf16, device=dev)                  # gradient into h_last
+        chunk = T if not loss_chunk else min(int(loss_chunk), T)
+        if self.dpo:
+            self.seq_len = int(wl.extra.get("seq_len", T // 4))
+            self.beta = float(wl.extra.get("beta", 0.1))
+            if T % (2 * self.seq_len):
+                raise ValueError(f"T={T} is not a whole number of (chosen, rejected) pairs of {self.seq_len}")
+            self.n_seq = T // self.seq_len
+            # a chunk covers whole sequences, so its rows find their sequence's scale
+            chunk = max(self.seq_len, chunk // self.seq_len * self.seq_len)
+            self.h_last_ref = synthgen.device_normal((T, H), 1.0, seed, "h_last_ref", dtype=bf16)
+            self.ref_logp = torch.empty(T, dtype=f32, device=dev)
+            self.ref_sums = torch.empty(self.n_seq, dtype=f32, device=dev)
+            self.pol_sums = torch.empty(self.n_seq, dtype=f32, device=dev)
+            self.loss = torch.empty(1, dtype=f32, device=dev)
+            self.coef = torch.empty(self.n_seq, dtype=f32, device=dev)
+        self.chunk = chunk
+        self.logits = torch.empty((chunk, V), dtype=bf16, device=dev)       # dlogits overwrite it in place
+        self.head_ws_bytes = max(256, lnf4.lora_linear_bwd_workspace(chunk, V, H, 0))
+        self.head_ws = torch.empty(self.head_ws_bytes, dtype=torch.uint8, device=dev)
+        self.res_head = None
+
     def enable_resident(self):
         """A second context over the same host shards with one device buffer per layer:
         every layer is copied once, then steps run with no host-to-device traffic (the same
@@ -138,6 +184,15 @@ class StreamedStack:
             self.res_bufs = [torch.empty(self.shard_bytes, dtype=torch.uint8, device=self.dev) for _ in range(self.L)]
             self.st_res = lnf4.stream_create(self.host, [self.shard_bytes] * self.L, self.res_bufs, self.shard_bytes,
                                              self.schedule, 1, self.copy)
+            if self.head:
+                # embed_tokens and lm_head each resident in a buffer of their own
+                self.res_head = []
+                for sid in self.head_ids:
+                    h = self.all_shards[sid]
+                    d = torch.empty(h.numel(), dtype=torch.uint8, device=self.dev)
+                    d.copy_(h)
+                    self.res_head.append(d)
+                torch.cuda.synchronize(self.dev)
         return self.st_res
 
     # ------------------------------------------------------------------ set-up helpers
@@ -176,54 +231,133 @@ class StreamedStack:
         return out
 
     # ------------------------------------------------------------------ one step
-    def _group_fwd(self, layer, gi, base, adapters):
+    def _mark(self, key, end: int):
         tm = self.timers
-        key = ("fwd", gi, adapters)
         if tm is not None and key in tm:
-            tm[key][0].append(torch.cuda.Event(enable_timing=True))
-            tm[key][0][-1].record(self.compute)
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(self.compute)
+            tm[key][end].append(ev)
+
+    def _lm_head(self, ptr):
+        return lnf4.make_weight(lnf4.FMT_BF16, ptr, None, self.wl.vocab, self.wl.hidden, 64)
+
+    def _chunks(self):
+        return [(c0, min(self.chunk, self.T - c0)) for c0 in range(0, self.T, self.chunk)]
+
+    def _logits(self, W, h, c0, n):
+        lnf4.lora_linear_fwd(W, h[c0:c0 + n], n, None, None, 0, 0.0, self.logits, None, self.compute)
+
+    def _head_dx(self, W, c0, n):
+        # dh = dlogits W (the lm_head is frozen: no weight gradient)
+        lnf4.lora_linear_bwd(W, self.h_last[c0:c0 + n], self.logits, n, None, None, 0, 0.0, None,
+                             self.dh[c0:c0 + n], None, None, 0, self.head_ws, self.head_ws_bytes, self.compute)
+
+    def _embed(self, table_ptr):
+        lnf4.lnf4_embed_gather(table_ptr, self.wl.vocab, self.wl.hidden, self.ids, self.T, self.h0, self.compute)
+
+    def _head_sft(self, ptr):
+        """Mean token cross-entropy: logits, log-probs and dlogits (in place), dh."""
+        self._mark(("head", "sft"), 0)
+        W, V = self._lm_head(ptr), self.wl.vocab
+        for c0, n in self._chunks():
+            self._logits(W, self.h_last, c0, n)
+            lnf4.lnf4_cross_entropy(self.logits, n, V, self.labels[c0:], 1.0 / self.T, None, 1, self.logp[c0:],
+                                    self.logits, self.compute)
+            self._head_dx(W, c0, n)
+        self._mark(("head", "sft"), 1)
+
+    def _head_ref(self, ptr):
+        """Reference pass (adapters off): token log-probs and their per-sequence sums."""
+        self._mark(("head", "ref"), 0)
+        W, V = self._lm_head(ptr), self.wl.vocab
+        for c0, n in self._chunks():
+            self._logits(W, self.h_last_ref, c0, n)
+            lnf4.lnf4_cross_entropy(self.logits, n, V, self.labels[c0:], 1.0, None, 1, self.ref_logp[c0:], None,
+                                    self.compute)
+        lnf4.lnf4_sequence_sums(self.ref_logp, self.n_seq, self.seq_len, self.ref_sums, self.compute)
+        self._mark(("head", "ref"), 1)
+
+    def _head_dpo(self, ptr):
+        """Policy pass: log-prob sums, the sigmoid preference loss and its coefficients,
+        then dlogits = -coef_seq * (softmax - onehot) and dh.  With one chunk the logits
+        are still in place for the gradient; with several they are computed again."""
+        self._mark(("head", "pol"), 0)
+        W, V, S = self._lm_head(ptr), self.wl.vocab, self.seq_len
+        chunks = self._chunks()
+        for c0, n in chunks:
+            self._logits(W, self.h_last, c0, n)
+            lnf4.lnf4_cross_entropy(self.logits, n, V, self.labels[c0:], 1.0, None, 1, self.logp[c0:], None,
+                                    self.compute)
+        lnf4.lnf4_sequence_sums(self.logp, self.n_seq, S, self.pol_sums, self.compute)
+        lnf4.lnf4_dpo_loss(self.pol_sums, self.ref_sums, self.n_seq // 2, self.beta, self.loss, self.coef,
+                           self.compute)
+        for c0, n in chunks:
+            if len(chunks) > 1:
+                self._logits(W, self.h_last, c0, n)
+            lnf4.lnf4_cross_entropy(self.logits, n, V, self.labels[c0:], -1.0, self.coef[c0 // S:], S, None,
+                                    self.logits, self.compute)
+            self._head_dx(W, c0, n)
+        self._mark(("head", "pol"), 1)
+
+    def _group_fwd(self, layer, gi, base, adapters):
+        key = ("fwd", gi, adapters)
+        self._mark(key, 0)
         lnf4.lora_group_fwd(self._projs(layer, gi, base, adapters=adapters), self.layers[layer].x[gi], self.T,
                             1 if adapters else 0, self.compute)
-        if tm is not None and key in tm:
-            tm[key][1].append(torch.cuda.Event(enable_timing=True))
-            tm[key][1][-1].record(self.compute)
+        self._mark(key, 1)
 
     def _group_bwd(self, layer, gi, base):
-        tm = self.timers
         key = ("bwd", gi, True)
-        if tm is not None and key in tm:
-            tm[key][0].append(torch.cuda.Event(enable_timing=True))
-            tm[key][0][-1].record(self.compute)
+        self._mark(key, 0)
         lnf4.lora_group_bwd(self._projs(layer, gi, base, bwd=True), self.layers[layer].x[gi], self.T, self.dx[gi],
                             0, self.ws, self.ws_bytes, self.compute)
-        if tm is not None and key in tm:
-            tm[key][1].append(torch.cuda.Event(enable_timing=True))
-            tm[key][1][-1].record(self.compute)
+        self._mark(key, 1)
 
     def step(self, resident: bool = False, compute: bool = True):
         """One training step over the whole stack (all calls asynchronous on the compute stream).
-        resident=True runs the same step from the resident context (no layer copies).
-        compute=False issues the same stream calls (copies, waits, slot loads) without the
-        GEMM calls: the time of the stream schedule alone."""
+        resident=True runs the same step from the resident context (no layer copies; the
+        head matrices sit in buffers of their own).  compute=False issues the same stream
+        calls (copies, waits, slot loads) without the kernels: the time of the stream
+        schedule alone."""
         L = self.L
         st = self.enable_resident() if resident else self.st
         slot = self.slot is not None and not resident
+        head = self.head and compute
         if slot:
             if not self._embed_in_slot:   # first step: nothing trickled in yet
                 lnf4.stream_slot_load(st, self.head_ids[0], self.compute)   # embed_tokens
-            lnf4.stream_slot_wait(st, self.compute)
+            ptr = lnf4.stream_slot_wait(st, self.compute)
             self._embed_in_slot = False
+            if head:
+                self._embed(ptr)
+        elif head:
+            self._embed(self.res_head[0])
         n_fwd = 2 * L if self.dpo else L
         for k, layer in enumerate(self.schedule):
             base = lnf4.stream_layer_step(st, k, self.compute)
+            if k == L or k == n_fwd:
+                # the output head of the forward pass that just ended.  It runs after this
+                # call's stream step, which released the last forward layer's buffer, so the
+                # next layer copy overlaps the head instead of waiting behind it.
+                if slot:
+                    ptr = lnf4.stream_slot_wait(st, self.compute)
+                elif head:
+                    ptr = self.res_head[1]
+                if head:
+                    if not self.dpo:
+                        self._head_sft(ptr)
+                    elif k == L:
+                        self._head_ref(ptr)
+                    else:
+                        self._head_dpo(ptr)
             if k < n_fwd:
                 ref_pass = self.dpo and k < L
                 for gi in range(len(GROUPS) if compute else 0):
                     self._group_fwd(layer, gi, base, adapters=not ref_pass)
-                if k == n_fwd - 1 and slot:
-                    # the untied lm_head takes the slot for the loss at the forward/backward turn
+                if slot and k == L - 1:
+                    # the untied lm_head takes the slot at the end of the first forward pass
+                    # and stays there for the second (DPO)
                     lnf4.stream_slot_load(st, self.head_ids[1], self.compute)
-                    lnf4.stream_slot_wait(st, self.compute)
             else:
                 if slot:
                     # the backward is compute-bound: the next step's embed_tokens trickles into

@@ -67,9 +67,10 @@ WORKLOADS = {
     "qwen3b_bf16": Workload("qwen3b_bf16", 2 * 1024, _decoder_shapes(2048, 16, 2, 128, 11008), 16, 32.0,
                             PROJ_ORDER, layers=36, fmt="bf16", hidden=2048),
     # DPO step on the llama8b stack: 2 pairs x (chosen, rejected) x 1024 tokens
+    # (beta: the preference loss's temperature; the pages give none, 0.1 is the common default)
     "llama8b_dpo": Workload("llama8b_dpo", 2 * 2 * 1024, _decoder_shapes(4096, 32, 8, 128, 14336), 8, 32.0,
                             ("q", "v"), layers=32, vocab=128256, hidden=4096,
-                            passes=("ref", "fwd", "recompute", "bwd")),
+                            passes=("ref", "fwd", "recompute", "bwd"), extra={"seq_len": 1024, "beta": 0.1}),
 }
 
 # q, k, v share the attention input; gate, up share the MLP input

@@ -4,7 +4,10 @@
   DPO schedules, resident mode) and every step's buffer holds its layer's shard bytes;
 * a streamed pass gives bitwise the same outputs and gradients as a resident pass
   (the pages hold the streamed-vs-resident logit difference at 0.0);
-* a small streamed stack step matches the oracle layer step for every layer.
+* a small streamed stack step matches the oracle layer step for every layer, and its
+  output side (embedding rows, token log-probs, the lm_head input gradient, the DPO loss
+  and coefficients) matches the oracle's head on the same shards, ids and labels;
+* the loss computed a chunk of tokens at a time equals the loss computed in one piece.
 """
 import numpy as np
 import pytest
@@ -18,7 +21,9 @@ if not torch.cuda.is_available():  # pragma: no cover
 import synthgen  # noqa: E402
 from lora_fine_tuning_nf4_amd import lnf4  # noqa: E402
 from lora_fine_tuning_nf4_amd.stack import StreamedStack  # noqa: E402
+from oracle import head as ohead  # noqa: E402
 from oracle import layer as olayer  # noqa: E402
+from oracle import lora as olora  # noqa: E402
 from oracle import nf4 as onf4  # noqa: E402
 from oracle import stream_sim as ss  # noqa: E402
 from helpers import bf16_f64, check_tol  # noqa: E402
@@ -93,19 +98,44 @@ def _small_workload(fmt="nf4", adapted=("q", "v"), rank=8):
                              vocab=320, hidden=256)
 
 
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).copy()
+
+
+HEAD_OUT = ("h0", "logp", "dh", "ref_logp", "ref_sums", "pol_sums", "loss", "coef")
+
+
 def _snapshot(stack):
     torch.cuda.synchronize()
     out = {"y": {p: t.view(torch.int16).cpu().numpy().copy() for p, t in stack.y.items()},
-           "dx": [t.view(torch.int16).cpu().numpy().copy() for t in stack.dx], "grads": []}
+           "dx": [t.view(torch.int16).cpu().numpy().copy() for t in stack.dx], "grads": [], "head": {}}
     for ls in stack.layers:
         out["grads"].append({p: (ls.dA[p].cpu().numpy().copy(), ls.dB[p].cpu().numpy().copy()) for p in ls.dA})
+    for name in HEAD_OUT:
+        t = getattr(stack, name, None)
+        if t is not None:
+            out["head"][name] = t.cpu().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).numpy().copy()
     return out
 
 
-@pytest.mark.parametrize("fmt", ["nf4", "bf16"])
-def test_streamed_equals_resident_bitwise(fmt):
+def _same(a, b):
+    for p in a["y"]:
+        assert np.array_equal(a["y"][p], b["y"][p]), p
+    for g in range(len(a["dx"])):
+        assert np.array_equal(a["dx"][g], b["dx"][g]), g
+    for l, gr in enumerate(a["grads"]):
+        for p in gr:
+            assert np.array_equal(gr[p][0], b["grads"][l][p][0])
+            assert np.array_equal(gr[p][1], b["grads"][l][p][1])
+    assert a["head"].keys() == b["head"].keys()
+    for k in a["head"]:
+        assert np.array_equal(a["head"][k], b["head"][k]), k
+
+
+@pytest.mark.parametrize("fmt,dpo", [("nf4", False), ("bf16", False), ("nf4", True)])
+def test_streamed_equals_resident_bitwise(fmt, dpo):
     wl = _small_workload(fmt)
-    stack = StreamedStack(wl, n_bufs=2, seed=3)
+    stack = StreamedStack(wl, n_bufs=2, seed=3, dpo=dpo)
     try:
         stack.step()
         a = _snapshot(stack)
@@ -115,15 +145,26 @@ def test_streamed_equals_resident_bitwise(fmt):
         c = _snapshot(stack)
     finally:
         stack.close()
+    assert "dh" in a["head"]
     for snap in (b, c):
-        for p in a["y"]:
-            assert np.array_equal(a["y"][p], snap["y"][p]), p
-        for g in range(len(a["dx"])):
-            assert np.array_equal(a["dx"][g], snap["dx"][g]), g
-        for l, gr in enumerate(a["grads"]):
-            for p in gr:
-                assert np.array_equal(gr[p][0], snap["grads"][l][p][0])
-                assert np.array_equal(gr[p][1], snap["grads"][l][p][1])
+        _same(a, snap)
+
+
+@pytest.mark.parametrize("dpo,chunk", [(False, 64), (False, 7), (True, 100)])
+def test_chunked_loss_equals_one_piece(dpo, chunk):
+    """The head and its loss over chunks of tokens (the last one ragged) give bitwise the
+    outputs of one piece: every row's logits, log-prob and gradient are the same sums."""
+    wl = _small_workload("nf4")
+    snaps = []
+    for lc in (None, chunk):
+        stack = StreamedStack(wl, n_bufs=2, seed=4, dpo=dpo, loss_chunk=lc)
+        try:
+            assert stack.chunk == (stack.T if lc is None else chunk)
+            stack.step()
+            snaps.append(_snapshot(stack))
+        finally:
+            stack.close()
+    _same(snaps[0], snaps[1])
 
 
 def _host_weights(stack, layer):
@@ -141,6 +182,59 @@ def _host_weights(stack, layer):
         else:
             W[p] = bf16_f64(blob[d0:d0 + o * i * 2].view(np.uint16).reshape(o, i))
     return W
+
+
+def _logp_bound(l, lab):
+    """|logp_gpu - logp| per token, l being the oracle's bf16-rounded logits: a GPU logit
+    (bf16 of an fp32 sum) can sit one bf16 step (relative 2^-8) away from the oracle's
+    where the fp32 and fp64 sums straddle a rounding boundary, so the bound is
+    2^-8 (|l_lab| + sum_j p_j |l_j|), plus 1e-4 for the fp32 accumulation and
+    log-sum-exp."""
+    lp, _ = ohead.log_softmax_rows(l)
+    rows = np.arange(l.shape[0])
+    return 2.0 ** -8 * (np.abs(l[rows, lab]) + (np.exp(lp) * np.abs(l)).sum(axis=1)) + 1e-4
+
+
+def _check_head(stack, dpo):
+    wl = stack.wl
+    V, H, T = wl.vocab, wl.hidden, stack.T
+    emb = stack.all_shards[stack.head_ids[0]].numpy().view(np.uint16).reshape(V, H)
+    lm = bf16_f64(stack.all_shards[stack.head_ids[1]].numpy().view(np.uint16).reshape(V, H))
+    ids, lab = stack.ids.cpu().numpy(), stack.labels.cpu().numpy()
+    assert np.array_equal(_bits(stack.h0), ohead.embed_gather(emb, ids))
+    h = bf16_f64(_bits(stack.h_last))
+    # the logits and their gradient are bf16 tensors by definition of the head's calls
+    # (lora_linear_fwd writes bf16(y), lnf4_cross_entropy writes bf16(dlogits)): the
+    # oracle rounds them where the definition does
+    def bf16(a):
+        return bf16_f64(onf4.bf16_rne_bits(a))
+
+    l = bf16(olora.linear_fwd(h, lm)[0])
+    bound = _logp_bound(l, lab)
+    logp = stack.logp.cpu().numpy()
+    if not dpo:
+        logp_o, _, d = ohead.cross_entropy(l, lab)
+        assert np.all(np.abs(logp - logp_o) <= bound)
+    else:
+        S, beta = stack.seq_len, stack.beta
+        l_ref = bf16(olora.linear_fwd(bf16_f64(_bits(stack.h_last_ref)), lm)[0])
+        bound_ref = _logp_bound(l_ref, lab)
+        logp_ref_o = ohead.cross_entropy(l_ref, lab)[0]
+        logp_o = ohead.cross_entropy(l, lab)[0]
+        assert np.all(np.abs(stack.ref_logp.cpu().numpy() - logp_ref_o) <= bound_ref)
+        assert np.all(np.abs(logp - logp_o) <= bound)
+        sums_ref_o, sums_o = ohead.sequence_sums(logp_ref_o, S), ohead.sequence_sums(logp_o, S)
+        bs_ref, bs = ohead.sequence_sums(bound_ref, S), ohead.sequence_sums(bound, S)
+        assert np.all(np.abs(stack.ref_sums.cpu().numpy() - sums_ref_o) <= bs_ref)
+        assert np.all(np.abs(stack.pol_sums.cpu().numpy() - sums_o) <= bs)
+        loss_o, coef_o = ohead.dpo_loss(sums_o, sums_ref_o, beta)
+        dm = beta * (bs + bs_ref).reshape(-1, 2).sum(axis=1)          # margin error bound per pair
+        P = len(dm)
+        assert abs(float(stack.loss.cpu()[0]) - loss_o) <= dm.mean() + 1e-6
+        assert np.all(np.abs(stack.coef.cpu().numpy() - coef_o) <= np.repeat(beta / P * dm / 4, 2) + 1e-6)
+        _, _, d = ohead.cross_entropy(l, lab, grad_scale=ohead.dpo_token_scale(coef_o, S))
+    dh_o = olora.linear_bwd(h, bf16(d), lm)[0]
+    check_tol(bf16_f64(_bits(stack.dh)), dh_o, "dh (lm_head input gradient)")
 
 
 @pytest.mark.parametrize("dpo", [False, True])
@@ -169,6 +263,7 @@ def test_stack_step_matches_oracle(dpo):
                 for gi, t in enumerate(stack.dx):
                     check_tol(bf16_f64(t.view(torch.int16).cpu().numpy().view(np.uint16)), ref["dx"][gi],
                               f"dx group {gi}")
+        _check_head(stack, dpo)
     finally:
         stack.close()
 
