@@ -266,6 +266,38 @@ def t_sweep(wl, seed: int, nbuf: int, steps: int, tokens=(2048, 4096, 8192)):
     return out
 
 
+def stream_variants(wl, args, L):
+    """The same streamed step with the stream variants: buffer reuse (a layer still in a
+    buffer is not copied again: at the forward/backward turn and at the next step's
+    start), and no recompute (the backward uses the forward's saved rank-r activations
+    and skips the forward re-run; the layer is still read twice, for dx)."""
+    import torch
+    from lora_fine_tuning_nf4_amd.stack import StreamedStack
+
+    out = {}
+    for name, kw in (("reuse", {"reuse": True}), ("no_recompute", {"recompute": False}),
+                     ("reuse_no_recompute", {"reuse": True, "recompute": False})):
+        stack = StreamedStack(wl, n_bufs=args.nbuf, seed=args.seed, layers=L, loss_chunk=args.loss_chunk, **kw)
+        try:
+            for _ in range(max(2, args.warmup)):
+                stack.step()
+            torch.cuda.synchronize()
+            b0 = stack.bytes_copied()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                stack.step()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+            out[name] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(stack.T / (ms / 1000.0), 2),
+                         "h2d_bytes_per_step": (stack.bytes_copied() - b0) // args.steps}
+        finally:
+            stack.close()
+            del stack
+            torch.cuda.empty_cache()
+        log(f"variant {name}: {out[name]}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +309,8 @@ def main():
     ap.add_argument("--no-resident", action="store_true", help="skip the H2D-removed reference run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the stream-variant runs (buffer reuse, no recompute)")
     ap.add_argument("--loss-chunk", type=int, default=None,
                     help="tokens per chunk of the output head and its loss (default: all tokens at once)")
     ap.add_argument("--study", action="store_true",
@@ -497,6 +531,9 @@ def main():
     stack.close()
     del stack
     torch.cuda.empty_cache()
+
+    if not args.no_variants:
+        result["stream_variants"] = stream_variants(wl, args, L)
 
     if args.study:
         log("study: dequant share ...")

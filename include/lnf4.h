@@ -265,6 +265,10 @@ int lnf4_dpo_loss(const float* pol_sums, const float* ref_sums, int32_t n_pairs,
 /* ------------------------------------------------------------------ layer stream */
 typedef struct lnf4_stream lnf4_stream;
 
+#define LNF4_STREAM_RING 0
+#define LNF4_STREAM_RESIDENT 1
+#define LNF4_STREAM_REUSE 2
+
 #define LNF4_EV_COPY 0      /* a layer copy was issued */
 #define LNF4_EV_STEP 1      /* a call made compute wait for its layer */
 #define LNF4_EV_SLOT_COPY 2 /* a head-slot copy was issued */
@@ -273,7 +277,9 @@ typedef struct lnf4_stream lnf4_stream;
 typedef struct lnf4_stream_event {
   int32_t kind;   /* LNF4_EV_* */
   int32_t call;   /* stream_layer_step call index at which it happened */
-  int32_t j;      /* COPY: schedule position (resident: shard); STEP: copy waited on; SLOT: slot load index */
+  int32_t j;      /* COPY: schedule position (resident: shard); STEP: copy waited on (reuse: the
+                     position whose copy filled the buffer, -1 for an earlier pass); SLOT: slot
+                     load index */
   int32_t layer;  /* shard index */
   int32_t buffer; /* device buffer index (-1 for the slot) */
   int32_t wait;   /* COPY: call whose release it waited for (-1: none); STEP: copy index;
@@ -288,18 +294,29 @@ typedef struct lnf4_stream_event {
  *   dev_bufs     n_bufs device buffers of buf_bytes each, 256-byte aligned
  *   n_bufs       ring mode: 2..8 (2 = double buffering).  Resident mode: == n_shards.
  *   schedule     sched_len shard indices, copied by the library
- *   resident     0: ring.  1: every shard gets its own buffer and is copied once at the
- *                first call (the "H2D removed" and bit-exactness reference run)
+ *   mode         LNF4_STREAM_RING (0): the ring below.  LNF4_STREAM_RESIDENT (1): every
+ *                shard gets its own buffer and is copied once at the first call (the "H2D
+ *                removed" and bit-exactness reference run).  LNF4_STREAM_REUSE (2): the ring
+ *                with buffer reuse (below)
  *   copy_stream  the side stream that carries every host-to-device copy
  *   slot_buf     optional device buffer for the shared embed / lm_head slot (or NULL)
  *   slot_bytes   its size
  * Ring rule: call k uses buffer k mod n_bufs; at call k every copy j <= k+n_bufs-1 not
  * yet issued is issued into buffer j mod n_bufs after the release of call j-n_bufs;
- * call k's compute waits for copy k.  Errors: EINVAL, ESHAPE, EALIGN, EHIP.
+ * call k's compute waits for copy k.
+ * Reuse rule (a stream variant beyond the pages' ring, which re-copies every read): each
+ * pass is planned from what the buffers hold.  A call whose shard sits intact in a
+ * buffer uses it with no copy (at the forward/backward turn the last n_bufs forward
+ * layers, at the next pass's start the first n_bufs layers).  Otherwise its shard is
+ * copied into the least recently used buffer (lowest index on ties), issued at call
+ * max(j - n_bufs + 1, u + 1) where u is that buffer's last user in the pass, after u's
+ * release.  A STEP event's j is then the position whose copy filled the buffer (-1: a
+ * previous pass).  SFT steady state: 2L - 2 n_bufs copies per pass instead of 2L.
+ * Errors: EINVAL (also mode outside 0..2), ESHAPE, EALIGN, EHIP.
  */
 int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards,
                   void* const* dev_bufs, size_t buf_bytes, int32_t n_bufs, const int32_t* schedule,
-                  int32_t sched_len, int32_t resident, hipStream_t copy_stream, void* slot_buf,
+                  int32_t sched_len, int32_t mode, hipStream_t copy_stream, void* slot_buf,
                   size_t slot_bytes, lnf4_stream** out);
 
 /*

@@ -463,6 +463,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
       bc1 = bn1;                                                                               \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                         \
+    /* the next block's first B fragments exist before the loop's exit test: otherwise */     \
+    /* their decode sinks past it and stalls the next block's first MFMAs */                  \
+    asm volatile("" ::"v"(bc0), "v"(bc1));                                                     \
     if (FMT == 0) {                                                                            \
       cw0 = nw0;                                                                               \
       cw1 = nw1;                                                                               \
@@ -1004,6 +1007,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       bc1 = bn1;                                                                               \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                         \
+    asm volatile("" ::"v"(bc0), "v"(bc1)); /* decoded before the exit test, as in k_fwd */    \
     cw0 = nw0;                                                                                 \
     cw1 = nw1;                                                                                 \
   }

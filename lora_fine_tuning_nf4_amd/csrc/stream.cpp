@@ -11,6 +11,12 @@
 // (copy j waits for release[j mod nbuf] of call j - nbuf); compute waits copy_done[k mod
 // nbuf].  Copies are hipMemcpyAsync from pinned memory, carried by the SDMA engines, so
 // they take no compute units.
+//
+// Reuse mode keeps the ring's prefetch depth but plans buffers per pass from what they
+// hold: a call whose shard already sits intact in a buffer (the last forward layers at
+// the forward/backward turn, the first layers at the start of the next step) uses it
+// with no copy; otherwise its shard is copied into the least recently used buffer, after
+// that buffer's last user is released.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -48,7 +54,52 @@ struct lnf4_stream {
   int64_t bytes_copied = 0;
   std::vector<lnf4_stream_event> log;
   bool alive = true;
+  // reuse mode: the plan of the current pass, what the buffers hold and when each was
+  // last used (a call counter that runs on across passes; -1: never)
+  bool reuse = false;
+  std::vector<int> plan_buf, plan_src, plan_wait, plan_issue;  // per schedule position
+  std::vector<int> holder;
+  std::vector<long> last_tick;
+  long tick = 0;
 };
+
+// Plan one pass in reuse mode from what the buffers hold now.  Position j: if a buffer
+// holds shard sched[j], use it (plan_src[j] = the position of this pass whose copy
+// filled it, -1 if an earlier pass did).  Otherwise copy into the least recently used
+// buffer (lowest index on ties), after the release of its last user (plan_wait[j]: that
+// position of this pass, -1 if the user was in an earlier pass), issued at call
+// plan_issue[j] = max(j - nbuf + 1, plan_wait[j] + 1, 0); plan_issue is -1 where there is
+// no copy.
+static void plan_pass(lnf4_stream* st) {
+  const int n = (int)st->sched.size(), nb = st->nbuf;
+  st->plan_buf.assign(n, 0);
+  st->plan_src.assign(n, -1);
+  st->plan_wait.assign(n, -1);
+  st->plan_issue.assign(n, -1);
+  std::vector<int> holder = st->holder, filled(nb, -1), last(nb, -1);
+  std::vector<long> age = st->last_tick;
+  for (int j = 0; j < n; ++j) {
+    const int s = st->sched[j];
+    int b = -1;
+    for (int q = 0; q < nb; ++q)
+      if (holder[q] == s) b = q;
+    if (b < 0) {
+      b = 0;
+      for (int q = 1; q < nb; ++q)
+        if (age[q] < age[b]) b = q;
+      int issue = j - nb + 1;
+      if (last[b] + 1 > issue) issue = last[b] + 1;
+      st->plan_wait[j] = last[b];
+      st->plan_issue[j] = issue < 0 ? 0 : issue;
+      holder[b] = s;
+      filled[b] = j;
+    }
+    st->plan_src[j] = filled[b];
+    st->plan_buf[j] = b;
+    last[b] = j;
+    age[b] = st->tick + j;
+  }
+}
 
 static void log_ev(lnf4_stream* st, int kind, int call, int j, int layer, int buffer, int wait) {
   lnf4_stream_event e;
@@ -85,11 +136,13 @@ static int copy_into(lnf4_stream* st, int buf, int shard) {
 extern "C" {
 
 int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards, void* const* dev_bufs,
-                  size_t buf_bytes, int32_t n_bufs, const int32_t* schedule, int32_t sched_len, int32_t resident,
+                  size_t buf_bytes, int32_t n_bufs, const int32_t* schedule, int32_t sched_len, int32_t mode,
                   hipStream_t copy_stream, void* slot_buf, size_t slot_bytes, lnf4_stream** out) {
   const char* who = "stream_create";
   if (!out) return fail(LNF4_EINVAL, "%s: out is NULL", who);
   *out = nullptr;
+  if (mode < 0 || mode > 2) return fail(LNF4_EINVAL, "%s: mode=%d (0 ring, 1 resident, 2 ring with reuse)", who, (int)mode);
+  const int32_t resident = mode == 1;
   if (!host_shards || !shard_bytes || !dev_bufs || !schedule) return fail(LNF4_EINVAL, "%s: NULL array", who);
   if (n_shards < 1 || n_shards > (1 << 20)) return fail(LNF4_EINVAL, "%s: n_shards=%d out of range", who, (int)n_shards);
   if (resident) {
@@ -149,6 +202,10 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
   st->copy_done.assign(n_bufs, nullptr);
   st->release.assign(n_bufs, nullptr);
   st->release_recorded.assign(n_bufs, 0);
+  st->reuse = mode == 2;
+  st->holder.assign(n_bufs, -1);
+  st->last_tick.assign(n_bufs, -1);
+  if (st->reuse) plan_pass(st);
   for (int b = 0; b < n_bufs; ++b) {
     hipError_t e = hipEventCreateWithFlags(&st->copy_done[b], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&st->release[b], hipEventDisableTiming);
@@ -196,6 +253,34 @@ int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** de
     return LNF4_OK;
   }
   const int nb = st->nbuf;
+  if (st->reuse) {
+    if (k > 0) {
+      const int b = st->plan_buf[k - 1];
+      if ((e = hipEventRecord(st->release[b], compute)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(release)");
+      st->release_recorded[b] = 1;
+    }
+    // copies in schedule order, each once its call has come (positions with no copy pass)
+    while (st->issued < n && st->plan_issue[st->issued] <= k) {
+      const int j = st->issued;
+      if (st->plan_issue[j] >= 0) {
+        const int b = st->plan_buf[j], layer = st->sched[j];
+        if (st->release_recorded[b])
+          if ((e = hipStreamWaitEvent(st->copy, st->release[b], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(release)");
+        if ((rc = copy_into(st, b, layer))) return rc;
+        st->holder[b] = layer;
+        log_ev(st, LNF4_EV_COPY, k, j, layer, b, st->plan_wait[j]);
+      }
+      st->issued = j + 1;
+    }
+    const int b = st->plan_buf[k];
+    // the last copy into b is the one that filled it with this shard (none was issued since)
+    if ((e = hipStreamWaitEvent(compute, st->copy_done[b], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(copy_done)");
+    log_ev(st, LNF4_EV_STEP, k, st->plan_src[k], st->sched[k], b, st->plan_src[k]);
+    st->last_tick[b] = st->tick + k;
+    st->next_call = k + 1;
+    *dev_ptr_out = st->bufs[b];
+    return LNF4_OK;
+  }
   if (k > 0) {
     const int b = (k - 1) % nb;
     if ((e = hipEventRecord(st->release[b], compute)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(release)");
@@ -301,15 +386,17 @@ int stream_reset(lnf4_stream* st, hipStream_t compute) {
   if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->resident && st->next_call > 0) {
     // release the last call's buffer; earlier buffers were released by later calls
-    const int b = (st->next_call - 1) % st->nbuf;
+    const int b = st->reuse ? st->plan_buf[st->next_call - 1] : (st->next_call - 1) % st->nbuf;
     hipError_t e = hipEventRecord(st->release[b], compute);
     if (e != hipSuccess) return hip_fail(e, "stream: hipEventRecord(release at reset)");
     st->release_recorded[b] = 1;
   }
+  if (st->reuse) st->tick += (long)st->sched.size();
   st->next_call = 0;
   st->issued = 0;
   st->pass += 1;
   st->log.clear();
+  if (st->reuse) plan_pass(st);  // from what the buffers hold now (copies of an unfinished pass included)
   return LNF4_OK;
 }
 

@@ -28,6 +28,7 @@ FMT_BF16 = 1
 MAX_RANK = 64
 MAX_GROUP = 8
 EV_COPY, EV_STEP, EV_SLOT_COPY, EV_SLOT_WAIT = 0, 1, 2, 3
+STREAM_RING, STREAM_RESIDENT, STREAM_REUSE = 0, 1, 2
 
 _ERRNAMES = {LNF4_EINVAL: "EINVAL", LNF4_ESHAPE: "ESHAPE", LNF4_EALIGN: "EALIGN", LNF4_EHIP: "EHIP",
              LNF4_ESTATE: "ESTATE"}
@@ -242,7 +243,7 @@ def lnf4_dpo_loss(pol_sums, ref_sums, n_pairs: int, beta: float, loss, coef, str
 
 
 # ------------------------------------------------------------------ layer stream
-def stream_create(host_shards, shard_bytes, dev_bufs, buf_bytes: int, schedule, resident: int, copy_stream,
+def stream_create(host_shards, shard_bytes, dev_bufs, buf_bytes: int, schedule, mode: int, copy_stream,
                   slot_buf=None, slot_bytes: int = 0):
     n = len(host_shards)
     hs = (c_void_p * n)(*[_ptr(h) for h in host_shards])
@@ -251,7 +252,7 @@ def stream_create(host_shards, shard_bytes, dev_bufs, buf_bytes: int, schedule, 
     db = (c_void_p * nb)(*[_ptr(d) for d in dev_bufs])
     sc = (c_int32 * len(schedule))(*schedule)
     out = c_void_p()
-    _check(lib().stream_create(hs, sb, n, db, buf_bytes, nb, sc, len(schedule), resident, _stream(copy_stream),
+    _check(lib().stream_create(hs, sb, n, db, buf_bytes, nb, sc, len(schedule), mode, _stream(copy_stream),
                                _ptr(slot_buf), slot_bytes, ctypes.byref(out)))
     return out.value
 

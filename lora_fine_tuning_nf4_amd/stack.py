@@ -57,7 +57,8 @@ class LayerState:
 class StreamedStack:
     def __init__(self, wl: synthgen.Workload, n_bufs: int = 2, seed: int = 0,
                  layers: int | None = None, tokens: int | None = None, head_slot: bool = True,
-                 dpo: bool | None = None, loss_chunk: int | None = None, device: str = "cuda"):
+                 dpo: bool | None = None, loss_chunk: int | None = None, reuse: bool = False,
+                 recompute: bool = True, device: str = "cuda"):
         self.wl = wl
         self.L = layers if layers is not None else wl.layers
         self.T = tokens if tokens is not None else wl.tokens
@@ -65,6 +66,8 @@ class StreamedStack:
         self.dpo = ("ref" in wl.passes) if dpo is None else dpo
         self.n_bufs = n_bufs
         self.seed = seed
+        self.reuse = reuse          # buffers that still hold a needed layer are used without a copy
+        self.recompute = recompute  # False: the backward uses the forward's saved u and skips the re-run
         dev = torch.device(device)
         self.dev = dev
         T = self.T
@@ -133,7 +136,8 @@ class StreamedStack:
         self.schedule = sched
         torch.cuda.synchronize(dev)
         slot_bytes = self.slot.numel() if self.slot is not None else 0
-        self.st = lnf4.stream_create(shards, sizes, self.bufs, self.shard_bytes, sched, 0, self.copy, self.slot,
+        mode = lnf4.STREAM_REUSE if reuse else lnf4.STREAM_RING
+        self.st = lnf4.stream_create(shards, sizes, self.bufs, self.shard_bytes, sched, mode, self.copy, self.slot,
                                      slot_bytes)
         self.timers = None
         self._embed_in_slot = False   # the next step's embed_tokens was loaded during the last backward
@@ -183,7 +187,7 @@ class StreamedStack:
         if self.st_res is None:
             self.res_bufs = [torch.empty(self.shard_bytes, dtype=torch.uint8, device=self.dev) for _ in range(self.L)]
             self.st_res = lnf4.stream_create(self.host, [self.shard_bytes] * self.L, self.res_bufs, self.shard_bytes,
-                                             self.schedule, 1, self.copy)
+                                             self.schedule, lnf4.STREAM_RESIDENT, self.copy)
             if self.head:
                 # embed_tokens and lm_head each resident in a buffer of their own
                 self.res_head = []
@@ -363,8 +367,8 @@ class StreamedStack:
                     # the backward is compute-bound: the next step's embed_tokens trickles into
                     # the slot in one piece per layer, between the layer copies
                     lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L, self.compute)
-                for gi in range(len(GROUPS) if compute else 0):   # recompute from the checkpointed inputs
-                    self._group_fwd(layer, gi, base, adapters=True)
+                for gi in range(len(GROUPS) if compute and self.recompute else 0):
+                    self._group_fwd(layer, gi, base, adapters=True)   # recompute from the checkpointed inputs
                 for gi in reversed(range(len(GROUPS) if compute else 0)):
                     self._group_bwd(layer, gi, base)
         lnf4.stream_reset(st, self.compute)

@@ -22,6 +22,14 @@ previous user) has finished; call k's compute waits for copy k.  In resident
 mode every shard has its own buffer, all shards are copied once on the first
 call, and call k waits for the copy of its own shard.
 
+Reuse variant (a reading beyond the pages' ring, which copies every read): each
+pass is planned from what the buffers hold.  A position whose shard sits intact in
+some buffer uses it without a copy; otherwise its shard goes into the least
+recently used buffer (lowest index on ties), after the release of that buffer's
+last user u in the pass, issued at call max(j - nbuf + 1, u + 1).  For a STEP of
+this variant, ``j`` is the position whose copy filled the buffer (-1: a previous
+pass).
+
 The event log is a list of tuples (kind, call, j, layer, buffer, wait):
   COPY  issued during call ``call``: schedule position j, shard ``layer``,
         into ``buffer``, after the release of call ``wait`` (-1: no wait)
@@ -96,3 +104,68 @@ def check_happens_before(log, schedule, n_bufs: int) -> None:
             made = call
             assert content.get(buf) == (j, layer), (call, buf, content.get(buf))
             assert layer == schedule[call]
+
+
+def simulate_reuse(schedule, n_bufs: int, passes: int = 1):
+    """Event logs of ``passes`` consecutive passes of the reuse variant (module header)."""
+    sched = list(schedule)
+    n = len(sched)
+    holder = [None] * n_bufs          # shard in each buffer
+    last_seen = [-1] * n_bufs         # when each buffer was last used (a clock over passes)
+    clock = 0
+    logs = []
+    for _ in range(passes):
+        # plan: buffer per position, and for copies the last user in this pass and the call
+        plan = []
+        last_user = [-1] * n_bufs
+        filled_by = [-1] * n_bufs
+        for j, shard in enumerate(sched):
+            held = [b for b in range(n_bufs) if holder[b] == shard]
+            if held:
+                b = held[-1]
+                plan.append((b, None))
+            else:
+                b = min(range(n_bufs), key=lambda q: (last_seen[q], q))
+                issue_at = max(j - n_bufs + 1, last_user[b] + 1, 0)
+                plan.append((b, (last_user[b], issue_at)))
+                holder[b] = shard
+                filled_by[b] = j
+            last_user[b] = j
+            last_seen[b] = clock + j
+            plan[-1] = plan[-1] + (filled_by[b],)
+        # events, in the order the calls produce them
+        log = []
+        nxt = 0
+        for k in range(n):
+            while nxt < n and (plan[nxt][1] is None or plan[nxt][1][1] <= k):
+                b, cp, _ = plan[nxt]
+                if cp is not None:
+                    log.append((COPY, k, nxt, sched[nxt], b, cp[0]))
+                nxt += 1
+            b, _, src = plan[k]
+            log.append((STEP, k, src, sched[k], b, src))
+        logs.append(log)
+        clock += n
+    return logs
+
+
+def check_reuse_log(logs, schedule, n_bufs: int) -> None:
+    """Replay passes of the reuse variant: every step finds its shard in its buffer, and
+    a copy overwrites a buffer only after the release of its last user, a call already
+    made when the copy is issued (or a call of an earlier pass)."""
+    content = {}
+    for log in logs:
+        last_user = {}
+        made = -1
+        for kind, call, j, layer, buf, wait in log:
+            if kind == COPY:
+                assert wait == last_user.get(buf, -1), (j, buf, wait, last_user.get(buf))
+                assert wait < call or wait == -1, "release not yet recorded when the copy is issued"
+                assert j <= call + n_bufs - 1, "copy issued more than nbuf - 1 calls ahead"
+                content[buf] = layer
+            else:
+                assert call == made + 1, "calls out of order"
+                made = call
+                assert layer == schedule[call]
+                assert content.get(buf) == layer, (call, buf, content.get(buf), layer)
+                last_user[buf] = call

@@ -126,6 +126,9 @@ def test_stream_validation(L):
     bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
     assert args(2, sched=bad) == lnf4.LNF4_EINVAL  # schedule names a missing shard
     assert args(3, res=1) == lnf4.LNF4_EINVAL    # resident needs one buffer per shard
+    assert args(2, res=3) == lnf4.LNF4_EINVAL    # mode outside ring / resident / reuse
+    assert args(2, res=-1) == lnf4.LNF4_EINVAL
+    assert args(9, res=2) == lnf4.LNF4_EINVAL    # reuse keeps the 2..8 buffer range
     db2 = (ctypes.c_void_p * 2)(FAKE + 16, FAKE)
     assert L.stream_create(hs, sb, 2, db2, 4096, 2, sc, 4, 0, None, None, 0, ctypes.byref(out)) == lnf4.LNF4_EALIGN
     p = ctypes.c_void_p()

@@ -66,13 +66,42 @@ def test_stream_log_and_buffers_match_simulator(nbuf, mode):
         lnf4.stream_destroy(st)
 
 
+@pytest.mark.parametrize("nbuf", [2, 3, 8])
+@pytest.mark.parametrize("mode", ["sft", "dpo"])
+def test_reuse_log_and_buffers_match_simulator(nbuf, mode):
+    """Reuse mode over three passes: the engine's log equals the oracle simulator's, and
+    every call finds its shard's bytes in the buffer it is given."""
+    L, nbytes = 5, 4096 + 512
+    shards = _pinned_shards(L, nbytes, seed=20 + nbuf)
+    bufs = [torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sched = ss.sft_schedule(L) if mode == "sft" else ss.dpo_schedule(L)
+    comp = torch.cuda.current_stream()
+    st = lnf4.stream_create(shards, [nbytes] * L, bufs, nbytes + 256, sched, lnf4.STREAM_REUSE, torch.cuda.Stream())
+    want = ss.simulate_reuse(sched, nbuf, passes=3)
+    try:
+        b0 = lnf4.stream_bytes_copied(st)
+        for step in range(3):
+            for k in range(len(sched)):
+                p = lnf4.stream_layer_step(st, k, comp)
+                j = [i for i, b in enumerate(bufs) if b.data_ptr() == p]
+                assert len(j) == 1
+                assert torch.equal(bufs[j[0]][:nbytes].cpu(), shards[sched[k]]), (step, k)
+            assert lnf4.stream_log(st) == want[step], step
+            lnf4.stream_reset(st, comp)
+        n_copies = sum(len(ss.copies(lg)) for lg in want)
+        assert lnf4.stream_bytes_copied(st) - b0 == n_copies * nbytes
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st)
+
+
 def test_resident_log_matches_simulator():
     L, nbytes = 4, 2048
     shards = _pinned_shards(L, nbytes, seed=7)
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(L)]
     sched = ss.sft_schedule(L)
     comp = torch.cuda.current_stream()
-    st = lnf4.stream_create(shards, [nbytes] * L, bufs, nbytes, sched, 1, torch.cuda.Stream())
+    st = lnf4.stream_create(shards, [nbytes] * L, bufs, nbytes, sched, lnf4.STREAM_RESIDENT, torch.cuda.Stream())
     try:
         for k in range(len(sched)):
             p = lnf4.stream_layer_step(st, k, comp)
@@ -132,10 +161,11 @@ def _same(a, b):
         assert np.array_equal(a["head"][k], b["head"][k]), k
 
 
-@pytest.mark.parametrize("fmt,dpo", [("nf4", False), ("bf16", False), ("nf4", True)])
-def test_streamed_equals_resident_bitwise(fmt, dpo):
+@pytest.mark.parametrize("fmt,dpo,reuse", [("nf4", False, False), ("bf16", False, False), ("nf4", True, False),
+                                           ("nf4", False, True), ("nf4", True, True)])
+def test_streamed_equals_resident_bitwise(fmt, dpo, reuse):
     wl = _small_workload(fmt)
-    stack = StreamedStack(wl, n_bufs=2, seed=3, dpo=dpo)
+    stack = StreamedStack(wl, n_bufs=2, seed=3, dpo=dpo, reuse=reuse)
     try:
         stack.step()
         a = _snapshot(stack)
@@ -297,3 +327,25 @@ def test_slot_load_in_parts(n_parts):
     finally:
         torch.cuda.synchronize()
         lnf4.stream_destroy(st)
+
+
+def test_no_recompute_gives_the_same_gradients():
+    """Skipping the backward's forward re-run (the saved u stands in for the recomputed
+    one, which is bitwise the same) changes no gradient."""
+    wl = _small_workload("nf4", adapted=("q", "k", "v", "o", "gate", "up", "down"), rank=4)
+    snaps = []
+    for rc in (True, False):
+        stack = StreamedStack(wl, n_bufs=2, seed=6, recompute=rc)
+        try:
+            stack.step()
+            snaps.append(_snapshot(stack))
+        finally:
+            stack.close()
+    a, b = snaps
+    for g in range(len(a["dx"])):
+        assert np.array_equal(a["dx"][g], b["dx"][g]), g
+    for l, gr in enumerate(a["grads"]):
+        for p in gr:
+            assert np.array_equal(gr[p][0], b["grads"][l][p][0])
+            assert np.array_equal(gr[p][1], b["grads"][l][p][1])
+    assert np.array_equal(a["head"]["dh"], b["head"]["dh"])

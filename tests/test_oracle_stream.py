@@ -61,3 +61,69 @@ def test_resident_copies_each_shard_once():
     assert sorted(e[3] for e in cps) == list(range(6))
     steps = [e for e in log if e[0] == ss.STEP]
     assert [e[3] for e in steps] == sched and all(e[4] == e[3] for e in steps)
+
+
+# ------------------------------------------------------------------ reuse variant
+def test_reuse_hand_worked_logs_l3_nbuf2():
+    # schedule [0, 1, 2, 2, 1, 0], two buffers, two passes.  Pass 0: shards 2 and 1 are
+    # still in their buffers at the turn; shard 0 then goes into the least recently used
+    # buffer (b0, last used at call 3), issued at call 4.  Pass 1 starts with shards 0
+    # and 1 in place.
+    C, S = ss.COPY, ss.STEP
+    p0, p1 = ss.simulate_reuse(ss.sft_schedule(3), 2, passes=2)
+    assert p0 == [
+        (C, 0, 0, 0, 0, -1), (C, 0, 1, 1, 1, -1), (S, 0, 0, 0, 0, 0),
+        (C, 1, 2, 2, 0, 0), (S, 1, 1, 1, 1, 1),
+        (S, 2, 2, 2, 0, 2),
+        (S, 3, 2, 2, 0, 2),
+        (C, 4, 5, 0, 0, 3), (S, 4, 1, 1, 1, 1),
+        (S, 5, 5, 0, 0, 5),
+    ]
+    assert p1 == [
+        (S, 0, -1, 0, 0, -1),
+        (C, 1, 2, 2, 0, 0), (S, 1, -1, 1, 1, -1),
+        (S, 2, 2, 2, 0, 2),
+        (S, 3, 2, 2, 0, 2),
+        (C, 4, 5, 0, 0, 3), (S, 4, -1, 1, 1, -1),
+        (S, 5, 5, 0, 0, 5),
+    ]
+
+
+@pytest.mark.parametrize("nbuf", [2, 3, 8])
+@pytest.mark.parametrize("L", [1, 2, 5, 32])
+def test_reuse_copy_counts(nbuf, L):
+    """Closed forms: with L > nbuf an SFT pass copies 2L - nbuf layers first (the last
+    nbuf forward layers serve the first backward calls), then 2L - 2 nbuf (the first
+    nbuf layers are still in place from the previous backward); DPO adds L to each (its
+    policy forward restarts at layer 0, long evicted).  With L <= nbuf every shard stays
+    resident after the first pass."""
+    for sched, extra in ((ss.sft_schedule(L), 0), (ss.dpo_schedule(L), L)):
+        counts = [len(ss.copies(log)) for log in ss.simulate_reuse(sched, nbuf, passes=3)]
+        if L > nbuf:
+            assert counts == [2 * L - nbuf + extra, 2 * L - 2 * nbuf + extra, 2 * L - 2 * nbuf + extra]
+        else:
+            assert counts == [L, 0, 0]
+
+
+@pytest.mark.parametrize("nbuf", range(2, 9))
+@pytest.mark.parametrize("L", [1, 2, 5, 32])
+def test_reuse_happens_before(nbuf, L):
+    for sched in (ss.sft_schedule(L), ss.dpo_schedule(L)):
+        ss.check_reuse_log(ss.simulate_reuse(sched, nbuf, passes=3), sched, nbuf)
+
+
+def test_reuse_check_catches_a_missing_wait_and_a_wrong_buffer():
+    sched = ss.sft_schedule(5)
+    logs = ss.simulate_reuse(sched, 2, passes=2)
+    first_copy_with_wait = next(i for i, e in enumerate(logs[0]) if e[0] == ss.COPY and e[5] >= 0)
+    bad = list(logs[0])
+    e = bad[first_copy_with_wait]
+    bad[first_copy_with_wait] = (e[0], e[1], e[2], e[3], e[4], -1)
+    with pytest.raises(AssertionError):
+        ss.check_reuse_log([bad], sched, 2)
+    step = next(i for i, e in enumerate(logs[1]) if e[0] == ss.STEP and e[2] == -1)
+    bad = list(logs[1])
+    e = bad[step]
+    bad[step] = (e[0], e[1], e[2], e[3], 1 - e[4], e[5])
+    with pytest.raises(AssertionError):
+        ss.check_reuse_log([logs[0], bad], sched, 2)
