@@ -22,4 +22,6 @@ lora        LoRA linear forward and backward (plain matrix definitions)
 stream_sim  the layer-stream schedule and its event log
 layer       one decoder layer's projections composed into a layer step
 head        embedding gather, token cross-entropy, sequence sums, sigmoid DPO
+decoder     RMSNorm, RoPE, causal GQA attention, SwiGLU, a whole decoder layer and a
+            whole-model SFT step, forward and hand-written backward
 """
