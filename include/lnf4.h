@@ -262,6 +262,87 @@ int lnf4_sequence_sums(const float* x, int32_t n_seq, int64_t seq_len, float* su
 int lnf4_dpo_loss(const float* pol_sums, const float* ref_sums, int32_t n_pairs, float beta, float* loss, float* coef,
                   hipStream_t stream);
 
+/* ------------------------------------------------------------------ decoder-layer glue
+ * The parts of a Llama/Qwen decoder layer between its projections: RMSNorm, rotary
+ * position embedding, causal grouped-query attention, the SwiGLU MLP activation and the
+ * residual adds (the layer shapes of the configs; the Soup deep dive, "Core feature: how
+ * layer streaming works", names the per-layer checkpoint recompute that re-runs them in
+ * backward).  The pages give no formulas; these are the standard Llama definitions.
+ * All tensors are bf16 [T, width] row-major with a 16-byte aligned base; every call
+ * computes in fp32 and rounds each stored value to bf16 once.
+ */
+
+/*
+ * RMSNorm forward: y = bf16(x * r * g), r = 1 / sqrt(mean(x^2) + eps) per row (fp32).
+ *   x, y   device bf16 [T, H], H a positive multiple of 8;  g device bf16 [H] (frozen)
+ *   rstd   device fp32 [T] receiving r (NULL to skip; the backward needs it)
+ * Errors: EINVAL (T, eps, NULL), ESHAPE (H), EALIGN, EHIP.
+ */
+int lnf4_rmsnorm_fwd(const uint16_t* x, int64_t T, int64_t H, const uint16_t* g, float eps, uint16_t* y,
+                     float* rstd, hipStream_t stream);
+
+/*
+ * RMSNorm backward (g frozen: no weight gradient), with the residual gradient added:
+ *   dx = bf16(dres + r g dy - x r^3 mean(x g dy))     (dres NULL: no residual term)
+ *   rstd the forward's r.  Errors: as lnf4_rmsnorm_fwd.
+ */
+int lnf4_rmsnorm_bwd(const uint16_t* x, int64_t T, int64_t H, const uint16_t* g, const float* rstd,
+                     const uint16_t* dy, const uint16_t* dres, uint16_t* dx, hipStream_t stream);
+
+/*
+ * RoPE table: table[2(p*D/2 + i)], table[2(p*D/2 + i) + 1] = cos, sin of p * base^(-2i/D)
+ * for positions p < seq_len and i < D/2, computed in fp64 and rounded to fp32.
+ *   table  device fp32 [seq_len * D] (8-byte aligned); D a multiple of 16; base > 1
+ * Errors: EINVAL, ESHAPE, EALIGN, EHIP.
+ */
+int lnf4_rope_table(int64_t seq_len, int32_t head_dim, double base, float* table, hipStream_t stream);
+
+/*
+ * Rotate-half RoPE in place on x [T, n_heads * D]: for each head the pair (i, i + D/2)
+ * turns by the angle of position t mod seq_len (inverse != 0: by minus that angle, the
+ * backward).  Errors: EINVAL, ESHAPE, EALIGN, EHIP.
+ */
+int lnf4_rope(uint16_t* x, int64_t T, int32_t n_heads, int32_t head_dim, int64_t seq_len, const float* table,
+              int32_t inverse, hipStream_t stream);
+
+/* SwiGLU: s = bf16(silu(g) * u), silu(z) = z / (1 + e^-z); n elements, a multiple of 8. */
+int lnf4_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* s, hipStream_t stream);
+
+/* SwiGLU backward: dg = ds u sig (1 + g (1 - sig)), du = ds silu(g), sig = 1/(1 + e^-g). */
+int lnf4_swiglu_bwd(const uint16_t* g, const uint16_t* u, const uint16_t* ds, int64_t n, uint16_t* dg,
+                    uint16_t* du, hipStream_t stream);
+
+/* Residual add: out = bf16(a + b); n elements, a multiple of 8 (out may alias a or b). */
+int lnf4_add(const uint16_t* a, const uint16_t* b, int64_t n, uint16_t* out, hipStream_t stream);
+
+/*
+ * Causal grouped-query attention forward, per sequence of seq_len tokens:
+ *   o = softmax(q k^T / sqrt(D) + causal mask) v, query head h reading kv head
+ *   h / (n_heads / n_kv);  lse[h][t] = log sum_j exp(q_t k_j / sqrt(D)) (natural log).
+ *   q, o  device bf16 [T, n_heads * D];  k, v device bf16 [T, n_kv * D]
+ *   lse   device fp32 [n_heads, T]
+ *   D = head_dim, 64 or 128; seq_len a positive multiple of 64 dividing T
+ * fp32 accumulation on the matrix cores; probabilities enter the value product as bf16.
+ * Errors: EINVAL (T, NULL), ESHAPE (head_dim, heads, seq_len), EALIGN, EHIP.
+ */
+int lnf4_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t T, int32_t n_heads,
+                  int32_t n_kv, int32_t head_dim, int64_t seq_len, uint16_t* o, float* lse, hipStream_t stream);
+
+/*
+ * Attention backward from the forward's o and lse:
+ *   P = exp(q k^T / sqrt(D) - lse), dV = P^T dO, dP = dO v^T, dS = P (dP - rowsum(dO o o)),
+ *   dq = dS k / sqrt(D), dk = dS^T q / sqrt(D), each kv head's dk, dv summed over its
+ *   query heads.  No atomics: bitwise reproducible.
+ *   dout        device bf16 [T, n_heads * D] (the output gradient)
+ *   dq, dk, dv  device bf16, shaped as q, k, v
+ *   workspace   device fp32 [n_heads * T] (rowsum(dO o o))
+ * Errors: as lnf4_attn_fwd.
+ */
+int lnf4_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o, const float* lse,
+                  const uint16_t* dout, int64_t T, int32_t n_heads, int32_t n_kv, int32_t head_dim,
+                  int64_t seq_len, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* workspace,
+                  hipStream_t stream);
+
 /* ------------------------------------------------------------------ layer stream */
 typedef struct lnf4_stream lnf4_stream;
 

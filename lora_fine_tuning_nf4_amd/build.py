@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "liblnf4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["nf4_codec.hip", "gemm.hip", "lora_skinny.hip", "head.hip", "abi.cpp", "head_abi.cpp", "stream.cpp"]
+SOURCES = ["nf4_codec.hip", "gemm.hip", "lora_skinny.hip", "head.hip", "decoder.hip", "attention.hip", "abi.cpp",
+           "head_abi.cpp", "decoder_abi.cpp", "stream.cpp"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,411 @@
+// Causal grouped-query attention of a decoder layer, forward and backward, on the
+// gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+// Layout: q and o are [T, n_heads * D] bf16, k and v [T, n_kv * D]; the T tokens are
+// n_seq sequences of seq_len tokens, attention is causal inside each sequence, and query
+// head h reads kv head h / (n_heads / n_kv).  Blocks of 64 queries and 64 keys; a
+// workgroup is two waves of 32 rows each.
+//
+// Orientation.  Scores are formed transposed, S^T = K Q^T, so that a lane's accumulator
+// column is one query: that query's softmax statistics (running max and sum, its
+// log-sum-exp, rowsum(dO o O)) stay in the lane, and the two half-waves that share the
+// column combine with one cross-half exchange.  The probabilities then feed the next
+// product straight from the accumulators: the 8 values a lane holds for a 16-key step
+// are keys {4h..4h+3, 8+4h..8+4h+3} of that step (h = lane / 32), an order the other
+// operand (a transposed tile in LDS: V^T, K^T, Q^T or dO^T) is read in.
+//
+// In backward the score gradients dS and the probabilities P enter their products as a
+// bf16 hi + lo pair (two products each), so dq, dk and dv carry about 16 significant bits
+// of them (the gradients of tokens attended by many queries sum many terms that cancel);
+// the forward's value product takes P as one bf16.
+//
+// Backward without atomics (bitwise reproducible): rowsum(dO o O) per query first, then
+// dq (a workgroup per query block, looping over its key blocks) and dk, dv (a workgroup
+// per key block and kv head, looping over the query heads of the group and the query
+// blocks at or after it).
+#include <math.h>
+
+#include "common.hpp"
+#include "decoder.hpp"
+
+namespace lnf4 {
+
+namespace {
+
+constexpr int BQ = 64;   // queries per workgroup
+constexpr int BK = 64;   // keys per block
+constexpr int NT = 128;  // two waves
+
+__device__ __forceinline__ floatx16 mma(const bf16x8& a, const bf16x8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld16(const uint16_t* p) { return *(const bf16x8*)p; }
+
+// two 8-byte runs (4 bf16 each) as one operand
+__device__ __forceinline__ bf16x8 ld8x2(const uint16_t* p0, const uint16_t* p1) {
+  const uint2 a = *(const uint2*)p0, b = *(const uint2*)p1;
+  const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// accumulator values 8*hs .. 8*hs+7 as bf16: rows 16hs + 8(p>>2) + 4h + (p&3), p = 0..7
+__device__ __forceinline__ bf16x8 rows_bf16(const floatx16& c, int hs) {
+  const uint4 v = make_uint4(pack_bf16x2(c[8 * hs + 0], c[8 * hs + 1]), pack_bf16x2(c[8 * hs + 2], c[8 * hs + 3]),
+                             pack_bf16x2(c[8 * hs + 4], c[8 * hs + 5]), pack_bf16x2(c[8 * hs + 6], c[8 * hs + 7]));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// the same values as a bf16 pair hi + lo (lo = bf16(x - hi)): about 16 significant bits
+// through two products, for the score gradients whose sums can cancel
+__device__ __forceinline__ void rows_bf16_split(const floatx16& c, int hs, bf16x8& hi, bf16x8& lo) {
+  uint32_t wh[4], wl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = c[8 * hs + 2 * j], b = c[8 * hs + 2 * j + 1];
+    wh[j] = pack_bf16x2(a, b);
+    wl[j] = pack_bf16x2(a - bf16_lo(wh[j]), b - bf16_hi(wh[j]));
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+}
+
+// A operand of rows m of a transposed tile Xt[m][r], matching rows_bf16 for the 16 r of
+// K-step base .. base+15
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* Xt, int stride, int m, int base, int h) {
+  const uint16_t* p = Xt + m * stride + base + 4 * h;
+  return ld8x2(p, p + 8);
+}
+
+__device__ __forceinline__ floatx16 zero16() {
+  floatx16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// rows [r0, r0+64) of a [.., ld] bf16 matrix, columns [c0, c0+D), into LDS row-major
+template <int D, int STRIDE>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t r0, int64_t ld, int64_t c0) {
+  for (int idx = threadIdx.x; idx < 64 * (D / 8); idx += NT) {
+    const int r = idx / (D / 8), c = idx - r * (D / 8);
+    *(u32x4*)&dst[r * STRIDE + 8 * c] = *(const u32x4*)(src + (r0 + r) * ld + c0 + 8 * c);
+  }
+}
+
+// the same 64 x D block transposed: dst[d][r], two rows per 4-byte LDS write
+template <int D, int STRIDE>
+__device__ __forceinline__ void stage_rows_t(uint16_t* dst, const uint16_t* src, int64_t r0, int64_t ld, int64_t c0) {
+  for (int idx = threadIdx.x; idx < 32 * (D / 8); idx += NT) {
+    const int rp = idx / (D / 8), c = idx - rp * (D / 8);
+    const u32x4 a = *(const u32x4*)(src + (r0 + 2 * rp) * ld + c0 + 8 * c);
+    const u32x4 b = *(const u32x4*)(src + (r0 + 2 * rp + 1) * ld + c0 + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t va = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const uint32_t vb = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      *(uint32_t*)&dst[(8 * c + e) * STRIDE + 2 * rp] = va | (vb << 16);
+    }
+  }
+}
+
+// accumulator rows d = 32dt + 8j + 4h + 0..3 of column `col` -> out[col][d], scaled, bf16
+template <int D>
+__device__ __forceinline__ void store_cols(uint16_t* out_row, const floatx16 (&acc)[D / 32], float f, int h) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * dt + 8 * j + 4 * h;
+      uint2 w;
+      w.x = pack_bf16x2(acc[dt][4 * j + 0] * f, acc[dt][4 * j + 1] * f);
+      w.y = pack_bf16x2(acc[dt][4 * j + 2] * f, acc[dt][4 * j + 3] * f);
+      *(uint2*)(out_row + d0) = w;
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ forward
+// Online softmax over key blocks in base 2: x = s * scale * log2(e), running max m and
+// sum l per query, O^T rescaled by 2^(m_old - m_new) when m grows.  lse is stored in
+// natural-log units: (m + log2 l) * ln 2.
+template <int D>
+__global__ __launch_bounds__(NT) void k_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                 const uint16_t* __restrict__ v, int64_t T, int nh, int nkv,
+                                                 int64_t S, float sl2e, uint16_t* __restrict__ o,
+                                                 float* __restrict__ lse) {
+  constexpr int KS = D + 8, VS = BK + 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+  const int nqb = (int)(S / BQ), n_seq = (int)(T / S);
+  const int seq = blockIdx.x % n_seq, qb = nqb - 1 - (int)(blockIdx.x / n_seq);  // longest rows first
+  const int hq = blockIdx.y, hk = hq / (nh / nkv);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, h = lane >> 5;
+  const int64_t ldq = (int64_t)nh * D, ldk = (int64_t)nkv * D, t0 = (int64_t)seq * S;
+  const int qpos = qb * BQ + wave * 32 + l32;  // this lane's query, position in its sequence
+
+  bf16x8 qf[D / 16];
+  const uint16_t* qrow = q + (t0 + qpos) * ldq + (int64_t)hq * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qf[s] = ld16(qrow + 16 * s + 8 * h);
+  floatx16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = zero16();
+  float m = -INFINITY, l = 0.0f;
+
+  for (int kb = 0; kb <= qb; ++kb) {
+    __syncthreads();  // the previous block's LDS reads are done
+    stage_rows<D, KS>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows_t<D, VS>(Vt, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    __syncthreads();
+    floatx16 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = zero16();
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) st[t] = mma(ld16(&Ks[(32 * t + l32) * KS + 16 * s + 8 * h]), qf[s], st[t]);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * BK + 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
+        const float x = key > qpos ? -INFINITY : st[t][i] * sl2e;
+        st[t][i] = x;
+        bm = fmaxf(bm, x);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float alpha = exp2f(m - mn);
+    float rs = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2f(st[t][i] - mn);
+        st[t][i] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const bf16x8 pb = rows_bf16(st[t], hs);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          oacc[dt] = mma(tr_operand(Vt, VS, 32 * dt + l32, 32 * t + 16 * hs, h), pb, oacc[dt]);
+      }
+  }
+  store_cols<D>(o + (t0 + qpos) * ldq + (int64_t)hq * D, oacc, 1.0f / l, h);
+  if (h == 0) lse[(int64_t)hq * T + t0 + qpos] = (m + log2f(l)) * 0.69314718055994531f;
+}
+
+// ------------------------------------------------------------------ backward
+// rowsum(dO o O) per head and token: dsum[h][t]
+__global__ __launch_bounds__(256) void k_attn_bwd_dsum(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
+                                                       int64_t T, int nh, int D, float* __restrict__ dsum) {
+  const int64_t ld = (int64_t)nh * D;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x)
+    for (int hh = threadIdx.x; hh < nh; hh += 256) {
+      float acc = 0.0f;
+      for (int c = 0; c < D / 8; ++c) {
+        const u32x4 a = *(const u32x4*)(o + t * ld + (int64_t)hh * D + 8 * c);
+        const u32x4 b = *(const u32x4*)(dO + t * ld + (int64_t)hh * D + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
+      }
+      dsum[(int64_t)hh * T + t] = acc;
+    }
+}
+
+// dq = scale * dS K with dS^T = P^T o (dP^T - dsum), P^T = exp(S^T - lse), dP^T = V dO^T
+template <int D>
+__global__ __launch_bounds__(NT) void k_attn_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v, const float* __restrict__ lse,
+                                                    const uint16_t* __restrict__ dO, const float* __restrict__ dsum,
+                                                    int64_t T, int nh, int nkv, int64_t S, float scale, float sl2e,
+                                                    uint16_t* __restrict__ dq) {
+  constexpr int KS = D + 8, TS = BK + 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
+  const int nqb = (int)(S / BQ), n_seq = (int)(T / S);
+  const int seq = blockIdx.x % n_seq, qb = nqb - 1 - (int)(blockIdx.x / n_seq);
+  const int hq = blockIdx.y, hk = hq / (nh / nkv);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, h = lane >> 5;
+  const int64_t ldq = (int64_t)nh * D, ldk = (int64_t)nkv * D, t0 = (int64_t)seq * S;
+  const int qpos = qb * BQ + wave * 32 + l32;
+
+  bf16x8 qf[D / 16], dof[D / 16];
+  const int64_t qoff = (t0 + qpos) * ldq + (int64_t)hq * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = ld16(q + qoff + 16 * s + 8 * h);
+    dof[s] = ld16(dO + qoff + 16 * s + 8 * h);
+  }
+  const float lse2 = lse[(int64_t)hq * T + t0 + qpos] * 1.44269504088896341f;
+  const float dd = dsum[(int64_t)hq * T + t0 + qpos];
+  floatx16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+
+  for (int kb = 0; kb <= qb; ++kb) {
+    __syncthreads();
+    stage_rows<D, KS>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows<D, KS>(Vs, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows_t<D, TS>(Kt, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      floatx16 st = zero16(), dp = zero16();
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        st = mma(ld16(&Ks[(32 * t + l32) * KS + 16 * s + 8 * h]), qf[s], st);
+        dp = mma(ld16(&Vs[(32 * t + l32) * KS + 16 * s + 8 * h]), dof[s], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * BK + 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
+        const float p = key > qpos ? 0.0f : exp2f(st[i] * sl2e - lse2);
+        st[i] = p * (dp[i] - dd);  // dS^T
+      }
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        bf16x8 bh, bl;
+        rows_bf16_split(st, hs, bh, bl);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const bf16x8 a = tr_operand(Kt, TS, 32 * dt + l32, 32 * t + 16 * hs, h);
+          acc[dt] = mma(a, bh, acc[dt]);
+          acc[dt] = mma(a, bl, acc[dt]);
+        }
+      }
+    }
+  }
+  store_cols<D>(dq + qoff, acc, scale, h);
+}
+
+// dk = scale * dS^T Q and dv = P^T dO, summed over the query heads of the kv head and
+// the query blocks at or after the key block.  S = Q K^T here (a lane's column is a key).
+template <int D>
+__global__ __launch_bounds__(NT) void k_attn_bwd_dkdv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v, const float* __restrict__ lse,
+                                                      const uint16_t* __restrict__ dO, const float* __restrict__ dsum,
+                                                      int64_t T, int nh, int nkv, int64_t S, float scale, float sl2e,
+                                                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  constexpr int QS = D + 8, TS = BQ + 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[BQ * QS];   // dO rows
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ot[D * TS];    // dO transposed
+  __shared__ float lse_s[BQ], dsum_s[BQ];
+  const int nkb = (int)(S / BK), n_seq = (int)(T / S);
+  const int seq = blockIdx.x % n_seq, kb = (int)(blockIdx.x / n_seq);  // early key blocks have the most work
+  const int hk = blockIdx.y, rep = nh / nkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, h = lane >> 5;
+  const int64_t ldq = (int64_t)nh * D, ldk = (int64_t)nkv * D, t0 = (int64_t)seq * S;
+  const int kpos = kb * BK + wave * 32 + l32;  // this lane's key
+
+  bf16x8 kf[D / 16], vf[D / 16];
+  const int64_t koff = (t0 + kpos) * ldk + (int64_t)hk * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kf[s] = ld16(k + koff + 16 * s + 8 * h);
+    vf[s] = ld16(v + koff + 16 * s + 8 * h);
+  }
+  floatx16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dka[dt] = zero16();
+    dva[dt] = zero16();
+  }
+
+  for (int hq = hk * rep; hq < (hk + 1) * rep; ++hq)
+    for (int qb = kb; qb < nkb; ++qb) {
+      __syncthreads();
+      const int64_t r0 = t0 + (int64_t)qb * BQ;
+      stage_rows<D, QS>(Qs, q, r0, ldq, (int64_t)hq * D);
+      stage_rows<D, QS>(Os, dO, r0, ldq, (int64_t)hq * D);
+      stage_rows_t<D, TS>(Qt, q, r0, ldq, (int64_t)hq * D);
+      stage_rows_t<D, TS>(Ot, dO, r0, ldq, (int64_t)hq * D);
+      if (threadIdx.x < BQ) {
+        lse_s[threadIdx.x] = lse[(int64_t)hq * T + r0 + threadIdx.x] * 1.44269504088896341f;
+        dsum_s[threadIdx.x] = dsum[(int64_t)hq * T + r0 + threadIdx.x];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        floatx16 sa = zero16(), dp = zero16();
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          sa = mma(ld16(&Qs[(32 * t + l32) * QS + 16 * s + 8 * h]), kf[s], sa);
+          dp = mma(ld16(&Os[(32 * t + l32) * QS + 16 * s + 8 * h]), vf[s], dp);
+        }
+        floatx16 ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qr = 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);  // query row in the block
+          const float p = kpos > qb * BQ + qr ? 0.0f : exp2f(sa[i] * sl2e - lse_s[qr]);
+          sa[i] = p;
+          ds[i] = p * (dp[i] - dsum_s[qr]);
+        }
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          bf16x8 ph, pl, sh, sl;
+          rows_bf16_split(sa, hs, ph, pl);
+          rows_bf16_split(ds, hs, sh, sl);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const bf16x8 ao = tr_operand(Ot, TS, 32 * dt + l32, 32 * t + 16 * hs, h);
+            dva[dt] = mma(ao, ph, dva[dt]);
+            dva[dt] = mma(ao, pl, dva[dt]);
+            const bf16x8 a = tr_operand(Qt, TS, 32 * dt + l32, 32 * t + 16 * hs, h);
+            dka[dt] = mma(a, sh, dka[dt]);
+            dka[dt] = mma(a, sl, dka[dt]);
+          }
+        }
+      }
+    }
+  store_cols<D>(dk + koff, dka, scale, h);
+  store_cols<D>(dv + koff, dva, 1.0f, h);
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t T, int nh, int nkv, int D,
+                           int64_t S, uint16_t* o, float* lse, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((S / BQ) * (T / S)), (unsigned)nh);
+  const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
+  if (D == 128) hipLaunchKernelGGL(k_attn_fwd<128>, grid, dim3(NT), 0, s, q, k, v, T, nh, nkv, S, sl2e, o, lse);
+  else hipLaunchKernelGGL(k_attn_fwd<64>, grid, dim3(NT), 0, s, q, k, v, T, nh, nkv, S, sl2e, o, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                           const float* lse, const uint16_t* dO, int64_t T, int nh, int nkv, int D, int64_t S,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dsum, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const float scale = (float)(1.0 / sqrt((double)D));
+  const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));  // as in the forward
+  hipLaunchKernelGGL(k_attn_bwd_dsum, dim3((unsigned)(T < 65536 ? T : 65536)), dim3(256), 0, s, o, dO, T, nh, D, dsum);
+  const dim3 gq((unsigned)((S / BQ) * (T / S)), (unsigned)nh), gk((unsigned)((S / BK) * (T / S)), (unsigned)nkv);
+  if (D == 128) {
+    hipLaunchKernelGGL(k_attn_bwd_dq<128>, gq, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dq);
+    hipLaunchKernelGGL(k_attn_bwd_dkdv<128>, gk, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dk, dv);
+  } else {
+    hipLaunchKernelGGL(k_attn_bwd_dq<64>, gq, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dq);
+    hipLaunchKernelGGL(k_attn_bwd_dkdv<64>, gk, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dk, dv);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lnf4

@@ -82,6 +82,15 @@ def _declare(L):
         "lnf4_cross_entropy": (i32, [vp, i64, i64, vp, f32, vp, i64, vp, vp, vp]),
         "lnf4_sequence_sums": (i32, [vp, i32, i64, vp, vp]),
         "lnf4_dpo_loss": (i32, [vp, vp, i32, f32, vp, vp, vp]),
+        "lnf4_rmsnorm_fwd": (i32, [vp, i64, i64, vp, f32, vp, vp, vp]),
+        "lnf4_rmsnorm_bwd": (i32, [vp, i64, i64, vp, vp, vp, vp, vp, vp]),
+        "lnf4_rope_table": (i32, [i64, i32, ctypes.c_double, vp, vp]),
+        "lnf4_rope": (i32, [vp, i64, i32, i32, i64, vp, i32, vp]),
+        "lnf4_swiglu_fwd": (i32, [vp, vp, i64, vp, vp]),
+        "lnf4_swiglu_bwd": (i32, [vp, vp, vp, i64, vp, vp, vp]),
+        "lnf4_add": (i32, [vp, vp, i64, vp, vp]),
+        "lnf4_attn_fwd": (i32, [vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp]),
+        "lnf4_attn_bwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]),
         "stream_create": (i32, [POINTER(c_void_p), POINTER(c_size_t), i32, POINTER(c_void_p), sz, i32,
                                 POINTER(c_int32), i32, i32, vp, vp, sz, POINTER(c_void_p)]),
         "stream_layer_step": (i32, [vp, i32, vp, POINTER(c_void_p)]),
@@ -240,6 +249,47 @@ def lnf4_sequence_sums(x, n_seq: int, seq_len: int, sums, stream=None):
 def lnf4_dpo_loss(pol_sums, ref_sums, n_pairs: int, beta: float, loss, coef, stream=None):
     _check(lib().lnf4_dpo_loss(_ptr(pol_sums), _ptr(ref_sums), n_pairs, beta, _ptr(loss), _ptr(coef),
                                _stream(stream)))
+
+
+# ------------------------------------------------------------------ decoder-layer glue
+def lnf4_rmsnorm_fwd(x, T: int, H: int, g, eps: float, y, rstd, stream=None):
+    _check(lib().lnf4_rmsnorm_fwd(_ptr(x), T, H, _ptr(g), eps, _ptr(y), _ptr(rstd), _stream(stream)))
+
+
+def lnf4_rmsnorm_bwd(x, T: int, H: int, g, rstd, dy, dres, dx, stream=None):
+    _check(lib().lnf4_rmsnorm_bwd(_ptr(x), T, H, _ptr(g), _ptr(rstd), _ptr(dy), _ptr(dres), _ptr(dx),
+                                  _stream(stream)))
+
+
+def lnf4_rope_table(seq_len: int, head_dim: int, base: float, table, stream=None):
+    _check(lib().lnf4_rope_table(seq_len, head_dim, base, _ptr(table), _stream(stream)))
+
+
+def lnf4_rope(x, T: int, n_heads: int, head_dim: int, seq_len: int, table, inverse: int, stream=None):
+    _check(lib().lnf4_rope(_ptr(x), T, n_heads, head_dim, seq_len, _ptr(table), inverse, _stream(stream)))
+
+
+def lnf4_swiglu_fwd(g, u, n: int, s, stream=None):
+    _check(lib().lnf4_swiglu_fwd(_ptr(g), _ptr(u), n, _ptr(s), _stream(stream)))
+
+
+def lnf4_swiglu_bwd(g, u, ds, n: int, dg, du, stream=None):
+    _check(lib().lnf4_swiglu_bwd(_ptr(g), _ptr(u), _ptr(ds), n, _ptr(dg), _ptr(du), _stream(stream)))
+
+
+def lnf4_add(a, b, n: int, out, stream=None):
+    _check(lib().lnf4_add(_ptr(a), _ptr(b), n, _ptr(out), _stream(stream)))
+
+
+def lnf4_attn_fwd(q, k, v, T: int, n_heads: int, n_kv: int, head_dim: int, seq_len: int, o, lse, stream=None):
+    _check(lib().lnf4_attn_fwd(_ptr(q), _ptr(k), _ptr(v), T, n_heads, n_kv, head_dim, seq_len, _ptr(o), _ptr(lse),
+                               _stream(stream)))
+
+
+def lnf4_attn_bwd(q, k, v, o, lse, dout, T: int, n_heads: int, n_kv: int, head_dim: int, seq_len: int, dq, dk, dv,
+                  workspace, stream=None):
+    _check(lib().lnf4_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), T, n_heads, n_kv,
+                               head_dim, seq_len, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _stream(stream)))
 
 
 # ------------------------------------------------------------------ layer stream

@@ -174,3 +174,26 @@ def test_output_side_validation(L):
     assert L.lnf4_dpo_loss(FAKE, FAKE, 2, 0.0, FAKE, FAKE, None) == lnf4.LNF4_EINVAL
     assert L.lnf4_dpo_loss(FAKE, None, 2, 0.1, FAKE, FAKE, None) == lnf4.LNF4_EINVAL
     assert L.lnf4_dpo_loss(FAKE, FAKE, 2, 0.1, FAKE + 1, FAKE, None) == lnf4.LNF4_EALIGN
+
+
+def test_decoder_glue_validation(L):
+    E = lnf4
+    assert L.lnf4_rmsnorm_fwd(FAKE, 4, 12, FAKE, 1e-5, FAKE, FAKE, None) == E.LNF4_ESHAPE      # H % 8
+    assert L.lnf4_rmsnorm_fwd(FAKE, 4, 16, FAKE, -1.0, FAKE, FAKE, None) == E.LNF4_EINVAL      # eps
+    assert L.lnf4_rmsnorm_fwd(FAKE + 8, 4, 16, FAKE, 1e-5, FAKE, None, None) == E.LNF4_EALIGN
+    assert L.lnf4_rmsnorm_fwd(None, 0, 16, None, 1e-5, None, None, None) == E.LNF4_OK          # T = 0
+    assert L.lnf4_rmsnorm_bwd(FAKE, 4, 16, FAKE, None, FAKE, None, FAKE, None) == E.LNF4_EINVAL  # rstd
+    assert L.lnf4_rope_table(64, 24, 1e4, FAKE, None) == E.LNF4_ESHAPE                         # D % 16
+    assert L.lnf4_rope_table(64, 64, 1.0, FAKE, None) == E.LNF4_EINVAL                         # base
+    assert L.lnf4_rope(FAKE, 4, 2, 64, 0, FAKE, 0, None) == E.LNF4_EINVAL                      # seq_len
+    assert L.lnf4_swiglu_fwd(FAKE, FAKE, 12, FAKE, None) == E.LNF4_ESHAPE
+    assert L.lnf4_swiglu_bwd(FAKE, FAKE, None, 16, FAKE, FAKE, None) == E.LNF4_EINVAL
+    assert L.lnf4_add(FAKE, FAKE + 4, 16, FAKE, None) == E.LNF4_EALIGN
+    fwd = L.lnf4_attn_fwd
+    assert fwd(FAKE, FAKE, FAKE, 128, 4, 2, 96, 64, FAKE, FAKE, None) == E.LNF4_ESHAPE   # head_dim
+    assert fwd(FAKE, FAKE, FAKE, 128, 6, 4, 64, 64, FAKE, FAKE, None) == E.LNF4_ESHAPE   # heads not grouped
+    assert fwd(FAKE, FAKE, FAKE, 128, 4, 2, 64, 48, FAKE, FAKE, None) == E.LNF4_ESHAPE   # seq_len % 64
+    assert fwd(FAKE, FAKE, FAKE, 160, 4, 2, 64, 64, FAKE, FAKE, None) == E.LNF4_ESHAPE   # T % seq_len
+    assert fwd(FAKE, FAKE, FAKE, 128, 4, 2, 64, 64, FAKE, None, None) == E.LNF4_EINVAL
+    assert L.lnf4_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 4, 2, 64, 64, FAKE, FAKE, FAKE, None,
+                           None) == E.LNF4_EINVAL                                         # workspace
