@@ -322,7 +322,8 @@ int lnf4_add(const uint16_t* a, const uint16_t* b, int64_t n, uint16_t* out, hip
  *   q, o  device bf16 [T, n_heads * D];  k, v device bf16 [T, n_kv * D]
  *   lse   device fp32 [n_heads, T]
  *   D = head_dim, 64 or 128; seq_len a positive multiple of 64 dividing T
- * fp32 accumulation on the matrix cores; probabilities enter the value product as bf16.
+ * fp32 accumulation on the matrix cores; probabilities (and in backward the score
+ * gradients) enter their products as a bf16 hi + lo pair, about 16 significant bits.
  * Errors: EINVAL (T, NULL), ESHAPE (head_dim, heads, seq_len), EALIGN, EHIP.
  */
 int lnf4_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t T, int32_t n_heads,

@@ -14,10 +14,10 @@
 // are keys {4h..4h+3, 8+4h..8+4h+3} of that step (h = lane / 32), an order the other
 // operand (a transposed tile in LDS: V^T, K^T, Q^T or dO^T) is read in.
 //
-// In backward the score gradients dS and the probabilities P enter their products as a
-// bf16 hi + lo pair (two products each), so dq, dk and dv carry about 16 significant bits
-// of them (the gradients of tokens attended by many queries sum many terms that cancel);
-// the forward's value product takes P as one bf16.
+// The probabilities P and the score gradients dS enter their products as a bf16 hi + lo
+// pair (two products each), so o, dq, dk and dv carry about 16 significant bits of them
+// (a single bf16 would put a 2^-9 relative error on every term, and the gradients of
+// tokens attended by many queries sum many terms that cancel).
 //
 // Backward without atomics (bitwise reproducible): rowsum(dO o O) per query first, then
 // dq (a workgroup per query block, looping over its key blocks) and dk, dv (a workgroup
@@ -199,10 +199,14 @@ __global__ __launch_bounds__(NT) void k_attn_fwd(const uint16_t* __restrict__ q,
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
-        const bf16x8 pb = rows_bf16(st[t], hs);
+        bf16x8 ph, pl;
+        rows_bf16_split(st[t], hs, ph, pl);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          oacc[dt] = mma(tr_operand(Vt, VS, 32 * dt + l32, 32 * t + 16 * hs, h), pb, oacc[dt]);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const bf16x8 a = tr_operand(Vt, VS, 32 * dt + l32, 32 * t + 16 * hs, h);
+          oacc[dt] = mma(a, ph, oacc[dt]);
+          oacc[dt] = mma(a, pl, oacc[dt]);
+        }
       }
   }
   store_cols<D>(o + (t0 + qpos) * ldq + (int64_t)hq * D, oacc, 1.0f / l, h);

@@ -27,6 +27,8 @@ fp64 for the finite-difference pins.
 """
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 
 from . import head as ohead
@@ -34,10 +36,32 @@ from . import lora
 from . import nf4
 
 
+_JITTER = None  # (rng, rel) while storage_jitter is active
+
+
+@contextlib.contextmanager
+def storage_jitter(rng, rel: float):
+    """Inside this block every value is perturbed by a relative N(0, rel) error before its
+    bf16 storage.  With rel the size of an fp32 accumulation error (~1e-6) this measures
+    the model's own sensitivity: how far two exact-up-to-fp32 computations drift apart
+    once bf16 roundings flip and the flips propagate (tolerances of whole-model checks)."""
+    global _JITTER
+    old, _JITTER = _JITTER, (rng, float(rel))
+    try:
+        yield
+    finally:
+        _JITTER = old
+
+
 def q16(a, rnd: bool = True):
     """bf16 storage of a tensor (fp64 -> fp32 -> bf16 RNE), or the identity."""
     a = np.asarray(a, dtype=np.float64)
-    return nf4.bf16_bits_to_f64(nf4.bf16_rne_bits(a)) if rnd else a
+    if not rnd:
+        return a
+    if _JITTER is not None:
+        rng, rel = _JITTER
+        a = a * (1.0 + rel * rng.standard_normal(a.shape))
+    return nf4.bf16_bits_to_f64(nf4.bf16_rne_bits(a))
 
 
 # ------------------------------------------------------------------ RMSNorm

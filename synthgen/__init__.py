@@ -54,23 +54,33 @@ class Workload:
         return self.alpha / self.rank
 
 
+def _arch(n_heads: int, n_kv: int, head_dim: int, seq_len: int, eps: float, rope_base: float):
+    """What a whole decoder layer needs beyond the projection shapes (the configs give the
+    head counts and dims; eps and the RoPE base are the models' published values)."""
+    return {"arch": {"n_heads": n_heads, "n_kv": n_kv, "head_dim": head_dim, "seq_len": seq_len, "eps": eps,
+                     "rope_base": rope_base}}
+
+
 WORKLOADS = {
     # single 896x896 linear, r8 alpha16, 256 tokens
     "linear896": Workload("linear896", 256, {"w": (896, 896)}, 8, 16.0, ("w",)),
     # Qwen2.5-0.5B-shaped layer x24, batch 4 x seq 512, r16 on all seven
     "qwen05b": Workload("qwen05b", 4 * 512, _decoder_shapes(896, 14, 2, 64, 4864), 16, 32.0,
-                        PROJ_ORDER, layers=24, hidden=896),
+                        PROJ_ORDER, layers=24, hidden=896, extra=_arch(14, 2, 64, 512, 1e-6, 1e6)),
     # Llama-3.1-8B-shaped stack x32 + head slot, batch 1 x seq 2048, r8 alpha32 on q, v
     "llama8b": Workload("llama8b", 2048, _decoder_shapes(4096, 32, 8, 128, 14336), 8, 32.0,
-                        ("q", "v"), layers=32, vocab=128256, hidden=4096),
+                        ("q", "v"), layers=32, vocab=128256, hidden=4096,
+                        extra=_arch(32, 8, 128, 2048, 1e-5, 500000.0)),
     # Qwen2.5-3B-shaped bf16 stack x36, batch 2 x seq 1024, r16 on all seven
     "qwen3b_bf16": Workload("qwen3b_bf16", 2 * 1024, _decoder_shapes(2048, 16, 2, 128, 11008), 16, 32.0,
-                            PROJ_ORDER, layers=36, fmt="bf16", hidden=2048),
+                            PROJ_ORDER, layers=36, fmt="bf16", hidden=2048,
+                            extra=_arch(16, 2, 128, 1024, 1e-6, 1e6)),
     # DPO step on the llama8b stack: 2 pairs x (chosen, rejected) x 1024 tokens
     # (beta: the preference loss's temperature; the pages give none, 0.1 is the common default)
     "llama8b_dpo": Workload("llama8b_dpo", 2 * 2 * 1024, _decoder_shapes(4096, 32, 8, 128, 14336), 8, 32.0,
                             ("q", "v"), layers=32, vocab=128256, hidden=4096,
-                            passes=("ref", "fwd", "recompute", "bwd"), extra={"seq_len": 1024, "beta": 0.1}),
+                            passes=("ref", "fwd", "recompute", "bwd"),
+                            extra={"seq_len": 1024, "beta": 0.1, **_arch(32, 8, 128, 1024, 1e-5, 500000.0)}),
 }
 
 # q, k, v share the attention input; gate, up share the MLP input

@@ -226,3 +226,15 @@ def test_layer_with_zero_output_projections_is_the_identity():
     x = RS.normal(size=(6, 8))
     y, _ = od.layer_fwd(P, CFG, x, rnd=False)
     assert np.array_equal(y, x)
+
+
+def test_storage_jitter_is_scoped_and_small():
+    x = RS.normal(size=(400, 400))
+    base = od.q16(x)
+    with od.storage_jitter(np.random.default_rng(0), 1e-6):
+        j = od.q16(x)
+        assert np.array_equal(od.q16(x, rnd=False), x)      # no storage, no jitter
+    assert np.array_equal(od.q16(x), base)                   # restored on exit
+    # a 1e-6 relative perturbation moves an element by at most one bf16 step, rarely
+    step = np.abs(j - base) / np.abs(base)
+    assert step.max() <= 2.0 ** -7 and 0 < np.count_nonzero(j != base) < x.size // 50
