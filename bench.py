@@ -298,6 +298,63 @@ def stream_variants(wl, args, L):
     return out
 
 
+def decoder_model_run(args):
+    """The whole decoder model on the 8B stack (embedding, 32 real decoder layers with
+    RMSNorm, RoPE, causal GQA attention, SwiGLU and residuals, final norm, lm_head and
+    loss, forward + recompute + backward), streamed and resident, and the attention
+    kernels alone at that shape (HIP events, 20 launches each)."""
+    import torch
+    import synthgen
+    from lora_fine_tuning_nf4_amd import lnf4
+    from lora_fine_tuning_nf4_amd.model import StreamedDecoder
+
+    wl = synthgen.WORKLOADS[args.workload]
+    if wl.extra.get("arch") is None or wl.vocab <= 0:
+        return None
+    out = {}
+    m = StreamedDecoder(wl, n_bufs=args.nbuf, seed=args.seed, loss_chunk=args.loss_chunk)
+    try:
+        for mode in ("streamed", "resident"):
+            res = mode == "resident"
+            for _ in range(max(1, args.warmup)):
+                m.step(resident=res)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                m.step(resident=res)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+            out[f"{mode}_ms_per_step"] = round(ms, 3)
+            out[f"{mode}_tokens_per_s"] = round(m.T / (ms / 1000.0), 2)
+        # attention alone, on the model's own buffers (the last layer's q, k, v, o)
+        T, nh, nkv, D, S = m.T, m.nh, m.nkv, m.D, m.S
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fwd_flops = 2.0 * 2.0 * nh * D * (S * (S + 1) / 2.0) * (T // S)   # causal (query, key) pairs
+        bwd_flops = 2.5 * fwd_flops
+        for name, fn, fl in (
+                ("fwd", lambda: lnf4.lnf4_attn_fwd(m.q, m.k, m.v, T, nh, nkv, D, S, m.o, m.lse), fwd_flops),
+                ("bwd", lambda: lnf4.lnf4_attn_bwd(m.q, m.k, m.v, m.o, m.lse, m.do, T, nh, nkv, D, S, m.dq, m.dk,
+                                                   m.dv, m.attn_ws, m.attn_ws_bytes), bwd_flops)):
+            fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            out[f"attention_{name}_ms"] = round(ms, 4)
+            out[f"attention_{name}_tflops"] = round(fl / (ms / 1000.0) / 1e12, 1)
+        out["attention_flops_note"] = ("algorithmic: fwd 2 products x 2 flops per causal (query, key) pair and head "
+                                       "dim; bwd 2.5x fwd (score recompute, dV, dP, dQ, dK)")
+    finally:
+        m.close()
+        del m
+        torch.cuda.empty_cache()
+    log(f"decoder model: {out}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +366,8 @@ def main():
     ap.add_argument("--no-resident", action="store_true", help="skip the H2D-removed reference run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-model", action="store_true",
+                    help="skip the whole-decoder-model run (attention, norms, SwiGLU between the projections)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the stream-variant runs (buffer reuse, no recompute)")
     ap.add_argument("--loss-chunk", type=int, default=None,
@@ -534,6 +593,8 @@ def main():
 
     if not args.no_variants:
         result["stream_variants"] = stream_variants(wl, args, L)
+    if not args.no_model and L == wl.layers:
+        result["decoder_model"] = decoder_model_run(args)
 
     if args.study:
         log("study: dequant share ...")

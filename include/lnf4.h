@@ -336,13 +336,18 @@ int lnf4_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
  *   query heads.  No atomics: bitwise reproducible.
  *   dout        device bf16 [T, n_heads * D] (the output gradient)
  *   dq, dk, dv  device bf16, shaped as q, k, v
- *   workspace   device fp32 [n_heads * T] (rowsum(dO o o))
- * Errors: as lnf4_attn_fwd.
+ *   workspace   device, 256-byte aligned, at least lnf4_attn_bwd_workspace(...) bytes:
+ *               rowsum(dO o o) per head and token, and with grouped kv heads the fp32
+ *               per-query-head shares of dk and dv (summed in head order at the end)
+ * Errors: as lnf4_attn_fwd; ESHAPE also for a workspace too small.
  */
 int lnf4_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o, const float* lse,
                   const uint16_t* dout, int64_t T, int32_t n_heads, int32_t n_kv, int32_t head_dim,
-                  int64_t seq_len, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* workspace,
+                  int64_t seq_len, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace, size_t ws_bytes,
                   hipStream_t stream);
+
+/* Workspace bytes lnf4_attn_bwd needs (0 for invalid sizes).  Host-only. */
+size_t lnf4_attn_bwd_workspace(int64_t T, int32_t n_heads, int32_t n_kv, int32_t head_dim);
 
 /* ------------------------------------------------------------------ layer stream */
 typedef struct lnf4_stream lnf4_stream;

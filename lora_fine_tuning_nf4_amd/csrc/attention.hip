@@ -21,8 +21,9 @@
 //
 // Backward without atomics (bitwise reproducible): rowsum(dO o O) per query first, then
 // dq (a workgroup per query block, looping over its key blocks) and dk, dv (a workgroup
-// per key block and kv head, looping over the query heads of the group and the query
-// blocks at or after it).
+// per key block and query head, looping over the query blocks at or after it; with
+// grouped kv heads each writes an fp32 share, and a last pass sums the shares of a kv
+// head in head order).
 #include <math.h>
 
 #include "common.hpp"
@@ -32,9 +33,10 @@ namespace lnf4 {
 
 namespace {
 
-constexpr int BQ = 64;   // queries per workgroup
-constexpr int BK = 64;   // keys per block
-constexpr int NT = 128;  // two waves
+constexpr int BQ = 64;   // queries per staged block (backward dk, dv)
+constexpr int BK = 64;   // keys per staged block (forward, backward dq)
+// a workgroup is NW waves of 32 rows each (queries in the forward and dq, keys in dk,
+// dv): 4 waves share each staged block when the sequence length allows 128-row blocks
 
 __device__ __forceinline__ floatx16 mma(const bf16x8& a, const bf16x8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -85,7 +87,7 @@ __device__ __forceinline__ floatx16 zero16() {
 }
 
 // rows [r0, r0+64) of a [.., ld] bf16 matrix, columns [c0, c0+D), into LDS row-major
-template <int D, int STRIDE>
+template <int D, int STRIDE, int NT>
 __device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t r0, int64_t ld, int64_t c0) {
   for (int idx = threadIdx.x; idx < 64 * (D / 8); idx += NT) {
     const int r = idx / (D / 8), c = idx - r * (D / 8);
@@ -94,7 +96,7 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, i
 }
 
 // the same 64 x D block transposed: dst[d][r], two rows per 4-byte LDS write
-template <int D, int STRIDE>
+template <int D, int STRIDE, int NT>
 __device__ __forceinline__ void stage_rows_t(uint16_t* dst, const uint16_t* src, int64_t r0, int64_t ld, int64_t c0) {
   for (int idx = threadIdx.x; idx < 32 * (D / 8); idx += NT) {
     const int rp = idx / (D / 8), c = idx - rp * (D / 8);
@@ -130,20 +132,21 @@ __device__ __forceinline__ void store_cols(uint16_t* out_row, const floatx16 (&a
 // Online softmax over key blocks in base 2: x = s * scale * log2(e), running max m and
 // sum l per query, O^T rescaled by 2^(m_old - m_new) when m grows.  lse is stored in
 // natural-log units: (m + log2 l) * ln 2.
-template <int D>
-__global__ __launch_bounds__(NT) void k_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v, int64_t T, int nh, int nkv,
                                                  int64_t S, float sl2e, uint16_t* __restrict__ o,
                                                  float* __restrict__ lse) {
-  constexpr int KS = D + 8, VS = BK + 4;
+  constexpr int KS = D + 8, VS = BK + 4, NT = 64 * NW, BR = 32 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
-  const int nqb = (int)(S / BQ), n_seq = (int)(T / S);
+  const int nqb = (int)(S / BR), n_seq = (int)(T / S);
   const int seq = blockIdx.x % n_seq, qb = nqb - 1 - (int)(blockIdx.x / n_seq);  // longest rows first
   const int hq = blockIdx.y, hk = hq / (nh / nkv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, h = lane >> 5;
   const int64_t ldq = (int64_t)nh * D, ldk = (int64_t)nkv * D, t0 = (int64_t)seq * S;
-  const int qpos = qb * BQ + wave * 32 + l32;  // this lane's query, position in its sequence
+  const int qpos = qb * BR + wave * 32 + l32;  // this lane's query, position in its sequence
+  const int kb_last = (qb * BR + BR - 1) / BK;
 
   bf16x8 qf[D / 16];
   const uint16_t* qrow = q + (t0 + qpos) * ldq + (int64_t)hq * D;
@@ -154,10 +157,10 @@ __global__ __launch_bounds__(NT) void k_attn_fwd(const uint16_t* __restrict__ q,
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = zero16();
   float m = -INFINITY, l = 0.0f;
 
-  for (int kb = 0; kb <= qb; ++kb) {
+  for (int kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();  // the previous block's LDS reads are done
-    stage_rows<D, KS>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
-    stage_rows_t<D, VS>(Vt, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows<D, KS, NT>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows_t<D, VS, NT>(Vt, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
     __syncthreads();
     floatx16 st[2];
 #pragma unroll
@@ -232,22 +235,23 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dsum(const uint16_t* __restric
 }
 
 // dq = scale * dS K with dS^T = P^T o (dP^T - dsum), P^T = exp(S^T - lse), dP^T = V dO^T
-template <int D>
-__global__ __launch_bounds__(NT) void k_attn_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, const float* __restrict__ lse,
                                                     const uint16_t* __restrict__ dO, const float* __restrict__ dsum,
                                                     int64_t T, int nh, int nkv, int64_t S, float scale, float sl2e,
                                                     uint16_t* __restrict__ dq) {
-  constexpr int KS = D + 8, TS = BK + 4;
+  constexpr int KS = D + 8, TS = BK + 4, NT = 64 * NW, BR = 32 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * KS];
   __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
-  const int nqb = (int)(S / BQ), n_seq = (int)(T / S);
+  const int nqb = (int)(S / BR), n_seq = (int)(T / S);
   const int seq = blockIdx.x % n_seq, qb = nqb - 1 - (int)(blockIdx.x / n_seq);
   const int hq = blockIdx.y, hk = hq / (nh / nkv);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, h = lane >> 5;
   const int64_t ldq = (int64_t)nh * D, ldk = (int64_t)nkv * D, t0 = (int64_t)seq * S;
-  const int qpos = qb * BQ + wave * 32 + l32;
+  const int qpos = qb * BR + wave * 32 + l32;
+  const int kb_last = (qb * BR + BR - 1) / BK;
 
   bf16x8 qf[D / 16], dof[D / 16];
   const int64_t qoff = (t0 + qpos) * ldq + (int64_t)hq * D;
@@ -262,11 +266,11 @@ __global__ __launch_bounds__(NT) void k_attn_bwd_dq(const uint16_t* __restrict__
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
 
-  for (int kb = 0; kb <= qb; ++kb) {
+  for (int kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();
-    stage_rows<D, KS>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
-    stage_rows<D, KS>(Vs, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
-    stage_rows_t<D, TS>(Kt, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows<D, KS, NT>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows<D, KS, NT>(Vs, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    stage_rows_t<D, TS, NT>(Kt, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -300,24 +304,30 @@ __global__ __launch_bounds__(NT) void k_attn_bwd_dq(const uint16_t* __restrict__
 
 // dk = scale * dS^T Q and dv = P^T dO, summed over the query heads of the kv head and
 // the query blocks at or after the key block.  S = Q K^T here (a lane's column is a key).
-template <int D>
-__global__ __launch_bounds__(NT) void k_attn_bwd_dkdv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, const float* __restrict__ lse,
                                                       const uint16_t* __restrict__ dO, const float* __restrict__ dsum,
                                                       int64_t T, int nh, int nkv, int64_t S, float scale, float sl2e,
-                                                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  constexpr int QS = D + 8, TS = BQ + 4;
+                                                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                                                      float* __restrict__ part) {
+  constexpr int QS = D + 8, TS = BQ + 4, NT = 64 * NW, BR = 32 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * QS];
   __shared__ __attribute__((aligned(16))) uint16_t Os[BQ * QS];   // dO rows
   __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TS];
   __shared__ __attribute__((aligned(16))) uint16_t Ot[D * TS];    // dO transposed
   __shared__ float lse_s[BQ], dsum_s[BQ];
-  const int nkb = (int)(S / BK), n_seq = (int)(T / S);
+  const int nqb = (int)(S / BQ), n_seq = (int)(T / S);
   const int seq = blockIdx.x % n_seq, kb = (int)(blockIdx.x / n_seq);  // early key blocks have the most work
-  const int hk = blockIdx.y, rep = nh / nkv;
+  // part == nullptr: blockIdx.y is a kv head and the workgroup sums its query heads;
+  // otherwise blockIdx.y is a query head and the workgroup writes that head's fp32 share
+  const int rep = nh / nkv;
+  const int hk = part ? (int)blockIdx.y / rep : (int)blockIdx.y;
+  const int hq0 = part ? (int)blockIdx.y : hk * rep, hq1 = part ? hq0 + 1 : hk * rep + rep;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, h = lane >> 5;
   const int64_t ldq = (int64_t)nh * D, ldk = (int64_t)nkv * D, t0 = (int64_t)seq * S;
-  const int kpos = kb * BK + wave * 32 + l32;  // this lane's key
+  const int kpos = kb * BR + wave * 32 + l32;  // this lane's key
+  const int qb_first = kb * BR / BQ;           // the first query block that sees these keys
 
   bf16x8 kf[D / 16], vf[D / 16];
   const int64_t koff = (t0 + kpos) * ldk + (int64_t)hk * D;
@@ -333,14 +343,14 @@ __global__ __launch_bounds__(NT) void k_attn_bwd_dkdv(const uint16_t* __restrict
     dva[dt] = zero16();
   }
 
-  for (int hq = hk * rep; hq < (hk + 1) * rep; ++hq)
-    for (int qb = kb; qb < nkb; ++qb) {
+  for (int hq = hq0; hq < hq1; ++hq)
+    for (int qb = qb_first; qb < nqb; ++qb) {
       __syncthreads();
       const int64_t r0 = t0 + (int64_t)qb * BQ;
-      stage_rows<D, QS>(Qs, q, r0, ldq, (int64_t)hq * D);
-      stage_rows<D, QS>(Os, dO, r0, ldq, (int64_t)hq * D);
-      stage_rows_t<D, TS>(Qt, q, r0, ldq, (int64_t)hq * D);
-      stage_rows_t<D, TS>(Ot, dO, r0, ldq, (int64_t)hq * D);
+      stage_rows<D, QS, NT>(Qs, q, r0, ldq, (int64_t)hq * D);
+      stage_rows<D, QS, NT>(Os, dO, r0, ldq, (int64_t)hq * D);
+      stage_rows_t<D, TS, NT>(Qt, q, r0, ldq, (int64_t)hq * D);
+      stage_rows_t<D, TS, NT>(Ot, dO, r0, ldq, (int64_t)hq * D);
       if (threadIdx.x < BQ) {
         lse_s[threadIdx.x] = lse[(int64_t)hq * T + r0 + threadIdx.x] * 1.44269504088896341f;
         dsum_s[threadIdx.x] = dsum[(int64_t)hq * T + r0 + threadIdx.x];
@@ -379,35 +389,104 @@ __global__ __launch_bounds__(NT) void k_attn_bwd_dkdv(const uint16_t* __restrict
         }
       }
     }
-  store_cols<D>(dk + koff, dka, scale, h);
-  store_cols<D>(dv + koff, dva, 1.0f, h);
+  if (part == nullptr) {
+    store_cols<D>(dk + koff, dka, scale, h);
+    store_cols<D>(dv + koff, dva, 1.0f, h);
+    return;
+  }
+  // fp32 shares: part[0][hq][t][d] for dk (scaled), part[1][hq][t][d] for dv
+  const int64_t plane = (int64_t)nh * T * D;
+  float* pk = part + ((int64_t)hq0 * T + t0 + kpos) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * dt + 8 * j + 4 * h;
+      *(floatx4*)(pk + d0) = floatx4{dka[dt][4 * j] * scale, dka[dt][4 * j + 1] * scale, dka[dt][4 * j + 2] * scale,
+                                     dka[dt][4 * j + 3] * scale};
+      *(floatx4*)(pk + plane + d0) = floatx4{dva[dt][4 * j], dva[dt][4 * j + 1], dva[dt][4 * j + 2], dva[dt][4 * j + 3]};
+    }
+}
+
+// dk, dv [T, n_kv * D] = bf16 of the sum over the rep query heads of each kv head, in
+// head order
+__global__ __launch_bounds__(256) void k_attn_bwd_kv_reduce(const float* __restrict__ part, int64_t T, int nh, int nkv,
+                                                            int D, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  const int rep = nh / nkv;
+  const int64_t plane = (int64_t)nh * T * D, n4 = (int64_t)nkv * T * D / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const int64_t e = 4 * i;                       // element of [T, nkv, D]
+    const int64_t t = e / ((int64_t)nkv * D);
+    const int hk = (int)((e / D) % nkv);
+    const int d = (int)(e % D);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < rep; ++j)
+        acc += *(const floatx4*)(part + w * plane + ((int64_t)(hk * rep + j) * T + t) * D + d);
+      uint2 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      *(uint2*)((w ? dv : dk) + e) = o;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t T, int nh, int nkv, int D,
                            int64_t S, uint16_t* o, float* lse, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((S / BQ) * (T / S)), (unsigned)nh);
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
-  if (D == 128) hipLaunchKernelGGL(k_attn_fwd<128>, grid, dim3(NT), 0, s, q, k, v, T, nh, nkv, S, sl2e, o, lse);
-  else hipLaunchKernelGGL(k_attn_fwd<64>, grid, dim3(NT), 0, s, q, k, v, T, nh, nkv, S, sl2e, o, lse);
+  const bool w4 = S % 128 == 0;
+  const dim3 grid((unsigned)((S / (w4 ? 128 : 64)) * (T / S)), (unsigned)nh), block(w4 ? 256 : 128);
+#define LNF4_FWD(D_, NW_) hipLaunchKernelGGL((k_attn_fwd<D_, NW_>), grid, block, 0, s, q, k, v, T, nh, nkv, S, sl2e, o, lse)
+  if (D == 128) {
+    if (w4) LNF4_FWD(128, 4); else LNF4_FWD(128, 2);
+  } else {
+    if (w4) LNF4_FWD(64, 4); else LNF4_FWD(64, 2);
+  }
+#undef LNF4_FWD
   return hipGetLastError();
+}
+
+size_t attn_bwd_workspace_bytes(int64_t T, int nh, int nkv, int D) {
+  const size_t dsum = (size_t)nh * T * 4;
+  const size_t part = nh == nkv ? 0 : 2 * (size_t)nh * T * D * 4;
+  return ((dsum + 255) & ~(size_t)255) + part;
 }
 
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                            const float* lse, const uint16_t* dO, int64_t T, int nh, int nkv, int D, int64_t S,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dsum, hipStream_t s) {
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const float scale = (float)(1.0 / sqrt((double)D));
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));  // as in the forward
+  float* dsum = (float*)workspace;
+  // with grouped kv heads every query head writes an fp32 share of dk, dv (4x the
+  // workgroups of one per kv head), summed afterwards in head order
+  float* part = nh == nkv ? nullptr : (float*)((uint8_t*)workspace + (((size_t)nh * T * 4 + 255) & ~(size_t)255));
   hipLaunchKernelGGL(k_attn_bwd_dsum, dim3((unsigned)(T < 65536 ? T : 65536)), dim3(256), 0, s, o, dO, T, nh, D, dsum);
-  const dim3 gq((unsigned)((S / BQ) * (T / S)), (unsigned)nh), gk((unsigned)((S / BK) * (T / S)), (unsigned)nkv);
+  const bool w4 = S % 128 == 0;
+  const int br = w4 ? 128 : 64;
+  const dim3 gq((unsigned)((S / br) * (T / S)), (unsigned)nh);
+  const dim3 gk((unsigned)((S / br) * (T / S)), (unsigned)(part ? nh : nkv));
+  const dim3 block(w4 ? 256 : 128);
+#define LNF4_BWD(D_, NW_)                                                                                   \
+  hipLaunchKernelGGL((k_attn_bwd_dq<D_, NW_>), gq, block, 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, \
+                     sl2e, dq);                                                                              \
+  hipLaunchKernelGGL((k_attn_bwd_dkdv<D_, NW_>), gk, block, 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S,      \
+                     scale, sl2e, dk, dv, part)
   if (D == 128) {
-    hipLaunchKernelGGL(k_attn_bwd_dq<128>, gq, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dq);
-    hipLaunchKernelGGL(k_attn_bwd_dkdv<128>, gk, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dk, dv);
+    if (w4) { LNF4_BWD(128, 4); } else { LNF4_BWD(128, 2); }
   } else {
-    hipLaunchKernelGGL(k_attn_bwd_dq<64>, gq, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dq);
-    hipLaunchKernelGGL(k_attn_bwd_dkdv<64>, gk, dim3(NT), 0, s, q, k, v, lse, dO, dsum, T, nh, nkv, S, scale, sl2e, dk, dv);
+    if (w4) { LNF4_BWD(64, 4); } else { LNF4_BWD(64, 2); }
+  }
+#undef LNF4_BWD
+  if (part) {
+    const int64_t n4 = (int64_t)nkv * T * D / 4;
+    const int64_t b = (n4 + 255) / 256;
+    hipLaunchKernelGGL(k_attn_bwd_kv_reduce, dim3((unsigned)(b < 8192 ? b : 8192)), dim3(256), 0, s, part, T, nh, nkv,
+                       D, dk, dv);
   }
   return hipGetLastError();
 }

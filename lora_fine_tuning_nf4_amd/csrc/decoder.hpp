@@ -21,8 +21,9 @@ hipError_t launch_swiglu_bwd(const uint16_t* g, const uint16_t* u, const uint16_
 hipError_t launch_add(const uint16_t* a, const uint16_t* b, int64_t n, uint16_t* out, hipStream_t s);
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t T, int nh, int nkv, int D,
                            int64_t S, uint16_t* o, float* lse, hipStream_t s);
+size_t attn_bwd_workspace_bytes(int64_t T, int nh, int nkv, int D);
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                            const float* lse, const uint16_t* dO, int64_t T, int nh, int nkv, int D, int64_t S,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dsum, hipStream_t s);
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace, hipStream_t s);
 
 }  // namespace lnf4

@@ -134,9 +134,14 @@ int lnf4_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64
   return e == hipSuccess ? LNF4_OK : hip_fail(e, "attention forward launch");
 }
 
+size_t lnf4_attn_bwd_workspace(int64_t T, int32_t n_heads, int32_t n_kv, int32_t head_dim) {
+  if (T < 0 || n_heads < 1 || n_kv < 1 || n_heads % n_kv != 0 || (head_dim != 64 && head_dim != 128)) return 0;
+  return attn_bwd_workspace_bytes(T, n_heads, n_kv, head_dim);
+}
+
 int lnf4_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o, const float* lse,
                   const uint16_t* dout, int64_t T, int32_t n_heads, int32_t n_kv, int32_t head_dim, int64_t seq_len,
-                  uint16_t* dq, uint16_t* dk, uint16_t* dv, float* workspace, hipStream_t stream) {
+                  uint16_t* dq, uint16_t* dk, uint16_t* dv, void* workspace, size_t ws_bytes, hipStream_t stream) {
   const char* who = "lnf4_attn_bwd";
   int rc = check_attn(T, n_heads, n_kv, head_dim, seq_len, who);
   if (rc) return rc;
@@ -144,8 +149,11 @@ int lnf4_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return fail(LNF4_EINVAL, "%s: NULL pointer", who);
   if (!a16(q) || !a16(k) || !a16(v) || !a16(o) || !a16(dout) || !a16(dq) || !a16(dk) || !a16(dv) ||
-      !aligned(lse, 4) || !aligned(workspace, 4))
-    return fail(LNF4_EALIGN, "%s: misaligned pointer", who);
+      !aligned(lse, 4) || !aligned(workspace, 256))
+    return fail(LNF4_EALIGN, "%s: misaligned pointer (workspace: 256 bytes)", who);
+  if (ws_bytes < attn_bwd_workspace_bytes(T, n_heads, n_kv, head_dim))
+    return fail(LNF4_ESHAPE, "%s: workspace of %zu bytes, %zu needed", who, ws_bytes,
+                attn_bwd_workspace_bytes(T, n_heads, n_kv, head_dim));
   const hipError_t e = launch_attn_bwd(q, k, v, o, lse, dout, T, n_heads, n_kv, head_dim, seq_len, dq, dk, dv,
                                        workspace, stream);
   return e == hipSuccess ? LNF4_OK : hip_fail(e, "attention backward launch");

@@ -90,7 +90,8 @@ def _declare(L):
         "lnf4_swiglu_bwd": (i32, [vp, vp, vp, i64, vp, vp, vp]),
         "lnf4_add": (i32, [vp, vp, i64, vp, vp]),
         "lnf4_attn_fwd": (i32, [vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp]),
-        "lnf4_attn_bwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]),
+        "lnf4_attn_bwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp]),
+        "lnf4_attn_bwd_workspace": (sz, [i64, i32, i32, i32]),
         "stream_create": (i32, [POINTER(c_void_p), POINTER(c_size_t), i32, POINTER(c_void_p), sz, i32,
                                 POINTER(c_int32), i32, i32, vp, vp, sz, POINTER(c_void_p)]),
         "stream_layer_step": (i32, [vp, i32, vp, POINTER(c_void_p)]),
@@ -286,10 +287,15 @@ def lnf4_attn_fwd(q, k, v, T: int, n_heads: int, n_kv: int, head_dim: int, seq_l
                                _stream(stream)))
 
 
+def lnf4_attn_bwd_workspace(T: int, n_heads: int, n_kv: int, head_dim: int) -> int:
+    return int(lib().lnf4_attn_bwd_workspace(T, n_heads, n_kv, head_dim))
+
+
 def lnf4_attn_bwd(q, k, v, o, lse, dout, T: int, n_heads: int, n_kv: int, head_dim: int, seq_len: int, dq, dk, dv,
-                  workspace, stream=None):
+                  workspace, ws_bytes: int, stream=None):
     _check(lib().lnf4_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), T, n_heads, n_kv,
-                               head_dim, seq_len, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _stream(stream)))
+                               head_dim, seq_len, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                               _stream(stream)))
 
 
 # ------------------------------------------------------------------ layer stream

@@ -119,7 +119,8 @@ class StreamedDecoder:
         self.dm, self.dh, self.da, self.do = E(T, H), E(T, H), E(T, H), E(T, nq)
         self.dq, self.dk, self.dv = E(T, nq), E(T, nk), E(T, nk)
         self.dx = [E(T, H), E(T, H)]
-        self.attn_ws = torch.empty(self.nh * T, dtype=f32, device=dev)
+        self.attn_ws_bytes = lnf4.lnf4_attn_bwd_workspace(T, self.nh, self.nkv, self.D)
+        self.attn_ws = torch.empty(self.attn_ws_bytes, dtype=torch.uint8, device=dev)
         self.hN, self.dhN = E(T, H), E(T, H)
         self.logp = torch.empty(T, dtype=f32, device=dev)
         chunk = T if not loss_chunk else min(int(loss_chunk), T)
@@ -233,7 +234,7 @@ class StreamedDecoder:
         lnf4.lnf4_rmsnorm_bwd(self.h, T, H, base + self.g2_off, self.rstd2, self.dm, dout, self.dh, cs)
         gb(O, self.o, (self.dh,), self.do)
         lnf4.lnf4_attn_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, T, self.nh, self.nkv, self.D, self.S,
-                           self.dq, self.dk, self.dv, self.attn_ws, cs)
+                           self.dq, self.dk, self.dv, self.attn_ws, self.attn_ws_bytes, cs)
         lnf4.lnf4_rope(self.dq, T, self.nh, self.D, self.S, self.rope, 1, cs)
         lnf4.lnf4_rope(self.dk, T, self.nkv, self.D, self.S, self.rope, 1, cs)
         gb(QKV, self.a, (self.dq, self.dk, self.dv), self.da)

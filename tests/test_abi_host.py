@@ -195,5 +195,10 @@ def test_decoder_glue_validation(L):
     assert fwd(FAKE, FAKE, FAKE, 128, 4, 2, 64, 48, FAKE, FAKE, None) == E.LNF4_ESHAPE   # seq_len % 64
     assert fwd(FAKE, FAKE, FAKE, 160, 4, 2, 64, 64, FAKE, FAKE, None) == E.LNF4_ESHAPE   # T % seq_len
     assert fwd(FAKE, FAKE, FAKE, 128, 4, 2, 64, 64, FAKE, None, None) == E.LNF4_EINVAL
-    assert L.lnf4_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 4, 2, 64, 64, FAKE, FAKE, FAKE, None,
+    assert L.lnf4_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 4, 2, 64, 64, FAKE, FAKE, FAKE, None, 0,
                            None) == E.LNF4_EINVAL                                         # workspace
+    need = L.lnf4_attn_bwd_workspace(128, 4, 2, 64)
+    assert need == 4 * 128 * 4 + 2 * 4 * 128 * 64 * 4                                     # rowsums + fp32 shares
+    assert L.lnf4_attn_bwd_workspace(128, 4, 4, 64) == 4 * 128 * 4                        # no grouping: no shares
+    assert L.lnf4_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 4, 2, 64, 64, FAKE, FAKE, FAKE, FAKE, need - 1,
+                           None) == E.LNF4_ESHAPE

@@ -153,8 +153,9 @@ def _run_attention(q, k, v, do, T, S, nh, nkv, D, o_in, lse_in):
     o, lse = empty16(T, nh * D), torch.empty(nh * T, dtype=torch.float32, device="cuda")
     lnf4.lnf4_attn_fwd(qd, kd, vd, T, nh, nkv, D, S, o, lse)
     dq, dk, dv = empty16(T, nh * D), empty16(T, nkv * D), empty16(T, nkv * D)
-    ws = torch.empty(nh * T, dtype=torch.float32, device="cuda")
-    lnf4.lnf4_attn_bwd(qd, kd, vd, dev_u16(o_in), dev_f32(lse_in), dod, T, nh, nkv, D, S, dq, dk, dv, ws)
+    wsb = lnf4.lnf4_attn_bwd_workspace(T, nh, nkv, D)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    lnf4.lnf4_attn_bwd(qd, kd, vd, dev_u16(o_in), dev_f32(lse_in), dod, T, nh, nkv, D, S, dq, dk, dv, ws, wsb)
     sync()
     return (bf16_f64(host_u16(o)), host_f32(lse).reshape(nh, T), bf16_f64(host_u16(dq)), bf16_f64(host_u16(dk)),
             bf16_f64(host_u16(dv)))
