@@ -86,30 +86,46 @@ __device__ __forceinline__ floatx16 zero16() {
   return z;
 }
 
-// rows [r0, r0+64) of a [.., ld] bf16 matrix, columns [c0, c0+D), into LDS row-major
-template <int D, int STRIDE, int NT>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t r0, int64_t ld, int64_t c0) {
-  for (int idx = threadIdx.x; idx < 64 * (D / 8); idx += NT) {
-    const int r = idx / (D / 8), c = idx - r * (D / 8);
-    *(u32x4*)&dst[r * STRIDE + 8 * c] = *(const u32x4*)(src + (r0 + r) * ld + c0 + 8 * c);
-  }
-}
+// A 64 x D bf16 block held in registers between its global load and its LDS writes, so
+// that the next block's loads are in flight while the current block computes.  Thread
+// items are row pairs (2rp, 2rp + 1) x 16-byte chunk c, which serve both the row-major
+// and the transposed LDS copy.
+template <int D, int NT>
+struct Staged {
+  static constexpr int ITEMS = 32 * (D / 8) / NT;
+  u32x4 a[ITEMS][2];
 
-// the same 64 x D block transposed: dst[d][r], two rows per 4-byte LDS write
-template <int D, int STRIDE, int NT>
-__device__ __forceinline__ void stage_rows_t(uint16_t* dst, const uint16_t* src, int64_t r0, int64_t ld, int64_t c0) {
-  for (int idx = threadIdx.x; idx < 32 * (D / 8); idx += NT) {
-    const int rp = idx / (D / 8), c = idx - rp * (D / 8);
-    const u32x4 a = *(const u32x4*)(src + (r0 + 2 * rp) * ld + c0 + 8 * c);
-    const u32x4 b = *(const u32x4*)(src + (r0 + 2 * rp + 1) * ld + c0 + 8 * c);
+  __device__ __forceinline__ void load(const uint16_t* src, int64_t r0, int64_t ld, int64_t c0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t va = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      const uint32_t vb = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      *(uint32_t*)&dst[(8 * c + e) * STRIDE + 2 * rp] = va | (vb << 16);
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = threadIdx.x + it * NT, rp = idx / (D / 8), c = idx - rp * (D / 8);
+      a[it][0] = *(const u32x4*)(src + (r0 + 2 * rp) * ld + c0 + 8 * c);
+      a[it][1] = *(const u32x4*)(src + (r0 + 2 * rp + 1) * ld + c0 + 8 * c);
     }
   }
-}
+  template <int STRIDE>
+  __device__ __forceinline__ void rows(uint16_t* dst) const {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = threadIdx.x + it * NT, rp = idx / (D / 8), c = idx - rp * (D / 8);
+      *(u32x4*)&dst[(2 * rp) * STRIDE + 8 * c] = a[it][0];
+      *(u32x4*)&dst[(2 * rp + 1) * STRIDE + 8 * c] = a[it][1];
+    }
+  }
+  template <int STRIDE>
+  __device__ __forceinline__ void transposed(uint16_t* dst) const {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = threadIdx.x + it * NT, rp = idx / (D / 8), c = idx - rp * (D / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t va = (a[it][0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const uint32_t vb = (a[it][1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        *(uint32_t*)&dst[(8 * c + e) * STRIDE + 2 * rp] = va | (vb << 16);
+      }
+    }
+  }
+};
 
 // accumulator rows d = 32dt + 8j + 4h + 0..3 of column `col` -> out[col][d], scaled, bf16
 template <int D>
@@ -157,11 +173,18 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fwd(const uint16_t* __restrict
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = zero16();
   float m = -INFINITY, l = 0.0f;
 
+  Staged<D, NT> pk, pv;
+  pk.load(k, t0, ldk, (int64_t)hk * D);
+  pv.load(v, t0, ldk, (int64_t)hk * D);
   for (int kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();  // the previous block's LDS reads are done
-    stage_rows<D, KS, NT>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
-    stage_rows_t<D, VS, NT>(Vt, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    pk.template rows<KS>(Ks);
+    pv.template transposed<VS>(Vt);
     __syncthreads();
+    if (kb < kb_last) {  // the next block's loads fly while this one computes
+      pk.load(k, t0 + (int64_t)(kb + 1) * BK, ldk, (int64_t)hk * D);
+      pv.load(v, t0 + (int64_t)(kb + 1) * BK, ldk, (int64_t)hk * D);
+    }
     floatx16 st[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -266,12 +289,19 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(const uint16_t* __restr
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
 
+  Staged<D, NT> pk, pv;
+  pk.load(k, t0, ldk, (int64_t)hk * D);
+  pv.load(v, t0, ldk, (int64_t)hk * D);
   for (int kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();
-    stage_rows<D, KS, NT>(Ks, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
-    stage_rows<D, KS, NT>(Vs, v, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
-    stage_rows_t<D, TS, NT>(Kt, k, t0 + (int64_t)kb * BK, ldk, (int64_t)hk * D);
+    pk.template rows<KS>(Ks);
+    pk.template transposed<TS>(Kt);
+    pv.template rows<KS>(Vs);
     __syncthreads();
+    if (kb < kb_last) {
+      pk.load(k, t0 + (int64_t)(kb + 1) * BK, ldk, (int64_t)hk * D);
+      pv.load(v, t0 + (int64_t)(kb + 1) * BK, ldk, (int64_t)hk * D);
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       floatx16 st = zero16(), dp = zero16();
@@ -343,19 +373,30 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
     dva[dt] = zero16();
   }
 
+  Staged<D, NT> pq, po;
+  pq.load(q, t0 + (int64_t)qb_first * BQ, ldq, (int64_t)hq0 * D);
+  po.load(dO, t0 + (int64_t)qb_first * BQ, ldq, (int64_t)hq0 * D);
   for (int hq = hq0; hq < hq1; ++hq)
     for (int qb = qb_first; qb < nqb; ++qb) {
       __syncthreads();
       const int64_t r0 = t0 + (int64_t)qb * BQ;
-      stage_rows<D, QS, NT>(Qs, q, r0, ldq, (int64_t)hq * D);
-      stage_rows<D, QS, NT>(Os, dO, r0, ldq, (int64_t)hq * D);
-      stage_rows_t<D, TS, NT>(Qt, q, r0, ldq, (int64_t)hq * D);
-      stage_rows_t<D, TS, NT>(Ot, dO, r0, ldq, (int64_t)hq * D);
+      pq.template rows<QS>(Qs);
+      pq.template transposed<TS>(Qt);
+      po.template rows<QS>(Os);
+      po.template transposed<TS>(Ot);
       if (threadIdx.x < BQ) {
         lse_s[threadIdx.x] = lse[(int64_t)hq * T + r0 + threadIdx.x] * 1.44269504088896341f;
         dsum_s[threadIdx.x] = dsum[(int64_t)hq * T + r0 + threadIdx.x];
       }
       __syncthreads();
+      {  // the next block (the next query block, or the next head's first) while this computes
+        const bool last_qb = qb + 1 == nqb;
+        if (!(last_qb && hq + 1 == hq1)) {
+          const int nq = last_qb ? qb_first : qb + 1, nhq = last_qb ? hq + 1 : hq;
+          pq.load(q, t0 + (int64_t)nq * BQ, ldq, (int64_t)nhq * D);
+          po.load(dO, t0 + (int64_t)nq * BQ, ldq, (int64_t)nhq * D);
+        }
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         floatx16 sa = zero16(), dp = zero16();
