@@ -2,12 +2,15 @@
 
     python -m lora_fine_tuning_nf4_amd.profsum trace   TRACE_DIR BENCH_JSON  "<command>"
     python -m lora_fine_tuning_nf4_amd.profsum traffic FETCH_DIR WRITE_DIR   "<command>"
+    python -m lora_fine_tuning_nf4_amd.profsum stats   TRACE_DIR -           "<command>"
 
 ``trace`` reads ``*_kernel_stats.csv`` and ``*_kernel_trace.csv`` of a ``--kernel-trace
 --stats -f csv`` run of bench.py and prints the per-kernel table plus the average
 duration of the dominant launch (the gate|up forward: grid = 896 workgroups x 256
 threads at the 8B shape) over the benchmark's timed launches, beside the benchmark's own
 HIP-event average from the same run.
+
+``stats`` prints the per-kernel table of a kernel-trace run (every kernel, by total time).
 
 ``traffic`` reads the ``*_counter_collection.csv`` of two ``--pmc FETCH_SIZE`` and
 ``--pmc WRITE_SIZE`` runs and scales each counter by what it reads for the benchmark's
@@ -114,11 +117,22 @@ def traffic(fetch_dir: str, write_dir: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def stats(trace_dir: str, _unused: str, command: str) -> str:
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    out = [f"# rocprofv3 kernel statistics: {command}", ""]
+    out.append(f"{'kernel':72s} {'calls':>6s} {'total_ms':>10s} {'avg_us':>10s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}")
+    for r in rows:
+        out.append(f"{_short(r['Name'], 72):72s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e6:10.2f} "
+                   f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                   f"{float(r['Percentage']):7.2f}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
-    if len(argv) != 5 or argv[1] not in ("trace", "traffic"):
+    fns = {"trace": trace, "traffic": traffic, "stats": stats}
+    if len(argv) != 5 or argv[1] not in fns:
         raise SystemExit(__doc__)
-    fn = trace if argv[1] == "trace" else traffic
-    sys.stdout.write(fn(argv[2], argv[3], argv[4]))
+    sys.stdout.write(fns[argv[1]](argv[2], argv[3], argv[4]))
 
 
 if __name__ == "__main__":
