@@ -51,15 +51,9 @@ __device__ __forceinline__ bf16x8 ld8x2(const uint16_t* p0, const uint16_t* p1) 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// accumulator values 8*hs .. 8*hs+7 as bf16: rows 16hs + 8(p>>2) + 4h + (p&3), p = 0..7
-__device__ __forceinline__ bf16x8 rows_bf16(const floatx16& c, int hs) {
-  const uint4 v = make_uint4(pack_bf16x2(c[8 * hs + 0], c[8 * hs + 1]), pack_bf16x2(c[8 * hs + 2], c[8 * hs + 3]),
-                             pack_bf16x2(c[8 * hs + 4], c[8 * hs + 5]), pack_bf16x2(c[8 * hs + 6], c[8 * hs + 7]));
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// the same values as a bf16 pair hi + lo (lo = bf16(x - hi)): about 16 significant bits
-// through two products, for the score gradients whose sums can cancel
+// accumulator values 8*hs .. 8*hs+7 (rows 16hs + 8(p>>2) + 4h + (p&3), p = 0..7) as a bf16
+// pair hi + lo (lo = bf16(x - hi)): about 16 significant bits through two products, for
+// the probabilities and score gradients fed back into MFMAs
 __device__ __forceinline__ void rows_bf16_split(const floatx16& c, int hs, bf16x8& hi, bf16x8& lo) {
   uint32_t wh[4], wl[4];
 #pragma unroll
@@ -72,7 +66,7 @@ __device__ __forceinline__ void rows_bf16_split(const floatx16& c, int hs, bf16x
   lo = __builtin_bit_cast(bf16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
 }
 
-// A operand of rows m of a transposed tile Xt[m][r], matching rows_bf16 for the 16 r of
+// A operand of rows m of a transposed tile Xt[m][r], matching rows_bf16_split for the 16 r of
 // K-step base .. base+15
 __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* Xt, int stride, int m, int base, int h) {
   const uint16_t* p = Xt + m * stride + base + 4 * h;

@@ -9,15 +9,16 @@
 //
 // Tiling.  A workgroup of 4 waves computes a BM x 256 tile (BM = 256 or 128), K-step 64.
 // Wave w owns the 64 columns [64w, 64w+64) and all BM rows: BM/32 x 2 MFMA blocks of
-// 32x32.  The activation tile (x or dy) is staged through LDS (double buffered, 16-byte
-// chunks XOR-swizzled by row).  The K order inside a 64-wide step is permuted so that a
+// 32x32.  The activation tile (x or dy) is staged through LDS (a ring of 3 or 4 stages
+// filled by direct-to-LDS loads, 16-byte chunks XOR-swizzled by row).  The K order inside a 64-wide step is permuted so that a
 // lane's B fragments for the four 16-wide MFMA steps are 32 consecutive K values: lane
 // (n, h) of a 32x32x16 MFMA supplies K = 32h + 8s .. 32h + 8s + 7 at step s.  Both
 // operands use the same permutation, so the sum is unchanged.
 //
 //  * Forward: K runs along a row of W, so each lane loads its own 16 bytes of codes
-//    (32 K values of one output column) straight from global memory and decodes them in
-//    registers: no LDS round trip for W, and every code is decoded once per workgroup.
+//    (32 K values of one output column) straight from global memory into registers and
+//    decodes them there: no LDS round trip for W, and every code is decoded once per
+//    workgroup.
 //  * dx: K runs across rows of W (W is N-contiguous here), so each thread loads an 8x8
 //    sub-block (8 rows x 4 bytes of codes), decodes it, and writes it transposed into LDS
 //    (the packed bf16 pairs are formed from two different rows, so the transpose costs
@@ -55,7 +56,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
 #else
 typedef const void* rsrc_t;
 __device__ inline rsrc_t make_rsrc(const void* p, int64_t) { return p; }
-#define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) ((void)0)
+#define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) ((void)(rsrc_), (void)(lds_), (void)(voff_), (void)(soff_))
 #endif
 
 // 16-byte-segment swizzle of a 128-byte code row (consecutive row pairs share it, so 16
@@ -161,44 +162,67 @@ constexpr int epi_bytes() { return (2 * BM + BN) * LNF4_EPI_RANK * 2; }
 // =====================================================================================
 // Forward
 // =====================================================================================
+// Buffer loads into registers (the per-lane weight words of the NF4 forward).  The host
+// pass gets inert stand-ins, as for the direct-to-LDS loads.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define LNF4_BUF_LD128(rsrc_, voff_, soff_) __builtin_amdgcn_raw_buffer_load_b128(rsrc_, voff_, soff_, 0)
+#define LNF4_BUF_LD32(rsrc_, voff_, soff_) __builtin_amdgcn_raw_buffer_load_b32(rsrc_, voff_, soff_, 0)
+#else
+#define LNF4_BUF_LD128(rsrc_, voff_, soff_) ((void)(rsrc_), (void)(voff_), (void)(soff_), u32x4{0u, 0u, 0u, 0u})
+#define LNF4_BUF_LD32(rsrc_, voff_, soff_) ((void)(rsrc_), (void)(voff_), (void)(soff_), 0u)
+#endif
+// wait until at most n vector-memory ops of this wave are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait")
+#define LNF4_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// ... and every LDS access of this wave completed (lgkmcnt 0)
+#define LNF4_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+
+// The weight words one lane needs for one K-block: 32 codes (its K half) of each of its two
+// columns, and the two columns' absmax of the block.
+struct CodeSet {
+  u32x4 w0, w1;
+  float a0, a1;
+};
+
+// NF4 forward.  A lane's B fragments need only its own 16 code bytes per column and
+// K-block, plus the block's absmax, so those come straight from global memory into
+// registers three K-blocks ahead; only the activation tile goes through LDS, in a 4-stage
+// ring.  Each 16-wide K step is split into two halves of MFMAs: the first half issues the
+// next step's code-table and activation reads (and a third of the loads for the block
+// three ahead), the second half the next fragments' fp32 products and bf16 packs.
 // NW = 4: each wave owns 64 columns x all BM rows (one wave per SIMD).  NW = 8: two waves
-// per column group, each on half of the rows (two waves per SIMD: more latency hiding,
-// each code decoded by both waves of its column group).
-template <int FMT, int BM, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
+// per column group, each on half of the rows (two waves per SIMD: more latency hiding for
+// grids of less than one tile per compute unit; each code is decoded by both waves).
+template <int BM, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
   constexpr int NT = 64 * NW;
   constexpr int WM = NW / 4;          // waves sharing a column group
   constexpr int MI = BM / 32 / WM;    // 32-row MFMA tiles per wave
-  constexpr int NM = 2 * MI;                       // MFMAs per 16-wide K step
-  // One ring stage: the activation tile [BM][64] bf16, then the weight tile of the 256
-  // columns (NF4: 32 code bytes + one fp32 absmax per column; bf16: 128 bytes per column).
+  constexpr int MH = MI / 2;          // MFMA rows of the first half-step
   constexpr int X_BYTES = BM * BK * 2;
-  constexpr int W_BYTES = FMT == 0 ? BN * 32 : BN * 128;
-  constexpr int A_BYTES = FMT == 0 ? BN * 4 : 0;
-  // Three distinct LDS objects, one per ring stage: the compiler then knows which
-  // direct-to-LDS loads each LDS read can alias and never waits for the loads still
-  // streaming into the other stages.  The LoRA staging (before the K loop) spreads over
-  // the three (hi, lo, adapter rows), so each stage holds at least a 64-rank slab.
-  constexpr int STAGE_RAW = X_BYTES + W_BYTES + A_BYTES;
+  // LoRA staging (before the K loop) spreads over three stages (hi, lo, adapter rows), so
+  // each stage holds at least a 64-rank slab
   constexpr int EPI_SLAB = BN * LNF4_EPI_RANK * 2;
-  constexpr int STAGE = STAGE_RAW > EPI_SLAB ? STAGE_RAW : EPI_SLAB;
-  static_assert(3 * STAGE + 64 <= 160 * 1024, "LDS budget");
+  constexpr int STAGE = X_BYTES > EPI_SLAB ? X_BYTES : EPI_SLAB;
+  static_assert(4 * STAGE + 2048 <= 160 * 1024, "LDS budget");
+  static_assert(MI % 2 == 0, "two half-steps");
+  // four distinct LDS objects, one per ring stage: the compiler then knows which
+  // direct-to-LDS loads each LDS read can alias and never waits for the loads still
+  // streaming into the other stages
   __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm3[STAGE];
   // byte-pair code table: entry b = (T[b >> 4], T[b & 15]), the fp32 levels of the two
-  // codes one byte holds (high nibble first).  The large alignment places it at LDS
-  // address 0, so an entry's address is just byte << 3: one byte-select shift per lookup.
+  // codes one byte holds (high nibble first)
   __shared__ __attribute__((aligned(2048))) float2 lut2[256];
-  __shared__ float lut1[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   if (tid < 256) lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);
-  if (tid < 16) lut1[tid] = c_gemm_table[tid];
-  const int wn = wave & 3;                 // column group
+  const int wn = wave & 3;                    // column group
   const int rbase = (wave >> 2) * (BM / WM);  // first tile row of this wave
 
   int tm, tn;
@@ -243,24 +267,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
     __syncthreads();
   }
 
-  // ---- global -> LDS operand streams (no register staging, two K-blocks ahead).
-  // Every direct load of a wave writes 64 consecutive 16-byte (or 4-byte) LDS slots, lane L
-  // to slot L, so each lane picks the global source that belongs in its slot.
-  //  * activation: load q of wave w fills tile rows (w*XQ+q)*8 .. +7; lane L holds row
-  //    (w*XQ+q)*8 + L/8, slot L%8 = logical chunk (L%8) ^ swz(row).  Rows >= M read row
-  //    M-1 (their outputs are discarded).
-  //  * NF4 codes: per column 32 bytes (K-block of 64 codes); wave w loads its 64 columns
-  //    in 2 loads, lane L -> column 64w + 32q + L/2, half L%2.  absmax: one dword load per
-  //    wave, lane L -> column 64w + L.
-  //  * bf16 weights: per column 128 bytes (8 chunks, swizzled like the activation rows);
-  //    wave w loads its 64 columns in 8 loads.
-  //  Columns >= out_f read column out_f-1 (outputs discarded).
+  // ---- activation stream (LDS).  Every direct load of a wave writes 64 consecutive
+  // 16-byte LDS slots, lane L to slot L: load q of wave w fills tile rows (w*XQ+q)*8 .. +7,
+  // lane L holds row (w*XQ+q)*8 + L/8, slot L%8 = logical chunk (L%8) ^ swz(row).  Rows >= M
+  // read row M-1 (their outputs are discarded).  A 32-bit per-lane offset plus the K-block
+  // advance as the wave-uniform offset: no per-lane address arithmetic in the K loop.
   constexpr int XQ = X_BYTES / 1024 / NW;
-  constexpr int WQ = (FMT == 0 ? 8 : 32) / NW;
-  constexpr int NLD = XQ + WQ + (FMT == 0 ? 1 : 0);  // vector-memory ops per wave per K-block
-  // Buffer loads: one resource per operand (scalar registers), a constant 32-bit per-lane
-  // byte offset per load, and the K-block advance as the wave-uniform offset, so no
-  // per-lane address arithmetic remains in the K loop.
+  static_assert(XQ % 2 == 0, "activation loads split over two steps");
+  constexpr int NLD = XQ + 4;  // vector-memory ops per wave per K-block
   const rsrc_t xrs = make_rsrc(args.x + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
   uint32_t xoff[XQ];
 #pragma unroll
@@ -269,64 +283,33 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
     const int lr = (m0 + row < M) ? row : (M - 1 - m0);
     xoff[q] = 2u * ((uint32_t)lr * (uint32_t)K + (uint32_t)(((lane & 7) ^ act_swz(row)) * 8));
   }
-  const rsrc_t wrs =
-      make_rsrc(P.w, FMT == 0 ? (int64_t)out_f * K / 2 : (int64_t)out_f * K * 2);
-  uint32_t woff[WQ];
-#pragma unroll
-  for (int q = 0; q < WQ; ++q) {
-    const int g = wave * WQ + q;  // 1 KB load index within the tile
-    if (FMT == 0) {
-      int n = nloc0 + 32 * g + (lane >> 1);
-      n = n < out_f ? n : out_f - 1;
-      woff[q] = (uint32_t)n * (uint32_t)(K / 2) + 16u * (lane & 1);
-    } else {
-      const int col = 8 * g + (lane >> 3);
-      int n = nloc0 + col;
-      n = n < out_f ? n : out_f - 1;
-      woff[q] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ act_swz(col)) * 16);
-    }
-  }
-  // absmax: wave w loads columns (256/NW)*w + lane (lanes past 256/NW stay idle)
-  constexpr int ACOL = 256 / NW;
-  const rsrc_t ars = make_rsrc(P.absmax, FMT == 0 ? (int64_t)out_f * (K / 64) * 4 : 0);
-  uint32_t aoff = 0;
-  if (FMT == 0) {
-    int n = nloc0 + ACOL * wave + (lane & (ACOL - 1));
-    n = n < out_f ? n : out_f - 1;
-    aoff = 4u * (uint32_t)n * (uint32_t)(K / 64);
-  }
+  // ---- weight words (registers): codes of columns nc0 / nc1, K half h; columns >= out_f
+  // read column out_f - 1 (their outputs are discarded)
+  const rsrc_t wrs = make_rsrc(P.w, (int64_t)out_f * K / 2);
+  const rsrc_t ars = make_rsrc(P.absmax, (int64_t)out_f * (K / 64) * 4);
+  const int g0 = nloc0 + nc0 < out_f ? nloc0 + nc0 : out_f - 1;
+  const int g1 = nloc0 + nc1 < out_f ? nloc0 + nc1 : out_f - 1;
+  const uint32_t woff0 = (uint32_t)g0 * (uint32_t)(K / 2) + 16u * h;
+  const uint32_t woff1 = (uint32_t)g1 * (uint32_t)(K / 2) + 16u * h;
+  const uint32_t aoff0 = 4u * (uint32_t)g0 * (uint32_t)(K / 64);
+  const uint32_t aoff1 = 4u * (uint32_t)g1 * (uint32_t)(K / 64);
 
-#define LNF4_ISSUE(kb_, SM_)                                                                    \
-  {                                                                                             \
-    uint8_t* sx_ = SM_;                                                                         \
-    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                              \
-        LNF4_BUF_LDS(xrs, sx_ + (wave_u * XQ + q) * 1024, 16, xoff[q], (kb_) * (BK * 2));       \
-    _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                              \
-        LNF4_BUF_LDS(wrs, sx_ + X_BYTES + (wave_u * WQ + q) * 1024, 16, woff[q],                \
-                     (kb_) * (FMT == 0 ? 32 : 128));                                            \
-    if (FMT == 0 && (NW == 4 || lane < ACOL))                                                   \
-      LNF4_BUF_LDS(ars, sx_ + X_BYTES + W_BYTES + wave_u * (4 * ACOL), 4, aoff, (kb_) * 4);     \
+#define LNF4_Q_XLOAD(kb_, SM_, part_)                                                        \
+  _Pragma("unroll") for (int q = (part_) * (XQ / 2); q < ((part_) + 1) * (XQ / 2); ++q)      \
+      LNF4_BUF_LDS(xrs, (SM_) + (wave_u * XQ + q) * 1024, 16, xoff[q], (kb_) * (BK * 2));
+  // Blocks past the last (the loop runs whole trips of 8 blocks) read absmax 0 through an
+  // out-of-range offset (the buffer load returns zero), so their decoded weights are zeros.
+#define LNF4_Q_WLOAD(kb_, CS_)                                                               \
+  {                                                                                          \
+    const int kw_ = (kb_) < nk ? (kb_) : nk - 1;                                             \
+    CS_.w0 = LNF4_BUF_LD128(wrs, woff0, kw_ * 32);                                           \
+    CS_.w1 = LNF4_BUF_LD128(wrs, woff1, kw_ * 32);                                           \
+    CS_.a0 = __uint_as_float(LNF4_BUF_LD32(ars, (kb_) < nk ? aoff0 : 0x7fff0000u, kw_ * 4));  \
+    CS_.a1 = __uint_as_float(LNF4_BUF_LD32(ars, (kb_) < nk ? aoff1 : 0x7fff0000u, kw_ * 4));  \
   }
-  // wait until at most n vector-memory ops of this wave are outstanding (gfx9 s_waitcnt
-  // encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait")
-#define LNF4_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-  // ... and every LDS access of this wave completed (lgkmcnt 0)
-#define LNF4_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
-
-  // NF4 B fragment (8 consecutive K of one column) for MFMA step s: table-read phase
-  // (nibble -> LDS table -> fp32 level) and finish phase (one fp32 product by the block's
-  // absmax, RNE pack to bf16), so the table reads go out early in a step and are consumed
-  // at its end.
-#ifdef LNF4_NIBBLE_LUT
-#define LNF4_LUT8(lv, cw_)                                                         \
-  {                                                                                \
-    const uint32_t c_ = (cw_);                                                     \
-    _Pragma("unroll") for (int b_ = 0; b_ < 4; ++b_) {                             \
-      lv[2 * b_] = lut1[(c_ >> (8 * b_ + 4)) & 15u];                               \
-      lv[2 * b_ + 1] = lut1[(c_ >> (8 * b_)) & 15u];                               \
-    }                                                                              \
-  }
-#else
+  // NF4 B fragment (8 consecutive K of one column): table-read phase (byte -> LDS table ->
+  // fp32 levels of its two codes) and finish phase (one fp32 product by the block's absmax,
+  // RNE pack to bf16), exactly the standalone decode
 #define LNF4_LUT8(lv, cw_)                                                         \
   {                                                                                \
     const uint32_t c_ = (cw_);                                                     \
@@ -336,20 +319,248 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
       lv[2 * b_ + 1] = p_.y;                                                       \
     }                                                                              \
   }
-#endif
 #define LNF4_FIN8(dst, lv, a_)                                                     \
   dst = as_bf16x8(pack_bf16x2(lv[0] * (a_), lv[1] * (a_)), pack_bf16x2(lv[2] * (a_), lv[3] * (a_)), \
                   pack_bf16x2(lv[4] * (a_), lv[5] * (a_)), pack_bf16x2(lv[6] * (a_), lv[7] * (a_)));
+#define LNF4_XS(SM_) ((const uint16_t*)(SM_))
+#define LNF4_AFRAG(SM_, i_, chunk_) (*(const bf16x8*)&LNF4_XS(SM_)[act_pos(rbase + 32 * (i_) + l32, (chunk_))])
 
-  // per-lane operand reads from a stage
-#define LNF4_READ_CODES(SM_, c0, c1, s0, s1)                                     \
-  {                                                                              \
-    c0 = *(const u32x4*)((SM_) + X_BYTES + nc0 * 32 + 16 * h);                   \
-    c1 = *(const u32x4*)((SM_) + X_BYTES + nc1 * 32 + 16 * h);                   \
-    s0 = ((const float*)((SM_) + X_BYTES + W_BYTES))[nc0];                       \
-    s1 = ((const float*)((SM_) + X_BYTES + W_BYTES))[nc1];                       \
+  // prologue: blocks 0, 1, 2 in flight (activations, then weight words, block by block);
+  // block 0 visible
+  CodeSet k0, k1, k2, k3;
+  LNF4_Q_XLOAD(0, sm0, 0);
+  LNF4_Q_XLOAD(0, sm0, 1);
+  LNF4_Q_WLOAD(0, k0);
+  LNF4_Q_XLOAD((nk > 1 ? 1 : nk - 1), sm1, 0);
+  LNF4_Q_XLOAD((nk > 1 ? 1 : nk - 1), sm1, 1);
+  LNF4_Q_WLOAD(1, k1);
+  LNF4_Q_XLOAD((nk > 2 ? 2 : nk - 1), sm2, 0);
+  LNF4_Q_XLOAD((nk > 2 ? 2 : nk - 1), sm2, 1);
+  LNF4_Q_WLOAD(2, k2);
+  LNF4_WAIT_VM(2 * NLD);
+  __syncthreads();
+
+  bf16x8 ac[MI], an_[MI];
+  bf16x8 bc0, bc1, bn0, bn1;
+  {
+    float l0[8], l1[8];
+    LNF4_LUT8(l0, k0.w0[0]);
+    LNF4_LUT8(l1, k0.w1[0]);
+    LNF4_FIN8(bc0, l0, k0.a0);
+    LNF4_FIN8(bc1, l1, k0.a1);
   }
-  // bf16 weights: chunk 4h+s of a column
+#pragma unroll
+  for (int i = 0; i < MI; ++i) ac[i] = LNF4_AFRAG(sm0, i, 4 * h);
+
+  // One K-block KB: stage SC holds it, SN the next one, SP receives the block three ahead;
+  // CC / CN are the weight words of this block / the next, CL receives those of the block
+  // three ahead.
+#define LNF4_Q_BLOCK(KB, SC, SN, SP, CC, CN, CL)                                               \
+  {                                                                                            \
+    const int kl_ = (KB) + 3 < nk ? (KB) + 3 : nk - 1; /* past the end: re-read the last */    \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 3) {                                                                            \
+        /* block KB+1 in LDS for every wave, and every wave done with stage SC before */      \
+        /* block KB+4 is issued into it (a bare s_barrier: a fenced __syncthreads would */     \
+        /* also wait for the loads of blocks KB+2 and KB+3, which are meant to stay in */     \
+        /* flight) */                                                                          \
+        LNF4_WAIT_VM_LGKM0(2 * NLD);                                                           \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
+      float l0[8], l1[8];                                                                      \
+      LNF4_LUT8(l0, (s < 3 ? CC.w0[s + 1 < 4 ? s + 1 : 0] : CN.w0[0]));                        \
+      LNF4_LUT8(l1, (s < 3 ? CC.w1[s + 1 < 4 ? s + 1 : 0] : CN.w1[0]));                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                  \
+          (s < 3) ? LNF4_AFRAG(SC, i, 4 * h + s + 1) : LNF4_AFRAG(SN, i, 4 * h);               \
+      if (s < 2) { LNF4_Q_XLOAD(kl_, SP, s); }                                                 \
+      if (s == 2) LNF4_Q_WLOAD((KB) + 3, CL);                                                  \
+      _Pragma("unroll") for (int i = 0; i < MH; ++i) {                                         \
+        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
+        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+      }                                                                                        \
+      /* first half: table addresses and reads, then activation reads and loads */            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
+      _Pragma("unroll") for (int g = 2; g < 2 * MH; ++g) {                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, (MI + 2 * MH - 3) / (2 * MH - 2), 0);      \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      }                                                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      _Pragma("unroll") for (int i = MH; i < MI; ++i) {                                        \
+        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
+        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+      }                                                                                        \
+      LNF4_FIN8(bn0, l0, (s < 3 ? CC.a0 : CN.a0));                                             \
+      LNF4_FIN8(bn1, l1, (s < 3 ? CC.a1 : CN.a1));                                             \
+      /* second half: products and packs of the next fragments between the MFMAs */           \
+      _Pragma("unroll") for (int g = 0; g < 2 * (MI - MH); ++g) {                              \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x002, (24 + 2 * (MI - MH) - 1) / (2 * (MI - MH)), 0); \
+      }                                                                                        \
+      /* with one wave per SIMD, the fragments this step's MFMAs read stay live to its end, */ \
+      /* so the next step's fragments go to other registers: overwriting a register that an */ \
+      /* MFMA in flight still reads stalls the wave (two waves per SIMD have no registers */   \
+      /* to spare for it) */                                                                   \
+      if (NW == 4) {                                                                           \
+        asm volatile("" ::"v"(bc0), "v"(bc1));                                                 \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) asm volatile("" ::"v"(ac[i]));          \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) ac[i] = an_[i];                           \
+      bc0 = bn0;                                                                               \
+      bc1 = bn1;                                                                               \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    /* the next block's first B fragments exist before the block ends: otherwise their */     \
+    /* decode sinks into the next block and stalls its first MFMAs */                         \
+    asm volatile("" ::"v"(bc0), "v"(bc1));                                                     \
+  }
+
+  // Whole trips over two turns of the 4-stage ring with one exit test per trip.  (With an
+  // exit after every block, the compiler's wait-count merging at the loop exits inserted a
+  // near-full drain of the loads in flight once per trip.)
+  const int nk8 = (nk + 7) & ~7;
+  for (int kb = 0; kb < nk8; kb += 8) {
+    LNF4_Q_BLOCK(kb + 0, sm0, sm1, sm3, k0, k1, k3);
+    LNF4_Q_BLOCK(kb + 1, sm1, sm2, sm0, k1, k2, k0);
+    LNF4_Q_BLOCK(kb + 2, sm2, sm3, sm1, k2, k3, k1);
+    LNF4_Q_BLOCK(kb + 3, sm3, sm0, sm2, k3, k0, k2);
+    LNF4_Q_BLOCK(kb + 4, sm0, sm1, sm3, k0, k1, k3);
+    LNF4_Q_BLOCK(kb + 5, sm1, sm2, sm0, k1, k2, k0);
+    LNF4_Q_BLOCK(kb + 6, sm2, sm3, sm1, k2, k3, k1);
+    LNF4_Q_BLOCK(kb + 7, sm3, sm0, sm2, k3, k0, k2);
+  }
+#undef LNF4_Q_BLOCK
+#undef LNF4_Q_XLOAD
+#undef LNF4_Q_WLOAD
+#undef LNF4_LUT8
+#undef LNF4_FIN8
+#undef LNF4_XS
+#undef LNF4_AFRAG
+
+  // ---- store bf16
+  const int n0g = nloc0 + nc0, n1g = nloc0 + nc1;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    __builtin_amdgcn_sched_barrier(0);  // bound the accumulator reads that are live at once
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = rbase + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      const int gm = m0 + row;
+      if (gm >= M) continue;
+      const float v0 = acc[i][0][q], v1 = acc[i][1][q];
+      uint16_t* yr = P.y + (size_t)gm * out_f;
+      if (n0g < out_f) yr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
+      if (n1g < out_f) yr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
+    }
+  }
+}
+
+// bf16 weights: the weight tile goes through LDS beside the activation tile (128 bytes per
+// column and K-block, 16-byte chunks swizzled like the activation rows), in a 3-stage ring;
+// its 4x larger weight tiles only fit LDS with 128-row tiles.  Wave w owns the 64 columns
+// [64w, 64w+64) and all BM rows.
+template <int BM>
+__global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16(const FwdArgs args) {
+  constexpr int MI = BM / 32;
+  constexpr int NM = 2 * MI;                       // MFMAs per 16-wide K step
+  constexpr int X_BYTES = BM * BK * 2;
+  constexpr int W_BYTES = BN * 128;
+  constexpr int STAGE_RAW = X_BYTES + W_BYTES;
+  constexpr int EPI_SLAB = BN * LNF4_EPI_RANK * 2;
+  constexpr int STAGE = STAGE_RAW > EPI_SLAB ? STAGE_RAW : EPI_SLAB;
+  static_assert(3 * STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  int tm, tn;
+  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  tn += args.tn_base;
+  int pi = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxGroup; ++q)
+    if (q < args.n_proj && tn >= args.p[q].tile_n0) pi = q;
+  const FwdProj P = select_fwd(args, pi);
+
+  const int M = args.M, K = args.K, out_f = P.out_f;
+  const int m0 = tm * BM;
+  const int nloc0 = (tn - P.tile_n0) * BN;
+  const int nk = K / BK;
+  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;
+
+  floatx16 acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  if (P.u != nullptr && P.r > 0) {
+    const int r = P.r, RP = (r + 15) & ~15;
+    uint16_t* Uh = (uint16_t*)sm0;
+    uint16_t* Ul = (uint16_t*)sm1;
+    uint16_t* V = (uint16_t*)sm2;
+    for (int idx = tid; idx < BM * RP; idx += NTHR) {
+      const int mm = idx / RP, kk = idx - mm * RP, gm = m0 + mm;
+      const float uv = (gm < M && kk < r) ? P.scale * P.u[(size_t)gm * r + kk] : 0.0f;
+      split_bf16(uv, Uh[idx], Ul[idx]);
+    }
+    for (int idx = tid; idx < BN * RP; idx += NTHR) {
+      const int nn = idx / RP, kk = idx - nn * RP, n = nloc0 + nn;
+      V[idx] = (n < out_f && kk < r) ? P.B[(size_t)n * r + kk] : (uint16_t)0;
+    }
+    __syncthreads();
+    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+    __syncthreads();
+  }
+
+  // global -> LDS streams, two K-blocks ahead (lane L of a direct load writes slot L):
+  //  * activation: load q of wave w fills tile rows (w*XQ+q)*8 .. +7, as in the NF4 kernel;
+  //  * weights: per column 128 bytes (8 chunks, swizzled like the activation rows); wave w
+  //    loads columns 8g .. 8g+7 for g = w*WQ .. w*WQ+WQ-1, lane L -> column 8g + L/8.
+  //  Columns >= out_f read column out_f-1 (outputs discarded).
+  constexpr int XQ = X_BYTES / 1024 / 4;
+  constexpr int WQ = 32 / 4;
+  constexpr int NLD = XQ + WQ;
+  const rsrc_t xrs = make_rsrc(args.x + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+  uint32_t xoff[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int row = (wave * XQ + q) * 8 + (lane >> 3);
+    const int lr = (m0 + row < M) ? row : (M - 1 - m0);
+    xoff[q] = 2u * ((uint32_t)lr * (uint32_t)K + (uint32_t)(((lane & 7) ^ act_swz(row)) * 8));
+  }
+  const rsrc_t wrs = make_rsrc(P.w, (int64_t)out_f * K * 2);
+  uint32_t woff[WQ];
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int col = 8 * (wave * WQ + q) + (lane >> 3);
+    int n = nloc0 + col;
+    n = n < out_f ? n : out_f - 1;
+    woff[q] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ act_swz(col)) * 16);
+  }
+
+#define LNF4_ISSUE(kb_, SM_)                                                                    \
+  {                                                                                             \
+    uint8_t* sx_ = SM_;                                                                         \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                              \
+        LNF4_BUF_LDS(xrs, sx_ + (wave_u * XQ + q) * 1024, 16, xoff[q], (kb_) * (BK * 2));       \
+    _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                              \
+        LNF4_BUF_LDS(wrs, sx_ + X_BYTES + (wave_u * WQ + q) * 1024, 16, woff[q], (kb_) * 128);  \
+  }
+  // chunk 4h+s of a column
 #define LNF4_READ_BW(SM_, s_, col_) \
   (*(const bf16x8*)((SM_) + X_BYTES + (col_) * 128 + (((4 * h + (s_)) ^ act_swz(col_)) * 16)))
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))
@@ -362,29 +573,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
 
   bf16x8 ac[MI], an_[MI];
   bf16x8 bc0, bc1, bn0, bn1;
-  u32x4 cw0, cw1;      // code words of the current block (NF4)
-  float sa0 = 0.f, sa1 = 0.f;
-  if (FMT == 0) {
-    LNF4_READ_CODES(sm0, cw0, cw1, sa0, sa1);
-    float l0[8], l1[8];
-    LNF4_LUT8(l0, cw0[0]);
-    LNF4_LUT8(l1, cw1[0]);
-    LNF4_FIN8(bc0, l0, sa0);
-    LNF4_FIN8(bc1, l1, sa1);
-  } else {
-    bc0 = LNF4_READ_BW(sm0, 0, nc0);
-    bc1 = LNF4_READ_BW(sm0, 0, nc1);
-  }
+  bc0 = LNF4_READ_BW(sm0, 0, nc0);
+  bc1 = LNF4_READ_BW(sm0, 0, nc1);
 #pragma unroll
-  for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(rbase + 32 * i + l32, 4 * h)];
+  for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(32 * i + l32, 4 * h)];
 
   // One K-block on stage SC; SN holds the next block, SP receives the block two ahead.
   // The loop is unrolled three times with the stages rotated, so every LDS access names
   // its stage statically.
 #define LNF4_FWD_BLOCK(SC, SN, SP)                                                             \
   {                                                                                            \
-    u32x4 nw0, nw1;                                                                            \
-    float ns0 = 0.f, ns1 = 0.f;                                                                \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
       __builtin_amdgcn_sched_barrier(0);                                                       \
       if (s == 1) {                                                                            \
@@ -396,82 +594,36 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
         __builtin_amdgcn_sched_barrier(0);                                                     \
       }                                                                                        \
       if (s == 3) {                                                                            \
-        /* block kb+1 (issued one block ago) must be in LDS for every wave, and every wave */  \
-        /* must be done with stage SC before block kb+3 is issued into it */                   \
-        /* (a bare s_barrier: a fenced __syncthreads would also wait for the loads of */     \
-        /* block kb+2, which are meant to stay in flight) */                                   \
+        /* block kb+1 (issued one block ago) in LDS for every wave, and every wave done */     \
+        /* with stage SC before block kb+3 is issued into it */                                \
         LNF4_WAIT_VM_LGKM0(NLD);                                                               \
         __builtin_amdgcn_s_barrier();                                                          \
         __builtin_amdgcn_sched_barrier(0);                                                     \
       }                                                                                        \
-      float l0[8], l1[8];                                                                      \
-      if (FMT == 0) {                                                                          \
-        if (s < 3) {                                                                           \
-          LNF4_LUT8(l0, cw0[s + 1 < 4 ? s + 1 : 0]);                                           \
-          LNF4_LUT8(l1, cw1[s + 1 < 4 ? s + 1 : 0]);                                           \
-        } else {                                                                               \
-          LNF4_READ_CODES(SN, nw0, nw1, ns0, ns1);                                             \
-          LNF4_LUT8(l0, nw0[0]);                                                               \
-          LNF4_LUT8(l1, nw1[0]);                                                               \
-        }                                                                                      \
-      } else {                                                                                 \
-        if (s < 3) {                                                                           \
-          bn0 = LNF4_READ_BW(SC, s + 1, nc0);                                                  \
-          bn1 = LNF4_READ_BW(SC, s + 1, nc1);                                                  \
-        } else {                                                                               \
-          bn0 = LNF4_READ_BW(SN, 0, nc0);                                                      \
-          bn1 = LNF4_READ_BW(SN, 0, nc1);                                                      \
-        }                                                                                      \
-      }                                                                                        \
       if (s < 3) {                                                                             \
+        bn0 = LNF4_READ_BW(SC, s + 1, nc0);                                                    \
+        bn1 = LNF4_READ_BW(SC, s + 1, nc1);                                                    \
         _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
-            *(const bf16x8*)&LNF4_XS(SC)[act_pos(rbase + 32 * i + l32, 4 * h + s + 1)];        \
+            *(const bf16x8*)&LNF4_XS(SC)[act_pos(32 * i + l32, 4 * h + s + 1)];                \
       } else {                                                                                 \
+        bn0 = LNF4_READ_BW(SN, 0, nc0);                                                        \
+        bn1 = LNF4_READ_BW(SN, 0, nc1);                                                        \
         _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
-            *(const bf16x8*)&LNF4_XS(SN)[act_pos(rbase + 32 * i + l32, 4 * h)];                \
+            *(const bf16x8*)&LNF4_XS(SN)[act_pos(32 * i + l32, 4 * h)];                        \
       }                                                                                        \
       _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
         acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
         acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
       }                                                                                        \
-      if (FMT == 0) {                                                                          \
-        LNF4_FIN8(bn0, l0, (s < 3 ? sa0 : ns0));                                               \
-        LNF4_FIN8(bn1, l1, (s < 3 ? sa1 : ns1));                                               \
-        /* issue order: table addresses and reads first, A-fragment reads, then the */         \
-        /* products and packs, spread between the MFMAs */                                     \
-        _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                        \
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                   \
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                                   \
-        }                                                                                      \
-        _Pragma("unroll") for (int g = 4; g < NM - NM / 4; ++g) {                              \
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
-          __builtin_amdgcn_sched_group_barrier(0x100, (MI + (NM - NM / 4 - 4) - 1) / (NM - NM / 4 - 4), 0); \
-        }                                                                                      \
-        _Pragma("unroll") for (int g = NM - NM / 4; g < NM; ++g) {                             \
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
-          __builtin_amdgcn_sched_group_barrier(0x002, (24 + NM / 4 - 1) / (NM / 4), 0);        \
-        }                                                                                      \
-      } else {                                                                                 \
-        _Pragma("unroll") for (int g = 0; g < NM; ++g) {                                       \
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   \
-        }                                                                                      \
+      _Pragma("unroll") for (int g = 0; g < NM; ++g) {                                         \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
       }                                                                                        \
       _Pragma("unroll") for (int i = 0; i < MI; ++i) ac[i] = an_[i];                           \
       bc0 = bn0;                                                                               \
       bc1 = bn1;                                                                               \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                         \
-    /* the next block's first B fragments exist before the loop's exit test: otherwise */     \
-    /* their decode sinks past it and stalls the next block's first MFMAs */                  \
-    asm volatile("" ::"v"(bc0), "v"(bc1));                                                     \
-    if (FMT == 0) {                                                                            \
-      cw0 = nw0;                                                                               \
-      cw1 = nw1;                                                                               \
-      sa0 = ns0;                                                                               \
-      sa1 = ns1;                                                                               \
-    }                                                                                          \
   }
 
   // unrolled twice over (six blocks per trip): the compiler drops the per-stage
@@ -491,23 +643,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(const FwdArgs args) {
     if (++kb == nk) break;
   }
 #undef LNF4_FWD_BLOCK
-#undef LNF4_READ_CODES
 #undef LNF4_READ_BW
 #undef LNF4_XS
 #undef LNF4_ISSUE
-#undef LNF4_WAIT_VM
-#undef LNF4_WAIT_VM_LGKM0
-#undef LNF4_LUT8
-#undef LNF4_FIN8
 
   // ---- store bf16
   const int n0g = nloc0 + nc0, n1g = nloc0 + nc1;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    __builtin_amdgcn_sched_barrier(0);  // bound the accumulator reads that are live at once
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int row = rbase + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      const int row = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
       const int gm = m0 + row;
       if (gm >= M) continue;
       const float v0 = acc[i][0][q], v1 = acc[i][1][q];
@@ -683,7 +830,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx(const DxArgs args) {
   const int nkb = args.total_kb;
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
-    LNF4_DX_LOAD(kb + 1 < nkb ? kb + 1 : kb);  // unconditional prefetch (see k_fwd)
+    LNF4_DX_LOAD(kb + 1 < nkb ? kb + 1 : kb);  // unconditional prefetch (the tail re-reads)
     const uint16_t* at = as0 + cur * BM * BK;
     const uint16_t* wt = ws0 + cur * BN * BK;
 #pragma unroll
@@ -764,7 +911,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
   // byte-pair code table in transposed order: a byte of a transposed read holds rows 2b
-  // (low nibble) and 2b+1 (high nibble) of one column; at LDS address 0 (see k_fwd)
+  // (low nibble) and 2b+1 (high nibble) of one column; the large alignment places it at LDS
+  // address 0, so an entry's address is just byte << 3
   __shared__ __attribute__((aligned(2048))) float2 lut2[256];
   __shared__ float lut1[16];
 
@@ -843,7 +991,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   pi_ = __builtin_amdgcn_readfirstlane(pi_);                                     \
   const DxProj& P_ = args.p[pi_];
 
-  // per-lane constant parts of the buffer-load offsets (see k_fwd); the projection and the
+  // per-lane constant parts of the buffer-load offsets (as in the forward kernels); the projection and the
   // K offset go into each block's resources, whose ranges end at the projection's last
   // row, so rows past out_f load as zeros: zero absmax, hence zero weights
   uint32_t dyr2[XQ], dyc[XQ];
@@ -877,8 +1025,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
         LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * 2 + q) * 1024, 16, cwoff[q], 0);          \
     LNF4_BUF_LDS(ars_, (SM_) + X_BYTES + W_BYTES + wave_u * 256, 4, caoff, 0);                    \
   }
-#define LNF4_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-#define LNF4_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
 
   typedef int v2i_t __attribute__((ext_vector_type(2)));
   // transposed code reads of one stage: cw[s] = 8 codes (rows 32h+8s .. +7) of the column
@@ -956,7 +1102,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     u32x4 nw0, nw1;                                                                            \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
       __builtin_amdgcn_sched_barrier(0);                                                       \
-      if (s == 1) { /* after step 0's LDS reads, as in k_fwd */                                \
+      if (s == 1) { /* after step 0's LDS reads, as in k_fwd_bf16 */                                \
         LNF4_DXQ_ISSUE((kb + 2 < nkb ? kb + 2 : nkb - 1), SP);                                 \
         __builtin_amdgcn_sched_barrier(0);                                                     \
       }                                                                                        \
@@ -1007,7 +1153,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       bc1 = bn1;                                                                               \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                         \
-    asm volatile("" ::"v"(bc0), "v"(bc1)); /* decoded before the exit test, as in k_fwd */    \
+    asm volatile("" ::"v"(bc0), "v"(bc1)); /* decoded before the exit test */            \
     cw0 = nw0;                                                                                 \
     cw1 = nw1;                                                                                 \
   }
@@ -1029,8 +1175,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #undef LNF4_DXQ_BLOCK
 #undef LNF4_DXQ_PROJ
 #undef LNF4_DXQ_ISSUE
-#undef LNF4_WAIT_VM
-#undef LNF4_WAIT_VM_LGKM0
 #undef LNF4_TR4
 #undef LNF4_DXQ_CODES
 #undef LNF4_DXQ_SCALES
@@ -1089,7 +1233,7 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   if (fmt != 0) {
     // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
     a.n_tiles_m = (a.M + 127) / 128;
-    hipLaunchKernelGGL((k_fwd<1, 128, 4>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((k_fwd_bf16<128>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
     return hipGetLastError();
   }
   const int cus = n_cus();
@@ -1098,17 +1242,17 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   const int t256 = tm256 * tn_all;
   if (pick_bm(a.M, tn_all) == 128) {
     a.n_tiles_m = (a.M + 127) / 128;
-    hipLaunchKernelGGL((k_fwd<0, 128, 4>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((k_fwd_nf4<128, 4>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
     return hipGetLastError();
   }
   if (t256 <= cus) {
     // one partial wave of tiles: two waves per SIMD hide more latency per tile
     a.n_tiles_m = tm256;
-    hipLaunchKernelGGL((k_fwd<0, 256, 8>), dim3(t256), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((k_fwd_nf4<256, 8>), dim3(t256), dim3(512), 0, s, a);
     return hipGetLastError();
   }
   a.n_tiles_m = tm256;
-  hipLaunchKernelGGL((k_fwd<0, 256, 4>), dim3(t256), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(t256), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 
