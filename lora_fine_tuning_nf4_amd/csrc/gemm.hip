@@ -906,10 +906,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   constexpr int SLAB_U = BM * LNF4_EPI_RANK * 2, SLAB_V = BN * LNF4_EPI_RANK * 2;
   constexpr int SLAB = SLAB_U > SLAB_V ? SLAB_U : SLAB_V;
   constexpr int STAGE = STAGE_RAW > SLAB ? STAGE_RAW : SLAB;
-  static_assert(3 * STAGE + 2048 <= 160 * 1024, "LDS budget");
+  // a 4-stage ring (blocks issued three ahead) where it fits LDS, else 3 stages
+  constexpr int NSTG = 4 * STAGE + 2048 + 64 <= 160 * 1024 ? 4 : 3;
+  static_assert(3 * STAGE + 2048 + 64 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm3[NSTG == 4 ? STAGE : 16];
   // byte-pair code table in transposed order: a byte of a transposed read holds rows 2b
   // (low nibble) and 2b+1 (high nibble) of one column; the large alignment places it at LDS
   // address 0, so an entry's address is just byte << 3
@@ -980,6 +983,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   //  Rows past the projection's out_f and columns past N read clamped addresses; their
   //  weights are zeroed by the decode (rows) or their outputs dropped (columns).
   constexpr int XQ = X_BYTES / 1024 / 4;
+  static_assert(XQ % 2 == 0, "dy loads split over two steps");
   constexpr int NLD = XQ + 3;
   const int halfN = N / 2, nblk = N / 64;
   const int cbyte_max = halfN - 16;
@@ -1010,20 +1014,35 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   }
   const uint32_t caoff = 4u * ((uint32_t)lane * (uint32_t)nblk + (uint32_t)ablk);
 
-#define LNF4_DXQ_ISSUE(kb_, SM_)                                                                 \
-  {                                                                                              \
+  // The loads of one K-block go out in three parts, one per step of the block before the
+  // ring wraps: dy rows of the first half, of the second half, then codes and absmax.
+  // Blocks past the last (the loop runs whole trips) belong to no projection's row range:
+  // their resources are empty and every load returns zeros (zero dy, zero absmax).
+#define LNF4_DXQ_RSRC(kb_)                                                                       \
     LNF4_DXQ_PROJ(kb_, Pi_)                                                                      \
     const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
-    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, ((int64_t)M * Kp_ - k0_) * 2);    \
-    const rsrc_t wrs_ =                                                          \
+    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, ((int64_t)M * Kp_ - k0_) * 2);                  \
+    const rsrc_t wrs_ =                                                                          \
         make_rsrc((const uint8_t*)Pi_.w + (size_t)k0_ * halfN, (int64_t)(Kp_ - k0_) * halfN);    \
-    const rsrc_t ars_ =                                                          \
-        make_rsrc(Pi_.absmax + (size_t)k0_ * nblk, (int64_t)(Kp_ - k0_) * nblk * 4);             \
-    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                               \
-        LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + q) * 1024, 16, dyr2[q] * (uint32_t)Kp_ + dyc[q], 0); \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                                \
-        LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * 2 + q) * 1024, 16, cwoff[q], 0);          \
-    LNF4_BUF_LDS(ars_, (SM_) + X_BYTES + W_BYTES + wave_u * 256, 4, caoff, 0);                    \
+    const rsrc_t ars_ =                                                                          \
+        make_rsrc(Pi_.absmax + (size_t)k0_ * nblk, (int64_t)(Kp_ - k0_) * nblk * 4);
+#define LNF4_DXQ_ISSUE_PART(SM_, part_)                                                          \
+  {                                                                                              \
+    if ((part_) < 2) {                                                                           \
+      _Pragma("unroll") for (int q = (part_) * (XQ / 2); q < ((part_) + 1) * (XQ / 2); ++q)      \
+          LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + q) * 1024, 16, dyr2[q] * (uint32_t)Kp_ + dyc[q], 0); \
+    } else {                                                                                     \
+      _Pragma("unroll") for (int q = 0; q < 2; ++q)                                              \
+          LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * 2 + q) * 1024, 16, cwoff[q], 0);        \
+      LNF4_BUF_LDS(ars_, (SM_) + X_BYTES + W_BYTES + wave_u * 256, 4, caoff, 0);                  \
+    }                                                                                            \
+  }
+#define LNF4_DXQ_ISSUE(kb_, SM_)                                                                 \
+  {                                                                                              \
+    LNF4_DXQ_RSRC(kb_)                                                                           \
+    LNF4_DXQ_ISSUE_PART(SM_, 0)                                                                  \
+    LNF4_DXQ_ISSUE_PART(SM_, 1)                                                                  \
+    LNF4_DXQ_ISSUE_PART(SM_, 2)                                                                  \
   }
 
   typedef int v2i_t __attribute__((ext_vector_type(2)));
@@ -1076,10 +1095,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
                   pack_bf16x2(lv[4] * a_[4], lv[5] * a_[5]), pack_bf16x2(lv[6] * a_[6], lv[7] * a_[7]));
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))
 
-  // prologue: blocks 0 and 1 in flight; block 0 visible
+  // prologue: blocks 0 .. NSTG-2 in flight; block 0 visible
   LNF4_DXQ_ISSUE(0, sm0);
-  LNF4_DXQ_ISSUE((nkb > 1 ? 1 : 0), sm1);
-  LNF4_WAIT_VM(NLD);
+  LNF4_DXQ_ISSUE(1, sm1);
+  if (NSTG == 4) LNF4_DXQ_ISSUE(2, sm2);
+  LNF4_WAIT_VM((NSTG - 2) * NLD);
   __syncthreads();
 
   bf16x8 ac[MI], an_[MI];
@@ -1097,17 +1117,17 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #pragma unroll
   for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(32 * i + l32, 4 * h)];
 
-#define LNF4_DXQ_BLOCK(SC, SN, SP)                                                             \
+  // One K-block KB on stage SC; SN holds block KB+1, SP receives block KB+NSTG-1 (issued in
+  // parts over steps 0..2, each after the step's LDS reads).
+#define LNF4_DXQ_BLOCK(KB, SC, SN, SP)                                                         \
   {                                                                                            \
     u32x4 nw0, nw1;                                                                            \
+    LNF4_DXQ_RSRC((KB) + NSTG - 1)                                                             \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
       __builtin_amdgcn_sched_barrier(0);                                                       \
-      if (s == 1) { /* after step 0's LDS reads, as in k_fwd_bf16 */                                \
-        LNF4_DXQ_ISSUE((kb + 2 < nkb ? kb + 2 : nkb - 1), SP);                                 \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-      }                                                                                        \
       if (s == 3) {                                                                            \
-        LNF4_WAIT_VM_LGKM0(NLD);                                                               \
+        /* block KB+1 in LDS for every wave; every wave done with SC */                        \
+        LNF4_WAIT_VM_LGKM0((NSTG - 2) * NLD);                                                  \
         __builtin_amdgcn_s_barrier();                                                          \
         __builtin_amdgcn_sched_barrier(0);                                                     \
       }                                                                                        \
@@ -1129,6 +1149,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
         _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
             *(const bf16x8*)&LNF4_XS(SN)[act_pos(32 * i + l32, 4 * h)];                        \
       }                                                                                        \
+      if (s < 3) LNF4_DXQ_ISSUE_PART(SP, s);                                                   \
       _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
         acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
         acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
@@ -1143,6 +1164,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       _Pragma("unroll") for (int g = 4; g < NM - NM / 4; ++g) {                                \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
         __builtin_amdgcn_sched_group_barrier(0x100, (MI + (NM - NM / 4 - 4) - 1) / (NM - NM / 4 - 4), 0); \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
       }                                                                                        \
       _Pragma("unroll") for (int g = NM - NM / 4; g < NM; ++g) {                               \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
@@ -1158,23 +1180,34 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     cw1 = nw1;                                                                                 \
   }
 
-  for (int kb = 0;;) {
-    LNF4_DXQ_BLOCK(sm0, sm1, sm2);
-    if (++kb == nkb) break;
-    LNF4_DXQ_BLOCK(sm1, sm2, sm0);
-    if (++kb == nkb) break;
-    LNF4_DXQ_BLOCK(sm2, sm0, sm1);
-    if (++kb == nkb) break;
-    LNF4_DXQ_BLOCK(sm0, sm1, sm2);
-    if (++kb == nkb) break;
-    LNF4_DXQ_BLOCK(sm1, sm2, sm0);
-    if (++kb == nkb) break;
-    LNF4_DXQ_BLOCK(sm2, sm0, sm1);
-    if (++kb == nkb) break;
+  // whole trips of two turns of the ring, one exit test per trip (blocks past the last
+  // add zeros)
+  if constexpr (NSTG == 4) {
+    for (int kb = 0; kb < nkb; kb += 8) {
+      LNF4_DXQ_BLOCK(kb + 0, sm0, sm1, sm3);
+      LNF4_DXQ_BLOCK(kb + 1, sm1, sm2, sm0);
+      LNF4_DXQ_BLOCK(kb + 2, sm2, sm3, sm1);
+      LNF4_DXQ_BLOCK(kb + 3, sm3, sm0, sm2);
+      LNF4_DXQ_BLOCK(kb + 4, sm0, sm1, sm3);
+      LNF4_DXQ_BLOCK(kb + 5, sm1, sm2, sm0);
+      LNF4_DXQ_BLOCK(kb + 6, sm2, sm3, sm1);
+      LNF4_DXQ_BLOCK(kb + 7, sm3, sm0, sm2);
+    }
+  } else {
+    for (int kb = 0; kb < nkb; kb += 6) {
+      LNF4_DXQ_BLOCK(kb + 0, sm0, sm1, sm2);
+      LNF4_DXQ_BLOCK(kb + 1, sm1, sm2, sm0);
+      LNF4_DXQ_BLOCK(kb + 2, sm2, sm0, sm1);
+      LNF4_DXQ_BLOCK(kb + 3, sm0, sm1, sm2);
+      LNF4_DXQ_BLOCK(kb + 4, sm1, sm2, sm0);
+      LNF4_DXQ_BLOCK(kb + 5, sm2, sm0, sm1);
+    }
   }
 #undef LNF4_DXQ_BLOCK
 #undef LNF4_DXQ_PROJ
 #undef LNF4_DXQ_ISSUE
+#undef LNF4_DXQ_ISSUE_PART
+#undef LNF4_DXQ_RSRC
 #undef LNF4_TR4
 #undef LNF4_DXQ_CODES
 #undef LNF4_DXQ_SCALES
