@@ -17,7 +17,8 @@
 // dA and dB (k_rank_grad): a job is Q [T, C] bf16 times P [T, R] fp32 reduced over T, for
 // the weights whose ranks are concatenated in P (dA of every adapted projection of a
 // group shares Q = x; each dB has its own Q = dy_p).  Each lane owns CPL columns and all
-// R ranks; P rows are wave-uniform (scalar loads).  The 4 waves of a workgroup split the
+// R ranks; P rows are the same for every lane of a wave and are read as LDS broadcasts from
+// a per-wave staging slice, 16 rows at a time.  The 4 waves of a workgroup split the
 // workgroup's T range and add through LDS in a fixed order; workgroups along T write
 // partials that k_rank_grad_reduce adds in a fixed order (no atomics).
 #include "common.hpp"
@@ -182,7 +183,9 @@ template <int RMAX>
 __global__ __launch_bounds__(256) void k_rank_grad(const GradArgs args) {
   constexpr int CPL = GradCfg<RMAX>::CPL, COLS = GradCfg<RMAX>::COLS;
   constexpr int NVAL = CPL * RMAX;
+  constexpr int RU = 16;  // rows per group
   __shared__ float red[4][64 * NVAL];
+  __shared__ __attribute__((aligned(16))) float pst[4][RU][RMAX];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const GradJob& J = args.job[blockIdx.z];
   const int T = args.T, C = J.C, R = J.R;
@@ -204,21 +207,42 @@ __global__ __launch_bounds__(256) void k_rank_grad(const GradArgs args) {
   for (int e = 0; e < CPL; ++e)
 #pragma unroll
     for (int k = 0; k < RMAX; ++k) acc[e][k] = 0.f;
-  for (int t = wb; t < we; ++t) {
-    float q[CPL];
-    if (CPL == 2) {
-      const uint32_t w = *(const uint32_t*)(J.Q + (size_t)t * C + cc);
-      q[0] = bf16_lo(w);
-      q[CPL - 1] = bf16_hi(w);
-    } else {
-      q[0] = bf16_to_f32(J.Q[(size_t)t * C + cc]);
+  // The wave's rows in groups of RU.  The group's P rows are staged in the wave's own LDS
+  // slice (zero past R and past the wave's last row), so the products read them without
+  // per-rank bounds branches, and all of the group's Q loads are in flight before the
+  // first product.  Products run in row order: every sum is the same sequence of adds.
+  float* pw = &pst[wave][0][0];
+  for (int t = wb; t < we; t += RU) {
+    __builtin_amdgcn_wave_barrier();
+    static_assert(RU * RMAX % 64 == 0, "staging covers whole waves");
+#pragma unroll
+    for (int j = 0; j < RU * RMAX / 64; ++j) {
+      const int i = 64 * j + lane, u = i / RMAX, k = i % RMAX;
+      pw[i] = (k < R && t + u < we) ? J.P[(size_t)(t + u) * J.pstride + k] : 0.f;
     }
-    const float* pr = J.P + (size_t)t * J.pstride;  // wave-uniform row
+    float q[RU][CPL];
 #pragma unroll
-    for (int k = 0; k < RMAX; ++k) {
-      const float pk = (k < R) ? pr[k] : 0.f;
+    for (int u = 0; u < RU; ++u) {
+      const int tr = t + u < we ? t + u : we - 1;  // rows past the end: P is zero there
+      if (CPL == 2) {
+        const uint32_t w = *(const uint32_t*)(J.Q + (size_t)tr * C + cc);
+        q[u][0] = bf16_lo(w);
+        q[u][CPL - 1] = bf16_hi(w);
+      } else {
+        q[u][0] = bf16_to_f32(J.Q[(size_t)tr * C + cc]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) acc[e][k] += pk * q[e];
+    for (int u = 0; u < RU; ++u) {
+#pragma unroll
+      for (int k4 = 0; k4 < RMAX; k4 += 4) {
+        const floatx4 p4 = *(const floatx4*)&pw[u * RMAX + k4];  // same address in every lane
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) acc[e][k4 + kk] += p4[kk] * q[u][e];
+      }
     }
   }
 #pragma unroll
