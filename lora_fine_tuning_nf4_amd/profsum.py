@@ -26,7 +26,7 @@ import json
 import os
 import sys
 
-DOM_NAME = "k_fwd<0, 256, 4>"
+DOM_NAME = "k_fwd_nf4<256, 4>"
 DOM_GRID = 896 * 256
 CAL_NAME = "neg_kernel"
 CAL_BYTES = 256 << 20
