@@ -19,10 +19,10 @@
 //    (32 K values of one output column) straight from global memory into registers and
 //    decodes them there: no LDS round trip for W, and every code is decoded once per
 //    workgroup.
-//  * dx: K runs across rows of W (W is N-contiguous here), so each thread loads an 8x8
-//    sub-block (8 rows x 4 bytes of codes), decodes it, and writes it transposed into LDS
-//    (the packed bf16 pairs are formed from two different rows, so the transpose costs
-//    nothing beyond the decode).  Waves then read B fragments from LDS.
+//  * dx: K runs across rows of W (W is N-contiguous here).  The weight tile goes to LDS
+//    row-major by direct loads and is read back transposed by gfx950's transposing LDS
+//    reads (4-bit for the codes, which are then decoded in registers with each row's
+//    absmax; 16-bit for bf16 weights), so each lane gets 8 consecutive K of one column.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -78,8 +78,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
 // each cover 8 distinct slots, so a 16-byte-per-lane read is conflict free.
 __device__ __forceinline__ int act_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int act_pos(int row, int c) { return row * BK + ((c ^ act_swz(row)) << 3); }
-// position of chunk c of decoded-weight row `n` in the dx kernel's transposed W tile
-__device__ __forceinline__ int wt_pos(int n, int c) { return n * BK + ((c ^ ((n ^ (n >> 3)) & 7)) << 3); }
 
 // Field-wise selection of a group member from the kernel arguments with a uniform
 // index: every candidate is read with a constant offset and selected in scalar
@@ -156,8 +154,6 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = __builtin_bit_cast(uint16_t, l);
 }
 
-template <int BM>
-constexpr int epi_bytes() { return (2 * BM + BN) * LNF4_EPI_RANK * 2; }
 
 // =====================================================================================
 // Forward
@@ -666,223 +662,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16(const FwdArgs args) {
 }
 
 // =====================================================================================
-// Input gradient
-// =====================================================================================
-template <int FMT, int BM>
-__global__ __launch_bounds__(NTHR, 1) void k_dx(const DxArgs args) {
-  constexpr int MI = BM / 32;
-  constexpr int AL = BM * BK / 8 / NTHR;
-  constexpr int MAIN_BYTES = 2 * BM * BK * 2 + 2 * BN * BK * 2;
-  constexpr int SMEM = MAIN_BYTES > epi_bytes<BM>() ? MAIN_BYTES : epi_bytes<BM>();
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  __shared__ float lut[16];
-  uint16_t* as0 = (uint16_t*)smem;            // [2][BM*BK] activation (dy) tiles
-  uint16_t* ws0 = as0 + 2 * BM * BK;          // [2][BN*BK] decoded, transposed W tiles
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h = lane >> 5;
-  if (tid < 16) lut[tid] = c_gemm_table[tid];
-
-  int tm, tn;
-  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
-  const int M = args.M, N = args.N;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // activation (dy) tile loader mapping
-  const int ac = tid & 7;
-  int arow_[AL];
-#pragma unroll
-  for (int q = 0; q < AL; ++q) {
-    const int gm = m0 + q * 32 + (tid >> 3);
-    arow_[q] = gm < M ? gm : M - 1;
-  }
-  // weight sub-block loader mapping: rows k0 + 8*kb8 + i, columns n0 + 8*nb8 + e
-  const int kb8 = tid >> 5, nb8 = tid & 31;
-  const int ncol = n0 + 8 * nb8;
-  const bool col_ok = ncol < N;
-
-  // projection of a K-block (uniform)
-  auto proj_of = [&](int kb) {
-    int pi = 0;
-#pragma unroll
-    for (int q = 1; q < kMaxGroup; ++q)
-      if (q < args.n_proj && kb >= args.p[q].kb0) pi = q;
-    return pi;
-  };
-
-  u32x4 ar[AL];
-  uint32_t wraw[8][FMT == 0 ? 1 : 4];
-  float wa[8];
-
-  // prefetch K-block kb_ of the group: dy chunk (16 B per thread per 32 rows) and an 8x8
-  // sub-block of W (8 rows x 4 bytes of codes, or 8 rows x 16 bytes of bf16)
-#define LNF4_DX_LOAD(kb_)                                                                      \
-  {                                                                                            \
-    const DxProj P = select_dx(args, proj_of(kb_));                                            \
-    const int k0 = ((kb_) - P.kb0) * BK;                                                       \
-    const int Kp = P.out_f;                                                                    \
-    const int kk = k0 + 8 * ac;                                                                \
-    const bool aok = kk < Kp;                                                                  \
-    const int kkc = aok ? kk : 0; /* always a valid address; the value is masked */           \
-    _Pragma("unroll") for (int q = 0; q < AL; ++q) {                                           \
-      const u32x4 v_ = *(const u32x4*)(P.dy + (size_t)arow_[q] * Kp + kkc);                    \
-      ar[q] = aok ? v_ : u32x4{0, 0, 0, 0};                                                    \
-    }                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                            \
-      const int k = k0 + 8 * kb8 + i;                                                          \
-      const bool ok = col_ok && k < Kp;                                                        \
-      const int kc = ok ? k : 0, cc = col_ok ? ncol : 0;                                       \
-      if (FMT == 0) {                                                                          \
-        const uint32_t c_ = *(const uint32_t*)((const uint8_t*)P.w + (size_t)kc * (N / 2) + cc / 2); \
-        const float a_ = P.absmax[(size_t)kc * (N / 64) + cc / 64];                            \
-        wraw[i][0] = ok ? c_ : 0x77777777u; /* code 7 is the zero level */                    \
-        wa[i] = ok ? a_ : 0.0f;                                                                \
-      } else {                                                                                 \
-        const u32x4 v_ = *(const u32x4*)((const uint16_t*)P.w + (size_t)kc * N + cc);          \
-        wraw[i][0] = ok ? v_.x : 0u;                                                           \
-        wraw[i][FMT == 0 ? 0 : 1] = ok ? v_.y : 0u;                                            \
-        wraw[i][FMT == 0 ? 0 : 2] = ok ? v_.z : 0u;                                            \
-        wraw[i][FMT == 0 ? 0 : 3] = ok ? v_.w : 0u;                                            \
-      }                                                                                        \
-    }                                                                                          \
-  }
-  // store the prefetched dy chunk, and decode + transpose the W sub-block into LDS:
-  // column e of the sub-block holds element e of each of the 8 rows (element 2b is the
-  // high nibble of byte b); pairs of consecutive rows pack into one dword
-#define LNF4_DX_STORE(buf_)                                                                    \
-  {                                                                                            \
-    uint16_t* at_ = as0 + (buf_) * BM * BK;                                                    \
-    uint16_t* wt_ = ws0 + (buf_) * BN * BK;                                                    \
-    _Pragma("unroll") for (int q = 0; q < AL; ++q)                                             \
-      *(u32x4*)&at_[act_pos(q * 32 + (tid >> 3), ac)] = ar[q];                                 \
-    _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                            \
-      u32x4 o;                                                                                 \
-      if (FMT == 0) {                                                                          \
-        const int sh = 8 * (e >> 1) + ((e & 1) ? 0 : 4);                                       \
-        float f[8];                                                                            \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) f[i] = lut[(wraw[i][0] >> sh) & 15u] * wa[i]; \
-        o.x = pack_bf16x2(f[0], f[1]);                                                         \
-        o.y = pack_bf16x2(f[2], f[3]);                                                         \
-        o.z = pack_bf16x2(f[4], f[5]);                                                         \
-        o.w = pack_bf16x2(f[6], f[7]);                                                         \
-      } else {                                                                                 \
-        const int wd = e >> 1, sh = (e & 1) * 16;                                              \
-        uint32_t hv[8];                                                                        \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) hv[i] = (wraw[i][FMT == 0 ? 0 : wd] >> sh) & 0xffffu; \
-        o.x = hv[0] | (hv[1] << 16);                                                           \
-        o.y = hv[2] | (hv[3] << 16);                                                           \
-        o.z = hv[4] | (hv[5] << 16);                                                           \
-        o.w = hv[6] | (hv[7] << 16);                                                           \
-      }                                                                                        \
-      *(u32x4*)&wt_[wt_pos(8 * nb8 + e, kb8)] = o;                                             \
-    }                                                                                          \
-  }
-
-  // ---- accumulators start at the rank-R LoRA term: the ranks of every adapted projection
-  // concatenated, each projection's v pre-scaled by its s:
-  //   U[row][off+k] = s_p v_p[row][k],   V[col][off+k] = A_p[k][col]
-  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;
-  floatx16 acc[MI][2];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-  int R = 0;
-  for (int pi = 0; pi < args.n_proj; ++pi) {
-    const DxProj P = select_dx(args, pi);
-    if (P.v != nullptr && P.r > 0) R += P.r;
-  }
-  if (R > 0) {
-    const int RP = (R + 15) & ~15;
-    uint16_t* Uh = (uint16_t*)smem;
-    uint16_t* Ul = Uh + BM * RP;
-    uint16_t* V = Ul + BM * RP;
-    for (int idx = tid; idx < BM * RP; idx += NTHR) Uh[idx] = Ul[idx] = 0;
-    for (int idx = tid; idx < BN * RP; idx += NTHR) V[idx] = 0;
-    __syncthreads();
-    int off = 0;
-    for (int pi = 0; pi < args.n_proj; ++pi) {
-      const DxProj P = select_dx(args, pi);
-      if (P.v == nullptr || P.r <= 0) continue;
-      const int r = P.r;
-      for (int idx = tid; idx < BM * r; idx += NTHR) {
-        const int mm = idx / r, kk = idx - mm * r, gm = m0 + mm;
-        if (gm < M) split_bf16(P.scale * P.v[(size_t)gm * P.v_stride + kk], Uh[mm * RP + off + kk], Ul[mm * RP + off + kk]);
-      }
-      for (int idx = tid; idx < BN * r; idx += NTHR) {
-        const int kk = idx / BN, nn = idx - kk * BN, n = n0 + nn;
-        if (n < N) V[nn * RP + off + kk] = P.A[(size_t)kk * N + n];
-      }
-      off += r;
-    }
-    __syncthreads();
-    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
-  }
-
-  __syncthreads();  // lut ready; LoRA staging no longer read
-  LNF4_DX_LOAD(0);
-  LNF4_DX_STORE(0);
-  __syncthreads();
-
-  const int nkb = args.total_kb;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    LNF4_DX_LOAD(kb + 1 < nkb ? kb + 1 : kb);  // unconditional prefetch (the tail re-reads)
-    const uint16_t* at = as0 + cur * BM * BK;
-    const uint16_t* wt = ws0 + cur * BN * BK;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 b0 = *(const bf16x8*)&wt[wt_pos(64 * wave + l32, 4 * h + s)];
-      const bf16x8 b1 = *(const bf16x8*)&wt[wt_pos(64 * wave + 32 + l32, 4 * h + s)];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const bf16x8 a = *(const bf16x8*)&at[act_pos(32 * i + l32, 4 * h + s)];
-        acc[i][0] = mfma32(a, b0, acc[i][0]);
-        acc[i][1] = mfma32(a, b1, acc[i][1]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    LNF4_DX_STORE(cur ^ 1);
-    __syncthreads();
-  }
-
-#undef LNF4_DX_LOAD
-#undef LNF4_DX_STORE
-  // ---- store bf16 (optionally accumulating into the existing dx)
-  const int n0g = n0 + nc0, n1g = n0 + nc1;
-  const bool c0ok = n0g < N, c1ok = n1g < N;
-  if (args.accumulate) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-        uint16_t* dr = args.dx + (size_t)gm * N;
-        if (gm < M && c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][0][q] + bf16_to_f32(dr[n0g])));
-        if (gm < M && c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][1][q] + bf16_to_f32(dr[n1g])));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-        uint16_t* dr = args.dx + (size_t)gm * N;
-        if (gm < M && c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][0][q]);
-        if (gm < M && c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][1][q]);
-      }
-    }
-  }
-}
-
-// =====================================================================================
 // Input gradient, NF4 weights: direct-to-LDS ring with transposing code reads
 // =====================================================================================
 // dx [T][N] = sum over the group's K space (the projections' out rows) of dy . W'.
@@ -917,14 +696,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   // (low nibble) and 2b+1 (high nibble) of one column; the large alignment places it at LDS
   // address 0, so an entry's address is just byte << 3
   __shared__ __attribute__((aligned(2048))) float2 lut2[256];
-  __shared__ float lut1[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   lut2[tid] = make_float2(c_gemm_table[tid & 15], c_gemm_table[tid >> 4]);  // NTHR == 256
-  if (tid < 16) lut1[tid] = c_gemm_table[tid];
 
   int tm, tn;
   tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
@@ -1070,16 +847,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     a_[0] = lo_[0]; a_[1] = lo_[1]; a_[2] = lo_[2]; a_[3] = lo_[3];                             \
     a_[4] = hi_[0]; a_[5] = hi_[1]; a_[6] = hi_[2]; a_[7] = hi_[3];                             \
   }
-#ifdef LNF4_NIBBLE_LUT
-#define LNF4_LUT8X(lv, cw_)                                                        \
-  {                                                                                \
-    const uint32_t c_ = (cw_);                                                     \
-    _Pragma("unroll") for (int b_ = 0; b_ < 4; ++b_) {                             \
-      lv[2 * b_] = lut1[(c_ >> (8 * b_)) & 15u];                                   \
-      lv[2 * b_ + 1] = lut1[(c_ >> (8 * b_ + 4)) & 15u];                           \
-    }                                                                              \
-  }
-#else
 #define LNF4_LUT8X(lv, cw_)                                                        \
   {                                                                                \
     const uint32_t c_ = (cw_);                                                     \
@@ -1089,7 +856,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       lv[2 * b_ + 1] = p_.y;                                                       \
     }                                                                              \
   }
-#endif
 #define LNF4_FIN8X(dst, lv, a_)                                                    \
   dst = as_bf16x8(pack_bf16x2(lv[0] * a_[0], lv[1] * a_[1]), pack_bf16x2(lv[2] * a_[2], lv[3] * a_[3]), \
                   pack_bf16x2(lv[4] * a_[4], lv[5] * a_[5]), pack_bf16x2(lv[6] * a_[6], lv[7] * a_[7]));
@@ -1238,6 +1004,254 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 }
 
 // =====================================================================================
+// Input gradient, bf16 weights: direct-to-LDS ring with transposing 16-bit reads
+// =====================================================================================
+// dx [T][N] = sum over the group's K space of dy . W' with W' bf16 [K rows][N], N
+// contiguous.  The weight tile [64 rows][256 cols] goes to LDS row-major by direct loads
+// (512-byte rows of 32 16-byte chunks, chunk c of row r stored at c ^ 4(r & 3)) and is read
+// back with ds_read_b64_tr_b16: in each group of 16 lanes, lane a + 4c names the 4-column
+// run (4a .. 4a+3) of row k0 + c, and lane i of the group receives column i of those four
+// rows.  Two such reads give a lane the 8 consecutive K of one column that the MFMA B
+// operand takes (in the activation tile's K order); the four rows of one read then cover
+// all 16 chunk banks, so a read takes the minimum two LDS cycles.
+template <int BM>
+__global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
+  constexpr int MI = BM / 32;
+  constexpr int NM = 2 * MI;
+  constexpr int X_BYTES = BM * BK * 2;     // dy tile [BM][64] bf16
+  constexpr int W_BYTES = BK * BN * 2;     // weight tile [64][256] bf16
+  constexpr int STAGE_RAW = X_BYTES + W_BYTES;
+  constexpr int SLAB_U = BM * LNF4_EPI_RANK * 2, SLAB_V = BN * LNF4_EPI_RANK * 2;
+  constexpr int SLAB = SLAB_U > SLAB_V ? SLAB_U : SLAB_V;
+  constexpr int STAGE = STAGE_RAW > SLAB ? STAGE_RAW : SLAB;
+  static_assert(3 * STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  int tm, tn;
+  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  const int M = args.M, N = args.N;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkb = args.total_kb;
+  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;
+
+  // ---- accumulators start at the rank-R LoRA term (ranks of the group concatenated)
+  floatx16 acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  int R = 0;
+  for (int pi = 0; pi < args.n_proj; ++pi) {
+    const DxProj P = select_dx(args, pi);
+    if (P.v != nullptr && P.r > 0) R += P.r;
+  }
+  if (R > 0) {
+    const int RP = (R + 15) & ~15;
+    uint16_t* Uh = (uint16_t*)sm0;
+    uint16_t* Ul = (uint16_t*)sm1;
+    uint16_t* V = (uint16_t*)sm2;
+    for (int idx = tid; idx < BM * RP; idx += NTHR) Uh[idx] = Ul[idx] = 0;
+    for (int idx = tid; idx < BN * RP; idx += NTHR) V[idx] = 0;
+    __syncthreads();
+    int off = 0;
+    for (int pi = 0; pi < args.n_proj; ++pi) {
+      const DxProj P = select_dx(args, pi);
+      if (P.v == nullptr || P.r <= 0) continue;
+      const int r = P.r;
+      for (int idx = tid; idx < BM * r; idx += NTHR) {
+        const int mm = idx / r, kk = idx - mm * r, gm = m0 + mm;
+        if (gm < M) split_bf16(P.scale * P.v[(size_t)gm * P.v_stride + kk], Uh[mm * RP + off + kk], Ul[mm * RP + off + kk]);
+      }
+      for (int idx = tid; idx < BN * r; idx += NTHR) {
+        const int kk = idx / BN, nn = idx - kk * BN, n = n0 + nn;
+        if (n < N) V[nn * RP + off + kk] = P.A[(size_t)kk * N + n];
+      }
+      off += r;
+    }
+    __syncthreads();
+    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+    __syncthreads();
+  }
+
+  // ---- direct global -> LDS loads of one K-block (64 rows of one projection)
+  //  * dy: load q of wave w fills tile rows (w*XQ+q)*8 .. +7 (as the forward's x)
+  //  * weights: load q of wave w fills rows 2g, 2g+1 (g = w*WQ+q); lane L -> row 2g + L/32,
+  //    stored chunk L%32, which holds global chunk (L%32) ^ 4(row & 3) of the row
+  //  Rows past the projection's out_f load zeros (the block's resources end there);
+  //  columns past N belong to outputs that are dropped.
+  constexpr int XQ = X_BYTES / 1024 / 4;
+  constexpr int WQ = W_BYTES / 1024 / 4;
+  constexpr int NLD = XQ + WQ;
+  static_assert(NLD % 3 == 0, "loads split over three steps");
+  uint32_t dyr2[XQ], dyc[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int row = (wave * XQ + q) * 8 + (lane >> 3);
+    dyr2[q] = 2u * (uint32_t)(m0 + row < M ? m0 + row : M - 1);
+    dyc[q] = 16u * (uint32_t)((lane & 7) ^ act_swz(row));
+  }
+  uint32_t woff[WQ];
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int row = 2 * (wave * WQ + q) + (lane >> 5);
+    const int cg = (lane & 31) ^ (4 * (row & 3));
+    woff[q] = 2u * ((uint32_t)row * (uint32_t)N + (uint32_t)(n0 + 8 * cg));
+  }
+
+#define LNF4_DXB_PROJ(kb_, P_)                                                   \
+  int pi_ = 0;                                                                   \
+  _Pragma("unroll") for (int q = 1; q < kMaxGroup; ++q) if (q < args.n_proj && (kb_) >= args.p[q].kb0) pi_ = q; \
+  pi_ = __builtin_amdgcn_readfirstlane(pi_);                                     \
+  const DxProj& P_ = args.p[pi_];
+  // Blocks past the last (the loop runs whole trips) belong to no projection's row range:
+  // their resources are empty and every load returns zeros.
+#define LNF4_DXB_RSRC(kb_)                                                                       \
+    LNF4_DXB_PROJ(kb_, Pi_)                                                                      \
+    const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
+    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, ((int64_t)M * Kp_ - k0_) * 2);                  \
+    const rsrc_t wrs_ = make_rsrc((const uint16_t*)Pi_.w + (size_t)k0_ * N, (int64_t)(Kp_ - k0_) * N * 2);
+  // load i of a block (0 .. NLD-1): dy loads first, then weight loads
+#define LNF4_DXB_LOAD1(SM_, i_)                                                                  \
+  {                                                                                              \
+    if ((i_) < XQ)                                                                               \
+      LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + (i_)) * 1024, 16, dyr2[(i_) < XQ ? (i_) : 0] * (uint32_t)Kp_ + dyc[(i_) < XQ ? (i_) : 0], 0); \
+    else                                                                                         \
+      LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * WQ + (i_) - XQ) * 1024, 16, woff[(i_) < XQ ? 0 : (i_) - XQ], 0); \
+  }
+#define LNF4_DXB_ISSUE_PART(SM_, part_)                                                          \
+  { _Pragma("unroll") for (int i = (part_) * (NLD / 3); i < ((part_) + 1) * (NLD / 3); ++i) LNF4_DXB_LOAD1(SM_, i) }
+#define LNF4_DXB_ISSUE(kb_, SM_)                                                                 \
+  {                                                                                              \
+    LNF4_DXB_RSRC(kb_)                                                                           \
+    LNF4_DXB_ISSUE_PART(SM_, 0)                                                                  \
+    LNF4_DXB_ISSUE_PART(SM_, 1)                                                                  \
+    LNF4_DXB_ISSUE_PART(SM_, 2)                                                                  \
+  }
+
+  typedef short v4s_t __attribute__((ext_vector_type(4)));
+  // transposing reads: lane j = a + 4c of its 16-lane group (j = lane % 16) names row
+  // base + c, columns 16g + 4a .. +3 of its 32-column block (g = l32 / 16)
+  const int tr_c = (lane & 15) >> 2, tr_col = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
+  // byte offset of the run for row `row` (row & 3 == tr_c) and column `col`
+#define LNF4_TRB(SM_, row_, col_)                                                                \
+  __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(           \
+      (SM_) + X_BYTES + (row_) * 512 + ((((col_) >> 3) ^ (4 * ((row_) & 3))) << 4) + (((col_) & 7) << 1)))
+  // B fragment of step s (K = 32h + 8s .. +7) for the 32-column block starting at cb
+#define LNF4_DXB_FRAG(SM_, s_, cb_)                                                              \
+  ({                                                                                             \
+    const int r0_ = 32 * h + 8 * (s_) + tr_c;                                                    \
+    const v4s_t lo_ = LNF4_TRB(SM_, r0_, (cb_) + tr_col);                                        \
+    const v4s_t hi_ = LNF4_TRB(SM_, r0_ + 4, (cb_) + tr_col);                                    \
+    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7));      \
+  })
+#define LNF4_XS(SM_) ((const uint16_t*)(SM_))
+
+  // prologue: blocks 0 and 1 in flight; block 0 visible
+  LNF4_DXB_ISSUE(0, sm0);
+  LNF4_DXB_ISSUE(1, sm1);
+  LNF4_WAIT_VM(NLD);
+  __syncthreads();
+
+  bf16x8 ac[MI], an_[MI];
+  bf16x8 bc0, bc1, bn0, bn1;
+  bc0 = LNF4_DXB_FRAG(sm0, 0, 64 * wave);
+  bc1 = LNF4_DXB_FRAG(sm0, 0, 64 * wave + 32);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) ac[i] = *(const bf16x8*)&LNF4_XS(sm0)[act_pos(32 * i + l32, 4 * h)];
+
+  // One K-block KB on stage SC; SN holds block KB+1, SP receives block KB+2 (issued in
+  // parts over steps 0..2, each after the step's LDS reads).
+#define LNF4_DXB_BLOCK(KB, SC, SN, SP)                                                         \
+  {                                                                                            \
+    LNF4_DXB_RSRC((KB) + 2)                                                                    \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 3) {                                                                            \
+        /* block KB+1 in LDS for every wave; every wave done with SC */                        \
+        LNF4_WAIT_VM_LGKM0(NLD);                                                               \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
+      if (s < 3) {                                                                             \
+        bn0 = LNF4_DXB_FRAG(SC, s + 1, 64 * wave);                                             \
+        bn1 = LNF4_DXB_FRAG(SC, s + 1, 64 * wave + 32);                                        \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
+            *(const bf16x8*)&LNF4_XS(SC)[act_pos(32 * i + l32, 4 * h + s + 1)];                \
+      } else {                                                                                 \
+        bn0 = LNF4_DXB_FRAG(SN, 0, 64 * wave);                                                 \
+        bn1 = LNF4_DXB_FRAG(SN, 0, 64 * wave + 32);                                            \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] =                                \
+            *(const bf16x8*)&LNF4_XS(SN)[act_pos(32 * i + l32, 4 * h)];                        \
+      }                                                                                        \
+      if (s < 3) LNF4_DXB_ISSUE_PART(SP, s);                                                   \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
+        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
+        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+      }                                                                                        \
+      _Pragma("unroll") for (int g = 0; g < NM; ++g) {                                         \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) ac[i] = an_[i];                           \
+      bc0 = bn0;                                                                               \
+      bc1 = bn1;                                                                               \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+  }
+
+  // whole trips of two turns of the 3-stage ring, one exit test per trip (blocks past the
+  // last add zeros)
+  for (int kb = 0; kb < nkb; kb += 6) {
+    LNF4_DXB_BLOCK(kb + 0, sm0, sm1, sm2);
+    LNF4_DXB_BLOCK(kb + 1, sm1, sm2, sm0);
+    LNF4_DXB_BLOCK(kb + 2, sm2, sm0, sm1);
+    LNF4_DXB_BLOCK(kb + 3, sm0, sm1, sm2);
+    LNF4_DXB_BLOCK(kb + 4, sm1, sm2, sm0);
+    LNF4_DXB_BLOCK(kb + 5, sm2, sm0, sm1);
+  }
+#undef LNF4_DXB_BLOCK
+#undef LNF4_DXB_PROJ
+#undef LNF4_DXB_RSRC
+#undef LNF4_DXB_LOAD1
+#undef LNF4_DXB_ISSUE_PART
+#undef LNF4_DXB_ISSUE
+#undef LNF4_TRB
+#undef LNF4_DXB_FRAG
+#undef LNF4_XS
+
+  // ---- store bf16 (optionally accumulating into the existing dx)
+  const int n0g = n0 + nc0, n1g = n0 + nc1;
+  const bool c0ok = n0g < N, c1ok = n1g < N;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      if (gm >= M) continue;
+      uint16_t* dr = args.dx + (size_t)gm * N;
+      float v0 = acc[i][0][q], v1 = acc[i][1][q];
+      if (args.accumulate) {
+        if (c0ok) v0 += bf16_to_f32(dr[n0g]);
+        if (c1ok) v1 += bf16_to_f32(dr[n1g]);
+      }
+      if (c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
+      if (c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
+    }
+  }
+}
+
+// =====================================================================================
 // Launchers
 // =====================================================================================
 static int pick_bm(int M, int tiles_n_256) {
@@ -1300,8 +1314,9 @@ hipError_t launch_dx(const DxArgs& a0, int fmt, hipStream_t s) {
     if (bm == 256) hipLaunchKernelGGL((k_dxq<256>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_dxq<128>), grid, block, 0, s, a);
   } else {
-    if (bm == 256) hipLaunchKernelGGL((k_dx<1, 256>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_dx<1, 128>), grid, block, 0, s, a);
+    // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
+    a.n_tiles_m = (a.M + 127) / 128;
+    hipLaunchKernelGGL((k_dx_bf16<128>), dim3(a.n_tiles_m * a.n_tiles_n), block, 0, s, a);
   }
   return hipGetLastError();
 }
