@@ -8,11 +8,12 @@
 // u and v (k_rank_proj): one launch serves several jobs (blockIdx.y).  A job is one
 // activation matrix src [T, K] and the weights that multiply it; weights that share src
 // (q and v both read x) are one job with their ranks concatenated (R = sum r_p <= 64), so
-// src is read from HBM once.  A workgroup owns RB rows of src and all of K: its 8 waves
-// take interleaved 512-wide K slices (lane = 8 consecutive K, one 16-byte load), each
-// lane accumulates RB x RMAX partial dot products, a butterfly reduce-scatter across the
-// wave leaves each lane NV/64 finished slice totals, and the 8 waves' totals are added in
-// a fixed order through LDS.  Results are fp32 and deterministic.
+// src is read from HBM once.  A workgroup owns RB rows of src and all of K: its waves (as
+// many as K/8 needs lanes, 1 to 8) take interleaved K slices (lane = 8 consecutive K, one
+// 16-byte load), each lane accumulates RB x RMAX partial dot products, a butterfly
+// reduce-scatter across the wave leaves each lane NV/64 finished slice totals, and the
+// waves' totals are added in a fixed order through LDS.  Results are fp32 and
+// deterministic.
 //
 // dA and dB (k_rank_grad): a job is Q [T, C] bf16 times P [T, R] fp32 reduced over T, for
 // the weights whose ranks are concatenated in P (dA of every adapted projection of a
@@ -82,6 +83,7 @@ __global__ __launch_bounds__(512) void k_rank_proj(const RankArgs args) {
   __shared__ float part[8][NV];
   __shared__ const uint16_t* wrow[RMAX];   // layout 0: row pointer of each concatenated rank
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = blockDim.x >> 6;  // waves of this launch (1..8)
   const RankJob& J = args.job[blockIdx.y];
   const int T = args.T, K = J.K, R = J.R, n = J.n;
   const int t0 = blockIdx.x * RB;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(512) void k_rank_proj(const RankArgs args) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.f;
   const int nch = K / 8;
-  for (int c = 64 * wave + lane; c - lane < nch; c += 512) {  // wave-uniform trip count
+  for (int c = 64 * wave + lane; c - lane < nch; c += 64 * nw) {  // wave-uniform trip count
     const bool ok = c < nch;
     const int cc = ok ? c : 0;
     u32x4 xq[RB];
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(512) void k_rank_proj(const RankArgs args) {
   if (tid < NV) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) s += part[w][tid];
+    for (int w = 0; w < nw; ++w) s += part[w][tid];
     const int rr = tid / RMAX, kk = tid % RMAX, t = t0 + rr;
     if (kk < R && t < T) {
       int off;
@@ -178,6 +180,11 @@ struct GradCfg {
   static constexpr int CPL = RMAX <= 32 ? 2 : 1;  // columns per lane
   static constexpr int COLS = 64 * CPL;          // columns per workgroup
 };
+
+// XOR swizzle of a lane's NVAL wave sums in LDS: the lanes' rows start NVAL floats apart,
+// so without it the 64 lanes of one store instruction hit only 64/NVAL of the 64 banks
+template <int NVAL>
+__device__ __forceinline__ int red_swz(int l) { return (NVAL >= 64 ? l : l / (64 / NVAL)) & (NVAL - 1); }
 
 template <int RMAX>
 __global__ __launch_bounds__(256) void k_rank_grad(const GradArgs args) {
@@ -209,29 +216,41 @@ __global__ __launch_bounds__(256) void k_rank_grad(const GradArgs args) {
     for (int k = 0; k < RMAX; ++k) acc[e][k] = 0.f;
   // The wave's rows in groups of RU.  The group's P rows are staged in the wave's own LDS
   // slice (zero past R and past the wave's last row), so the products read them without
-  // per-rank bounds branches, and all of the group's Q loads are in flight before the
-  // first product.  Products run in row order: every sum is the same sequence of adds.
+  // per-rank bounds branches.  The next group's P and Q loads are issued before the
+  // current group's products, so their latency hides behind them.  Products run in row
+  // order: every sum is the same sequence of adds.
+  static_assert(RU * RMAX % 64 == 0, "staging covers whole waves");
+  constexpr int PL = RU * RMAX / 64;  // staged P values per lane per group
   float* pw = &pst[wave][0][0];
+  float pn[PL], qn[RU][CPL];
+#define LNF4_RG_LOAD(t_)                                                                 \
+  {                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < PL; ++j) {                                     \
+      const int i = 64 * j + lane, u = i / RMAX, k = i % RMAX;                           \
+      pn[j] = (k < R && (t_) + u < we) ? J.P[(size_t)((t_) + u) * J.pstride + k] : 0.f;  \
+    }                                                                                    \
+    _Pragma("unroll") for (int u = 0; u < RU; ++u) {                                     \
+      const int tr = (t_) + u < we ? (t_) + u : we - 1; /* past the end: P is zero */   \
+      if (CPL == 2) {                                                                    \
+        const uint32_t w = *(const uint32_t*)(J.Q + (size_t)tr * C + cc);                \
+        qn[u][0] = bf16_lo(w);                                                           \
+        qn[u][CPL - 1] = bf16_hi(w);                                                     \
+      } else {                                                                           \
+        qn[u][0] = bf16_to_f32(J.Q[(size_t)tr * C + cc]);                                \
+      }                                                                                  \
+    }                                                                                    \
+  }
+  if (wb < we) LNF4_RG_LOAD(wb);
   for (int t = wb; t < we; t += RU) {
-    __builtin_amdgcn_wave_barrier();
-    static_assert(RU * RMAX % 64 == 0, "staging covers whole waves");
-#pragma unroll
-    for (int j = 0; j < RU * RMAX / 64; ++j) {
-      const int i = 64 * j + lane, u = i / RMAX, k = i % RMAX;
-      pw[i] = (k < R && t + u < we) ? J.P[(size_t)(t + u) * J.pstride + k] : 0.f;
-    }
     float q[RU][CPL];
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int tr = t + u < we ? t + u : we - 1;  // rows past the end: P is zero there
-      if (CPL == 2) {
-        const uint32_t w = *(const uint32_t*)(J.Q + (size_t)tr * C + cc);
-        q[u][0] = bf16_lo(w);
-        q[u][CPL - 1] = bf16_hi(w);
-      } else {
-        q[u][0] = bf16_to_f32(J.Q[(size_t)tr * C + cc]);
-      }
-    }
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) q[u][e] = qn[u][e];
+    __builtin_amdgcn_wave_barrier();  // the previous group's reads of the slice come first
+#pragma unroll
+    for (int j = 0; j < PL; ++j) pw[64 * j + lane] = pn[j];
+    if (t + RU < we) LNF4_RG_LOAD(t + RU);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
@@ -245,16 +264,17 @@ __global__ __launch_bounds__(256) void k_rank_grad(const GradArgs args) {
       }
     }
   }
+#undef LNF4_RG_LOAD
 #pragma unroll
   for (int e = 0; e < CPL; ++e)
 #pragma unroll
-    for (int k = 0; k < RMAX; ++k) red[wave][lane * NVAL + e * RMAX + k] = acc[e][k];
+    for (int k = 0; k < RMAX; ++k) red[wave][lane * NVAL + ((e * RMAX + k) ^ red_swz<NVAL>(lane))] = acc[e][k];
   __syncthreads();
   // fixed-order sum of the 4 waves; partial layout [split][c][R]
   float* dst = J.part + (size_t)split * C * R;
   for (int i = tid; i < 64 * NVAL; i += 256) {
-    const float s = red[0][i] + red[1][i] + red[2][i] + red[3][i];
-    const int l = i / NVAL, e = (i % NVAL) / RMAX, k = i % RMAX;
+    const int l = i / NVAL, e = (i % NVAL) / RMAX, k = i % RMAX, ri = l * NVAL + ((i % NVAL) ^ red_swz<NVAL>(l));
+    const float s = red[0][ri] + red[1][ri] + red[2][ri] + red[3][ri];
     const int c = cb + l * CPL + e;
     if (c < C && k < R) dst[(size_t)c * R + k] = s;
   }
@@ -297,7 +317,11 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
 
 template <int LAYOUT>
 static hipError_t launch_rank_layout(const RankArgs& a, int rmax, hipStream_t s) {
-  const dim3 blk(512);
+  // one lane per 8 K of the widest job, 1 to 8 waves: small K does not leave most lanes idle
+  int kmax = 8;
+  for (int j = 0; j < a.n_jobs; ++j) kmax = a.job[j].K > kmax ? a.job[j].K : kmax;
+  const int waves = (kmax / 8 + 63) / 64;
+  const dim3 blk(64 * (waves < 1 ? 1 : (waves > 8 ? 8 : waves)));
   switch (rmax) {
     case 8:
       hipLaunchKernelGGL((k_rank_proj<8, LAYOUT>), dim3((a.T + RankCfg<8>::RB - 1) / RankCfg<8>::RB, a.n_jobs), blk,
@@ -327,21 +351,21 @@ hipError_t launch_rank_proj(const RankArgs& a, hipStream_t s) {
   return a.job[0].layout == 0 ? launch_rank_layout<0>(a, rmax, s) : launch_rank_layout<1>(a, rmax, s);
 }
 
-int grad_nsplit(int T) {
-  int ns = T / 128;
-  return ns < 1 ? 1 : (ns > 8 ? 8 : ns);
+// most T splits a launch may use (at least 64 rows each, at most 32 splits): the partial
+// workspace of a job is sized for this many
+static int grad_max_split(int T) {
+  const int ns = T / 64;
+  return ns < 1 ? 1 : (ns > 32 ? 32 : ns);
 }
 
 size_t grad_partial_bytes(int32_t T, int32_t C, int32_t R) {
   if (T <= 0 || R <= 0 || C <= 0) return 0;
-  return (size_t)grad_nsplit(T) * (size_t)C * (size_t)R * sizeof(float);
+  return (size_t)grad_max_split(T) * (size_t)C * (size_t)R * sizeof(float);
 }
 
 hipError_t launch_rank_grad(const GradArgs& a0, hipStream_t s) {
   if (a0.T <= 0 || a0.n_jobs <= 0) return hipSuccess;
   GradArgs a = a0;
-  a.nsplit = grad_nsplit(a.T);
-  a.tchunk = (a.T + a.nsplit - 1) / a.nsplit;
   int rmax = 8, cmax = 0;
   int64_t nmax = 0;
   for (int j = 0; j < a.n_jobs; ++j) {
@@ -350,6 +374,16 @@ hipError_t launch_rank_grad(const GradArgs& a0, hipStream_t s) {
     const int64_t n = (int64_t)a.job[j].C * a.job[j].R;
     nmax = n > nmax ? n : nmax;
   }
+  // T splits: enough workgroups with work (about 576, a little over two per compute unit)
+  // for narrow jobs, at least 8 splits when T allows; the split count depends only on the
+  // shapes, so results stay deterministic
+  const int cols = rmax <= 32 ? GradCfg<8>::COLS : GradCfg<64>::COLS;
+  int cb_total = 0;
+  for (int j = 0; j < a.n_jobs; ++j) cb_total += (a.job[j].C + cols - 1) / cols;
+  const int maxs = grad_max_split(a.T), mins = maxs < 8 ? maxs : 8;
+  int ns = (576 + cb_total - 1) / (cb_total > 0 ? cb_total : 1);
+  a.nsplit = ns < mins ? mins : (ns > maxs ? maxs : ns);
+  a.tchunk = (a.T + a.nsplit - 1) / a.nsplit;
   const dim3 blk(256);
   switch (rmax) {
     case 8:
