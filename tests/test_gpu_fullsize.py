@@ -1,6 +1,8 @@
-"""Parity at the full Llama-3.1-8B layer shapes, in the launch configuration the benchmark
-times (grouped q|k|v and gate|up calls, T = 2048), on sampled outputs the oracle computes
-one by one: whole rows of y and dx, whole columns of dA, whole rows of dB."""
+"""Parity at the full layer shapes of the benchmark configurations, in the launch
+configuration the benchmark times (grouped q|k|v, gate|up and down calls at the
+configuration's T), on sampled outputs the oracle computes one by one: whole rows of y and
+dx, whole columns of dA, whole rows of dB.  Llama-3.1-8B NF4 (T = 2048, and the DPO step's
+T = 4096), Qwen2.5-0.5B NF4 with rank 16 on every projection, Qwen2.5-3B bf16 weights."""
 import numpy as np
 import pytest
 
@@ -15,33 +17,38 @@ from lora_fine_tuning_nf4_amd import lnf4  # noqa: E402
 from oracle import nf4 as onf4  # noqa: E402
 from helpers import bf16_f64, check_tol, dev_f32, dev_u16, dev_u8, host_f32, host_u16  # noqa: E402
 
-WL = synthgen.WORKLOADS["llama8b"]
-T = WL.tokens
-ROWS = [0, 1, 777, 1500, T - 1]
+CASES = [("llama8b", ("q", "k", "v")), ("llama8b", ("gate", "up")), ("llama8b_dpo", ("gate", "up")),
+         ("qwen05b", ("q", "k", "v")), ("qwen05b", ("gate", "up")), ("qwen05b", ("down",)),
+         ("qwen3b_bf16", ("q", "k", "v")), ("qwen3b_bf16", ("gate", "up"))]
 
 
-def _group(names, seed=0):
+def _group(WL, names, seed=0):
+    T = WL.tokens
     in_f = WL.shapes[names[0]][1]
     x = synthgen.act_bits(T, in_f, seed, "full-x", *names)
     P = {}
     for p in names:
         o, i = WL.shapes[p]
-        codes, absmax = onf4.quantize(synthgen.weight_f32(o, i, seed, "full", p))
+        w = synthgen.weight_f32(o, i, seed, "full", p)
         on = p in WL.adapted
-        P[p] = dict(codes=codes, absmax=absmax, on=on, o=o,
-                    A=synthgen.adapter_a_bits(WL.rank, i, seed, "full", p) if on else None,
-                    B=synthgen.adapter_b_bits(o, WL.rank, seed, "full", p) if on else None,
-                    dy=synthgen.act_bits(T, o, seed, "full-dy", p))
+        d = dict(on=on, o=o, A=synthgen.adapter_a_bits(WL.rank, i, seed, "full", p) if on else None,
+                 B=synthgen.adapter_b_bits(o, WL.rank, seed, "full", p) if on else None,
+                 dy=synthgen.act_bits(T, o, seed, "full-dy", p))
+        if WL.fmt == "nf4":
+            d["codes"], d["absmax"] = onf4.quantize(w)
+        else:
+            d["wbits"] = synthgen.to_bf16_bits(w)
+        P[p] = d
     return x, P
 
 
-def _dev(names, x, P):
+def _dev(WL, names, x, P):
+    T = WL.tokens
     dev = {"x": dev_u16(x)}
     projs = []
     for p in names:
         d = P[p]
         o, i = WL.shapes[p]
-        d["dcodes"], d["dabsmax"] = dev_u8(d["codes"]), dev_f32(d["absmax"])
         d["y"] = torch.empty((T, o), dtype=torch.int16, device="cuda")
         d["ddy"] = dev_u16(d["dy"])
         if d["on"]:
@@ -49,17 +56,25 @@ def _dev(names, x, P):
             d["u"] = torch.empty((T, WL.rank), dtype=torch.float32, device="cuda")
             d["dA"] = torch.empty((WL.rank, i), dtype=torch.float32, device="cuda")
             d["dB"] = torch.empty((o, WL.rank), dtype=torch.float32, device="cuda")
-        W = lnf4.make_weight(lnf4.FMT_NF4, d["dcodes"], d["dabsmax"], o, i, 64)
+        if WL.fmt == "nf4":
+            d["dcodes"], d["dabsmax"] = dev_u8(d["codes"]), dev_f32(d["absmax"])
+            W = lnf4.make_weight(lnf4.FMT_NF4, d["dcodes"], d["dabsmax"], o, i, 64)
+        else:
+            d["dw"] = dev_u16(d["wbits"])
+            W = lnf4.make_weight(lnf4.FMT_BF16, d["dw"], None, o, i, 64)
         projs.append(lnf4.make_proj(W, A=d.get("dA_in"), B=d.get("dB_in"), r=WL.rank if d["on"] else 0,
                                     scale=WL.scale if d["on"] else 0.0, y=d["y"], u=d.get("u"), dy=d["ddy"],
                                     dA=d.get("dA"), dB=d.get("dB")))
     return dev, projs
 
 
-@pytest.mark.parametrize("names", [("q", "k", "v"), ("gate", "up")], ids=["qkv", "gate_up"])
-def test_full_size_group_sampled(names):
-    x, P = _group(names)
-    dev, projs = _dev(names, x, P)
+@pytest.mark.parametrize("wl_name,names", CASES, ids=[f"{w}-{'_'.join(n)}" for w, n in CASES])
+def test_full_size_group_sampled(wl_name, names):
+    WL = synthgen.WORKLOADS[wl_name]
+    T = WL.tokens
+    ROWS = [0, 1, 777, T // 2 + 3, T - 1]
+    x, P = _group(WL, names)
+    dev, projs = _dev(WL, names, x, P)
     in_f = WL.shapes[names[0]][1]
     lnf4.lora_group_fwd(projs, dev["x"], T, 1)
     dx = torch.empty((T, in_f), dtype=torch.int16, device="cuda")
@@ -73,7 +88,7 @@ def test_full_size_group_sampled(names):
     xf = None
     for p in names:
         d = P[p]
-        Wd = onf4.decode_f64(d["codes"], d["absmax"])
+        Wd = onf4.decode_f64(d["codes"], d["absmax"]) if WL.fmt == "nf4" else bf16_f64(d["wbits"])
         y_ref = xs @ Wd.T
         dyr = bf16_f64(d["dy"][ROWS])
         dx_ref += dyr @ Wd
