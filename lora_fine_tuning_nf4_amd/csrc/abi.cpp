@@ -178,6 +178,7 @@ struct BwdPlan {
   size_t pa_off[LNF4_MAX_GROUP];  // per chunk: dA partials (-1: no dA asked in the chunk)
   size_t u_off[LNF4_MAX_GROUP];   // per projection: recomputed u (-1: saved or not needed)
   size_t pb_off[LNF4_MAX_GROUP];  // per projection: dB partials (-1: no dB)
+  size_t dx_off;                  // split-K fp32 sums of dx (-1: the dx GEMM does not split)
   size_t total;
 };
 
@@ -222,6 +223,15 @@ static void plan_bwd(const lnf4_proj* projs, int32_t n, int64_t T, const int* on
     pl.pb_off[p] = off;
     off += round256(grad_partial_bytes((int32_t)T, (int32_t)projs[p].W.out_f, projs[p].r));
   }
+  // split-K sums of the dx GEMM, sized for either weight format (the workspace query of a
+  // single linear does not know the format)
+  int total_kb = 0;
+  for (int p = 0; p < n; ++p) total_kb += (int)((projs[p].W.out_f + 63) / 64);
+  size_t dxb = dx_split_bytes((int)T, in_f, total_kb, 0);
+  const size_t dxb1 = dx_split_bytes((int)T, in_f, total_kb, 1);
+  dxb = dxb > dxb1 ? dxb : dxb1;
+  pl.dx_off = dxb ? off : none;
+  off += round256(dxb);
   pl.total = off;
 }
 
@@ -421,6 +431,7 @@ int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
       kb += (int)((P.W.out_f + 63) / 64);
     }
     a.total_kb = kb;
+    a.part = pl.dx_off != (size_t)-1 ? (float*)(wsb + pl.dx_off) : nullptr;
     if ((e = launch_dx(a, projs[0].W.fmt, s)) != hipSuccess) return hip_fail(e, "fused dx GEMM launch");
   }
   // adapter gradients: dA of each chunk against x, dB of each projection against its dy

@@ -704,10 +704,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   lut2[tid] = make_float2(c_gemm_table[tid & 15], c_gemm_table[tid >> 4]);  // NTHR == 256
 
   int tm, tn;
-  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  // split-K: workgroup b takes tile b % tiles and the split b / tiles of the K space
+  const int n_tiles = args.n_tiles_m * args.n_tiles_n;
+  const int split = (int)blockIdx.x / n_tiles;
+  tile_coords((int)blockIdx.x - split * n_tiles, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
   const int M = args.M, N = args.N;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int nkb = args.total_kb;
+  const int kb_beg = split * args.kb_per_split;
+  const int kb_end = kb_beg + args.kb_per_split < args.total_kb ? kb_beg + args.kb_per_split : args.total_kb;
   // this lane's two accumulator columns within the tile (see the header comment)
   const int nc0 = 64 * wave + (l32 ^ 1), nc1 = nc0 + 32;
 
@@ -724,7 +728,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     const DxProj P = select_dx(args, pi);
     if (P.v != nullptr && P.r > 0) R += P.r;
   }
-  if (R > 0) {
+  if (R > 0 && split == 0) {  // the rank-R term once, in split 0
     const int RP = (R + 15) & ~15;
     uint16_t* Uh = (uint16_t*)sm0;
     uint16_t* Ul = (uint16_t*)sm1;
@@ -798,11 +802,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #define LNF4_DXQ_RSRC(kb_)                                                                       \
     LNF4_DXQ_PROJ(kb_, Pi_)                                                                      \
     const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
-    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, ((int64_t)M * Kp_ - k0_) * 2);                  \
+    const int64_t lv_ = (kb_) < kb_end ? 1 : 0; /* blocks past the split: empty ranges */       \
+    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, lv_ * ((int64_t)M * Kp_ - k0_) * 2);            \
     const rsrc_t wrs_ =                                                                          \
-        make_rsrc((const uint8_t*)Pi_.w + (size_t)k0_ * halfN, (int64_t)(Kp_ - k0_) * halfN);    \
+        make_rsrc((const uint8_t*)Pi_.w + (size_t)k0_ * halfN, lv_ * (int64_t)(Kp_ - k0_) * halfN); \
     const rsrc_t ars_ =                                                                          \
-        make_rsrc(Pi_.absmax + (size_t)k0_ * nblk, (int64_t)(Kp_ - k0_) * nblk * 4);
+        make_rsrc(Pi_.absmax + (size_t)k0_ * nblk, lv_ * (int64_t)(Kp_ - k0_) * nblk * 4);
 #define LNF4_DXQ_ISSUE_PART(SM_, part_)                                                          \
   {                                                                                              \
     if ((part_) < 2) {                                                                           \
@@ -862,9 +867,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))
 
   // prologue: blocks 0 .. NSTG-2 in flight; block 0 visible
-  LNF4_DXQ_ISSUE(0, sm0);
-  LNF4_DXQ_ISSUE(1, sm1);
-  if (NSTG == 4) LNF4_DXQ_ISSUE(2, sm2);
+  LNF4_DXQ_ISSUE(kb_beg, sm0);
+  LNF4_DXQ_ISSUE(kb_beg + 1, sm1);
+  if (NSTG == 4) LNF4_DXQ_ISSUE(kb_beg + 2, sm2);
   LNF4_WAIT_VM((NSTG - 2) * NLD);
   __syncthreads();
 
@@ -949,7 +954,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   // whole trips of two turns of the ring, one exit test per trip (blocks past the last
   // add zeros)
   if constexpr (NSTG == 4) {
-    for (int kb = 0; kb < nkb; kb += 8) {
+    for (int kb = kb_beg; kb < kb_end; kb += 8) {
       LNF4_DXQ_BLOCK(kb + 0, sm0, sm1, sm3);
       LNF4_DXQ_BLOCK(kb + 1, sm1, sm2, sm0);
       LNF4_DXQ_BLOCK(kb + 2, sm2, sm3, sm1);
@@ -960,7 +965,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       LNF4_DXQ_BLOCK(kb + 7, sm3, sm0, sm2);
     }
   } else {
-    for (int kb = 0; kb < nkb; kb += 6) {
+    for (int kb = kb_beg; kb < kb_end; kb += 6) {
       LNF4_DXQ_BLOCK(kb + 0, sm0, sm1, sm2);
       LNF4_DXQ_BLOCK(kb + 1, sm1, sm2, sm0);
       LNF4_DXQ_BLOCK(kb + 2, sm2, sm0, sm1);
@@ -984,6 +989,21 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   // ---- store bf16 (optionally accumulating into the existing dx)
   const int n0g = n0 + nc0, n1g = n0 + nc1;
   const bool c0ok = n0g < N, c1ok = n1g < N;
+  if (args.part != nullptr) {  // split-K: this split's fp32 sums, added up by k_dx_split_sum
+    float* pp = args.part + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (gm >= M) continue;
+        if (c0ok) pp[(size_t)gm * N + n0g] = acc[i][0][q];
+        if (c1ok) pp[(size_t)gm * N + n1g] = acc[i][1][q];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1035,10 +1055,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   int tm, tn;
-  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  // split-K: workgroup b takes tile b % tiles and the split b / tiles of the K space
+  const int n_tiles = args.n_tiles_m * args.n_tiles_n;
+  const int split = (int)blockIdx.x / n_tiles;
+  tile_coords((int)blockIdx.x - split * n_tiles, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
   const int M = args.M, N = args.N;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int nkb = args.total_kb;
+  const int kb_beg = split * args.kb_per_split;
+  const int kb_end = kb_beg + args.kb_per_split < args.total_kb ? kb_beg + args.kb_per_split : args.total_kb;
   const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;
 
   // ---- accumulators start at the rank-R LoRA term (ranks of the group concatenated)
@@ -1054,7 +1078,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
     const DxProj P = select_dx(args, pi);
     if (P.v != nullptr && P.r > 0) R += P.r;
   }
-  if (R > 0) {
+  if (R > 0 && split == 0) {  // the rank-R term once, in split 0
     const int RP = (R + 15) & ~15;
     uint16_t* Uh = (uint16_t*)sm0;
     uint16_t* Ul = (uint16_t*)sm1;
@@ -1117,8 +1141,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
 #define LNF4_DXB_RSRC(kb_)                                                                       \
     LNF4_DXB_PROJ(kb_, Pi_)                                                                      \
     const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
-    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, ((int64_t)M * Kp_ - k0_) * 2);                  \
-    const rsrc_t wrs_ = make_rsrc((const uint16_t*)Pi_.w + (size_t)k0_ * N, (int64_t)(Kp_ - k0_) * N * 2);
+    const int64_t lv_ = (kb_) < kb_end ? 1 : 0; /* blocks past the split: empty ranges */       \
+    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, lv_ * ((int64_t)M * Kp_ - k0_) * 2);            \
+    const rsrc_t wrs_ = make_rsrc((const uint16_t*)Pi_.w + (size_t)k0_ * N, lv_ * (int64_t)(Kp_ - k0_) * N * 2);
   // load i of a block (0 .. NLD-1): dy loads first, then weight loads
 #define LNF4_DXB_LOAD1(SM_, i_)                                                                  \
   {                                                                                              \
@@ -1156,8 +1181,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))
 
   // prologue: blocks 0 and 1 in flight; block 0 visible
-  LNF4_DXB_ISSUE(0, sm0);
-  LNF4_DXB_ISSUE(1, sm1);
+  LNF4_DXB_ISSUE(kb_beg, sm0);
+  LNF4_DXB_ISSUE(kb_beg + 1, sm1);
   LNF4_WAIT_VM(NLD);
   __syncthreads();
 
@@ -1211,7 +1236,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
 
   // whole trips of two turns of the 3-stage ring, one exit test per trip (blocks past the
   // last add zeros)
-  for (int kb = 0; kb < nkb; kb += 6) {
+  for (int kb = kb_beg; kb < kb_end; kb += 6) {
     LNF4_DXB_BLOCK(kb + 0, sm0, sm1, sm2);
     LNF4_DXB_BLOCK(kb + 1, sm1, sm2, sm0);
     LNF4_DXB_BLOCK(kb + 2, sm2, sm0, sm1);
@@ -1232,6 +1257,21 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
   // ---- store bf16 (optionally accumulating into the existing dx)
   const int n0g = n0 + nc0, n1g = n0 + nc1;
   const bool c0ok = n0g < N, c1ok = n1g < N;
+  if (args.part != nullptr) {  // split-K: this split's fp32 sums, added up by k_dx_split_sum
+    float* pp = args.part + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (gm >= M) continue;
+        if (c0ok) pp[(size_t)gm * N + n0g] = acc[i][0][q];
+        if (c1ok) pp[(size_t)gm * N + n1g] = acc[i][1][q];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     __builtin_amdgcn_sched_barrier(0);
@@ -1248,6 +1288,33 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
       if (c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
       if (c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
     }
+  }
+}
+
+// Split-K input gradient: dx = bf16(sum of the splits' fp32 sums in split order, plus the
+// existing dx when accumulating), 4 elements per thread.
+__global__ __launch_bounds__(256) void k_dx_split_sum(const float* __restrict__ part, int n_split, int64_t n,
+                                                      int accumulate, uint16_t* __restrict__ dx) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  if (i4 + 4 <= n && ((uintptr_t)dx & 7) == 0) {  // dx itself is only 2-byte aligned in general
+    floatx4 s = *(const floatx4*)(part + i4);
+    for (int sp = 1; sp < n_split; ++sp) {
+      const floatx4 t = *(const floatx4*)(part + (size_t)sp * n + i4);
+      s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
+    }
+    if (accumulate) {
+      const uint2 o = *(const uint2*)(dx + i4);
+      s[0] += bf16_lo(o.x); s[1] += bf16_hi(o.x); s[2] += bf16_lo(o.y); s[3] += bf16_hi(o.y);
+    }
+    *(uint2*)(dx + i4) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+    return;
+  }
+  for (int64_t i = i4; i < i4 + 4 && i < n; ++i) {
+    float s = part[i];
+    for (int sp = 1; sp < n_split; ++sp) s += part[(size_t)sp * n + i];
+    if (accumulate) s += bf16_to_f32(dx[i]);
+    dx[i] = __builtin_bit_cast(uint16_t, (__bf16)s);
   }
 }
 
@@ -1303,21 +1370,52 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Row-tile height of the input-gradient kernels (bf16 weight tiles are 4x the NF4 bytes:
+// their 3-stage ring only fits LDS with 128 rows).
+static int dx_bm(int M, int N, int fmt) { return fmt == 0 ? pick_bm(M, (N + BN - 1) / BN) : 128; }
+
+// Splits of the K space for the input gradient: when the tiles cover less than 3/4 of the
+// compute units, split K so that about one wave of workgroups runs, keeping at least 16
+// K-blocks per split (at most 8 splits).
+int dx_split_count(int M, int N, int total_kb, int fmt) {
+  if (M <= 0 || N <= 0 || total_kb <= 0) return 1;
+  const int bm = dx_bm(M, N, fmt);
+  const int tiles = ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+  if (tiles >= 192) return 1;
+  int ns = (256 + tiles - 1) / tiles;
+  const int by_k = total_kb / 16;
+  ns = ns < by_k ? ns : by_k;
+  ns = ns > 8 ? 8 : ns;
+  return ns < 1 ? 1 : ns;
+}
+
+size_t dx_split_bytes(int M, int N, int total_kb, int fmt) {
+  const int ns = dx_split_count(M, N, total_kb, fmt);
+  return ns > 1 ? (size_t)ns * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 hipError_t launch_dx(const DxArgs& a0, int fmt, hipStream_t s) {
   DxArgs a = a0;
   if (a.M <= 0 || a.N <= 0 || a.total_kb <= 0) return hipSuccess;
   a.n_tiles_n = (a.N + BN - 1) / BN;
-  const int bm = pick_bm(a.M, a.n_tiles_n);
+  const int bm = dx_bm(a.M, a.N, fmt);
   a.n_tiles_m = (a.M + bm - 1) / bm;
-  const dim3 grid(a.n_tiles_m * a.n_tiles_n), block(NTHR);
+  const int ns = a.part != nullptr ? dx_split_count(a.M, a.N, a.total_kb, fmt) : 1;
+  a.kb_per_split = (a.total_kb + ns - 1) / ns;
+  if (ns == 1) a.part = nullptr;
+  const dim3 grid(a.n_tiles_m * a.n_tiles_n * ns), block(NTHR);
   if (fmt == 0) {
     if (bm == 256) hipLaunchKernelGGL((k_dxq<256>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_dxq<128>), grid, block, 0, s, a);
   } else {
-    // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
-    a.n_tiles_m = (a.M + 127) / 128;
-    hipLaunchKernelGGL((k_dx_bf16<128>), dim3(a.n_tiles_m * a.n_tiles_n), block, 0, s, a);
+    hipLaunchKernelGGL((k_dx_bf16<128>), grid, block, 0, s, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  const int64_t n = (int64_t)a.M * a.N;
+  const int64_t blocks = (n / 4 + 255) / 256 + 1;
+  hipLaunchKernelGGL(k_dx_split_sum, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)a.part, ns, n,
+                     a.accumulate, a.dx);
   return hipGetLastError();
 }
 

@@ -57,8 +57,13 @@ struct DxArgs {
   int32_t n_tiles_m;
   int32_t n_tiles_n;
   int32_t accumulate;
+  int32_t kb_per_split; // K-blocks per split (set by launch_dx)
+  float* part;          // split-K workspace [splits][M][N] fp32 (dx_split_bytes), or null
   DxProj p[kMaxGroup];
 };
+// split-K of the input gradient: split count and workspace bytes for (T, in, K-blocks, fmt)
+int dx_split_count(int M, int N, int total_kb, int fmt);
+size_t dx_split_bytes(int M, int N, int total_kb, int fmt);
 
 hipError_t launch_fwd(const FwdArgs& a, int fmt, hipStream_t s);
 hipError_t launch_dx(const DxArgs& a, int fmt, hipStream_t s);

@@ -155,6 +155,27 @@ def test_accumulate_adds_to_existing():
     check_tol(host_f32(d.dB)[:, :8], dB1[:, :8] + dB_ref, "dB accumulated")
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_backward_split_k(fmt):
+    # few output tiles and a long K space: the dx GEMM splits K (fp32 sums per split, then a
+    # fixed-order sum); checked alone and accumulating into the existing dx
+    c = make_case(19, 256, 2048, 256, 8, 16.0, fmt, tag="split-k")
+    d = DevCase(c)
+    _run_bwd(d)
+    sync()
+    dx_ref, dA_ref, dB_ref = oracle_bwd(c)
+    check_tol(bf16_f64(host_u16(d.dx)), dx_ref, "dx split-K")
+    check_tol(host_f32(d.dA)[:8], dA_ref, "dA")
+    check_tol(host_f32(d.dB)[:, :8], dB_ref, "dB")
+    first = host_u16(d.dx).copy()
+    _run_bwd(d)
+    sync()
+    assert np.array_equal(host_u16(d.dx), first)  # deterministic
+    _run_bwd(d, accumulate=1)
+    sync()
+    check_tol(bf16_f64(host_u16(d.dx)), 2 * dx_ref, "dx split-K accumulated")
+
+
 # ------------------------------------------------------------------ bitwise special cases
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_identity_input_gives_decoded_weight_exactly(fmt):
