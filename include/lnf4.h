@@ -143,7 +143,10 @@ size_t lora_linear_bwd_workspace(int64_t T, int64_t out_f, int64_t in_f, int32_t
  *   dx, dA, dB   device outputs; each may be NULL to skip it (dA, dB ignored when the
  *                adapter is off)
  *   workspace    device, at least lora_linear_bwd_workspace(T, out, in, r) bytes
- * Gradient reductions over T use a fixed split and a fixed-order second pass.
+ * Gradient reductions over T use a fixed split and a fixed-order second pass.  When the
+ * dx GEMM has few output tiles and a long K (few tokens, many output features), it splits
+ * K: each split's fp32 sums go to the workspace and a fixed-order pass adds them, so dx is
+ * still deterministic.  The split count depends only on the shapes.
  * Errors: EINVAL, ESHAPE (also workspace too small), EALIGN, EHIP.
  */
 int lora_linear_bwd(const lnf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t T,
