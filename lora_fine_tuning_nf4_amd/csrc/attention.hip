@@ -12,7 +12,8 @@
 // column combine with one cross-half exchange.  The probabilities then feed the next
 // product straight from the accumulators: the 8 values a lane holds for a 16-key step
 // are keys {4h..4h+3, 8+4h..8+4h+3} of that step (h = lane / 32), an order the other
-// operand (a transposed tile in LDS: V^T, K^T, Q^T or dO^T) is read in.
+// operand (V^T, K^T, Q^T or dO^T) is read in: from a row-major LDS tile with gfx950's
+// transposing 16-bit reads.
 //
 // The probabilities P and the score gradients dS enter their products as a bf16 hi + lo
 // pair (two products each), so o, dq, dk and dv carry about 16 significant bits of them
@@ -44,13 +45,6 @@ __device__ __forceinline__ floatx16 mma(const bf16x8& a, const bf16x8& b, const 
 
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p) { return *(const bf16x8*)p; }
 
-// two 8-byte runs (4 bf16 each) as one operand
-__device__ __forceinline__ bf16x8 ld8x2(const uint16_t* p0, const uint16_t* p1) {
-  const uint2 a = *(const uint2*)p0, b = *(const uint2*)p1;
-  const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // accumulator values 8*hs .. 8*hs+7 (rows 16hs + 8(p>>2) + 4h + (p&3), p = 0..7) as a bf16
 // pair hi + lo (lo = bf16(x - hi)): about 16 significant bits through two products, for
 // the probabilities and score gradients fed back into MFMAs
@@ -66,11 +60,29 @@ __device__ __forceinline__ void rows_bf16_split(const floatx16& c, int hs, bf16x
   lo = __builtin_bit_cast(bf16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
 }
 
-// A operand of rows m of a transposed tile Xt[m][r], matching rows_bf16_split for the 16 r of
-// K-step base .. base+15
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* Xt, int stride, int m, int base, int h) {
-  const uint16_t* p = Xt + m * stride + base + 4 * h;
-  return ld8x2(p, p + 8);
+// Row-major [rows][D] bf16 tile whose 16-byte chunks are swizzled by row (chunk c of row r
+// at c ^ swz_chunk(r)), for operands read transposed with ds_read_b64_tr_b16: in each
+// group of 16 lanes, lane a + 4c names the 4-column run 4a..4a+3 of row c and lane i
+// receives column i of those four rows.  A read covers 8 rows and 32 columns; the swizzle
+// puts rows r..r+3 on disjoint banks, so it takes the minimum two LDS cycles.
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+// A operand of rows m = mbase + l32 of the transpose of a swizzled row-major tile X[r][m],
+// for the 16 r of K-step kbase .. kbase+15 in the order rows_bf16_split produces
+// (r = kbase + 4h + 0..3, then kbase + 8 + 4h + 0..3)
+template <int D>
+__device__ __forceinline__ bf16x8 tr16_operand(const uint16_t* X, int mbase, int kbase, int lane) {
+  const int h = lane >> 5, c = (lane & 15) >> 2;
+  const int col = mbase + 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
+  const int r0 = kbase + 4 * h + c, r1 = r0 + 8;
+  const uint16_t* p0 = X + r0 * D + 8 * ((col >> 3) ^ swz_chunk<D>(r0)) + (col & 7);
+  const uint16_t* p1 = X + r1 * D + 8 * ((col >> 3) ^ swz_chunk<D>(r1)) + (col & 7);
+  const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)p0);
+  const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)p1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ floatx16 zero16() {
@@ -82,8 +94,8 @@ __device__ __forceinline__ floatx16 zero16() {
 
 // A 64 x D bf16 block held in registers between its global load and its LDS writes, so
 // that the next block's loads are in flight while the current block computes.  Thread
-// items are row pairs (2rp, 2rp + 1) x 16-byte chunk c, which serve both the row-major
-// and the transposed LDS copy.
+// items are row pairs (2rp, 2rp + 1) x 16-byte chunk c, written either to a padded
+// row-major tile (rows read whole) or to a swizzled one (read transposed).
 template <int D, int NT>
 struct Staged {
   static constexpr int ITEMS = 32 * (D / 8) / NT;
@@ -106,17 +118,13 @@ struct Staged {
       *(u32x4*)&dst[(2 * rp + 1) * STRIDE + 8 * c] = a[it][1];
     }
   }
-  template <int STRIDE>
-  __device__ __forceinline__ void transposed(uint16_t* dst) const {
+  // row-major, no padding, chunks swizzled for transposing reads (tr16_operand)
+  __device__ __forceinline__ void rows_swz(uint16_t* dst) const {
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
       const int idx = threadIdx.x + it * NT, rp = idx / (D / 8), c = idx - rp * (D / 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t va = (a[it][0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t vb = (a[it][1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        *(uint32_t*)&dst[(8 * c + e) * STRIDE + 2 * rp] = va | (vb << 16);
-      }
+      *(u32x4*)&dst[(2 * rp) * D + 8 * (c ^ swz_chunk<D>(2 * rp))] = a[it][0];
+      *(u32x4*)&dst[(2 * rp + 1) * D + 8 * (c ^ swz_chunk<D>(2 * rp + 1))] = a[it][1];
     }
   }
 };
@@ -147,9 +155,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fwd(const uint16_t* __restrict
                                                  const uint16_t* __restrict__ v, int64_t T, int nh, int nkv,
                                                  int64_t S, float sl2e, uint16_t* __restrict__ o,
                                                  float* __restrict__ lse) {
-  constexpr int KS = D + 8, VS = BK + 4, NT = 64 * NW, BR = 32 * NW;
+  constexpr int KS = D + 8, NT = 64 * NW, BR = 32 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vr[BK * D];  // row-major, swizzled
   const int nqb = (int)(S / BR), n_seq = (int)(T / S);
   const int seq = blockIdx.x % n_seq, qb = nqb - 1 - (int)(blockIdx.x / n_seq);  // longest rows first
   const int hq = blockIdx.y, hk = hq / (nh / nkv);
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fwd(const uint16_t* __restrict
   for (int kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();  // the previous block's LDS reads are done
     pk.template rows<KS>(Ks);
-    pv.template transposed<VS>(Vt);
+    pv.rows_swz(Vr);
     __syncthreads();
     if (kb < kb_last) {  // the next block's loads fly while this one computes
       pk.load(k, t0 + (int64_t)(kb + 1) * BK, ldk, (int64_t)hk * D);
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fwd(const uint16_t* __restrict
         rows_bf16_split(st[t], hs, ph, pl);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 a = tr_operand(Vt, VS, 32 * dt + l32, 32 * t + 16 * hs, h);
+          const bf16x8 a = tr16_operand<D>(Vr, 32 * dt, 32 * t + 16 * hs, lane);
           oacc[dt] = mma(a, ph, oacc[dt]);
           oacc[dt] = mma(a, pl, oacc[dt]);
         }
@@ -258,10 +266,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(const uint16_t* __restr
                                                     const uint16_t* __restrict__ dO, const float* __restrict__ dsum,
                                                     int64_t T, int nh, int nkv, int64_t S, float scale, float sl2e,
                                                     uint16_t* __restrict__ dq) {
-  constexpr int KS = D + 8, TS = BK + 4, NT = 64 * NW, BR = 32 * NW;
+  constexpr int KS = D + 8, NT = 64 * NW, BR = 32 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t Kr[BK * D];  // row-major, swizzled
   const int nqb = (int)(S / BR), n_seq = (int)(T / S);
   const int seq = blockIdx.x % n_seq, qb = nqb - 1 - (int)(blockIdx.x / n_seq);
   const int hq = blockIdx.y, hk = hq / (nh / nkv);
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(const uint16_t* __restr
   for (int kb = 0; kb <= kb_last; ++kb) {
     __syncthreads();
     pk.template rows<KS>(Ks);
-    pk.template transposed<TS>(Kt);
+    pk.rows_swz(Kr);
     pv.template rows<KS>(Vs);
     __syncthreads();
     if (kb < kb_last) {
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(const uint16_t* __restr
         rows_bf16_split(st, hs, bh, bl);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 a = tr_operand(Kt, TS, 32 * dt + l32, 32 * t + 16 * hs, h);
+          const bf16x8 a = tr16_operand<D>(Kr, 32 * dt, 32 * t + 16 * hs, lane);
           acc[dt] = mma(a, bh, acc[dt]);
           acc[dt] = mma(a, bl, acc[dt]);
         }
@@ -335,11 +343,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
                                                       int64_t T, int nh, int nkv, int64_t S, float scale, float sl2e,
                                                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
                                                       float* __restrict__ part) {
-  constexpr int QS = D + 8, TS = BQ + 4, NT = 64 * NW, BR = 32 * NW;
+  constexpr int QS = D + 8, NT = 64 * NW, BR = 32 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * QS];
   __shared__ __attribute__((aligned(16))) uint16_t Os[BQ * QS];   // dO rows
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[D * TS];    // dO transposed
+  __shared__ __attribute__((aligned(16))) uint16_t Qr[BQ * D];  // row-major, swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t Or[BQ * D];  // dO rows, row-major, swizzled
   __shared__ float lse_s[BQ], dsum_s[BQ];
   const int nqb = (int)(S / BQ), n_seq = (int)(T / S);
   const int seq = blockIdx.x % n_seq, kb = (int)(blockIdx.x / n_seq);  // early key blocks have the most work
@@ -375,9 +383,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
       __syncthreads();
       const int64_t r0 = t0 + (int64_t)qb * BQ;
       pq.template rows<QS>(Qs);
-      pq.template transposed<TS>(Qt);
+      pq.rows_swz(Qr);
       po.template rows<QS>(Os);
-      po.template transposed<TS>(Ot);
+      po.rows_swz(Or);
       if (threadIdx.x < BQ) {
         lse_s[threadIdx.x] = lse[(int64_t)hq * T + r0 + threadIdx.x] * 1.44269504088896341f;
         dsum_s[threadIdx.x] = dsum[(int64_t)hq * T + r0 + threadIdx.x];
@@ -414,10 +422,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
           rows_bf16_split(ds, hs, sh, sl);
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
-            const bf16x8 ao = tr_operand(Ot, TS, 32 * dt + l32, 32 * t + 16 * hs, h);
+            const bf16x8 ao = tr16_operand<D>(Or, 32 * dt, 32 * t + 16 * hs, lane);
             dva[dt] = mma(ao, ph, dva[dt]);
             dva[dt] = mma(ao, pl, dva[dt]);
-            const bf16x8 a = tr_operand(Qt, TS, 32 * dt + l32, 32 * t + 16 * hs, h);
+            const bf16x8 a = tr16_operand<D>(Qr, 32 * dt, 32 * t + 16 * hs, lane);
             dka[dt] = mma(a, sh, dka[dt]);
             dka[dt] = mma(a, sl, dka[dt]);
           }
