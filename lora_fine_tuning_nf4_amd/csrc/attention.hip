@@ -150,8 +150,10 @@ __device__ __forceinline__ void store_cols(uint16_t* out_row, const floatx16 (&a
 // Online softmax over key blocks in base 2: x = s * scale * log2(e), running max m and
 // sum l per query, O^T rescaled by 2^(m_old - m_new) when m grows.  lse is stored in
 // natural-log units: (m + log2 l) * ln 2.
+// Four-wave workgroups are compiled for two workgroups per compute unit (at most 256
+// registers per lane), so one workgroup's softmax overlaps the other's MFMAs.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void k_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v, int64_t T, int nh, int nkv,
                                                  int64_t S, float sl2e, uint16_t* __restrict__ o,
                                                  float* __restrict__ lse) {
@@ -260,8 +262,10 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dsum(const uint16_t* __restric
 }
 
 // dq = scale * dS K with dS^T = P^T o (dP^T - dsum), P^T = exp(S^T - lse), dP^T = V dO^T
+// two four-wave workgroups per compute unit, as in the forward (dk, dv keep one: their
+// accumulators do not fit in 256 registers)
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void k_attn_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, const float* __restrict__ lse,
                                                     const uint16_t* __restrict__ dO, const float* __restrict__ dsum,
                                                     int64_t T, int nh, int nkv, int64_t S, float scale, float sl2e,
