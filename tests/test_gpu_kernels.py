@@ -174,6 +174,14 @@ def test_backward_split_k(fmt):
     _run_bwd(d, accumulate=1)
     sync()
     check_tol(bf16_f64(host_u16(d.dx)), 2 * dx_ref, "dx split-K accumulated")
+    # dx need only be 2-byte aligned: an output 2 bytes past an 8-byte boundary takes the
+    # split sum's element-wise path and must give the same bits
+    import torch
+    buf = torch.zeros(c.T * c.in_f + 4, dtype=torch.int16, device="cuda")
+    d.dx = buf[1:1 + c.T * c.in_f].view(c.T, c.in_f)
+    _run_bwd(d)
+    sync()
+    assert np.array_equal(host_u16(d.dx), first)
 
 
 # ------------------------------------------------------------------ bitwise special cases
