@@ -1365,6 +1365,26 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
     hipLaunchKernelGGL((k_fwd_nf4<256, 8>), dim3(t256), dim3(512), 0, s, a);
     return hipGetLastError();
   }
+  // Several rounds of 256-row tiles whose last round leaves many compute units idle: the
+  // column panels of that last round can run as 128-row tiles in a second launch (a 128-row
+  // tile takes a little over half the time of a 256-row one).  Chosen when the estimated
+  // rounds drop, e.g. 896 tiles = 3.5 rounds on 256 units become 768 + 256 half tiles.
+  const int rem = t256 % cus;
+  const int tail_n = (rem + tm256 - 1) / tm256;
+  const int tm128 = (a.M + 127) / 128;
+  const int full = t256 - tail_n * tm256;
+  const auto rounds = [cus](int tiles) { return (tiles + cus - 1) / cus; };
+  if (t256 > cus && rem > 0 && full > 0 &&
+      rounds(full) + 0.55 * rounds(tm128 * tail_n) < rounds(t256) - 0.2) {
+    a.n_tiles_m = tm256;
+    a.n_tiles_n = tn_all - tail_n;
+    hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(tm256 * a.n_tiles_n), dim3(NTHR), 0, s, a);
+    a.n_tiles_m = tm128;
+    a.n_tiles_n = tail_n;
+    a.tn_base = tn_all - tail_n;
+    hipLaunchKernelGGL((k_fwd_nf4<128, 4>), dim3(tm128 * tail_n), dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+  }
   a.n_tiles_m = tm256;
   hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(t256), dim3(NTHR), 0, s, a);
   return hipGetLastError();

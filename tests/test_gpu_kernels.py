@@ -184,6 +184,28 @@ def test_backward_split_k(fmt):
     assert np.array_equal(host_u16(d.dx), first)
 
 
+def test_forward_tail_as_128_row_tiles():
+    # 2 x 136 tiles of 256 x 256 on 256 compute units: the last 8 column panels run as
+    # 128-row tiles in a second launch.  Parity with the oracle, and the tail columns must
+    # equal bit for bit a call on those rows of W alone (same K order, other tile shape).
+    T, out_f, in_f, r = 512, 136 * 256, 128, 8
+    c = make_case(23, T, out_f, in_f, r, 16.0, 0, tag="tail-split")
+    d = DevCase(c)
+    _run_fwd(d)
+    sync()
+    y_ref, u_ref = oracle_fwd(c)
+    check_tol(bf16_f64(host_u16(d.y)), y_ref, "y")
+    check_tol(host_f32(d.u)[:T, :r], u_ref, "u")
+    n0 = 128 * 256
+    W2 = lnf4.make_weight(0, d.wdata.reshape(-1)[n0 * in_f // 2:], d.absmax.reshape(-1)[n0 * in_f // 64:],
+                          out_f - n0, in_f, 64)
+    y2 = torch.empty((T, out_f - n0), dtype=torch.int16, device="cuda")
+    u2 = torch.empty((T, r), dtype=torch.float32, device="cuda")
+    lnf4.lora_linear_fwd(W2, d.x, T, d.A, d.B[n0:], r, c.scale, y2, u2)
+    sync()
+    assert np.array_equal(host_u16(d.y)[:, n0:], host_u16(y2))
+
+
 # ------------------------------------------------------------------ bitwise special cases
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_identity_input_gives_decoded_weight_exactly(fmt):
