@@ -489,7 +489,8 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "traffic_source": traffic_src,
             "algorithmic_bytes_per_launch": fwd_bytes(wl, GROUPS[2]),
             "kernel": (f"k_fwd_nf4<BM=256,4 waves> gate|up forward: M={stack.T} N={sum(wl.shapes[p][0] for p in GROUPS[2])} "
-                       f"K={wl.shapes[GROUPS[2][0]][1]} (fused NF4 decode), one launch"),
+                       f"K={wl.shapes[GROUPS[2][0]][1]} (fused NF4 decode), one launch (256x256 tiles; a last "
+                       f"round that would leave compute units idle runs as 128x256 tiles in the same launch)"),
             "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4),
             "launches_timed": len(dom),
         },

@@ -18,7 +18,9 @@
 //  * Forward: K runs along a row of W, so each lane loads its own 16 bytes of codes
 //    (32 K values of one output column) straight from global memory into registers and
 //    decodes them there: no LDS round trip for W, and every code is decoded once per
-//    workgroup.
+//    workgroup.  The decoded weights are the MFMA's A operand and the activations its B
+//    operand, so the accumulators hold the tile transposed: a lane's consecutive
+//    accumulator rows are adjacent outputs of one token, stored 8 bytes at a time.
 //  * dx: K runs across rows of W (W is N-contiguous here).  The weight tile goes to LDS
 //    row-major by direct loads and is read back transposed by gfx950's transposing LDS
 //    reads (4-bit for the codes, which are then decoded in registers with each row's
@@ -127,7 +129,8 @@ __device__ __forceinline__ DxProj select_dx(const DxArgs& a, int idx) {
 // V [256][RP] holds the bf16 adapter rows of the tile's columns (B rows, or A columns).
 // acc += hi . V^T + lo . V^T runs on the MFMA units with K = RP (the rank padded to 16
 // with zeros), writing straight into the accumulators.
-template <int MI>
+// TR: the accumulators hold the transposed tile (MFMA A operand = adapter rows, B = U).
+template <int MI, bool TR = false>
 __device__ __forceinline__ void rank_update(floatx16 (&acc)[MI][2], const uint16_t* Uh, const uint16_t* Ul,
                                             const uint16_t* V, int RP, int l32, int h, int nc0, int nc1,
                                             int row0 = 0) {
@@ -139,10 +142,17 @@ __device__ __forceinline__ void rank_update(floatx16 (&acc)[MI][2], const uint16
       const int row = row0 + 32 * i + l32;
       const bf16x8 ah = *(const bf16x8*)&Uh[row * RP + ks + 8 * h];
       const bf16x8 al = *(const bf16x8*)&Ul[row * RP + ks + 8 * h];
-      acc[i][0] = mfma32(ah, b0, acc[i][0]);
-      acc[i][1] = mfma32(ah, b1, acc[i][1]);
-      acc[i][0] = mfma32(al, b0, acc[i][0]);
-      acc[i][1] = mfma32(al, b1, acc[i][1]);
+      if (TR) {
+        acc[i][0] = mfma32(b0, ah, acc[i][0]);
+        acc[i][1] = mfma32(b1, ah, acc[i][1]);
+        acc[i][0] = mfma32(b0, al, acc[i][0]);
+        acc[i][1] = mfma32(b1, al, acc[i][1]);
+      } else {
+        acc[i][0] = mfma32(ah, b0, acc[i][0]);
+        acc[i][1] = mfma32(ah, b1, acc[i][1]);
+        acc[i][0] = mfma32(al, b0, acc[i][0]);
+        acc[i][1] = mfma32(al, b1, acc[i][1]);
+      }
     }
   }
 }
@@ -189,41 +199,31 @@ struct CodeSet {
 // NW = 4: each wave owns 64 columns x all BM rows (one wave per SIMD).  NW = 8: two waves
 // per column group, each on half of the rows (two waves per SIMD: more latency hiding for
 // grids of less than one tile per compute unit; each code is decoded by both waves).
+// LDS bytes of one ring stage: an activation tile, or (LoRA staging before the K loop,
+// spread over three stages: hi, lo, adapter rows) a 64-rank slab
+constexpr int fwd_stage_bytes(int BM) {
+  return BM * BK * 2 > BN * LNF4_EPI_RANK * 2 ? BM * BK * 2 : BN * LNF4_EPI_RANK * 2;
+}
+
+// One BM x 256 output tile (tm, tn); sm0..sm3 are the ring stages (fwd_stage_bytes(BM)
+// each), lut2 the byte-pair code table, filled by the caller.
 template <int BM, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
+__device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn, uint8_t* sm0, uint8_t* sm1,
+                                             uint8_t* sm2, uint8_t* sm3, const float2* lut2) {
   constexpr int NT = 64 * NW;
   constexpr int WM = NW / 4;          // waves sharing a column group
   constexpr int MI = BM / 32 / WM;    // 32-row MFMA tiles per wave
   constexpr int MH = MI / 2;          // MFMA rows of the first half-step
   constexpr int X_BYTES = BM * BK * 2;
-  // LoRA staging (before the K loop) spreads over three stages (hi, lo, adapter rows), so
-  // each stage holds at least a 64-rank slab
-  constexpr int EPI_SLAB = BN * LNF4_EPI_RANK * 2;
-  constexpr int STAGE = X_BYTES > EPI_SLAB ? X_BYTES : EPI_SLAB;
-  static_assert(4 * STAGE + 2048 <= 160 * 1024, "LDS budget");
   static_assert(MI % 2 == 0, "two half-steps");
-  // four distinct LDS objects, one per ring stage: the compiler then knows which
-  // direct-to-LDS loads each LDS read can alias and never waits for the loads still
-  // streaming into the other stages
-  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sm3[STAGE];
-  // byte-pair code table: entry b = (T[b >> 4], T[b & 15]), the fp32 levels of the two
-  // codes one byte holds (high nibble first)
-  __shared__ __attribute__((aligned(2048))) float2 lut2[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  if (tid < 256) lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);
   const int wn = wave & 3;                    // column group
   const int rbase = (wave >> 2) * (BM / WM);  // first tile row of this wave
 
-  int tm, tn;
-  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
-  tn += args.tn_base;
   int pi = 0;
 #pragma unroll
   for (int q = 1; q < kMaxGroup; ++q)
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
       V[idx] = (n < out_f && kk < r) ? P.B[(size_t)n * r + kk] : (uint16_t)0;
     }
     __syncthreads();
-    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1, rbase);
+    rank_update<MI, true>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1, rbase);
     __syncthreads();
   }
 
@@ -373,8 +373,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
       if (s < 2) { LNF4_Q_XLOAD(kl_, SP, s); }                                                 \
       if (s == 2) LNF4_Q_WLOAD((KB) + 3, CL);                                                  \
       _Pragma("unroll") for (int i = 0; i < MH; ++i) {                                         \
-        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
-        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+        acc[i][0] = mfma32(bc0, ac[i], acc[i][0]);                                             \
+        acc[i][1] = mfma32(bc1, ac[i], acc[i][1]);                                             \
       }                                                                                        \
       /* first half: table addresses and reads, then activation reads and loads */            \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
@@ -390,8 +390,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
       }                                                                                        \
       __builtin_amdgcn_sched_barrier(0);                                                       \
       _Pragma("unroll") for (int i = MH; i < MI; ++i) {                                        \
-        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
-        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+        acc[i][0] = mfma32(bc0, ac[i], acc[i][0]);                                             \
+        acc[i][1] = mfma32(bc1, ac[i], acc[i][1]);                                             \
       }                                                                                        \
       LNF4_FIN8(bn0, l0, (s < 3 ? CC.a0 : CN.a0));                                             \
       LNF4_FIN8(bn1, l1, (s < 3 ? CC.a1 : CN.a1));                                             \
@@ -440,22 +440,72 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
 #undef LNF4_XS
 #undef LNF4_AFRAG
 
-  // ---- store bf16
-  const int n0g = nloc0 + nc0, n1g = nloc0 + nc1;
+  // ---- store bf16.  The accumulators hold the transposed tile: lane (l32, h) has token
+  // rbase + 32i + l32 and, for q = 4g..4g+3, the four adjacent outputs 32j + 8g + 4h + 0..3
+  // of its column group, so each group of four goes out as one 8-byte store.
+  const bool vec4 = (out_f & 3) == 0;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     __builtin_amdgcn_sched_barrier(0);  // bound the accumulator reads that are live at once
+    const int gm = m0 + rbase + 32 * i + l32;
+    if (gm >= M) continue;
+    uint16_t* yr = P.y + (size_t)gm * out_f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = rbase + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-      const int gm = m0 + row;
-      if (gm >= M) continue;
-      const float v0 = acc[i][0][q], v1 = acc[i][1][q];
-      uint16_t* yr = P.y + (size_t)gm * out_f;
-      if (n0g < out_f) yr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
-      if (n1g < out_f) yr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nloc0 + 64 * wn + 32 * j + 8 * g + 4 * h;
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if (vec4 && n < out_f) {
+          *(uint2*)(yr + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < out_f) yr[n + e] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+        }
+      }
+  }
+}
+
+// Blocks compute BM-row tiles over n_tiles_m x n_tiles_n.  With BM = 256 and 4 waves, a
+// tail of 128-row tiles over the tail_n column panels that follow can be mixed in: a last
+// round of tiles that would leave compute units idle runs as twice as many half-height
+// tiles.  Half of those tiles can be dispatched right after the first half round of full
+// tiles, so half of the compute units run half a tile out of step with the other half and
+// the output stores at the end of each tile do not all hit memory at once.
+template <int BM, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
+  constexpr int STAGE = fwd_stage_bytes(BM);
+  static_assert(4 * STAGE + 2048 <= 160 * 1024, "LDS budget");
+  static_assert(fwd_stage_bytes(128) <= STAGE, "128-row tiles share the ring");
+  // four distinct LDS objects, one per ring stage: the compiler then knows which
+  // direct-to-LDS loads each LDS read can alias and never waits for the loads still
+  // streaming into the other stages
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm3[STAGE];
+  // byte-pair code table: entry b = (T[b >> 4], T[b & 15]), the fp32 levels of the two
+  // codes one byte holds (high nibble first)
+  __shared__ __attribute__((aligned(2048))) float2 lut2[256];
+  const int tid = threadIdx.x;
+  if (tid < 256) lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);
+
+  int tm, tn;
+  int b = blockIdx.x;
+  if constexpr (BM == 256 && NW == 4) {
+    int hb = -1;
+    if (b >= args.split_block) hb = b - args.split_block + args.stag_h;
+    else if (b >= args.stag_f + args.stag_h) b -= args.stag_h;
+    else if (b >= args.stag_f) hb = b - args.stag_f;
+    if (hb >= 0) {
+      tile_coords(hb, args.tail_m, args.tail_n, kGroupM, tm, tn);
+      fwd_nf4_tile<128, 4>(args, tm, tn + args.tn_base + args.n_tiles_n, sm0, sm1, sm2, sm3, lut2);
+      return;
     }
   }
+  tile_coords(b, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  fwd_nf4_tile<BM, NW>(args, tm, tn + args.tn_base, sm0, sm1, sm2, sm3, lut2);
 }
 
 // bf16 weights: the weight tile goes through LDS beside the activation tile (128 bytes per
@@ -1344,6 +1394,8 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   FwdArgs a = a0;
   if (a.M <= 0 || a.n_tiles_n <= 0) return hipSuccess;
   a.tn_base = 0;
+  a.split_block = 0x7fffffff;
+  a.tail_m = a.tail_n = a.stag_f = a.stag_h = 0;
   if (fmt != 0) {
     // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
     a.n_tiles_m = (a.M + 127) / 128;
@@ -1366,26 +1418,30 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
     return hipGetLastError();
   }
   // Several rounds of 256-row tiles whose last round leaves many compute units idle: the
-  // column panels of that last round can run as 128-row tiles in a second launch (a 128-row
-  // tile takes a little over half the time of a 256-row one).  Chosen when the estimated
-  // rounds drop, e.g. 896 tiles = 3.5 rounds on 256 units become 768 + 256 half tiles.
+  // column panels of that last round can run as 128-row tiles, dispatched last in the same
+  // launch (a 128-row tile takes a little over half the time of a 256-row one).  Chosen when
+  // the estimated rounds drop, e.g. 896 tiles = 3.5 rounds on 256 units become 768 + 256
+  // half-height tiles.
   const int rem = t256 % cus;
   const int tail_n = (rem + tm256 - 1) / tm256;
   const int tm128 = (a.M + 127) / 128;
   const int full = t256 - tail_n * tm256;
   const auto rounds = [cus](int tiles) { return (tiles + cus - 1) / cus; };
+  a.n_tiles_m = tm256;
   if (t256 > cus && rem > 0 && full > 0 &&
       rounds(full) + 0.55 * rounds(tm128 * tail_n) < rounds(t256) - 0.2) {
-    a.n_tiles_m = tm256;
     a.n_tiles_n = tn_all - tail_n;
-    hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(tm256 * a.n_tiles_n), dim3(NTHR), 0, s, a);
-    a.n_tiles_m = tm128;
-    a.n_tiles_n = tail_n;
-    a.tn_base = tn_all - tail_n;
-    hipLaunchKernelGGL((k_fwd_nf4<128, 4>), dim3(tm128 * tail_n), dim3(NTHR), 0, s, a);
+    a.tail_m = tm128;
+    a.tail_n = tail_n;
+    const int half = tm128 * tail_n;
+    if (half == cus && full >= cus) {
+      // one round of half tiles: half of the units take theirs first
+      a.stag_f = a.stag_h = cus / 2;
+    }
+    a.split_block = full + a.stag_h;
+    hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(full + half), dim3(NTHR), 0, s, a);
     return hipGetLastError();
   }
-  a.n_tiles_m = tm256;
   hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(t256), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }

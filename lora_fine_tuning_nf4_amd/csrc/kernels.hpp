@@ -31,6 +31,14 @@ struct FwdArgs {
   int32_t n_tiles_n;    // N-tiles covered by this launch
   int32_t n_tiles_m;
   int32_t tn_base;      // first N-tile of this launch in the group's tile space
+  // 128-row tail (set by launch_fwd): tail_m x tail_n tiles over the N-tiles that follow
+  // n_tiles_n.  Blocks [stag_f, stag_f + stag_h) run the first stag_h of them, blocks from
+  // split_block on the rest; all other blocks run the BM-row tiles in order.
+  int32_t split_block;
+  int32_t tail_m;
+  int32_t tail_n;
+  int32_t stag_f;
+  int32_t stag_h;
   FwdProj p[kMaxGroup];
 };
 

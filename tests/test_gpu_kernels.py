@@ -184,19 +184,23 @@ def test_backward_split_k(fmt):
     assert np.array_equal(host_u16(d.dx), first)
 
 
-def test_forward_tail_as_128_row_tiles():
-    # 2 x 136 tiles of 256 x 256 on 256 compute units: the last 8 column panels run as
-    # 128-row tiles in a second launch.  Parity with the oracle, and the tail columns must
-    # equal bit for bit a call on those rows of W alone (same K order, other tile shape).
-    T, out_f, in_f, r = 512, 136 * 256, 128, 8
-    c = make_case(23, T, out_f, in_f, r, 16.0, 0, tag="tail-split")
+@pytest.mark.parametrize("T,n_panels,n_tail", [(512, 136, 8), (1024, 96, 32)])
+def test_forward_tail_as_128_row_tiles(T, n_panels, n_tail):
+    # More than one round of 256 x 256 tiles on 256 compute units with a last round that
+    # would leave units idle: the last n_tail column panels run as 128-row tiles in the same
+    # launch (2 x 136 tiles: 8 panels after the full tiles; 4 x 96 tiles: 32 panels, one
+    # round of half tiles, half of them dispatched first).  Parity with the oracle, and the
+    # tail columns must equal bit for bit a call on those rows of W alone (same K order,
+    # other tile shape).
+    out_f, in_f, r = n_panels * 256, 128, 8
+    c = make_case(23, T, out_f, in_f, r, 16.0, 0, tag=f"tail-split-{T}")
     d = DevCase(c)
     _run_fwd(d)
     sync()
     y_ref, u_ref = oracle_fwd(c)
     check_tol(bf16_f64(host_u16(d.y)), y_ref, "y")
     check_tol(host_f32(d.u)[:T, :r], u_ref, "u")
-    n0 = 128 * 256
+    n0 = (n_panels - n_tail) * 256
     W2 = lnf4.make_weight(0, d.wdata.reshape(-1)[n0 * in_f // 2:], d.absmax.reshape(-1)[n0 * in_f // 64:],
                           out_f - n0, in_f, 64)
     y2 = torch.empty((T, out_f - n0), dtype=torch.int16, device="cuda")
