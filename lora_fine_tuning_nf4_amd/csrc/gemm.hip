@@ -1448,14 +1448,29 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
 
 // Row-tile height of the input-gradient kernels (bf16 weight tiles are 4x the NF4 bytes:
 // their 3-stage ring only fits LDS with 128 rows).
-static int dx_bm(int M, int N, int fmt) { return fmt == 0 ? pick_bm(M, (N + BN - 1) / BN) : 128; }
+// Row tile of the input gradient.  NF4: 256-row tiles decode each weight element half as
+// often per MFMA as 128-row tiles; when they are too few to fill the compute units, K splits
+// make up the count (dx_split_count).  Kept only where every split still runs at least 64
+// K-blocks: shorter splits lose more to the fp32 partials and the per-tile start than the
+// decode saves (measured: gate|up of the 8B shape, K = 28672, 2 splits: 17 % faster;
+// K = 4096 or 9728 in 2 or 8 splits: slower).  bf16 weight tiles only fit LDS with 128 rows.
+static int dx_bm(int M, int N, int total_kb, int fmt) {
+  if (fmt != 0) return 128;
+  const int tn = (N + BN - 1) / BN;
+  if (pick_bm(M, tn) == 256) return 256;
+  if (M <= 128) return 128;
+  const int tiles = ((M + 255) / 256) * tn;
+  int ns = (256 + tiles - 1) / tiles;
+  ns = ns > 8 ? 8 : ns;
+  return total_kb / ns >= 64 ? 256 : 128;
+}
 
 // Splits of the K space for the input gradient: when the tiles cover less than 3/4 of the
 // compute units, split K so that about one wave of workgroups runs, keeping at least 16
 // K-blocks per split (at most 8 splits).
 int dx_split_count(int M, int N, int total_kb, int fmt) {
   if (M <= 0 || N <= 0 || total_kb <= 0) return 1;
-  const int bm = dx_bm(M, N, fmt);
+  const int bm = dx_bm(M, N, total_kb, fmt);
   const int tiles = ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
   if (tiles >= 192) return 1;
   int ns = (256 + tiles - 1) / tiles;
@@ -1474,7 +1489,7 @@ hipError_t launch_dx(const DxArgs& a0, int fmt, hipStream_t s) {
   DxArgs a = a0;
   if (a.M <= 0 || a.N <= 0 || a.total_kb <= 0) return hipSuccess;
   a.n_tiles_n = (a.N + BN - 1) / BN;
-  const int bm = dx_bm(a.M, a.N, fmt);
+  const int bm = dx_bm(a.M, a.N, a.total_kb, fmt);
   a.n_tiles_m = (a.M + bm - 1) / bm;
   const int ns = a.part != nullptr ? dx_split_count(a.M, a.N, a.total_kb, fmt) : 1;
   a.kb_per_split = (a.total_kb + ns - 1) / ns;

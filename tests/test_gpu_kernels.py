@@ -155,11 +155,12 @@ def test_accumulate_adds_to_existing():
     check_tol(host_f32(d.dB)[:, :8], dB1[:, :8] + dB_ref, "dB accumulated")
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
-def test_backward_split_k(fmt):
+@pytest.mark.parametrize("fmt,out_f", [(0, 2048), (1, 2048), (0, 32768)])
+def test_backward_split_k(fmt, out_f):
     # few output tiles and a long K space: the dx GEMM splits K (fp32 sums per split, then a
-    # fixed-order sum); checked alone and accumulating into the existing dx
-    c = make_case(19, 256, 2048, 256, 8, 16.0, fmt, tag="split-k")
+    # fixed-order sum); checked alone and accumulating into the existing dx.  K = 2048: 128-row
+    # tiles; NF4 with K = 32768: 256-row tiles in 8 splits of 64 K-blocks
+    c = make_case(19, 256, out_f, 256, 8, 16.0, fmt, tag=f"split-k-{out_f}")
     d = DevCase(c)
     _run_bwd(d)
     sync()
