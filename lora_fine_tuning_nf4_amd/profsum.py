@@ -27,7 +27,7 @@ import os
 import sys
 
 DOM_NAME = "k_fwd_nf4<256, 4>"
-DOM_GRID = 896 * 256
+DOM_GRID = (768 + 256) * 256  # threads: 768 tiles of 256 x 256 and 256 tiles of 128 x 256
 CAL_NAME = "neg_kernel"
 CAL_BYTES = 256 << 20
 
