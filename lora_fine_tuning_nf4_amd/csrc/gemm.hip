@@ -838,7 +838,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       off += r;
     }
     __syncthreads();
-    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+    rank_update<MI, true>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
     __syncthreads();
   }
 
@@ -1008,8 +1008,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
       }                                                                                        \
       if (s < 3) LNF4_DXQ_ISSUE_PART(SP, s);                                                   \
       _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
-        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
-        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+        acc[i][0] = mfma32(bc0, ac[i], acc[i][0]);                                             \
+        acc[i][1] = mfma32(bc1, ac[i], acc[i][1]);                                             \
       }                                                                                        \
       LNF4_FIN8X(bn0, l0, a);                                                                  \
       LNF4_FIN8X(bn1, l1, a);                                                                  \
@@ -1072,40 +1072,79 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #undef LNF4_FIN8X
 #undef LNF4_XS
 
-  // ---- store bf16 (optionally accumulating into the existing dx)
-  const int n0g = n0 + nc0, n1g = n0 + nc1;
-  const bool c0ok = n0g < N, c1ok = n1g < N;
-  if (args.part != nullptr) {  // split-K: this split's fp32 sums, added up by k_dx_split_sum
-    float* pp = args.part + (size_t)split * M * N;
+  // ---- store.  The decoded weights are the MFMA's A operand, so the accumulators hold the
+  // tile transposed: lane (l32, h) has token 32i + l32 and, for q = 4g..4g+3, accumulator
+  // rows 8g + 4h + 0..3, i.e. tile columns 64 wave + 32j + 8g + 4h + (e ^ 1) for e = 0..3
+  // (a lane's weight column is l32 ^ 1, see the header comment).  Rows go out through LDS
+  // in passes of 64: each wave stages its 64 columns of them as fp32 (16-byte chunk c of row
+  // r at c ^ (r & 15)) and reads back whole rows, 16 lanes per row, so every store covers
+  // full 128-byte lines of the output.  fp32 staging keeps one rounding when accumulating.
+  const int n_w = n0 + 64 * wave;
+  float* const pp = args.part != nullptr ? args.part + (size_t)split * M * N : nullptr;
+  if (pp != nullptr || (((uintptr_t)args.dx) & 7) == 0) {
+    LNF4_WAIT_VM_LGKM0(0);  // the ring's last (past-the-end) loads have landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* const rg = (wave < 2 ? sm0 : sm1) + (wave & 1) * 16384;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
+    for (int pass = 0; pass < MI / 2; ++pass) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (gm >= M) continue;
-        if (c0ok) pp[(size_t)gm * N + n0g] = acc[i][0][q];
-        if (c1ok) pp[(size_t)gm * N + n1g] = acc[i][1][q];
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * pass + ii, row = 32 * ii + l32;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int pc = (8 * j + 2 * g + h) ^ (row & 15);
+            floatx4 v;
+            v[0] = acc[i][j][4 * g + 1];
+            v[1] = acc[i][j][4 * g];
+            v[2] = acc[i][j][4 * g + 3];
+            v[3] = acc[i][j][4 * g + 2];
+            *(floatx4*)(rg + row * 256 + pc * 16) = v;
+          }
       }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_sched_barrier(0);
+      const int c = lane & 15, n = n_w + 4 * c;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int row = 4 * k + (lane >> 4);
+        floatx4 v = *(const floatx4*)(rg + row * 256 + ((c ^ (row & 15)) * 16));
+        const int gm = m0 + 64 * pass + row;
+        if (gm >= M || n >= N) continue;
+        if (pp != nullptr) {
+          *(floatx4*)(pp + (size_t)gm * N + n) = v;
+        } else {
+          uint16_t* d = args.dx + (size_t)gm * N + n;
+          if (args.accumulate) {
+            const uint2 o = *(const uint2*)d;
+            v[0] += bf16_lo(o.x); v[1] += bf16_hi(o.x); v[2] += bf16_lo(o.y); v[3] += bf16_hi(o.y);
+          }
+          *(uint2*)d = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     return;
   }
+  // dx only 2-byte aligned: element by element
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     __builtin_amdgcn_sched_barrier(0);
+    const int gm = m0 + 32 * i + l32;
+    if (gm >= M) continue;
+    uint16_t* dr = args.dx + (size_t)gm * N;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-      if (gm >= M) continue;
-      uint16_t* dr = args.dx + (size_t)gm * N;
-      float v0 = acc[i][0][q], v1 = acc[i][1][q];
-      if (args.accumulate) {
-        if (c0ok) v0 += bf16_to_f32(dr[n0g]);
-        if (c1ok) v1 += bf16_to_f32(dr[n1g]);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int n = n_w + 32 * j + 8 * (q >> 2) + 4 * h + ((q & 3) ^ 1);
+        if (n >= N) continue;
+        float v = acc[i][j][q];
+        if (args.accumulate) v += bf16_to_f32(dr[n]);
+        dr[n] = __builtin_bit_cast(uint16_t, (__bf16)v);
       }
-      if (c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
-      if (c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
-    }
   }
 }
 
