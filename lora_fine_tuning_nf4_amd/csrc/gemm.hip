@@ -25,6 +25,9 @@
 //    row-major by direct loads and is read back transposed by gfx950's transposing LDS
 //    reads (4-bit for the codes, which are then decoded in registers with each row's
 //    absmax; 16-bit for bf16 weights), so each lane gets 8 consecutive K of one column.
+//    For NF4 the decoded weights are again the A operand (transposed accumulators).
+//  * Both NF4 kernels write their output through LDS: each wave stages its 64 columns of a
+//    group of rows and stores whole 128-byte lines of the output.
 #include "common.hpp"
 #include "kernels.hpp"
 
