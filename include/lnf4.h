@@ -453,7 +453,45 @@ int stream_log(const lnf4_stream* st, lnf4_stream_event* ev, int32_t cap, int32_
 /* Bytes copied host-to-device by this context since creation (layers + slot). */
 int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes);
 
-/* Release the context and its events.  NULL is accepted; safe to call once per object. */
+/*
+ * Disk tier (Soup deep dive, "Core feature: how layer streaming works" and its table of
+ * streaming settings: when host RAM is short the frozen shards are read from an NVMe
+ * file, and a read-ahead depth of 1..8 layers sets how many are staged in pinned RAM
+ * ahead of the copies).  A ring-mode stream (LNF4_STREAM_RING rules above) whose layer
+ * copies come from `path` instead of host shards:
+ *   file_offsets  n_shards byte offsets of the shards in the file (only scheduled shards
+ *                 are read)
+ *   drop_cache    nonzero: each shard's pages are dropped from the page cache after its
+ *                 read (posix_fadvise DONTNEED), so every pass reads the device and not
+ *                 host RAM.  (O_DIRECT reads cannot target HIP page-locked memory.)
+ *   stage_bufs    n_stage (1..8, the read-ahead depth) page-locked staging buffers of
+ *                 stage_bytes each, caller-owned
+ *   host_shards   NULL, or n_shards page-locked pointers with NULL entries allowed: only
+ *                 shards with a host copy can be loaded into the slot
+ *   the rest      as in stream_create (ring mode)
+ * A reader thread owned by the context walks the schedule positions g = 0, 1, ... (on
+ * across passes) and reads position g's shard into staging buffer g mod n_stage once the
+ * copy out of that buffer for position g - n_stage has completed; the copy of position g
+ * is issued (inside stream_layer_step) once its read is done, so stream_layer_step may
+ * block on the reader.  No GPU work waits on the host.  A failed read is reported by the
+ * stream_layer_step call that needs it (EINVAL, with the errno text).  The file must stay
+ * unchanged while the context lives.
+ * Errors: EINVAL (NULL arguments, n_stage outside 1..8, cannot open the file, a staging
+ * buffer not page-locked), ESHAPE (a shard larger than stage_bytes or past the end of the
+ * file, and stream_create's), EALIGN (stream_create's), EHIP.
+ */
+int stream_create_disk(const char* path, const int64_t* file_offsets, int32_t drop_cache, void* const* stage_bufs,
+                       size_t stage_bytes, int32_t n_stage, const void* const* host_shards, const size_t* shard_bytes,
+                       int32_t n_shards, void* const* dev_bufs, size_t buf_bytes, int32_t n_bufs,
+                       const int32_t* schedule, int32_t sched_len, hipStream_t copy_stream, void* slot_buf,
+                       size_t slot_bytes, lnf4_stream** out);
+
+/* Disk tier only: bytes read from the file so far and the reader's time inside the reads
+ * (seconds), for the disk's achieved rate.  Errors: EINVAL (no disk tier), ESTATE. */
+int stream_disk_stats(const lnf4_stream* st, int64_t* bytes_read, double* read_seconds);
+
+/* Release the context and its events (and a disk tier's reader thread, after the reads
+ * and copies in flight).  NULL is accepted; safe to call once per object. */
 int stream_destroy(lnf4_stream* st);
 
 #ifdef __cplusplus

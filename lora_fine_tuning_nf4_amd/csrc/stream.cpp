@@ -17,16 +17,53 @@
 // the forward/backward turn, the first layers at the start of the next step) uses it
 // with no copy; otherwise its shard is copied into the least recently used buffer, after
 // that buffer's last user is released.
+//
+// Disk tier (the Soup deep dive, "how layer streaming works" and its table of streaming
+// settings: frozen shards read from NVMe when host RAM is short, with a read-ahead depth
+// of 1..8 layers, each step of depth costing one layer of pinned RAM): a reader thread
+// walks the schedule, position g = pass * sched_len + j on across passes, and reads shard
+// sched[j] from the file into pinned staging buffer g mod n_stage once the copy out of
+// that buffer for position g - n_stage has completed (its event, recorded when that copy
+// was issued).  The ring's copy of position g is issued once that read is done.  The only
+// waits are host waits on the reader and the reader's waits on copy events; no GPU work
+// waits on the host.
+#include <fcntl.h>
 #include <hip/hip_runtime.h>
+#include <sys/stat.h>
+#include <unistd.h>
 
+#include <cerrno>
+#include <chrono>
+#include <condition_variable>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "abi_internal.hpp"
 #include "lnf4.h"
 
 using namespace lnf4;
+
+struct DiskTier {
+  int fd = -1;
+  bool drop_cache = false;          // drop each shard's pages from the page cache after its read
+  std::vector<int64_t> off;         // file offset of each shard
+  std::vector<void*> stage;         // n_stage pinned staging buffers (caller-owned)
+  size_t stage_bytes = 0;
+  std::vector<hipEvent_t> stage_ev; // recorded after the copy out of each staging buffer
+  std::thread reader;
+  std::mutex mu;
+  std::condition_variable cv;
+  long read_done = 0;               // positions whose read has finished (or failed)
+  long issued = 0;                  // positions whose copy has been enqueued
+  bool stop = false;
+  int err = 0;                      // first error: errno of a failed read, -1 a HIP wait
+  long err_pos = -1;
+  double read_seconds = 0.0;        // time spent in pread
+  int64_t bytes_read = 0;
+};
 
 struct lnf4_stream {
   std::vector<const void*> host;
@@ -61,6 +98,7 @@ struct lnf4_stream {
   std::vector<int> holder;
   std::vector<long> last_tick;
   long tick = 0;
+  DiskTier* disk = nullptr;  // ring mode only: layer shards come from a file
 };
 
 // Plan one pass in reuse mode from what the buffers hold now.  Position j: if a buffer
@@ -124,6 +162,99 @@ static void destroy_events(lnf4_stream* st) {
   st->slot_release = st->slot_done = nullptr;
 }
 
+// Reader thread of the disk tier (see the header comment).
+static void disk_reader(lnf4_stream* st) {
+  DiskTier* d = st->disk;
+  const long n = (long)st->sched.size();
+  const long ns = (long)d->stage.size();
+  for (long g = 0;; ++g) {
+    const int s = (int)(g % ns);
+    {
+      std::unique_lock<std::mutex> lk(d->mu);
+      d->cv.wait(lk, [&] { return d->stop || d->issued > g - ns; });
+      if (d->stop) return;
+    }
+    int err = 0;
+    // the copy out of this staging buffer for position g - ns was issued (above); wait
+    // until it has read the buffer
+    if (g >= ns && hipEventSynchronize(d->stage_ev[s]) != hipSuccess) err = -1;
+    const int shard = st->sched[g % n];
+    const size_t want = st->bytes[shard];
+    size_t got = 0;
+    const auto t0 = std::chrono::steady_clock::now();
+    while (!err && got < want) {
+      const ssize_t r = pread(d->fd, (char*)d->stage[s] + got, want - got, (off_t)(d->off[shard] + (int64_t)got));
+      if (r < 0) {
+        if (errno == EINTR) continue;
+        err = errno ? errno : EIO;
+      } else if (r == 0) {
+        err = EIO;  // the file ends inside the shard
+      } else {
+        got += (size_t)r;
+      }
+    }
+    // (the pages of a file that is being read are clean, so they can be dropped at once)
+    if (d->drop_cache) (void)posix_fadvise(d->fd, (off_t)d->off[shard], (off_t)want, POSIX_FADV_DONTNEED);
+    const double secs = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    {
+      std::lock_guard<std::mutex> lk(d->mu);
+      if (err && !d->err) {
+        d->err = err;
+        d->err_pos = g;
+      }
+      d->read_done = g + 1;
+      d->read_seconds += secs;
+      d->bytes_read += (int64_t)(got < want ? got : want);
+    }
+    d->cv.notify_all();
+  }
+}
+
+static void disk_close(lnf4_stream* st) {
+  DiskTier* d = st->disk;
+  if (!d) return;
+  if (d->reader.joinable()) {
+    {
+      std::lock_guard<std::mutex> lk(d->mu);
+      d->stop = true;
+    }
+    d->cv.notify_all();
+    d->reader.join();
+  }
+  for (hipEvent_t e : d->stage_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (d->fd >= 0) close(d->fd);
+  delete d;
+  st->disk = nullptr;
+}
+
+// Disk tier: copy schedule position g (whose shard is `shard`) into layer buffer `buf`
+// from its staging buffer, once the reader has filled it.
+static int disk_copy_into(lnf4_stream* st, int buf, int shard, long g) {
+  DiskTier* d = st->disk;
+  const int s = (int)(g % (long)d->stage.size());
+  {
+    std::unique_lock<std::mutex> lk(d->mu);
+    d->cv.wait(lk, [&] { return d->read_done > g; });
+    if (d->err) {
+      if (d->err < 0) return fail(LNF4_EHIP, "stream (disk tier): the reader's wait for a staging copy failed");
+      return fail(LNF4_EINVAL, "stream (disk tier): reading schedule position %ld (shard %d) failed: %s", d->err_pos,
+                  (int)st->sched[d->err_pos % (long)st->sched.size()], std::strerror(d->err));
+    }
+  }
+  hipError_t e = hipMemcpyAsync(st->bufs[buf], d->stage[s], st->bytes[shard], hipMemcpyHostToDevice, st->copy);
+  if (e != hipSuccess) return hip_fail(e, "stream: hipMemcpyAsync (staging buffer -> layer buffer)");
+  if ((e = hipEventRecord(d->stage_ev[s], st->copy)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(stage)");
+  if ((e = hipEventRecord(st->copy_done[buf], st->copy)) != hipSuccess) return hip_fail(e, "stream: hipEventRecord(copy_done)");
+  st->bytes_copied += (int64_t)st->bytes[shard];
+  {
+    std::lock_guard<std::mutex> lk(d->mu);
+    d->issued = g + 1;
+  }
+  d->cv.notify_all();
+  return LNF4_OK;
+}
+
 static int copy_into(lnf4_stream* st, int buf, int shard) {
   hipError_t e = hipMemcpyAsync(st->bufs[buf], st->host[shard], st->bytes[shard], hipMemcpyHostToDevice, st->copy);
   if (e != hipSuccess) return hip_fail(e, "stream: hipMemcpyAsync (host shard -> layer buffer)");
@@ -133,17 +264,17 @@ static int copy_into(lnf4_stream* st, int buf, int shard) {
   return LNF4_OK;
 }
 
-extern "C" {
-
-int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards, void* const* dev_bufs,
-                  size_t buf_bytes, int32_t n_bufs, const int32_t* schedule, int32_t sched_len, int32_t mode,
-                  hipStream_t copy_stream, void* slot_buf, size_t slot_bytes, lnf4_stream** out) {
-  const char* who = "stream_create";
+// host_optional (disk tier): host_shards may be NULL or hold NULL entries (shards with no
+// host copy); the entries given must still be page-locked.
+static int create_impl(const char* who, const void* const* host_shards, bool host_optional, const size_t* shard_bytes,
+                       int32_t n_shards, void* const* dev_bufs, size_t buf_bytes, int32_t n_bufs,
+                       const int32_t* schedule, int32_t sched_len, int32_t mode, hipStream_t copy_stream,
+                       void* slot_buf, size_t slot_bytes, lnf4_stream** out) {
   if (!out) return fail(LNF4_EINVAL, "%s: out is NULL", who);
   *out = nullptr;
   if (mode < 0 || mode > 2) return fail(LNF4_EINVAL, "%s: mode=%d (0 ring, 1 resident, 2 ring with reuse)", who, (int)mode);
   const int32_t resident = mode == 1;
-  if (!host_shards || !shard_bytes || !dev_bufs || !schedule) return fail(LNF4_EINVAL, "%s: NULL array", who);
+  if ((!host_shards && !host_optional) || !shard_bytes || !dev_bufs || !schedule) return fail(LNF4_EINVAL, "%s: NULL array", who);
   if (n_shards < 1 || n_shards > (1 << 20)) return fail(LNF4_EINVAL, "%s: n_shards=%d out of range", who, (int)n_shards);
   if (resident) {
     if (n_bufs != n_shards) return fail(LNF4_EINVAL, "%s: resident mode needs n_bufs == n_shards (%d != %d)", who, (int)n_bufs, (int)n_shards);
@@ -153,7 +284,7 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
   if (sched_len < 1 || sched_len > (1 << 24)) return fail(LNF4_EINVAL, "%s: sched_len=%d out of range", who, (int)sched_len);
   if (buf_bytes == 0) return fail(LNF4_ESHAPE, "%s: buf_bytes is 0", who);
   for (int s = 0; s < n_shards; ++s) {
-    if (!host_shards[s]) return fail(LNF4_EINVAL, "%s: host shard %d is NULL", who, s);
+    if (!host_optional && !host_shards[s]) return fail(LNF4_EINVAL, "%s: host shard %d is NULL", who, s);
     if (shard_bytes[s] == 0) return fail(LNF4_ESHAPE, "%s: shard %d is empty", who, s);
   }
   for (int b = 0; b < n_bufs; ++b) {
@@ -179,6 +310,7 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
   }
   // host memory must be page-locked, so that copies are true asynchronous DMA
   for (int s = 0; s < n_shards; ++s) {
+    if (!host_shards || !host_shards[s]) continue;  // (host_optional only, checked above)
     hipPointerAttribute_t attr;
     std::memset(&attr, 0, sizeof attr);
     hipError_t e = hipPointerGetAttributes(&attr, host_shards[s]);
@@ -189,7 +321,10 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
   }
   lnf4_stream* st = new (std::nothrow) lnf4_stream();
   if (!st) return fail(LNF4_EINVAL, "%s: out of host memory", who);
-  st->host.assign(host_shards, host_shards + n_shards);
+  if (host_shards)
+    st->host.assign(host_shards, host_shards + n_shards);
+  else
+    st->host.assign(n_shards, nullptr);
   st->bytes.assign(shard_bytes, shard_bytes + n_shards);
   st->bufs.assign(dev_bufs, dev_bufs + n_bufs);
   st->buf_bytes = buf_bytes;
@@ -225,6 +360,107 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
     }
   }
   *out = st;
+  return LNF4_OK;
+}
+
+extern "C" {
+
+int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards, void* const* dev_bufs,
+                  size_t buf_bytes, int32_t n_bufs, const int32_t* schedule, int32_t sched_len, int32_t mode,
+                  hipStream_t copy_stream, void* slot_buf, size_t slot_bytes, lnf4_stream** out) {
+  return create_impl("stream_create", host_shards, false, shard_bytes, n_shards, dev_bufs, buf_bytes, n_bufs,
+                     schedule, sched_len, mode, copy_stream, slot_buf, slot_bytes, out);
+}
+
+int stream_create_disk(const char* path, const int64_t* file_offsets, int32_t drop_cache, void* const* stage_bufs,
+                       size_t stage_bytes, int32_t n_stage, const void* const* host_shards, const size_t* shard_bytes,
+                       int32_t n_shards, void* const* dev_bufs, size_t buf_bytes, int32_t n_bufs,
+                       const int32_t* schedule, int32_t sched_len, hipStream_t copy_stream, void* slot_buf,
+                       size_t slot_bytes, lnf4_stream** out) {
+  const char* who = "stream_create_disk";
+  if (!out) return fail(LNF4_EINVAL, "%s: out is NULL", who);
+  *out = nullptr;
+  if (!path || !file_offsets || !stage_bufs || !shard_bytes || !schedule) return fail(LNF4_EINVAL, "%s: NULL argument", who);
+  if (n_stage < 1 || n_stage > 8) return fail(LNF4_EINVAL, "%s: n_stage=%d outside 1..8", who, (int)n_stage);
+  if (n_shards < 1 || n_shards > (1 << 20)) return fail(LNF4_EINVAL, "%s: n_shards=%d out of range", who, (int)n_shards);
+  if (sched_len < 1 || sched_len > (1 << 24)) return fail(LNF4_EINVAL, "%s: sched_len=%d out of range", who, (int)sched_len);
+  for (int i = 0; i < n_stage; ++i)
+    if (!stage_bufs[i]) return fail(LNF4_EINVAL, "%s: staging buffer %d is NULL", who, i);
+  for (int k = 0; k < sched_len; ++k) {
+    const int s = schedule[k];
+    if (s < 0 || s >= n_shards) return fail(LNF4_EINVAL, "%s: schedule[%d]=%d outside 0..%d", who, k, s, (int)n_shards - 1);
+    if (file_offsets[s] < 0) return fail(LNF4_EINVAL, "%s: file offset of shard %d is negative", who, s);
+    if (shard_bytes[s] > stage_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds stage_bytes %zu", who, s, shard_bytes[s], stage_bytes);
+  }
+  const int fd = open(path, O_RDONLY | O_CLOEXEC);
+  if (fd < 0) return fail(LNF4_EINVAL, "%s: cannot open %s: %s", who, path, std::strerror(errno));
+  struct stat sb;
+  if (fstat(fd, &sb) != 0) {
+    close(fd);
+    return fail(LNF4_EINVAL, "%s: cannot stat %s", who, path);
+  }
+  for (int k = 0; k < sched_len; ++k) {
+    const int s = schedule[k];
+    if (file_offsets[s] + (int64_t)shard_bytes[s] > (int64_t)sb.st_size) {
+      close(fd);
+      return fail(LNF4_ESHAPE, "%s: shard %d ends past the end of %s", who, s, path);
+    }
+  }
+  lnf4_stream* st = nullptr;
+  int rc = create_impl(who, host_shards, true, shard_bytes, n_shards, dev_bufs, buf_bytes, n_bufs, schedule, sched_len,
+                       LNF4_STREAM_RING, copy_stream, slot_buf, slot_bytes, &st);
+  if (rc) {
+    close(fd);
+    return rc;
+  }
+  for (int i = 0; i < n_stage; ++i) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t e = hipPointerGetAttributes(&attr, stage_bufs[i]);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      close(fd);
+      stream_destroy(st);
+      return fail(LNF4_EINVAL, "%s: staging buffer %d is not page-locked host memory", who, i);
+    }
+  }
+  DiskTier* d = new (std::nothrow) DiskTier();
+  if (!d) {
+    close(fd);
+    stream_destroy(st);
+    return fail(LNF4_EINVAL, "%s: out of host memory", who);
+  }
+  d->fd = fd;
+  d->drop_cache = drop_cache != 0;
+  d->off.assign(file_offsets, file_offsets + n_shards);
+  d->stage.assign(stage_bufs, stage_bufs + n_stage);
+  d->stage_bytes = stage_bytes;
+  d->stage_ev.assign(n_stage, nullptr);
+  st->disk = d;
+  for (int i = 0; i < n_stage; ++i) {
+    hipError_t e = hipEventCreateWithFlags(&d->stage_ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      stream_destroy(st);
+      return hip_fail(e, "stream_create_disk: hipEventCreate");
+    }
+  }
+  try {
+    d->reader = std::thread(disk_reader, st);
+  } catch (...) {
+    stream_destroy(st);
+    return fail(LNF4_EINVAL, "%s: cannot start the reader thread", who);
+  }
+  *out = st;
+  return LNF4_OK;
+}
+
+int stream_disk_stats(const lnf4_stream* st, int64_t* bytes_read, double* read_seconds) {
+  if (!st || !st->alive) return fail(LNF4_ESTATE, "stream_disk_stats: stream context is NULL or destroyed");
+  if (!st->disk) return fail(LNF4_EINVAL, "stream_disk_stats: the context has no disk tier");
+  if (!bytes_read || !read_seconds) return fail(LNF4_EINVAL, "stream_disk_stats: NULL output");
+  std::lock_guard<std::mutex> lk(st->disk->mu);
+  *bytes_read = st->disk->bytes_read;
+  *read_seconds = st->disk->read_seconds;
   return LNF4_OK;
 }
 
@@ -292,7 +528,7 @@ int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** de
     // last user of b in the previous pass
     if (st->release_recorded[b])
       if ((e = hipStreamWaitEvent(st->copy, st->release[b], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(release)");
-    if ((rc = copy_into(st, b, layer))) return rc;
+    if ((rc = st->disk ? disk_copy_into(st, b, layer, (long)st->pass * n + j) : copy_into(st, b, layer))) return rc;
     log_ev(st, LNF4_EV_COPY, k, j, layer, b, j >= nb ? j - nb : -1);
     st->issued = j + 1;
   }
@@ -309,6 +545,7 @@ int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute) {
   if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
   if (shard < 0 || shard >= (int)st->host.size()) return fail(LNF4_EINVAL, "%s: shard %d out of range", who, (int)shard);
+  if (!st->host[shard]) return fail(LNF4_EINVAL, "%s: shard %d has no host copy (the disk tier streams the layer schedule only)", who, (int)shard);
   if (st->bytes[shard] > st->slot_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds the slot (%zu)", who, (int)shard, st->bytes[shard], st->slot_bytes);
   if (st->slot_part_next != 0) return fail(LNF4_ESTATE, "%s: a part-wise slot load is under way", who);
   hipError_t e;
@@ -329,6 +566,7 @@ int stream_slot_load_part(lnf4_stream* st, int32_t shard, int32_t part, int32_t 
   if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
   if (shard < 0 || shard >= (int)st->host.size()) return fail(LNF4_EINVAL, "%s: shard %d out of range", who, (int)shard);
+  if (!st->host[shard]) return fail(LNF4_EINVAL, "%s: shard %d has no host copy (the disk tier streams the layer schedule only)", who, (int)shard);
   if (n_parts < 1 || n_parts > 1024 || part < 0 || part >= n_parts)
     return fail(LNF4_EINVAL, "%s: part %d of %d out of range (1 <= n_parts <= 1024)", who, (int)part, (int)n_parts);
   if (st->bytes[shard] > st->slot_bytes) return fail(LNF4_ESHAPE, "%s: shard %d (%zu bytes) exceeds the slot (%zu)", who, (int)shard, st->bytes[shard], st->slot_bytes);
@@ -419,6 +657,7 @@ int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes) {
 
 int stream_destroy(lnf4_stream* st) {
   if (!st) return LNF4_OK;
+  disk_close(st);
   destroy_events(st);
   delete st;
   return LNF4_OK;

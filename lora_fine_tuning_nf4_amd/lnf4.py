@@ -101,6 +101,10 @@ def _declare(L):
         "stream_reset": (i32, [vp, vp]),
         "stream_log": (i32, [vp, POINTER(lnf4_stream_event), i32, POINTER(c_int32)]),
         "stream_bytes_copied": (i32, [vp, POINTER(c_int64)]),
+        "stream_create_disk": (i32, [ctypes.c_char_p, POINTER(c_int64), i32, POINTER(c_void_p), sz, i32,
+                                     POINTER(c_void_p), POINTER(c_size_t), i32, POINTER(c_void_p), sz, i32,
+                                     POINTER(c_int32), i32, vp, vp, sz, POINTER(c_void_p)]),
+        "stream_disk_stats": (i32, [vp, POINTER(c_int64), POINTER(ctypes.c_double)]),
         "stream_destroy": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
@@ -311,6 +315,35 @@ def stream_create(host_shards, shard_bytes, dev_bufs, buf_bytes: int, schedule, 
     _check(lib().stream_create(hs, sb, n, db, buf_bytes, nb, sc, len(schedule), mode, _stream(copy_stream),
                                _ptr(slot_buf), slot_bytes, ctypes.byref(out)))
     return out.value
+
+
+def stream_create_disk(path: str, file_offsets, stage_bufs, stage_bytes: int, shard_bytes, dev_bufs,
+                       buf_bytes: int, schedule, copy_stream, host_shards=None, drop_cache: bool = False,
+                       slot_buf=None, slot_bytes: int = 0):
+    """Ring-mode layer stream whose layer shards are read from `path` through the pinned
+    staging buffers (the read-ahead depth is len(stage_bufs)); see stream_create_disk in
+    include/lnf4.h."""
+    n = len(shard_bytes)
+    fo = (c_int64 * n)(*file_offsets)
+    ns = len(stage_bufs)
+    stg = (c_void_p * ns)(*[_ptr(b) for b in stage_bufs])
+    hs = None if host_shards is None else (c_void_p * n)(*[_ptr(h) for h in host_shards])
+    sb = (c_size_t * n)(*shard_bytes)
+    nb = len(dev_bufs)
+    db = (c_void_p * nb)(*[_ptr(d) for d in dev_bufs])
+    sc = (c_int32 * len(schedule))(*schedule)
+    out = c_void_p()
+    _check(lib().stream_create_disk(os.fsencode(path), fo, int(drop_cache), stg, stage_bytes, ns, hs, sb, n, db,
+                                    buf_bytes, nb, sc, len(schedule), _stream(copy_stream), _ptr(slot_buf),
+                                    slot_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def stream_disk_stats(st):
+    """(bytes read from the file, seconds the reader spent in reads)."""
+    b, t = c_int64(), ctypes.c_double()
+    _check(lib().stream_disk_stats(st, ctypes.byref(b), ctypes.byref(t)))
+    return b.value, t.value
 
 
 def stream_layer_step(st, k: int, compute=None) -> int:

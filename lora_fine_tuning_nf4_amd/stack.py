@@ -24,6 +24,7 @@ this module only lays out memory and orders the calls.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 
 import torch
@@ -377,6 +378,46 @@ class StreamedStack:
 
     def log(self):
         return lnf4.stream_log(self.st)
+
+    def use_disk(self, path: str, read_ahead: int = 2, drop_cache: bool = True):
+        """Disk tier: write the layer shards to `path` (each at a 4 KiB-aligned offset) and
+        stream them from there through `read_ahead` pinned staging buffers; the head
+        shards stay in pinned RAM.  With drop_cache the file's pages leave the page cache
+        once written and after every read, so each pass reads the device.  Replaces the
+        ring context (same schedule and buffers)."""
+        torch.cuda.synchronize(self.dev)
+        align = 4096
+        stride = (self.shard_bytes + align - 1) // align * align
+        pad = bytes(stride - self.shard_bytes)
+        with open(path, "wb") as f:
+            for h in self.host:
+                f.write(memoryview(h.numpy()))
+                f.write(pad)
+            if drop_cache:
+                f.flush()
+                os.fsync(f.fileno())
+                os.posix_fadvise(f.fileno(), 0, 0, os.POSIX_FADV_DONTNEED)
+        n = len(self.all_shards)
+        offsets = [i * stride for i in range(self.L)] + [0] * (n - self.L)
+        self.stage = []
+        addrs = []
+        for _ in range(read_ahead):
+            t = torch.empty(stride + align, dtype=torch.uint8, pin_memory=True)
+            self.stage.append(t)
+            addrs.append((t.data_ptr() + align - 1) // align * align)
+        host = [None] * self.L + list(self.all_shards[self.L:])
+        sizes = [self.shard_bytes] * self.L + [h.numel() for h in self.all_shards[self.L:]]
+        slot_bytes = self.slot.numel() if self.slot is not None else 0
+        st = lnf4.stream_create_disk(path, offsets, addrs, stride, sizes, self.bufs, self.shard_bytes, self.schedule,
+                                     self.copy, host_shards=host, drop_cache=drop_cache, slot_buf=self.slot,
+                                     slot_bytes=slot_bytes)
+        lnf4.stream_destroy(self.st)
+        self.st = st
+        self.disk_path = path
+
+    def disk_stats(self):
+        """(bytes read from the disk file, seconds in reads) of a disk-tier context."""
+        return lnf4.stream_disk_stats(self.st)
 
     def bytes_copied(self) -> int:
         return lnf4.stream_bytes_copied(self.st)

@@ -139,6 +139,35 @@ def test_stream_validation(L):
     assert L.stream_destroy(None) == lnf4.LNF4_OK
 
 
+def test_stream_disk_validation(L, tmp_path):
+    # the disk tier rejects bad arguments before any HIP call (the file is opened and
+    # sized first; page-locking is checked last)
+    f = tmp_path / "shards.bin"
+    f.write_bytes(bytes(3 * 4096))
+    out = ctypes.c_void_p()
+    sb = (ctypes.c_size_t * 2)(4096, 4096)
+    db = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    sc = (ctypes.c_int32 * 4)(0, 1, 1, 0)
+    stg = (ctypes.c_void_p * 9)(*([FAKE] * 9))
+
+    def call(path=str(f), offs=(0, 4096), n_stage=2, stage_bytes=4096, sched=sc, stages=stg):
+        fo = (ctypes.c_int64 * 2)(*offs)
+        return L.stream_create_disk(path.encode(), fo, 1, stages, stage_bytes, n_stage, None, sb, 2, db, 4096,
+                                    2, sched, 4, None, None, 0, ctypes.byref(out))
+
+    assert call(n_stage=0) == lnf4.LNF4_EINVAL                   # read-ahead depth 1..8
+    assert call(n_stage=9) == lnf4.LNF4_EINVAL
+    assert call(stage_bytes=2048) == lnf4.LNF4_ESHAPE            # a shard larger than staging
+    assert call(path=str(tmp_path / "missing.bin")) == lnf4.LNF4_EINVAL
+    assert call(offs=(0, 3 * 4096)) == lnf4.LNF4_ESHAPE          # shard 1 ends past the file
+    assert call(offs=(0, -4096)) == lnf4.LNF4_EINVAL
+    assert call(stages=(ctypes.c_void_p * 2)(FAKE, None)) == lnf4.LNF4_EINVAL  # a NULL staging buffer
+    bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
+    assert call(sched=bad) == lnf4.LNF4_EINVAL                   # schedule names a missing shard
+    b, t = ctypes.c_int64(), ctypes.c_double()
+    assert L.stream_disk_stats(None, ctypes.byref(b), ctypes.byref(t)) == lnf4.LNF4_ESTATE
+
+
 def test_size_limits(L):
     # a weight or activation beyond 2^31-1 bytes is rejected before any HIP call
     big = lnf4.make_weight(lnf4.FMT_BF16, FAKE, None, 1 << 16, 1 << 15, 64)  # 2^32 bytes of bf16

@@ -95,6 +95,46 @@ def test_reuse_log_and_buffers_match_simulator(nbuf, mode):
         lnf4.stream_destroy(st)
 
 
+@pytest.mark.parametrize("nbuf,n_stage,drop", [(2, 1, False), (2, 2, True), (3, 8, False), (8, 3, True)])
+def test_disk_tier_log_and_buffers_match_simulator(nbuf, n_stage, drop, tmp_path):
+    """Layer shards read from a file through n_stage pinned staging buffers: over three
+    passes the engine's log equals the ring's simulator log (the disk tier only delays
+    copies), every call finds its shard's bytes, and the reader has read every position."""
+    import os
+    L, nbytes = 5, 4096 + 512
+    shards = _pinned_shards(L, nbytes, seed=40 + nbuf)
+    stride = 8192
+    path = tmp_path / "shards.bin"
+    with open(path, "wb") as f:
+        for h in shards:
+            f.write(h.numpy().tobytes() + bytes(stride - nbytes))
+    stage = [torch.empty(stride + 4096, dtype=torch.uint8, pin_memory=True) for _ in range(n_stage)]
+    addrs = [(t.data_ptr() + 4095) // 4096 * 4096 for t in stage]
+    bufs = [torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sched = ss.sft_schedule(L)
+    comp = torch.cuda.current_stream()
+    st = lnf4.stream_create_disk(str(path), [i * stride for i in range(L)], addrs, stride, [nbytes] * L, bufs,
+                                 nbytes + 256, sched, torch.cuda.Stream(), drop_cache=drop)
+    try:
+        for step in range(3):
+            for k in range(len(sched)):
+                p = lnf4.stream_layer_step(st, k, comp)
+                j = [i for i, b in enumerate(bufs) if b.data_ptr() == p]
+                assert j == [k % nbuf]
+                assert torch.equal(bufs[j[0]][:nbytes].cpu(), shards[sched[k]]), (step, k)
+            assert lnf4.stream_log(st) == ss.simulate(sched, nbuf)
+            lnf4.stream_reset(st, comp)
+        torch.cuda.synchronize()
+        got, secs = lnf4.stream_disk_stats(st)
+        assert got >= 3 * len(sched) * nbytes and secs >= 0.0
+        with pytest.raises(lnf4.LNF4Error):
+            lnf4.stream_slot_load(st, 0, comp)   # no slot, and no host copy of the shard
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st)
+    os.remove(path)
+
+
 def test_resident_log_matches_simulator():
     L, nbytes = 4, 2048
     shards = _pinned_shards(L, nbytes, seed=7)
@@ -176,6 +216,27 @@ def test_streamed_equals_resident_bitwise(fmt, dpo, reuse):
     finally:
         stack.close()
     assert "dh" in a["head"]
+    for snap in (b, c):
+        _same(a, snap)
+
+
+@pytest.mark.parametrize("dpo,drop", [(False, True), (True, False)])
+def test_disk_tier_step_equals_resident_bitwise(dpo, drop, tmp_path):
+    """A stack step whose layers stream from a file (head slot from pinned RAM) gives
+    bitwise the same outputs and gradients as the resident step."""
+    stack = StreamedStack(_small_workload("nf4"), n_bufs=2, seed=5, dpo=dpo)
+    try:
+        stack.step(resident=True)
+        a = _snapshot(stack)
+        stack.use_disk(str(tmp_path / "layers.bin"), read_ahead=2, drop_cache=drop)
+        stack.step()
+        b = _snapshot(stack)
+        stack.step()
+        c = _snapshot(stack)
+        got, _ = stack.disk_stats()
+        assert got >= 2 * len(stack.schedule) * stack.shard_bytes
+    finally:
+        stack.close()
     for snap in (b, c):
         _same(a, snap)
 
