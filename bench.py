@@ -295,7 +295,46 @@ def stream_variants(wl, args, L):
             del stack
             torch.cuda.empty_cache()
         log(f"variant {name}: {out[name]}")
+    out["disk"] = disk_variant(wl, args, L)
+    log(f"variant disk: {out['disk']}")
     return out
+
+
+def disk_variant(wl, args, L):
+    """The disk tier: the layer shards are written to a file and every step reads them back
+    from the device (their pages are dropped from the page cache after each read) through
+    two pinned staging buffers (the pages' default read-ahead), then copies them through
+    the same ring; the head slot stays in pinned RAM.  One warm-up step and at most two
+    timed steps: the step is bound by the disk."""
+    import shutil
+    import tempfile
+    import torch
+    from lora_fine_tuning_nf4_amd.stack import StreamedStack
+
+    d = tempfile.mkdtemp(prefix="lnf4_disk_", dir=os.environ.get("TMPDIR", "/tmp"))
+    stack = StreamedStack(wl, n_bufs=args.nbuf, seed=args.seed, layers=L, loss_chunk=args.loss_chunk)
+    try:
+        stack.use_disk(os.path.join(d, "layers.bin"), read_ahead=2, drop_cache=True)
+        stack.step()
+        torch.cuda.synchronize()
+        r0, s0 = stack.disk_stats()
+        b0 = stack.bytes_copied()
+        n = max(1, min(2, args.steps))
+        t0 = time.perf_counter()
+        for _ in range(n):
+            stack.step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1000.0 / n
+        r1, s1 = stack.disk_stats()
+        return {"ms_per_step": round(ms, 3), "tokens_per_s": round(stack.T / (ms / 1000.0), 2),
+                "read_ahead": 2, "disk_bytes_per_step": (r1 - r0) // n,
+                "disk_read_GBps": round((r1 - r0) / max(s1 - s0, 1e-9) / 1e9, 2),
+                "h2d_bytes_per_step": (stack.bytes_copied() - b0) // n, "steps_timed": n}
+    finally:
+        stack.close()
+        del stack
+        torch.cuda.empty_cache()
+        shutil.rmtree(d, ignore_errors=True)
 
 
 def decoder_model_run(args):
@@ -369,7 +408,7 @@ def main():
     ap.add_argument("--no-model", action="store_true",
                     help="skip the whole-decoder-model run (attention, norms, SwiGLU between the projections)")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the stream-variant runs (buffer reuse, no recompute)")
+                    help="skip the stream-variant runs (buffer reuse, no recompute, disk tier)")
     ap.add_argument("--loss-chunk", type=int, default=None,
                     help="tokens per chunk of the output head and its loss (default: all tokens at once)")
     ap.add_argument("--study", action="store_true",
