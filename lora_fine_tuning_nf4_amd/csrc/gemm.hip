@@ -1496,10 +1496,10 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
     return hipGetLastError();
   }
   // Several rounds of 256-row tiles whose last round leaves many compute units idle: the
-  // column panels of that last round can run as 128-row tiles, dispatched last in the same
-  // launch (a 128-row tile takes a little over half the time of a 256-row one).  Chosen when
-  // the estimated rounds drop, e.g. 896 tiles = 3.5 rounds on 256 units become 768 + 256
-  // half-height tiles.
+  // column panels of that last round can run as 128-row tiles in the same launch (a
+  // 128-row tile's K loop takes about 0.62 of a 256-row one's: 62 vs 100 us at the 8B
+  // gate|up shape).  Chosen when the estimated rounds drop, e.g. 896 tiles = 3.5 rounds on
+  // 256 units become 768 + 256 half-height tiles (3.62 estimated rounds instead of 4).
   const int rem = t256 % cus;
   const int tail_n = (rem + tm256 - 1) / tm256;
   const int tm128 = (a.M + 127) / 128;
@@ -1507,7 +1507,7 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   const auto rounds = [cus](int tiles) { return (tiles + cus - 1) / cus; };
   a.n_tiles_m = tm256;
   if (t256 > cus && rem > 0 && full > 0 &&
-      rounds(full) + 0.55 * rounds(tm128 * tail_n) < rounds(t256) - 0.2) {
+      rounds(full) + 0.62 * rounds(tm128 * tail_n) < rounds(t256) - 0.2) {
     a.n_tiles_n = tn_all - tail_n;
     a.tail_m = tm128;
     a.tail_n = tail_n;
