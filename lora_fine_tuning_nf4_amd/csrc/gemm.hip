@@ -482,7 +482,7 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
     }
     return;
   }
-  const bool vec4 = (out_f & 3) == 0;
+  const bool vec4 = (out_f & 3) == 0 && (((uintptr_t)P.y) & 7) == 0;  // y need only be 2-byte aligned
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     __builtin_amdgcn_sched_barrier(0);  // bound the accumulator reads that are live at once

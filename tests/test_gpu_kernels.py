@@ -185,6 +185,50 @@ def test_backward_split_k(fmt, out_f):
     assert np.array_equal(host_u16(d.dx), first)
 
 
+@pytest.mark.parametrize("out_f", [333, 1100, 1096])
+def test_forward_store_paths_and_unaligned_y(out_f):
+    # The forward writes y in whole lines through LDS (out_f % 8 == 0, y 16-byte aligned), in
+    # 8-byte groups (out_f % 4 == 0, y 8-byte aligned) or element by element; y need only be
+    # 2-byte aligned.  Every path gives the same bits; checked against the oracle once.
+    T, in_f, r = 300, 256, 8
+    c = make_case(29, T, out_f, in_f, r, 16.0, 0, tag=f"store-{out_f}")
+    d = DevCase(c)
+    _run_fwd(d)
+    sync()
+    ref = host_u16(d.y).copy()
+    y_ref, _ = oracle_fwd(c)
+    check_tol(bf16_f64(ref), y_ref, "y")
+    for off in (1, 2, 3):   # y 2, 4 and 6 bytes past a 16-byte boundary
+        buf = torch.zeros(T * out_f + 8, dtype=torch.int16, device="cuda")
+        d.y = buf[off:off + T * out_f].view(T, out_f)
+        _run_fwd(d)
+        sync()
+        assert np.array_equal(host_u16(d.y), ref), off
+
+
+def test_backward_unaligned_dx_same_bits():
+    # no K split here: the dx GEMM writes dx itself, through LDS and 8-byte stores when dx is
+    # 8-byte aligned, element by element otherwise (dx need only be 2-byte aligned); both
+    # with and without accumulating into the existing dx
+    c = make_case(31, 256, 896, 896, 8, 16.0, 0, tag="dx-unaligned")
+    d = DevCase(c)
+    _run_bwd(d)
+    sync()
+    ref = host_u16(d.dx).copy()
+    _run_bwd(d, accumulate=1)
+    sync()
+    ref2 = host_u16(d.dx).copy()
+    for off in (1, 2, 3):
+        buf = torch.zeros(c.T * c.in_f + 8, dtype=torch.int16, device="cuda")
+        d.dx = buf[off:off + c.T * c.in_f].view(c.T, c.in_f)
+        _run_bwd(d)
+        sync()
+        assert np.array_equal(host_u16(d.dx), ref), off
+        _run_bwd(d, accumulate=1)
+        sync()
+        assert np.array_equal(host_u16(d.dx), ref2), off
+
+
 @pytest.mark.parametrize("T,n_panels,n_tail", [(512, 136, 8), (1024, 96, 32)])
 def test_forward_tail_as_128_row_tiles(T, n_panels, n_tail):
     # More than one round of 256 x 256 tiles on 256 compute units with a last round that
