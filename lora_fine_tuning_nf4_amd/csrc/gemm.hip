@@ -607,7 +607,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16(const FwdArgs args) {
       V[idx] = (n < out_f && kk < r) ? P.B[(size_t)n * r + kk] : (uint16_t)0;
     }
     __syncthreads();
-    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+    rank_update<MI, true>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
     __syncthreads();
   }
 
@@ -697,8 +697,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16(const FwdArgs args) {
             *(const bf16x8*)&LNF4_XS(SN)[act_pos(32 * i + l32, 4 * h)];                        \
       }                                                                                        \
       _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
-        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
-        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+        acc[i][0] = mfma32(bc0, ac[i], acc[i][0]);                                             \
+        acc[i][1] = mfma32(bc1, ac[i], acc[i][1]);                                             \
       }                                                                                        \
       _Pragma("unroll") for (int g = 0; g < NM; ++g) {                                         \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
@@ -732,21 +732,64 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16(const FwdArgs args) {
 #undef LNF4_XS
 #undef LNF4_ISSUE
 
-  // ---- store bf16
-  const int n0g = nloc0 + nc0, n1g = nloc0 + nc1;
+  // ---- store bf16.  As in the NF4 forward the weights are the MFMA's A operand, so the
+  // accumulators hold the tile transposed: lane (l32, h) has token 32i + l32 and, for
+  // q = 4g..4g+3, the outputs 64 wave + 32j + 8g + 4h + 0..3.  With out_f % 8 == 0 and y
+  // 16-byte aligned each wave stages its rows in LDS (16-byte chunk c of row r at
+  // c ^ ((r >> 1) & 7), in the first two ring stages, free once every wave is past its last
+  // K-block) and stores whole 128-byte lines; else 8-byte groups or single elements.
+  if ((out_f & 7) == 0 && (((uintptr_t)P.y) & 15) == 0) {
+    LNF4_WAIT_VM_LGKM0(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* const rg = (wave < 2 ? sm0 : sm1) + (wave & 1) * (BM * 128);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = 32 * i + l32;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int pc = (4 * j + g) ^ ((row >> 1) & 7);
+          *(uint2*)(rg + row * 128 + pc * 16 + 8 * h) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                         pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_sched_barrier(0);
+    const int c = lane & 7;
+    const int n = nloc0 + 64 * wave + 8 * c;
+#pragma unroll
+    for (int k = 0; k < BM / 8; ++k) {
+      const int row = 8 * k + (lane >> 3);
+      const u32x4 v = *(const u32x4*)(rg + row * 128 + ((c ^ ((row >> 1) & 7)) * 16));
+      const int gm = m0 + row;
+      if (gm < M && n < out_f) *(u32x4*)(P.y + (size_t)gm * out_f + n) = v;
+    }
+    return;
+  }
+  const bool vec4 = (out_f & 3) == 0 && (((uintptr_t)P.y) & 7) == 0;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     __builtin_amdgcn_sched_barrier(0);
+    const int gm = m0 + 32 * i + l32;
+    if (gm >= M) continue;
+    uint16_t* yr = P.y + (size_t)gm * out_f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-      const int gm = m0 + row;
-      if (gm >= M) continue;
-      const float v0 = acc[i][0][q], v1 = acc[i][1][q];
-      uint16_t* yr = P.y + (size_t)gm * out_f;
-      if (n0g < out_f) yr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
-      if (n1g < out_f) yr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nloc0 + 64 * wave + 32 * j + 8 * g + 4 * h;
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if (vec4 && n < out_f) {
+          *(uint2*)(yr + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < out_f) yr[n + e] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+        }
+      }
   }
 }
 
