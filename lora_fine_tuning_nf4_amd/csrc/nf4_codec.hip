@@ -11,34 +11,48 @@ namespace lnf4 {
 
 __constant__ float c_nf4_table[16] = LNF4_TABLE_INIT;
 
-__global__ __launch_bounds__(256) void k_nf4_dequant(const uint4* __restrict__ codes,
+// Each wave takes 2048 consecutive elements (256 groups of 8) per trip: lane L decodes
+// groups 64s + L (s = 0..3), so every load instruction reads 256 contiguous bytes of codes
+// and every store writes 1 KB of contiguous output (whole lines; a lane writing 64 bytes of
+// its own would spread each store over 64 partial lines).  The loads of a trip are all in
+// flight before the first decode.
+__global__ __launch_bounds__(256) void k_nf4_dequant(const uint32_t* __restrict__ codes,
                                                      const float* __restrict__ absmax,
-                                                     uint4* __restrict__ out, int64_t n32) {
+                                                     uint4* __restrict__ out, int64_t n8) {
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = c_nf4_table[threadIdx.x];
   __syncthreads();
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n32; i += stride) {
-    const uint4 c = codes[i];
-    const float a = absmax[i >> 1];
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t wv = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; wv * 256 < n8; wv += nwaves) {
+    uint32_t c[4];
+    float a[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t o[4];
-      decode8(w[q], a, lut, o);
-      out[4 * i + q] = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int s = 0; s < 4; ++s) {
+      const int64_t g = wv * 256 + 64 * s + lane;  // group of 8 elements (4 code bytes)
+      c[s] = g < n8 ? codes[g] : 0u;
+      a[s] = g < n8 ? absmax[g >> 3] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t g = wv * 256 + 64 * s + lane;
+      if (g < n8) {
+        uint32_t o[4];
+        decode8(c[s], a[s], lut, o);
+        out[g] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
 }
 
 hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n_elems, uint16_t* out,
                               hipStream_t s) {
-  const int64_t n32 = n_elems / 32;
-  if (n32 == 0) return hipSuccess;
-  int64_t blocks = (n32 + 255) / 256;
+  const int64_t n8 = n_elems / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t blocks = (n8 + 1023) / 1024;  // 4 waves x 256 groups per trip
   if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(k_nf4_dequant, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4*)codes, absmax,
-                     (uint4*)out, n32);
+  hipLaunchKernelGGL(k_nf4_dequant, dim3((unsigned)blocks), dim3(256), 0, s, (const uint32_t*)codes, absmax,
+                     (uint4*)out, n8);
   return hipGetLastError();
 }
 
