@@ -65,14 +65,16 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // column-tiles, so the 32 blocks resident on one XCD at a time cover gm row-panels and
 // 32/gm column-panels: each activation panel and each weight panel they stream is read
 // from HBM once for the XCD and shared through its L2.
-__device__ __forceinline__ void tile_coords(int b, int n_m, int n_n, int gm, int& tm, int& tn) {
-  const int t = xcd_remap(b, n_m * n_n);
+__device__ __forceinline__ void tile_from_seq(int t, int n_m, int n_n, int gm, int& tm, int& tn) {
   const int per_group = gm * n_n;
   const int g = t / per_group, first = g * gm;
   const int gsz = n_m - first < gm ? n_m - first : gm;
   const int r = t - g * per_group;
   tm = first + r % gsz;
   tn = r / gsz;
+}
+__device__ __forceinline__ void tile_coords(int b, int n_m, int n_n, int gm, int& tm, int& tn) {
+  tile_from_seq(xcd_remap(b, n_m * n_n), n_m, n_n, gm, tm, tn);
 }
 
 }  // namespace lnf4

@@ -509,9 +509,9 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
 // Blocks compute BM-row tiles over n_tiles_m x n_tiles_n.  With BM = 256 and 4 waves, a
 // tail of 128-row tiles over the tail_n column panels that follow can be mixed in: a last
 // round of tiles that would leave compute units idle runs as twice as many half-height
-// tiles.  Half of those tiles can be dispatched right after the first half round of full
-// tiles, so half of the compute units run half a tile out of step with the other half and
-// the output stores at the end of each tile do not all hit memory at once.
+// tiles.  When the tail is one round, four of the eight XCDs run their tail tiles first, so
+// those XCDs are half a tile out of step with the other four and the output stores at the
+// end of each tile do not all hit memory at once.
 template <int BM, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
   constexpr int STAGE = fwd_stage_bytes(BM);
@@ -531,14 +531,28 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
   if (tid < 256) lut2[tid] = make_float2(c_gemm_table[tid >> 4], c_gemm_table[tid & 15]);
 
   int tm, tn;
-  int b = blockIdx.x;
+  const int b = blockIdx.x;
   if constexpr (BM == 256 && NW == 4) {
-    int hb = -1;
-    if (b >= args.split_block) hb = b - args.split_block + args.stag_h;
-    else if (b >= args.stag_f + args.stag_h) b -= args.stag_h;
-    else if (b >= args.stag_f) hb = b - args.stag_f;
-    if (hb >= 0) {
-      tile_coords(hb, args.tail_m, args.tail_n, kGroupM, tm, tn);
+    if (args.xcd_f > 0) {
+      // XCD x = b mod 8 runs its blocks i = b / 8 in order; its tiles are the contiguous
+      // ranges [x xcd_f, (x+1) xcd_f) of the full-tile sequence and [x xcd_h, (x+1) xcd_h)
+      // of the tail sequence, as tile_coords would give it
+      const int x = b & 7, i = b >> 3;
+      const bool tail_first = x >= 4;
+      const int n_first = tail_first ? args.xcd_h : args.xcd_f;
+      const bool is_tail = tail_first ? i < n_first : i >= n_first;
+      const int j = i < n_first ? i : i - n_first;
+      if (is_tail) {
+        tile_from_seq(args.xcd_h * x + j, args.tail_m, args.tail_n, kGroupM, tm, tn);
+        fwd_nf4_tile<128, 4>(args, tm, tn + args.tn_base + args.n_tiles_n, sm0, sm1, sm2, sm3, lut2);
+      } else {
+        tile_from_seq(args.xcd_f * x + j, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+        fwd_nf4_tile<BM, NW>(args, tm, tn + args.tn_base, sm0, sm1, sm2, sm3, lut2);
+      }
+      return;
+    }
+    if (b >= args.split_block) {
+      tile_coords(b - args.split_block, args.tail_m, args.tail_n, kGroupM, tm, tn);
       fwd_nf4_tile<128, 4>(args, tm, tn + args.tn_base + args.n_tiles_n, sm0, sm1, sm2, sm3, lut2);
       return;
     }
@@ -1516,7 +1530,7 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   if (a.M <= 0 || a.n_tiles_n <= 0) return hipSuccess;
   a.tn_base = 0;
   a.split_block = 0x7fffffff;
-  a.tail_m = a.tail_n = a.stag_f = a.stag_h = 0;
+  a.tail_m = a.tail_n = a.xcd_f = a.xcd_h = 0;
   if (fmt != 0) {
     // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
     a.n_tiles_m = (a.M + 127) / 128;
@@ -1555,11 +1569,14 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
     a.tail_m = tm128;
     a.tail_n = tail_n;
     const int half = tm128 * tail_n;
-    if (half == cus && full >= cus) {
-      // one round of half tiles: half of the units take theirs first
-      a.stag_f = a.stag_h = cus / 2;
+    if (half == cus && full >= cus && full % 8 == 0 && half % 8 == 0) {
+      // one round of half tiles: the units of four XCDs take theirs first, so those XCDs
+      // run half a tile out of step with the other four (each XCD stays in step with
+      // itself, so its L2 still serves one set of activation and code panels at a time)
+      a.xcd_f = full / 8;
+      a.xcd_h = half / 8;
     }
-    a.split_block = full + a.stag_h;
+    a.split_block = full;
     hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(full + half), dim3(NTHR), 0, s, a);
     return hipGetLastError();
   }

@@ -32,13 +32,14 @@ struct FwdArgs {
   int32_t n_tiles_m;
   int32_t tn_base;      // first N-tile of this launch in the group's tile space
   // 128-row tail (set by launch_fwd): tail_m x tail_n tiles over the N-tiles that follow
-  // n_tiles_n.  Blocks [stag_f, stag_f + stag_h) run the first stag_h of them, blocks from
-  // split_block on the rest; all other blocks run the BM-row tiles in order.
+  // n_tiles_n.  xcd_f == 0: blocks from split_block on run the tail.  xcd_f > 0: the XCD of
+  // block b (b mod 8) takes xcd_f full and xcd_h tail tiles, XCDs 0-3 full tiles first,
+  // XCDs 4-7 tail tiles first.
   int32_t split_block;
   int32_t tail_m;
   int32_t tail_n;
-  int32_t stag_f;
-  int32_t stag_h;
+  int32_t xcd_f;
+  int32_t xcd_h;
   FwdProj p[kMaxGroup];
 };
 

@@ -234,7 +234,7 @@ def test_forward_tail_as_128_row_tiles(T, n_panels, n_tail):
     # More than one round of 256 x 256 tiles on 256 compute units with a last round that
     # would leave units idle: the last n_tail column panels run as 128-row tiles in the same
     # launch (2 x 136 tiles: 8 panels after the full tiles; 4 x 96 tiles: 32 panels, one
-    # round of half tiles, half of them dispatched first).  Parity with the oracle, and the
+    # round of half tiles, which four of the eight XCDs run first).  Parity with the oracle, and the
     # tail columns must equal bit for bit a call on those rows of W alone (same K order,
     # other tile shape).
     out_f, in_f, r = n_panels * 256, 128, 8
