@@ -220,6 +220,34 @@ def test_streamed_equals_resident_bitwise(fmt, dpo, reuse):
         _same(a, snap)
 
 
+def test_disk_tier_read_error_is_reported(tmp_path):
+    """A shard that can no longer be read (the file shrank after the context was created)
+    fails the stream_layer_step call that needs it, with the errno text; the reader thread
+    stops cleanly at destroy."""
+    L, nbytes = 3, 4096
+    shards = _pinned_shards(L, nbytes, seed=7)
+    path = tmp_path / "shards.bin"
+    with open(path, "wb") as f:
+        for h in shards:
+            f.write(h.numpy().tobytes())
+    stage = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    sched = ss.sft_schedule(L)
+    comp = torch.cuda.current_stream()
+    os_truncate = __import__("os").truncate
+    st = lnf4.stream_create_disk(str(path), [i * nbytes for i in range(L)], stage, nbytes, [nbytes] * L, bufs,
+                                 nbytes, sched, torch.cuda.Stream())
+    try:
+        os_truncate(path, nbytes)   # shards 1 and 2 are gone (the reader may hold shard 1 already)
+        with pytest.raises(lnf4.LNF4Error) as ei:
+            for k in range(len(sched)):   # position 2 (shard 2) is read only after call 0
+                lnf4.stream_layer_step(st, k, comp)
+        assert "failed" in str(ei.value)
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st)
+
+
 @pytest.mark.parametrize("dpo,drop", [(False, True), (True, False)])
 def test_disk_tier_step_equals_resident_bitwise(dpo, drop, tmp_path):
     """A stack step whose layers stream from a file (head slot from pinned RAM) gives
