@@ -185,13 +185,15 @@ def test_backward_split_k(fmt, out_f):
     assert np.array_equal(host_u16(d.dx), first)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("out_f", [333, 1100, 1096])
-def test_forward_store_paths_and_unaligned_y(out_f):
-    # The forward writes y in whole lines through LDS (out_f % 8 == 0, y 16-byte aligned), in
-    # 8-byte groups (out_f % 4 == 0, y 8-byte aligned) or element by element; y need only be
-    # 2-byte aligned.  Every path gives the same bits; checked against the oracle once.
+def test_forward_store_paths_and_unaligned_y(out_f, fmt):
+    # The forward (NF4 and bf16 weights) writes y in whole lines through LDS (out_f % 8 == 0,
+    # y 16-byte aligned), in 8-byte groups (out_f % 4 == 0, y 8-byte aligned) or element by
+    # element; y need only be 2-byte aligned.  Every path gives the same bits; checked
+    # against the oracle once.
     T, in_f, r = 300, 256, 8
-    c = make_case(29, T, out_f, in_f, r, 16.0, 0, tag=f"store-{out_f}")
+    c = make_case(29, T, out_f, in_f, r, 16.0, fmt, tag=f"store-{out_f}-{fmt}")
     d = DevCase(c)
     _run_fwd(d)
     sync()
