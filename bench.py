@@ -295,7 +295,10 @@ def stream_variants(wl, args, L):
             del stack
             torch.cuda.empty_cache()
         log(f"variant {name}: {out[name]}")
-    out["disk"] = disk_variant(wl, args, L)
+    try:
+        out["disk"] = disk_variant(wl, args, L)
+    except (OSError, RuntimeError) as e:  # e.g. no room for the 3.9 GB shard file: report, do not fail the bench
+        out["disk"] = {"error": f"{type(e).__name__}: {e}"}
     log(f"variant disk: {out['disk']}")
     return out
 
