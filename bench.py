@@ -32,6 +32,12 @@ CSRC = os.path.join(ROOT, "lora_fine_tuning_nf4_amd", "csrc")
 FWD_KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp", "nf4_table.hpp")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fwd_nf4_gate_up_llama8b_T2048.traffic.txt")
 CAL_ELEMS = 64 << 20        # float32 elements of the calibration copy (256 MiB read + 256 MiB written)
+# the dominant launch (gate|up forward at the 8B shape, T = 2048) and the input-gradient
+# launch of the same group, as rocprofv3 names them: kernel symbol and grid in threads
+DOM_KERNEL = "k_fwd_nf4<256, 4>"
+DOM_GRID = (768 + 256) * 256        # 768 tiles of 256 x 256 and 256 tiles of 128 x 256
+DX_KERNEL = "k_dxq<256>"
+DX_GRID = 128 * 2 * 256             # 128 tiles of 256 x 256, K in 2 splits
 
 
 def log(*a):
@@ -58,6 +64,25 @@ def fwd_bytes(wl, group):
         if p in wl.adapted:
             b += 2 * o * wl.rank + 4 * T * wl.rank
     return b
+
+
+def dx_bytes(wl, group):
+    """Algorithmic HBM bytes of one grouped NF4 input-gradient launch: each projection's dy
+    and codes + absmax read once, dx written once (bf16), plus v and A when adapted."""
+    T = wl.tokens
+    in_f = wl.shapes[group[0]][1]
+    b = 2 * T * in_f
+    for p in group:
+        o = wl.shapes[p][0]
+        b += 2 * T * o + o * in_f // 2 + 4 * (o * in_f // 64)
+        if p in wl.adapted:
+            b += 2 * wl.rank * in_f + 4 * T * wl.rank
+    return b
+
+
+def workload(name):
+    import synthgen
+    return synthgen.WORKLOADS[name]
 
 
 def head_summary(wl, stack, head_ms):

@@ -112,7 +112,11 @@ typedef struct lnf4_weight {
 } lnf4_weight;
 
 /*
- * LoRA linear forward (one projection):
+ * LoRA linear forward (one projection).  The frozen linear plus the low-rank update
+ * scaled by alpha / r (20B-RLHF-on-24GB article, sections "Low-rank adaptation via PEFT"
+ * and "Step 2": trainable low-rank A and B beside a frozen W), run on the layer that the
+ * stream has just placed on the device (Soup deep dive, "Core feature: how layer
+ * streaming works"):
  *   u = x A^T (fp32, [T, r]);   y = bf16( x W'^T + scale * u B^T )
  * with W' the decoded weight (NF4 decode fused into the GEMM: W' never exists in
  * memory) and fp32 accumulation.  The forward is also the backward's recompute.
@@ -130,11 +134,18 @@ int lora_linear_fwd(const lnf4_weight* W, const uint16_t* x, int64_t T, const ui
                     const uint16_t* B, int32_t r, float scale, uint16_t* y, float* u, hipStream_t stream);
 
 /* Bytes of device workspace lora_linear_bwd needs for these sizes (0 if r == 0 and
- * the shapes need no split reduction).  Host-only. */
+ * the shapes need no split reduction): v = dy B and, for a split input-gradient GEMM, its
+ * fp32 partial sums.  The backward it sizes is the one the Soup deep dive ("Core feature:
+ * how layer streaming works") describes: W is read again for dL/dx = W^T dL/dy while only
+ * the adapters receive gradients.  The caller allocates it once (fwd and bwd never
+ * allocate).  Host-only; returns 0 for invalid sizes. */
 size_t lora_linear_bwd_workspace(int64_t T, int64_t out_f, int64_t in_f, int32_t r);
 
 /*
- * LoRA linear backward (one projection), W gets no gradient:
+ * LoRA linear backward (one projection).  The layer is on the device a second time
+ * because the input gradient needs the frozen weight again, dL/dx = W^T dL/dy, while only
+ * the adapters (their gradients and optimizer state held in device memory) are trained
+ * (Soup deep dive, "Core feature: how layer streaming works"); W gets no gradient:
  *   v  = dy B                                     (fp32 [T, r], in workspace)
  *   dx = bf16( dy W' + scale * v A )              (+ old dx if accumulate)
  *   dA = scale * v^T x                            (fp32 [r, in], += old if accumulate)
@@ -147,7 +158,8 @@ size_t lora_linear_bwd_workspace(int64_t T, int64_t out_f, int64_t in_f, int32_t
  * dx GEMM has few output tiles and a long K (few tokens, many output features), it splits
  * K: each split's fp32 sums go to the workspace and a fixed-order pass adds them, so dx is
  * still deterministic.  The split count depends only on the shapes.
- * Errors: EINVAL, ESHAPE (also workspace too small), EALIGN, EHIP.
+ * Errors: EINVAL, ESHAPE (in % 64, blocksize, out_f not a multiple of 8, workspace too
+ * small), EALIGN, EHIP.
  */
 int lora_linear_bwd(const lnf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t T,
                     const uint16_t* A, const uint16_t* B, int32_t r, float scale, const float* u_saved,
@@ -182,14 +194,17 @@ int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
  * same descriptors as the call.  Host-only. */
 size_t lora_group_bwd_workspace(const lnf4_proj* projs, int32_t n, int64_t T);
 
-/* Grouped backward: dx [T, in] = sum over the group (NULL to skip), per-projection dA/dB. */
+/* Grouped backward: dx [T, in] = sum over the group (NULL to skip), per-projection dA/dB.
+ * Errors: as lora_linear_bwd (every projection's out_f a multiple of 8). */
 int lora_group_bwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, uint16_t* dx,
                    int32_t accumulate, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Shard layout of one decoder layer: projections in the caller's order (q, k, v, o,
- * gate, up, down), each as [data][absmax] sections, every section starting on a
- * 256-byte boundary.  offsets[2p] = data offset, offsets[2p+1] = absmax offset (-1 for
+ * Shard layout of one decoder layer.  The frozen base is kept as one page-locked host
+ * blob per decoder layer, and a step copies whole layers (Soup deep dive, "Core feature:
+ * how layer streaming works"): projections in the caller's order (q, k, v, o, gate, up,
+ * down), each as [data][absmax] sections, every section starting on a 256-byte
+ * boundary.  offsets[2p] = data offset, offsets[2p+1] = absmax offset (-1 for
  * BF16).  total_bytes = shard size.  Host-only.
  * Errors: EINVAL, ESHAPE (in % 64).
  */
@@ -378,7 +393,12 @@ typedef struct lnf4_stream_event {
 
 /*
  * Create a layer stream over one pass of `schedule` (shard indices, e.g. layers
- * 0..L-1 then L-1..0 for an SFT step: forward, then recompute + backward).
+ * 0..L-1 then L-1..0 for an SFT step: forward, then recompute + backward).  The frozen
+ * layers stay in page-locked host RAM and a separate stream copies them into a few
+ * preallocated device buffers ahead of the compute (Soup deep dive, "Core feature: how
+ * layer streaming works", and its settings table, "Streaming config keys": stream_buffers,
+ * default 2, range 2..8; 4 GB-laptop article, "Layer streaming: technical implementation
+ * and memory efficiency": prefetch on a dedicated stream).
  *   host_shards  n_shards page-locked host pointers (one contiguous blob per layer)
  *   shard_bytes  size of each shard, each <= buf_bytes
  *   dev_bufs     n_bufs device buffers of buf_bytes each, 256-byte aligned
@@ -410,7 +430,10 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
                   size_t slot_bytes, lnf4_stream** out);
 
 /*
- * Call k of the pass (k = 0, 1, ... in order).  Records the release of call k-1's
+ * Call k of the pass (k = 0, 1, ... in order): while layer k computes, the next layer's
+ * copy is already running into another buffer, and every layer is read twice in an SFT
+ * step (forward, then recompute + backward) (Soup deep dive, "Core feature: how layer
+ * streaming works").  Records the release of call k-1's
  * buffer on `compute`, issues the copies the ring rule allows, makes `compute` wait
  * for layer k's copy and returns its device address in *dev_ptr_out.  Every kernel
  * that reads layer k must be enqueued on `compute` before call k+1.
@@ -444,13 +467,23 @@ int stream_slot_load_part(lnf4_stream* st, int32_t shard, int32_t part, int32_t 
 int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out);
 
 /* Rewind a finished (or unfinished) pass so the same schedule runs again (next step).
- * The first copies of the new pass wait for the release of the old pass's buffers. */
+ * The first copies of the new pass wait for the release of the old pass's buffers.  On a
+ * disk-tier context whose pass did not issue all its copies (a step abandoned, e.g. after
+ * a failed call), the reader thread is stopped, the copies out of the staging buffers
+ * already issued are waited for on the host, and the reader restarts at the first
+ * position of the next pass with any read error cleared.
+ * Errors: ESTATE (NULL or destroyed), EINVAL (the reader cannot restart), EHIP. */
 int stream_reset(lnf4_stream* st, hipStream_t compute);
 
-/* Copy up to cap events of the current pass to ev; *n = number copied. */
+/* Copy up to cap events of the current pass to ev; *n = number copied.  The log shows,
+ * per call, which copies were issued and which copy the compute waited on: the stream
+ * schedule whose cost the Soup deep dive ("Core feature: how layer streaming works")
+ * accounts for as compute time spent waiting on copies.
+ * Errors: ESTATE (NULL or destroyed context), EINVAL (n NULL, cap < 0, ev NULL with cap > 0). */
 int stream_log(const lnf4_stream* st, lnf4_stream_event* ev, int32_t cap, int32_t* n);
 
-/* Bytes copied host-to-device by this context since creation (layers + slot). */
+/* Bytes copied host-to-device by this context since creation (layers + slot).
+ * Errors: ESTATE (NULL or destroyed), EINVAL (bytes NULL). */
 int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes);
 
 /*
@@ -490,8 +523,20 @@ int stream_create_disk(const char* path, const int64_t* file_offsets, int32_t dr
  * (seconds), for the disk's achieved rate.  Errors: EINVAL (no disk tier), ESTATE. */
 int stream_disk_stats(const lnf4_stream* st, int64_t* bytes_read, double* read_seconds);
 
-/* Release the context and its events (and a disk tier's reader thread, after the reads
- * and copies in flight).  NULL is accepted; safe to call once per object. */
+/*
+ * Release a context.  A handle is checked before it is used, never trusted (the Soup deep
+ * dive, "Structure: a CLI whose settings schema is the product", refuses unknown settings
+ * instead of acting on them; the same strictness applies to handles):
+ *  - Idempotent: NULL, or a handle already destroyed, returns LNF4_OK and does nothing.
+ *  - Before it returns, every copy the context issued (layer copies, slot loads, a disk
+ *    tier's staging copies) has completed and a disk tier's reader thread has ended, so
+ *    the caller may then free or reuse its host shards, staging buffers, device buffers
+ *    and slot.  Compute work the caller enqueued is not waited for.
+ *  - Every later call on the handle returns LNF4_ESTATE.  The context's events, thread and
+ *    tables are released; its small host struct is kept for the life of the process, so a
+ *    later context never gets the same address and a stale handle cannot name it.
+ * Errors: EHIP if waiting for a copy failed (the context is released all the same).
+ */
 int stream_destroy(lnf4_stream* st);
 
 #ifdef __cplusplus

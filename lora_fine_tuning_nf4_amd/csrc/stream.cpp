@@ -27,6 +27,13 @@
 // was issued).  The ring's copy of position g is issued once that read is done.  The only
 // waits are host waits on the reader and the reader's waits on copy events; no GPU work
 // waits on the host.
+//
+// Handles.  The library keeps the set of live contexts; every entry point looks its handle
+// up there before touching it, so a NULL or destroyed handle gets ESTATE and is never
+// dereferenced, and stream_destroy of a handle that is not live does nothing.  A destroyed
+// context gives back its events, its reader thread and its tables, but its small struct is
+// kept (a tombstone of a few hundred bytes), so a later context never reuses its address
+// and a stale handle can never name another context.
 #include <fcntl.h>
 #include <hip/hip_runtime.h>
 #include <sys/stat.h>
@@ -39,6 +46,7 @@
 #include <mutex>
 #include <new>
 #include <thread>
+#include <unordered_set>
 #include <vector>
 
 #include "abi_internal.hpp"
@@ -56,6 +64,7 @@ struct DiskTier {
   std::thread reader;
   std::mutex mu;
   std::condition_variable cv;
+  long base = 0;                    // first position of the reader's current run
   long read_done = 0;               // positions whose read has finished (or failed)
   long issued = 0;                  // positions whose copy has been enqueued
   bool stop = false;
@@ -90,7 +99,6 @@ struct lnf4_stream {
   int slot_loads = 0;
   int64_t bytes_copied = 0;
   std::vector<lnf4_stream_event> log;
-  bool alive = true;
   // reuse mode: the plan of the current pass, what the buffers hold and when each was
   // last used (a call counter that runs on across passes; -1: never)
   bool reuse = false;
@@ -100,6 +108,21 @@ struct lnf4_stream {
   long tick = 0;
   DiskTier* disk = nullptr;  // ring mode only: layer shards come from a file
 };
+
+// The set of live contexts (never destroyed itself, so it outlives every caller).
+static std::mutex& live_mu() {
+  static std::mutex* m = new std::mutex();
+  return *m;
+}
+static std::unordered_set<const lnf4_stream*>& live_set() {
+  static auto* s = new std::unordered_set<const lnf4_stream*>();
+  return *s;
+}
+static bool is_live(const lnf4_stream* st) {
+  if (!st) return false;
+  std::lock_guard<std::mutex> lk(live_mu());
+  return live_set().count(st) != 0;
+}
 
 // Plan one pass in reuse mode from what the buffers hold now.  Position j: if a buffer
 // holds shard sched[j], use it (plan_src[j] = the position of this pass whose copy
@@ -167,7 +190,12 @@ static void disk_reader(lnf4_stream* st) {
   DiskTier* d = st->disk;
   const long n = (long)st->sched.size();
   const long ns = (long)d->stage.size();
-  for (long g = 0;; ++g) {
+  long g0;
+  {
+    std::lock_guard<std::mutex> lk(d->mu);
+    g0 = d->base;
+  }
+  for (long g = g0;; ++g) {
     const int s = (int)(g % ns);
     {
       std::unique_lock<std::mutex> lk(d->mu);
@@ -176,8 +204,8 @@ static void disk_reader(lnf4_stream* st) {
     }
     int err = 0;
     // the copy out of this staging buffer for position g - ns was issued (above); wait
-    // until it has read the buffer
-    if (g >= ns && hipEventSynchronize(d->stage_ev[s]) != hipSuccess) err = -1;
+    // until it has read the buffer (a run starts with every staging copy complete)
+    if (g - g0 >= ns && hipEventSynchronize(d->stage_ev[s]) != hipSuccess) err = -1;
     const int shard = st->sched[g % n];
     const size_t want = st->bytes[shard];
     size_t got = 0;
@@ -210,22 +238,67 @@ static void disk_reader(lnf4_stream* st) {
   }
 }
 
-static void disk_close(lnf4_stream* st) {
-  DiskTier* d = st->disk;
-  if (!d) return;
-  if (d->reader.joinable()) {
-    {
-      std::lock_guard<std::mutex> lk(d->mu);
-      d->stop = true;
-    }
-    d->cv.notify_all();
-    d->reader.join();
+static void disk_stop_reader(DiskTier* d) {
+  if (!d->reader.joinable()) return;
+  {
+    std::lock_guard<std::mutex> lk(d->mu);
+    d->stop = true;
   }
-  for (hipEvent_t e : d->stage_ev)
-    if (e) (void)hipEventDestroy(e);
+  d->cv.notify_all();
+  d->reader.join();
+}
+
+// Wait until every copy out of the staging buffers has completed (an event never
+// recorded counts as complete).
+static hipError_t disk_wait_stage_copies(DiskTier* d) {
+  hipError_t first = hipSuccess;
+  for (hipEvent_t e : d->stage_ev) {
+    if (!e) continue;
+    const hipError_t r = hipEventSynchronize(e);
+    if (r != hipSuccess && first == hipSuccess) first = r;
+  }
+  return first;
+}
+
+// Stop the reader, wait for the copies out of the staging buffers and release the tier.
+static hipError_t disk_close(lnf4_stream* st) {
+  DiskTier* d = st->disk;
+  if (!d) return hipSuccess;
+  disk_stop_reader(d);
+  const hipError_t e = disk_wait_stage_copies(d);
+  for (hipEvent_t ev : d->stage_ev)
+    if (ev) (void)hipEventDestroy(ev);
   if (d->fd >= 0) close(d->fd);
   delete d;
   st->disk = nullptr;
+  return e;
+}
+
+// A pass reset before every copy of the pass was issued: the reader has read (or is
+// reading) positions whose copies will never be issued, so it would wait for them for
+// ever.  Stop it, wait for the copies already issued out of the staging buffers, and start
+// a new run at the first position of the next pass, with any earlier read error cleared
+// (a read that fails again is reported again).
+static int disk_restart(lnf4_stream* st, long g0) {
+  DiskTier* d = st->disk;
+  disk_stop_reader(d);
+  const hipError_t e = disk_wait_stage_copies(d);
+  if (e != hipSuccess) return hip_fail(e, "stream_reset (disk tier): waiting for the staging copies");
+  {
+    std::lock_guard<std::mutex> lk(d->mu);
+    d->stop = false;
+    d->base = g0;
+    d->read_done = g0;
+    d->issued = g0;
+    d->err = 0;
+    d->err_pos = -1;
+  }
+  try {
+    d->reader = std::thread(disk_reader, st);
+  } catch (...) {
+    return fail(LNF4_EINVAL, "stream_reset (disk tier): cannot restart the reader thread");
+  }
+  return LNF4_OK;
 }
 
 // Disk tier: copy schedule position g (whose shard is `shard`) into layer buffer `buf`
@@ -235,12 +308,15 @@ static int disk_copy_into(lnf4_stream* st, int buf, int shard, long g) {
   const int s = (int)(g % (long)d->stage.size());
   {
     std::unique_lock<std::mutex> lk(d->mu);
-    d->cv.wait(lk, [&] { return d->read_done > g; });
-    if (d->err) {
+    // a failed read (at this position or an earlier one) ends the wait: the reader may
+    // never reach g after an error
+    d->cv.wait(lk, [&] { return d->read_done > g || (d->err != 0 && d->err_pos <= g) || d->stop; });
+    if (d->err && d->err_pos <= g) {
       if (d->err < 0) return fail(LNF4_EHIP, "stream (disk tier): the reader's wait for a staging copy failed");
       return fail(LNF4_EINVAL, "stream (disk tier): reading schedule position %ld (shard %d) failed: %s", d->err_pos,
                   (int)st->sched[d->err_pos % (long)st->sched.size()], std::strerror(d->err));
     }
+    if (d->read_done <= g) return fail(LNF4_ESTATE, "stream (disk tier): the reader has stopped");
   }
   hipError_t e = hipMemcpyAsync(st->bufs[buf], d->stage[s], st->bytes[shard], hipMemcpyHostToDevice, st->copy);
   if (e != hipSuccess) return hip_fail(e, "stream: hipMemcpyAsync (staging buffer -> layer buffer)");
@@ -359,6 +435,10 @@ static int create_impl(const char* who, const void* const* host_shards, bool hos
       return hip_fail(e, "stream_create: hipEventCreate(slot)");
     }
   }
+  {
+    std::lock_guard<std::mutex> lk(live_mu());
+    live_set().insert(st);
+  }
   *out = st;
   return LNF4_OK;
 }
@@ -455,7 +535,7 @@ int stream_create_disk(const char* path, const int64_t* file_offsets, int32_t dr
 }
 
 int stream_disk_stats(const lnf4_stream* st, int64_t* bytes_read, double* read_seconds) {
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "stream_disk_stats: stream context is NULL or destroyed");
+  if (!is_live(st)) return fail(LNF4_ESTATE, "stream_disk_stats: stream context is NULL or destroyed");
   if (!st->disk) return fail(LNF4_EINVAL, "stream_disk_stats: the context has no disk tier");
   if (!bytes_read || !read_seconds) return fail(LNF4_EINVAL, "stream_disk_stats: NULL output");
   std::lock_guard<std::mutex> lk(st->disk->mu);
@@ -466,7 +546,7 @@ int stream_disk_stats(const lnf4_stream* st, int64_t* bytes_read, double* read_s
 
 int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** dev_ptr_out) {
   const char* who = "stream_layer_step";
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!is_live(st)) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!dev_ptr_out) return fail(LNF4_EINVAL, "%s: dev_ptr_out is NULL", who);
   const int n = (int)st->sched.size();
   if (k != st->next_call) return fail(LNF4_ESTATE, "%s: call %d out of order (expected %d)", who, (int)k, st->next_call);
@@ -542,7 +622,7 @@ int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** de
 
 int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute) {
   const char* who = "stream_slot_load";
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!is_live(st)) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
   if (shard < 0 || shard >= (int)st->host.size()) return fail(LNF4_EINVAL, "%s: shard %d out of range", who, (int)shard);
   if (!st->host[shard]) return fail(LNF4_EINVAL, "%s: shard %d has no host copy (the disk tier streams the layer schedule only)", who, (int)shard);
@@ -563,7 +643,7 @@ int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute) {
 
 int stream_slot_load_part(lnf4_stream* st, int32_t shard, int32_t part, int32_t n_parts, hipStream_t compute) {
   const char* who = "stream_slot_load_part";
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!is_live(st)) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
   if (shard < 0 || shard >= (int)st->host.size()) return fail(LNF4_EINVAL, "%s: shard %d out of range", who, (int)shard);
   if (!st->host[shard]) return fail(LNF4_EINVAL, "%s: shard %d has no host copy (the disk tier streams the layer schedule only)", who, (int)shard);
@@ -609,7 +689,7 @@ int stream_slot_load_part(lnf4_stream* st, int32_t shard, int32_t part, int32_t 
 
 int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out) {
   const char* who = "stream_slot_wait";
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!is_live(st)) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->slot) return fail(LNF4_EINVAL, "%s: the context has no slot buffer", who);
   if (!st->slot_loaded) return fail(LNF4_ESTATE, "%s: no complete slot load issued", who);
   hipError_t e = hipStreamWaitEvent(compute, st->slot_done, 0);
@@ -621,13 +701,17 @@ int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out) 
 
 int stream_reset(lnf4_stream* st, hipStream_t compute) {
   const char* who = "stream_reset";
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
+  if (!is_live(st)) return fail(LNF4_ESTATE, "%s: stream context is NULL or destroyed", who);
   if (!st->resident && st->next_call > 0) {
     // release the last call's buffer; earlier buffers were released by later calls
     const int b = st->reuse ? st->plan_buf[st->next_call - 1] : (st->next_call - 1) % st->nbuf;
     hipError_t e = hipEventRecord(st->release[b], compute);
     if (e != hipSuccess) return hip_fail(e, "stream: hipEventRecord(release at reset)");
     st->release_recorded[b] = 1;
+  }
+  if (st->disk && st->issued < (int)st->sched.size()) {
+    const int rc = disk_restart(st, (long)(st->pass + 1) * (long)st->sched.size());
+    if (rc) return rc;
   }
   if (st->reuse) st->tick += (long)st->sched.size();
   st->next_call = 0;
@@ -639,7 +723,7 @@ int stream_reset(lnf4_stream* st, hipStream_t compute) {
 }
 
 int stream_log(const lnf4_stream* st, lnf4_stream_event* ev, int32_t cap, int32_t* n) {
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "stream_log: stream context is NULL or destroyed");
+  if (!is_live(st)) return fail(LNF4_ESTATE, "stream_log: stream context is NULL or destroyed");
   if (!n) return fail(LNF4_EINVAL, "stream_log: n is NULL");
   if (cap < 0 || (cap > 0 && !ev)) return fail(LNF4_EINVAL, "stream_log: bad buffer");
   const int m = (int)st->log.size() < cap ? (int)st->log.size() : cap;
@@ -649,7 +733,7 @@ int stream_log(const lnf4_stream* st, lnf4_stream_event* ev, int32_t cap, int32_
 }
 
 int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes) {
-  if (!st || !st->alive) return fail(LNF4_ESTATE, "stream_bytes_copied: stream context is NULL or destroyed");
+  if (!is_live(st)) return fail(LNF4_ESTATE, "stream_bytes_copied: stream context is NULL or destroyed");
   if (!bytes) return fail(LNF4_EINVAL, "stream_bytes_copied: bytes is NULL");
   *bytes = st->bytes_copied;
   return LNF4_OK;
@@ -657,9 +741,35 @@ int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes) {
 
 int stream_destroy(lnf4_stream* st) {
   if (!st) return LNF4_OK;
-  disk_close(st);
+  {
+    std::lock_guard<std::mutex> lk(live_mu());
+    if (live_set().erase(st) == 0) return LNF4_OK;  // destroyed before (or never a context)
+  }
+  // every copy this context issued has completed before its buffers go back to the caller
+  hipError_t first = disk_close(st);
+  for (hipEvent_t e : st->copy_done) {
+    const hipError_t r = e ? hipEventSynchronize(e) : hipSuccess;
+    if (r != hipSuccess && first == hipSuccess) first = r;
+  }
+  if (st->slot_done) {
+    const hipError_t r = hipEventSynchronize(st->slot_done);
+    if (r != hipSuccess && first == hipSuccess) first = r;
+  }
   destroy_events(st);
-  delete st;
+  // the tombstone keeps only the struct itself
+  std::vector<const void*>().swap(st->host);
+  std::vector<size_t>().swap(st->bytes);
+  std::vector<void*>().swap(st->bufs);
+  std::vector<int32_t>().swap(st->sched);
+  std::vector<char>().swap(st->release_recorded);
+  std::vector<lnf4_stream_event>().swap(st->log);
+  std::vector<int>().swap(st->plan_buf);
+  std::vector<int>().swap(st->plan_src);
+  std::vector<int>().swap(st->plan_wait);
+  std::vector<int>().swap(st->plan_issue);
+  std::vector<int>().swap(st->holder);
+  std::vector<long>().swap(st->last_tick);
+  if (first != hipSuccess) return hip_fail(first, "stream_destroy: waiting for the copies in flight (the context is released)");
   return LNF4_OK;
 }
 

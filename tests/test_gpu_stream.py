@@ -438,3 +438,95 @@ def test_no_recompute_gives_the_same_gradients():
             assert np.array_equal(gr[p][0], b["grads"][l][p][0])
             assert np.array_equal(gr[p][1], b["grads"][l][p][1])
     assert np.array_equal(a["head"]["dh"], b["head"]["dh"])
+
+
+def _estate(fn, *a):
+    with pytest.raises(lnf4.LNF4Error) as ei:
+        fn(*a)
+    assert ei.value.code == lnf4.LNF4_ESTATE, str(ei.value)
+
+
+@pytest.mark.parametrize("disk", [False, True])
+def test_destroy_is_idempotent_and_a_destroyed_context_gives_estate(disk, tmp_path):
+    """stream_destroy twice returns OK both times; every stream call on the destroyed
+    handle returns ESTATE without touching it; a context created afterwards gets another
+    address and works, and the old handle still gives ESTATE."""
+    L, nbytes = 3, 4096
+    shards = _pinned_shards(L, nbytes, seed=11)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    slot = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sched = ss.sft_schedule(L)
+    comp = torch.cuda.current_stream()
+    if disk:
+        path = tmp_path / "shards.bin"
+        with open(path, "wb") as f:
+            for h in shards:
+                f.write(h.numpy().tobytes())
+        stage = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+
+        def make():
+            return lnf4.stream_create_disk(str(path), [i * nbytes for i in range(L)], stage, nbytes, [nbytes] * L,
+                                           bufs, nbytes, sched, torch.cuda.Stream(), host_shards=shards,
+                                           slot_buf=slot, slot_bytes=nbytes)
+    else:
+        def make():
+            return lnf4.stream_create(shards, [nbytes] * L, bufs, nbytes, sched, 0, torch.cuda.Stream(),
+                                      slot_buf=slot, slot_bytes=nbytes)
+    st = make()
+    lnf4.stream_layer_step(st, 0, comp)
+    lnf4.stream_slot_load(st, 0, comp)
+    lib = lnf4.lib()
+    assert lib.stream_destroy(st) == lnf4.LNF4_OK
+    assert lib.stream_destroy(st) == lnf4.LNF4_OK
+    for fn, a in ((lnf4.stream_layer_step, (st, 1, comp)), (lnf4.stream_log, (st,)),
+                  (lnf4.stream_reset, (st, comp)), (lnf4.stream_slot_load, (st, 0, comp)),
+                  (lnf4.stream_slot_load_part, (st, 0, 0, 2, comp)), (lnf4.stream_slot_wait, (st, comp)),
+                  (lnf4.stream_bytes_copied, (st,)), (lnf4.stream_disk_stats, (st,))):
+        _estate(fn, *a)
+    st2 = make()
+    try:
+        assert st2 != st
+        for k in range(len(sched)):
+            p = lnf4.stream_layer_step(st2, k, comp)
+            j = [i for i, b in enumerate(bufs) if b.data_ptr() == p]
+            assert torch.equal(bufs[j[0]].cpu(), shards[sched[k]]), k
+        assert lnf4.stream_log(st2) == ss.simulate(sched, 2)
+        _estate(lnf4.stream_log, st)
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st2)
+    _estate(lnf4.stream_layer_step, st2, 0, comp)
+
+
+@pytest.mark.parametrize("n_stage", [1, 2, 3])
+def test_disk_tier_reset_in_the_middle_of_a_pass(n_stage, tmp_path):
+    """A disk-tier pass abandoned after 3 calls and reset: the reader restarts at the next
+    pass, and a whole pass then runs with the log of the ring simulator and every buffer
+    holding its shard; a second reset after a finished pass keeps working."""
+    L, nbytes, nbuf = 4, 4096, 2
+    shards = _pinned_shards(L, nbytes, seed=60 + n_stage)
+    path = tmp_path / "shards.bin"
+    with open(path, "wb") as f:
+        for h in shards:
+            f.write(h.numpy().tobytes())
+    stage = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(n_stage)]
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sched = ss.sft_schedule(L)
+    comp = torch.cuda.current_stream()
+    st = lnf4.stream_create_disk(str(path), [i * nbytes for i in range(L)], stage, nbytes, [nbytes] * L, bufs,
+                                 nbytes, sched, torch.cuda.Stream())
+    try:
+        for k in range(3):
+            lnf4.stream_layer_step(st, k, comp)
+        lnf4.stream_reset(st, comp)
+        for rep in range(2):
+            for k in range(len(sched)):
+                p = lnf4.stream_layer_step(st, k, comp)
+                j = [i for i, b in enumerate(bufs) if b.data_ptr() == p]
+                assert j == [k % nbuf]
+                assert torch.equal(bufs[j[0]].cpu(), shards[sched[k]]), (rep, k)
+            assert lnf4.stream_log(st) == ss.simulate(sched, nbuf)
+            lnf4.stream_reset(st, comp)
+    finally:
+        torch.cuda.synchronize()
+        lnf4.stream_destroy(st)
