@@ -130,23 +130,33 @@ def measured_traffic():
         return None, "no counter summary"
 
 
-def cpu_baseline(wl, seed: int, layers: int):
-    """The oracle, as it stands, on one layer of the workload (timed on the host cores)."""
-    import numpy as np
+def _oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _oracle_layer_time(wl, seed: int):
+    """The oracle, as it stands, on one layer-step of a workload: NF4 decode of the seven
+    projections once per read of the layer (2 reads for SFT, 3 with the DPO reference pass;
+    none for bf16 weights), then the layer step (fwd, recompute, bwd [+ adapter-off fwd])
+    at the workload's T.  Returns (seconds, detail)."""
     import synthgen
     from oracle import layer as olayer
     from oracle import nf4 as onf4
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
     T = wl.tokens
-    codes, absmax = {}, {}
+    dpo = "ref" in wl.passes
+    codes, absmax, wbf = {}, {}, {}
     for p in synthgen.PROJ_ORDER:
         o, i = wl.shapes[p]
-        codes[p], absmax[p] = onf4.quantize(synthgen.weight_f32(o, i, seed, "cpu", p))
+        w = synthgen.weight_f32(o, i, seed, "cpu", p)
+        if wl.fmt == "nf4":
+            codes[p], absmax[p] = onf4.quantize(w)
+        else:
+            wbf[p] = onf4.bf16_bits_to_f64(synthgen.to_bf16_bits(w))
     xs = {gi: onf4.bf16_bits_to_f64(synthgen.act_bits(T, wl.shapes[g[0]][1], seed, "cpu-x", gi))
           for gi, g in enumerate(synthgen.GROUPS)}
     dys = {p: onf4.bf16_bits_to_f64(synthgen.act_bits(T, wl.shapes[p][0], seed, "cpu-dy", p))
@@ -156,22 +166,95 @@ def cpu_baseline(wl, seed: int, layers: int):
         o, i = wl.shapes[p]
         ad[p] = (onf4.bf16_bits_to_f64(synthgen.adapter_a_bits(wl.rank, i, seed, "cpu", p)),
                  onf4.bf16_bits_to_f64(synthgen.adapter_b_bits(o, wl.rank, seed, "cpu", p)), wl.scale)
+    reads = 3 if dpo else 2
     t0 = time.perf_counter()
-    Wd = {p: onf4.decode_f64(codes[p], absmax[p]) for p in synthgen.PROJ_ORDER}
+    Wd = ({p: onf4.decode_f64(codes[p], absmax[p]) for p in synthgen.PROJ_ORDER} if wl.fmt == "nf4" else wbf)
     t1 = time.perf_counter()
-    olayer.layer_step(Wd, ad, xs, dys, dpo="ref" in wl.passes)
+    olayer.layer_step(Wd, ad, xs, dys, dpo=dpo)
     t2 = time.perf_counter()
-    t_layer = 2.0 * (t1 - t0) + (t2 - t1)      # two reads (decodes) per layer per step
-    return {
-        "value": T / (layers * t_layer),
-        "unit": "tokens/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": (f"one {wl.name} layer at T={T}: NF4 decode of the 7 projections ({t1 - t0:.2f} s, counted twice: "
-                   f"one decode per read) + oracle layer step fwd/recompute/bwd ({t2 - t1:.2f} s); "
-                   f"stack step = {layers} x layer"),
-        "seconds_per_layer_step": t_layer,
-    }
+    dec = (t1 - t0) if wl.fmt == "nf4" else 0.0
+    secs = reads * dec + (t2 - t1)
+    return secs, {"decode_s": round(dec, 3), "decodes_per_layer_step": reads if wl.fmt == "nf4" else 0,
+                  "layer_step_s": round(t2 - t1, 3)}
+
+
+def _oracle_linear_time(wl, seed: int):
+    """The oracle on the single-linear workload in full: one NF4 decode, forward, backward."""
+    import synthgen
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+
+    (o, i), = wl.shapes.values()
+    T = wl.tokens
+    codes, absmax = onf4.quantize(synthgen.weight_f32(o, i, seed, "cpu-lin"))
+    x = onf4.bf16_bits_to_f64(synthgen.act_bits(T, i, seed, "cpu-lin", "x"))
+    dy = onf4.bf16_bits_to_f64(synthgen.act_bits(T, o, seed, "cpu-lin", "dy"))
+    A = onf4.bf16_bits_to_f64(synthgen.adapter_a_bits(wl.rank, i, seed, "cpu-lin"))
+    B = onf4.bf16_bits_to_f64(synthgen.adapter_b_bits(o, wl.rank, seed, "cpu-lin"))
+    t0 = time.perf_counter()
+    Wd = onf4.decode_f64(codes, absmax)
+    olora.linear_fwd(x, Wd, A, B, wl.scale)
+    olora.linear_bwd(x, dy, Wd, A, B, wl.scale)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, seed: int, layers: int):
+    """The oracle, as it stands (fp64 numpy, never tuned for speed), timed on the host cores.
+
+    The reported value is the benchmark's own workload: one layer-step at its T, scaled
+    to the stack (tokens per second of a step of `layers` layer-steps; the output side is
+    not included).  Beside it, per configuration: the single linear in full (fwd + bwd) on
+    one thread and on all threads, one Qwen2.5-0.5B layer-step on one thread and on all
+    threads, and one layer-step of the Qwen2.5-3B bf16 and the 8B DPO workloads on all
+    threads, each at its real T."""
+    import synthgen
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cores = _oracle_threads()
+    per = {}
+
+    def one_thread(fn):
+        if threadpool_limits is None:
+            return None
+        with threadpool_limits(limits=1):
+            return fn()
+
+    lin = synthgen.WORKLOADS["linear896"]
+    t_all = _oracle_linear_time(lin, seed)
+    t_one = one_thread(lambda: _oracle_linear_time(lin, seed))
+    per["linear896"] = {"what": "one NF4 decode + fwd + bwd of the 896x896 linear, T=256",
+                        "seconds": {"all_threads": round(t_all, 4), "one_thread": None if t_one is None else round(t_one, 4)},
+                        "tokens_per_s": {"all_threads": round(lin.tokens / t_all, 1),
+                                         "one_thread": None if t_one is None else round(lin.tokens / t_one, 1)}}
+    for name, single in (("qwen05b", True), (wl.name, False), ("qwen3b_bf16", False), ("llama8b_dpo", False)):
+        if name in per:
+            continue
+        w = synthgen.WORKLOADS[name]
+        s_all, det = _oracle_layer_time(w, seed)
+        rec = {"what": f"one {name} layer-step at T={w.tokens}", "seconds": {"all_threads": round(s_all, 3)},
+               "tokens_per_s_layer": {"all_threads": round(w.tokens / s_all, 2)},
+               "tokens_per_s_stack": {"all_threads": round(w.tokens / (w.layers * s_all), 3)}, **det}
+        if single:
+            s_one, _ = one_thread(lambda: _oracle_layer_time(w, seed)) or (None, None)
+            rec["seconds"]["one_thread"] = None if s_one is None else round(s_one, 3)
+            rec["tokens_per_s_layer"]["one_thread"] = None if s_one is None else round(w.tokens / s_one, 2)
+        per[name] = rec
+        log(f"cpu baseline {name}: {rec}")
+    main = per[wl.name] if wl.name in per else None
+    if main is None:   # the single linear as the benchmark workload
+        value = per["linear896"]["tokens_per_s"]["all_threads"]
+        sample = per["linear896"]["what"]
+        secs = per["linear896"]["seconds"]["all_threads"]
+    else:
+        secs = main["seconds"]["all_threads"]
+        value = wl.tokens / (layers * secs)
+        sample = (f"one {wl.name} layer at T={wl.tokens}: NF4 decode of the 7 projections once per read of the "
+                  f"layer + oracle layer step fwd/recompute/bwd; stack step = {layers} x layer (output side not "
+                  f"included)")
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": sample,
+            "seconds_per_layer_step": secs, "per_config": per}
 
 
 def dequant_share(wl, seed: int, reps: int = 10):
@@ -365,6 +448,91 @@ def disk_variant(wl, args, L):
         shutil.rmtree(d, ignore_errors=True)
 
 
+def _timed_steps(stack, steps: int, warmup: int, resident: bool = False):
+    import torch
+    for _ in range(warmup):
+        stack.step(resident=resident)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack.step(resident=resident)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1000.0 / steps
+
+
+def _gemm_rate(stack, wl, resident: bool = False):
+    """TFLOP/s of the grouped GEMM calls (skinny LoRA kernels included) over one step, HIP
+    events around every call."""
+    import torch
+    from lora_fine_tuning_nf4_amd.stack import GROUPS
+    keys = [("fwd", gi, True) for gi in range(len(GROUPS))] + [("bwd", gi, True) for gi in range(len(GROUPS))]
+    if stack.dpo:
+        keys += [("fwd", gi, False) for gi in range(len(GROUPS))]
+    stack.timers = {k: ([], []) for k in keys}
+    stack.step(resident=resident)
+    torch.cuda.synchronize()
+    tm, stack.timers = stack.timers, None
+    ms = flops = 0.0
+    for (kind, gi, _on), (st, en) in tm.items():
+        ms += sum(a.elapsed_time(b) for a, b in zip(st, en))
+        flops += gemm_flops(wl, GROUPS[gi], kind) * len(st)
+    return {"gemm_ms_per_step": round(ms, 3), "gemm_tflops": round(flops / (ms / 1000.0) / 1e12, 2),
+            "gemm_frac_of_peak": round(flops / (ms / 1000.0) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def _blocked_on_copies(stack, steps: int = 1):
+    """Compute-stream time per step blocked on copies (layer copies and slot loads): HIP
+    events on the compute stream right before and after every call that enqueues such a
+    wait; no kernel runs between the two, so their distance is the blocked time."""
+    import torch
+    stack.wait_events = []
+    for _ in range(steps):
+        stack.step()
+    torch.cuda.synchronize()
+    we, stack.wait_events = stack.wait_events, None
+    return sum(a.elapsed_time(b) for a, b in we) / steps
+
+
+def other_configs(args):
+    """The other workloads of the path, two or more timed steps each: the Qwen2.5-0.5B-shaped
+    NF4 stack streamed and resident, the Qwen2.5-3B-shaped bf16 stack at 2, 4 and 8 device
+    buffers (and resident), and the DPO step on the 8B stack streamed and resident."""
+    import torch
+    import synthgen
+    from lora_fine_tuning_nf4_amd.stack import StreamedStack
+
+    out = {}
+    for name, nbufs, steps, warm in (("qwen05b", (2,), 5, 2), ("qwen3b_bf16", (2, 4, 8), 2, 1),
+                                     ("llama8b_dpo", (2,), 2, 1)):
+        wl = synthgen.WORKLOADS[name]
+        t0 = time.perf_counter()
+        stack = StreamedStack(wl, n_bufs=nbufs[0], seed=args.seed)
+        rec = {"layers": stack.L, "tokens_per_step": stack.T, "weights": wl.fmt,
+               "lora": {"r": wl.rank, "alpha": wl.alpha, "targets": list(wl.adapted)},
+               "setup_s": round(time.perf_counter() - t0, 1)}
+        try:
+            for nb in nbufs:
+                if nb != stack.n_bufs:
+                    stack.rebuffer(nb)
+                b0 = stack.bytes_copied()
+                ms = _timed_steps(stack, steps, warm)
+                h2d = (stack.bytes_copied() - b0) // (steps + warm)
+                rec[f"streamed_nbuf{nb}"] = {"ms_per_step": round(ms, 3),
+                                             "tokens_per_s": round(stack.T / (ms / 1000.0), 1),
+                                             "h2d_bytes_per_step": h2d,
+                                             "compute_blocked_on_copies_ms": round(_blocked_on_copies(stack), 3)}
+            ms = _timed_steps(stack, steps, warm, resident=True)
+            rec["resident"] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(stack.T / (ms / 1000.0), 1),
+                               **_gemm_rate(stack, wl, resident=True)}
+        finally:
+            stack.close()
+            del stack
+            torch.cuda.empty_cache()
+        out[name] = rec
+        log(f"config {name}: {rec}")
+    return out
+
+
 def decoder_model_run(args):
     """The whole decoder model on the 8B stack (embedding, 32 real decoder layers with
     RMSNorm, RoPE, causal GQA attention, SwiGLU and residuals, final norm, lm_head and
@@ -437,6 +605,8 @@ def main():
                     help="skip the whole-decoder-model run (attention, norms, SwiGLU between the projections)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the stream-variant runs (buffer reuse, no recompute, disk tier)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (Qwen2.5-0.5B NF4, Qwen2.5-3B bf16 at 2/4/8 buffers, 8B DPO)")
     ap.add_argument("--loss-chunk", type=int, default=None,
                     help="tokens per chunk of the output head and its loss (default: all tokens at once)")
     ap.add_argument("--study", action="store_true",
@@ -514,6 +684,7 @@ def main():
             head_ms[k[1]] = sum(ms) / max(1, len(ms))
         else:
             call_ms[k] = ms
+    blocked_ms = _blocked_on_copies(stack, n_bd)
     gemm_time_ms = sum(sum(v) for v in call_ms.values()) / n_bd
     gemm_flops_step = 0.0
     for (kind, gi, _on), ts in call_ms.items():
@@ -573,6 +744,8 @@ def main():
         "h2d": {
             "bytes_per_step": (b1 - b0) // args.steps,
             "avg_GBps_over_step": round((b1 - b0) / args.steps / (ms_per_step / 1000.0) / 1e9, 2),
+            "compute_blocked_on_copies_ms_per_step": round(blocked_ms, 3),
+            "compute_blocked_share_of_step": round(blocked_ms / ms_per_step, 4),
         },
     }
 
@@ -635,16 +808,6 @@ def main():
         torch.cuda.synchronize()
         head[f"embed_in_{L}_parts_GBps"] = round(h.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
         result["h2d"]["head_slot"] = head
-    # the stream schedule alone: the same copies, waits and slot loads with no GEMMs
-    for _ in range(2):
-        stack.step(compute=False)
-    torch.cuda.synchronize()
-    c0 = time.perf_counter()
-    for _ in range(args.steps):
-        stack.step(compute=False)
-    torch.cuda.synchronize()
-    result["h2d"]["schedule_only_ms_per_step"] = round((time.perf_counter() - c0) * 1000.0 / args.steps, 3)
-
     # a plain device copy of known size, the reference point that scales rocprofv3's
     # FETCH_SIZE / WRITE_SIZE counters to bytes in a counter run of this same command
     ca = torch.ones(CAL_ELEMS, dtype=torch.float32, device="cuda")
@@ -661,6 +824,8 @@ def main():
 
     if not args.no_variants:
         result["stream_variants"] = stream_variants(wl, args, L)
+    if not args.no_configs and wl.name == "llama8b" and L == wl.layers:
+        result["other_configs"] = other_configs(args)
     if not args.no_model and L == wl.layers:
         result["decoder_model"] = decoder_model_run(args)
 

@@ -120,6 +120,9 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c \"import __graft_entry__ as g; "
                                f"g.build()\"` (hipcc, gfx950)")
+        # torch brings its own HIP runtime; loading it first makes the library bind to that
+        # same runtime (one HIP runtime per process), whatever the caller imported first
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         _declare(L)
         _lib = L

@@ -141,6 +141,10 @@ class StreamedStack:
         self.st = lnf4.stream_create(shards, sizes, self.bufs, self.shard_bytes, sched, mode, self.copy, self.slot,
                                      slot_bytes)
         self.timers = None
+        # when a list: (event before, event after) on the compute stream around every call that
+        # makes compute wait for a copy (layer steps and slot waits); between the two events
+        # the stream runs no kernel, so their distance is the time compute was blocked
+        self.wait_events = None
         self._embed_in_slot = False   # the next step's embed_tokens was loaded during the last backward
         self.st_res = None
         self.res_bufs = None
@@ -243,6 +247,19 @@ class StreamedStack:
             ev.record(self.compute)
             tm[key][end].append(ev)
 
+    def _waited(self, fn):
+        """Run a stream call that enqueues a wait on the compute stream, bracketed by timing
+        events when wait_events is set."""
+        we = self.wait_events
+        if we is None:
+            return fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.compute)
+        out = fn()
+        e1.record(self.compute)
+        we.append((e0, e1))
+        return out
+
     def _lm_head(self, ptr):
         return lnf4.make_weight(lnf4.FMT_BF16, ptr, None, self.wl.vocab, self.wl.hidden, 64)
 
@@ -331,7 +348,7 @@ class StreamedStack:
         if slot:
             if not self._embed_in_slot:   # first step: nothing trickled in yet
                 lnf4.stream_slot_load(st, self.head_ids[0], self.compute)   # embed_tokens
-            ptr = lnf4.stream_slot_wait(st, self.compute)
+            ptr = self._waited(lambda: lnf4.stream_slot_wait(st, self.compute))
             self._embed_in_slot = False
             if head:
                 self._embed(ptr)
@@ -339,13 +356,13 @@ class StreamedStack:
             self._embed(self.res_head[0])
         n_fwd = 2 * L if self.dpo else L
         for k, layer in enumerate(self.schedule):
-            base = lnf4.stream_layer_step(st, k, self.compute)
+            base = self._waited(lambda: lnf4.stream_layer_step(st, k, self.compute))
             if k == L or k == n_fwd:
                 # the output head of the forward pass that just ended.  It runs after this
                 # call's stream step, which released the last forward layer's buffer, so the
                 # next layer copy overlaps the head instead of waiting behind it.
                 if slot:
-                    ptr = lnf4.stream_slot_wait(st, self.compute)
+                    ptr = self._waited(lambda: lnf4.stream_slot_wait(st, self.compute))
                 elif head:
                     ptr = self.res_head[1]
                 if head:
@@ -375,6 +392,21 @@ class StreamedStack:
         lnf4.stream_reset(st, self.compute)
         if slot:
             self._embed_in_slot = True
+
+    def rebuffer(self, n_bufs: int):
+        """Replace the ring context with one over n_bufs device buffers (same host shards,
+        schedule, slot and mode)."""
+        torch.cuda.synchronize(self.dev)
+        lnf4.stream_destroy(self.st)
+        self.st = None
+        self.n_bufs = n_bufs
+        self.bufs = [torch.empty(self.shard_bytes, dtype=torch.uint8, device=self.dev) for _ in range(n_bufs)]
+        sizes = [self.shard_bytes] * self.L + [h.numel() for h in self.all_shards[self.L:]]
+        slot_bytes = self.slot.numel() if self.slot is not None else 0
+        mode = lnf4.STREAM_REUSE if self.reuse else lnf4.STREAM_RING
+        self.st = lnf4.stream_create(self.all_shards, sizes, self.bufs, self.shard_bytes, self.schedule, mode,
+                                     self.copy, self.slot, slot_bytes)
+        self._embed_in_slot = False
 
     def log(self):
         return lnf4.stream_log(self.st)

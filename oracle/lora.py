@@ -67,16 +67,6 @@ def linear_bwd(x, dy, Wd, A=None, B=None, scale: float = 0.0):
     return dx, dA, dB
 
 
-def lora_u(x, A):
-    """u = x A^T, the rank-r activation the forward saves."""
-    return _f64(x) @ _f64(A).T
-
-
-def lora_v(dy, B):
-    """v = dy B, the rank-r gradient the backward forms first."""
-    return _f64(dy) @ _f64(B)
-
-
 def trainable_params(shapes, r: int) -> int:
     """Adapter parameter count r * (in + out) summed over adapted [out, in] projections."""
     return sum(r * (o + i) for (o, i) in shapes)
