@@ -167,6 +167,29 @@ int lora_linear_bwd(const lnf4_weight* W, const uint16_t* x, const uint16_t* dy,
                     size_t ws_bytes, hipStream_t stream);
 
 /*
+ * lora_linear_bwd for callers that cannot allocate device memory or take a workspace
+ * argument (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and arguments minus the workspace, which is instead
+ * a fixed array of LNF4_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until
+ * the process ends).  The call allocates nothing.
+ *  - Limit: shapes whose workspace (v = dy B, a recomputed u and the adapter-gradient
+ *    partial sums) exceeds LNF4_NOALLOC_SCRATCH_BYTES are rejected with ESHAPE.  For
+ *    example a single 14336 x 4096 projection at T = 2048 with r = 16 needs about 38 MB.
+ *  - The input-gradient GEMM is never split over K here (lora_linear_bwd splits it for few
+ *    output tiles and a long K): dA and dB are bitwise those of lora_linear_bwd; dx is
+ *    bitwise the same where lora_linear_bwd does not split, else equal up to the order of
+ *    its fp32 sums.
+ *  - Every call on one GPU uses that GPU's one array: calls that overlap in time on one
+ *    GPU (on different streams, or from different threads) race and give wrong results.
+ *    Calls ordered on one stream are safe.
+ * Errors: as lora_linear_bwd (ESHAPE also for a workspace need above the limit).
+ */
+#define LNF4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lora_linear_bwd_noalloc(const lnf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t T,
+                            const uint16_t* A, const uint16_t* B, int32_t r, float scale, const float* u_saved,
+                            uint16_t* dx, float* dA, float* dB, int32_t accumulate, hipStream_t stream);
+
+/*
  * Projections that read the same input (q, k, v read the attention input; gate and
  * up read the MLP input) run as one grouped launch.  In the forward each projection
  * writes its own y; in backward the group's input gradient is the sum over its

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "lnf4.h"
@@ -182,7 +183,9 @@ struct BwdPlan {
   size_t total;
 };
 
-static void plan_bwd(const lnf4_proj* projs, int32_t n, int64_t T, const int* on, BwdPlan& pl) {
+// split_ok = false: the dx GEMM is launched unsplit, so no split-K sums are planned
+static void plan_bwd(const lnf4_proj* projs, int32_t n, int64_t T, const int* on, BwdPlan& pl,
+                     bool split_ok = true) {
   const size_t none = (size_t)-1;
   pl.n_chunks = 0;
   for (int p = 0; p < LNF4_MAX_GROUP; ++p) {
@@ -227,8 +230,8 @@ static void plan_bwd(const lnf4_proj* projs, int32_t n, int64_t T, const int* on
   // single linear does not know the format)
   int total_kb = 0;
   for (int p = 0; p < n; ++p) total_kb += (int)((projs[p].W.out_f + 63) / 64);
-  size_t dxb = dx_split_bytes((int)T, in_f, total_kb, 0);
-  const size_t dxb1 = dx_split_bytes((int)T, in_f, total_kb, 1);
+  size_t dxb = split_ok ? dx_split_bytes((int)T, in_f, total_kb, 0) : 0;
+  const size_t dxb1 = split_ok ? dx_split_bytes((int)T, in_f, total_kb, 1) : 0;
   dxb = dxb > dxb1 ? dxb : dxb1;
   pl.dx_off = dxb ? off : none;
   off += round256(dxb);
@@ -292,8 +295,40 @@ size_t group_bwd_ws(const lnf4_proj* projs, int32_t n, int64_t T) {
   return pl.total;
 }
 
+// ---------------------------------------------------------------- library scratch
+// The workspace of lora_linear_bwd_noalloc: a fixed device array that every call on a GPU
+// shares (each GPU holds its own copy, for the life of the process).  In host code the
+// array's name is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = LNF4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_address(void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice (library scratch)");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LNF4_EINVAL, "%s: device %d beyond the %d the library tracks", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress (library scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LNF4_OK;
+}
+
+// lib_scratch: the workspace is the library's scratch array (ws, ws_bytes ignored); the dx
+// GEMM is then never split, so the workspace holds only v, a recomputed u and the
+// adapter-gradient partial sums.
 int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, uint16_t* dx,
-                   int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t s, const char* who) {
+                   int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t s, const char* who,
+                   bool lib_scratch = false) {
   if (!projs) return fail(LNF4_EINVAL, "%s: projs is NULL", who);
   if (n < 1 || n > LNF4_MAX_GROUP) return fail(LNF4_EINVAL, "%s: n=%d outside 1..%d", who, (int)n, LNF4_MAX_GROUP);
   int rc = check_tokens(T, who);
@@ -333,7 +368,15 @@ int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
   }
   (void)need_dy;
   BwdPlan pl;
-  plan_bwd(projs, n, T, on, pl);
+  plan_bwd(projs, n, T, on, pl, !lib_scratch);
+  if (lib_scratch) {
+    if (pl.total > kScratchBytes)
+      return fail(LNF4_ESHAPE, "%s: these shapes need %zu bytes of scratch; the library's fixed scratch holds %zu", who,
+                  pl.total, kScratchBytes);
+    ws = nullptr;
+    ws_bytes = kScratchBytes;
+    if (pl.total > 0 && (rc = scratch_address(&ws, who))) return rc;
+  }
   if (pl.total > 0) {
     if (!ws) return fail(LNF4_EINVAL, "%s: workspace is NULL (%zu bytes needed)", who, pl.total);
     if (ws_bytes < pl.total) return fail(LNF4_ESHAPE, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, pl.total);
@@ -431,7 +474,7 @@ int group_bwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
       kb += (int)((P.W.out_f + 63) / 64);
     }
     a.total_kb = kb;
-    a.part = pl.dx_off != (size_t)-1 ? (float*)(wsb + pl.dx_off) : nullptr;
+    a.part = pl.dx_off != (size_t)-1 ? (float*)(wsb + pl.dx_off) : nullptr;  // NULL: unsplit
     if ((e = launch_dx(a, projs[0].W.fmt, s)) != hipSuccess) return hip_fail(e, "fused dx GEMM launch");
   }
   // adapter gradients: dA of each chunk against x, dB of each projection against its dy
@@ -563,6 +606,24 @@ int lora_linear_bwd(const lnf4_weight* W, const uint16_t* x, const uint16_t* dy,
   p.dA = dA;
   p.dB = dB;
   return group_bwd_impl(&p, 1, x, T, dx, accumulate, workspace, ws_bytes, stream, "lora_linear_bwd");
+}
+
+int lora_linear_bwd_noalloc(const lnf4_weight* W, const uint16_t* x, const uint16_t* dy, int64_t T,
+                            const uint16_t* A, const uint16_t* B, int32_t r, float scale, const float* u_saved,
+                            uint16_t* dx, float* dA, float* dB, int32_t accumulate, hipStream_t stream) {
+  if (!W) return fail(LNF4_EINVAL, "lora_linear_bwd_noalloc: weight descriptor is NULL");
+  lnf4_proj p;
+  std::memset(&p, 0, sizeof p);
+  p.W = *W;
+  p.A = A;
+  p.B = B;
+  p.r = r;
+  p.scale = scale;
+  p.u = const_cast<float*>(u_saved);
+  p.dy = dy;
+  p.dA = dA;
+  p.dB = dB;
+  return group_bwd_impl(&p, 1, x, T, dx, accumulate, nullptr, 0, stream, "lora_linear_bwd_noalloc", true);
 }
 
 int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,

@@ -73,6 +73,8 @@ def _declare(L):
         "lora_linear_bwd_workspace": (sz, [i64, i64, i64, i32]),
         "lora_linear_bwd": (i32, [POINTER(lnf4_weight), vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, i32, vp,
                                   sz, vp]),
+        "lora_linear_bwd_noalloc": (i32, [POINTER(lnf4_weight), vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, i32,
+                                          vp]),
         "lora_group_fwd": (i32, [POINTER(lnf4_proj), i32, vp, i64, i32, vp]),
         "lora_group_bwd_workspace": (sz, [POINTER(lnf4_proj), i32, i64]),
         "lora_group_bwd": (i32, [POINTER(lnf4_proj), i32, vp, i64, vp, i32, vp, sz, vp]),
@@ -201,6 +203,13 @@ def lora_linear_bwd(W: lnf4_weight, x, dy, T: int, A, B, r: int, scale: float, u
     _check(lib().lora_linear_bwd(ctypes.byref(W), _ptr(x), _ptr(dy), T, _ptr(A), _ptr(B), r, scale, _ptr(u_saved),
                                  _ptr(dx), _ptr(dA), _ptr(dB), accumulate, _ptr(workspace), ws_bytes,
                                  _stream(stream)))
+
+
+def lora_linear_bwd_noalloc(W: lnf4_weight, x, dy, T: int, A, B, r: int, scale: float, u_saved, dx, dA, dB,
+                            accumulate: int, stream=None):
+    """lora_linear_bwd with the library's fixed scratch as its workspace (allocates nothing)."""
+    _check(lib().lora_linear_bwd_noalloc(ctypes.byref(W), _ptr(x), _ptr(dy), T, _ptr(A), _ptr(B), r, scale,
+                                         _ptr(u_saved), _ptr(dx), _ptr(dA), _ptr(dB), accumulate, _stream(stream)))
 
 
 def make_proj(W: lnf4_weight, A=None, B=None, r: int = 0, scale: float = 0.0, y=None, u=None, dy=None, dA=None,

@@ -1,0 +1,83 @@
+"""lora_linear_bwd_noalloc, the backward that takes no workspace and allocates nothing (its
+workspace is a fixed device array inside the library), against lora_linear_bwd through the
+C ABI: two calls in a row on one stream, the second with a smaller input, and both against
+the oracle.  dA and dB are the same kernels on the same partial layout, so they must be
+bitwise equal; dx is bitwise equal where lora_linear_bwd does not split the input-gradient
+GEMM over K, and within max|err| <= 2e-2 rms(ref) of it where it does.  A shape whose
+workspace exceeds the fixed scratch is rejected with ESHAPE before any device work."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from lora_fine_tuning_nf4_amd import lnf4
+
+FAKE = 1 << 20  # a 16-byte aligned non-NULL address that is never dereferenced
+
+
+def test_noalloc_rejects_a_workspace_beyond_the_scratch():
+    L = lnf4.lib()
+    # r = 64 over in = 16384 at T = 2048: 32 T-split partials of 16384 x 64 fp32 for dA alone
+    W = lnf4.lnf4_weight(0, FAKE, FAKE, 64, 16384, 64)
+    rc = L.lora_linear_bwd_noalloc(ctypes.byref(W), FAKE, FAKE, 2048, FAKE, FAKE, 64, 1.0, None, FAKE, FAKE, FAKE,
+                                   0, None)
+    assert rc == lnf4.LNF4_ESHAPE
+    assert "scratch" in lnf4.lnf4_last_error()
+    assert L.lora_linear_bwd_noalloc(None, FAKE, FAKE, 4, None, None, 0, 0.0, None, FAKE, None, None, 0,
+                                     None) == lnf4.LNF4_EINVAL
+    # T = 0 with no gradients asked for is a no-op that touches no device
+    W = lnf4.lnf4_weight(0, FAKE, FAKE, 128, 128, 64)
+    assert L.lora_linear_bwd_noalloc(ctypes.byref(W), None, None, 0, None, None, 0, 0.0, None, None, None, None, 0,
+                                     None) == lnf4.LNF4_OK
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_the_workspace_call_twice_in_a_row():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():  # pragma: no cover
+        pytest.skip("needs a GPU")
+    from helpers import DevCase, bf16_f64, check_tol, host_f32, host_u16, make_case, oracle_bwd
+
+    # (T, out, in, r, alpha, u saved, accumulate): the first splits dx over K in
+    # lora_linear_bwd (one 128-row tile over two 256-column tiles, K = 4096 in 4 splits);
+    # the second is smaller, recomputes u and accumulates
+    cases = [(128, 4096, 512, 8, 16.0, True, 0), (64, 896, 256, 4, 8.0, False, 1)]
+    stream = torch.cuda.current_stream()
+    for i, (T, out_f, in_f, r, alpha, saved, acc) in enumerate(cases):
+        c = make_case(70 + i, T, out_f, in_f, r, alpha, 0, tag=f"noalloc{i}")
+        d = DevCase(c)
+        u = None
+        if saved:
+            lnf4.lora_linear_fwd(d.W, d.x, T, d.A, d.B, r, c.scale, d.y, d.u)
+            u = d.u
+        outs = {}
+        for name in ("ws", "noalloc"):
+            dx = torch.zeros_like(d.dx) if acc else torch.empty_like(d.dx)
+            dA = torch.zeros_like(d.dA) if acc else torch.empty_like(d.dA)
+            dB = torch.zeros_like(d.dB) if acc else torch.empty_like(d.dB)
+            if acc:   # accumulate onto a known start
+                dx.copy_(d.dy[:, :in_f] if out_f >= in_f else torch.zeros_like(d.dx))
+                dA.fill_(0.5)
+                dB.fill_(-0.25)
+            if name == "ws":
+                ws_bytes = lnf4.lora_linear_bwd_workspace(T, out_f, in_f, r)
+                ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+                lnf4.lora_linear_bwd(d.W, d.x, d.dy, T, d.A, d.B, r, c.scale, u, dx, dA, dB, acc, ws, ws_bytes,
+                                     stream)
+            else:
+                lnf4.lora_linear_bwd_noalloc(d.W, d.x, d.dy, T, d.A, d.B, r, c.scale, u, dx, dA, dB, acc, stream)
+            outs[name] = (dx, dA, dB)
+        torch.cuda.synchronize()
+        (dx0, dA0, dB0), (dx1, dA1, dB1) = outs["ws"], outs["noalloc"]
+        assert np.array_equal(host_f32(dA0).view(np.uint32), host_f32(dA1).view(np.uint32)), i
+        assert np.array_equal(host_f32(dB0).view(np.uint32), host_f32(dB1).view(np.uint32)), i
+        g0, g1 = bf16_f64(host_u16(dx0)), bf16_f64(host_u16(dx1))
+        if i == 1:
+            assert np.array_equal(host_u16(dx0), host_u16(dx1))   # no split in either call
+        check_tol(g1, g0, f"dx (noalloc vs workspace call) case {i}")
+        # and both against the oracle
+        dx_ref, dA_ref, dB_ref = oracle_bwd(c)
+        start_dx = bf16_f64(host_u16(d.dy[:, :in_f])) if (acc and out_f >= in_f) else 0.0
+        check_tol(g1, dx_ref + start_dx, f"dx case {i}")
+        check_tol(host_f32(dA1).astype(np.float64), dA_ref + (0.5 if acc else 0.0), f"dA case {i}")
+        check_tol(host_f32(dB1).astype(np.float64), dB_ref + (-0.25 if acc else 0.0), f"dB case {i}")
