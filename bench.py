@@ -377,14 +377,18 @@ def t_sweep(wl, seed: int, nbuf: int, steps: int, tokens=(2048, 4096, 8192)):
 def stream_variants(wl, args, L):
     """The same streamed step with the stream variants: buffer reuse (a layer still in a
     buffer is not copied again: at the forward/backward turn and at the next step's
-    start), and no recompute (the backward uses the forward's saved rank-r activations
-    and skips the forward re-run; the layer is still read twice, for dx)."""
+    start), no recompute (the backward uses the forward's saved rank-r activations
+    and skips the forward re-run; the layer is still read twice, for dx), and the
+    embedding rows read from the page-locked host table (the slot then keeps lm_head
+    from step to step: no per-step slot copies)."""
     import torch
     from lora_fine_tuning_nf4_amd.stack import StreamedStack
 
     out = {}
     for name, kw in (("reuse", {"reuse": True}), ("no_recompute", {"recompute": False}),
-                     ("reuse_no_recompute", {"reuse": True, "recompute": False})):
+                     ("reuse_no_recompute", {"reuse": True, "recompute": False}),
+                     ("embed_from_host", {"embed_from_host": True}),
+                     ("embed_from_host_reuse", {"embed_from_host": True, "reuse": True})):
         stack = StreamedStack(wl, n_bufs=args.nbuf, seed=args.seed, layers=L, loss_chunk=args.loss_chunk, **kw)
         try:
             for _ in range(max(2, args.warmup)):
@@ -397,7 +401,8 @@ def stream_variants(wl, args, L):
             torch.cuda.synchronize()
             ms = (time.perf_counter() - t0) * 1000.0 / args.steps
             out[name] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(stack.T / (ms / 1000.0), 2),
-                         "h2d_bytes_per_step": (stack.bytes_copied() - b0) // args.steps}
+                         "h2d_bytes_per_step": (stack.bytes_copied() - b0) // args.steps,
+                         "compute_blocked_on_copies_ms": round(_blocked_on_copies(stack), 3)}
         finally:
             stack.close()
             del stack

@@ -246,12 +246,17 @@ int lnf4_shard_layout(int32_t n_proj, const int64_t* out_f, const int64_t* in_f,
 
 /*
  * Embedding lookup: out[t][:] = table[ids[t]][:] (bf16 rows copied bitwise).
- *   table   device bf16 [vocab, hidden] (the slot holding embed_tokens), 16-byte aligned
+ *   table   bf16 [vocab, hidden], 16-byte aligned: either device memory (the slot holding
+ *           embed_tokens) or page-locked host memory mapped for the device, whose T rows
+ *           the kernel then reads over the host link (the step's rows only, instead of
+ *           copying the whole table into the slot)
  *   hidden  a positive multiple of 8
  *   ids     device int32 [T]; an id outside [0, vocab) yields a zero row (device ids
  *           cannot be checked by the host)
  *   out     device bf16 [T, hidden], 16-byte aligned
- * Errors: EINVAL (T, NULL), ESHAPE (vocab, hidden), EALIGN, EHIP.
+ * After the argument checks the runtime is asked what kind of memory the table is.
+ * Errors: EINVAL (T, NULL, a table that is neither device memory nor mapped page-locked
+ * host memory), ESHAPE (vocab, hidden), EALIGN, EHIP.
  */
 int lnf4_embed_gather(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* ids, int64_t T,
                       uint16_t* out, hipStream_t stream);

@@ -1,10 +1,12 @@
 // C ABI of the output side of a step: embedding gather, token cross-entropy, sequence
 // sums and the sigmoid preference loss.  Validation is host code and runs before any HIP
-// call; the contracts are in include/lnf4.h.
+// call (the embedding gather then asks the runtime what kind of memory its table is); the
+// contracts are in include/lnf4.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "lnf4.h"
 #include "head.hpp"
@@ -30,7 +32,22 @@ int lnf4_embed_gather(const uint16_t* table, int64_t vocab, int64_t hidden, cons
   if (T == 0) return LNF4_OK;
   if (!table || !ids || !out) return fail(LNF4_EINVAL, "%s: NULL pointer", who);
   if (!aligned(table, 16) || !aligned(out, 16) || !aligned(ids, 4)) return fail(LNF4_EALIGN, "%s: misaligned pointer", who);
-  const hipError_t e = launch_embed_gather(table, vocab, hidden, ids, T, out, stream);
+  // the table may be device memory or page-locked host memory mapped for the device (the
+  // rows are then read over the host link): ask the runtime which, and take the device's
+  // address of a host table, so that a pointer the device cannot read is refused here
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof attr);
+  if (hipPointerGetAttributes(&attr, table) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(LNF4_EINVAL, "%s: table is neither device memory nor page-locked host memory", who);
+  }
+  const uint16_t* dtab = table;
+  if (attr.type == hipMemoryTypeHost) {
+    if (!attr.devicePointer) return fail(LNF4_EINVAL, "%s: the page-locked host table is not mapped for the device", who);
+    dtab = (const uint16_t*)((const char*)attr.devicePointer + ((const char*)table - (const char*)attr.hostPointer));
+    if (!aligned(dtab, 16)) return fail(LNF4_EALIGN, "%s: misaligned device address of the host table", who);
+  }
+  const hipError_t e = launch_embed_gather(dtab, vocab, hidden, ids, T, out, stream);
   return e == hipSuccess ? LNF4_OK : hip_fail(e, "embed gather launch");
 }
 

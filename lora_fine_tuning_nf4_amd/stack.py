@@ -59,7 +59,7 @@ class StreamedStack:
     def __init__(self, wl: synthgen.Workload, n_bufs: int = 2, seed: int = 0,
                  layers: int | None = None, tokens: int | None = None, head_slot: bool = True,
                  dpo: bool | None = None, loss_chunk: int | None = None, reuse: bool = False,
-                 recompute: bool = True, device: str = "cuda"):
+                 recompute: bool = True, embed_from_host: bool = False, device: str = "cuda"):
         self.wl = wl
         self.L = layers if layers is not None else wl.layers
         self.T = tokens if tokens is not None else wl.tokens
@@ -69,6 +69,9 @@ class StreamedStack:
         self.seed = seed
         self.reuse = reuse          # buffers that still hold a needed layer are used without a copy
         self.recompute = recompute  # False: the backward uses the forward's saved u and skips the re-run
+        # True: the embedding lookup reads its T rows straight from the page-locked host table
+        # and the slot keeps the untied lm_head from one step to the next (no per-step slot copies)
+        self.embed_from_host = embed_from_host
         dev = torch.device(device)
         self.dev = dev
         T = self.T
@@ -145,7 +148,10 @@ class StreamedStack:
         # makes compute wait for a copy (layer steps and slot waits); between the two events
         # the stream runs no kernel, so their distance is the time compute was blocked
         self.wait_events = None
+        self.keep_log = False        # True: step() keeps the pass's event log in last_log
+        self.last_log = None
         self._embed_in_slot = False   # the next step's embed_tokens was loaded during the last backward
+        self._lm_head_in_slot = False  # embed_from_host: the lm_head was loaded into the slot
         self.st_res = None
         self.res_bufs = None
 
@@ -345,7 +351,13 @@ class StreamedStack:
         st = self.enable_resident() if resident else self.st
         slot = self.slot is not None and not resident
         head = self.head and compute
-        if slot:
+        if slot and self.embed_from_host:
+            if not self._lm_head_in_slot:   # loaded once; the embedding never enters the slot
+                lnf4.stream_slot_load(st, self.head_ids[1], self.compute)
+                self._lm_head_in_slot = True
+            if head:
+                self._embed(self.all_shards[self.head_ids[0]])   # T rows over the host link
+        elif slot:
             if not self._embed_in_slot:   # first step: nothing trickled in yet
                 lnf4.stream_slot_load(st, self.head_ids[0], self.compute)   # embed_tokens
             ptr = self._waited(lambda: lnf4.stream_slot_wait(st, self.compute))
@@ -376,12 +388,12 @@ class StreamedStack:
                 ref_pass = self.dpo and k < L
                 for gi in range(len(GROUPS) if compute else 0):
                     self._group_fwd(layer, gi, base, adapters=not ref_pass)
-                if slot and k == L - 1:
+                if slot and k == L - 1 and not self.embed_from_host:
                     # the untied lm_head takes the slot at the end of the first forward pass
                     # and stays there for the second (DPO)
                     lnf4.stream_slot_load(st, self.head_ids[1], self.compute)
             else:
-                if slot:
+                if slot and not self.embed_from_host:
                     # the backward is compute-bound: the next step's embed_tokens trickles into
                     # the slot in one piece per layer, between the layer copies
                     lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L, self.compute)
@@ -389,8 +401,10 @@ class StreamedStack:
                     self._group_fwd(layer, gi, base, adapters=True)   # recompute from the checkpointed inputs
                 for gi in reversed(range(len(GROUPS) if compute else 0)):
                     self._group_bwd(layer, gi, base)
+        if self.keep_log:
+            self.last_log = lnf4.stream_log(st)
         lnf4.stream_reset(st, self.compute)
-        if slot:
+        if slot and not self.embed_from_host:
             self._embed_in_slot = True
 
     def rebuffer(self, n_bufs: int):
@@ -407,6 +421,7 @@ class StreamedStack:
         self.st = lnf4.stream_create(self.all_shards, sizes, self.bufs, self.shard_bytes, self.schedule, mode,
                                      self.copy, self.slot, slot_bytes)
         self._embed_in_slot = False
+        self._lm_head_in_slot = False
 
     def log(self):
         return lnf4.stream_log(self.st)
@@ -446,6 +461,8 @@ class StreamedStack:
         lnf4.stream_destroy(self.st)
         self.st = st
         self.disk_path = path
+        self._embed_in_slot = False
+        self._lm_head_in_slot = False
 
     def disk_stats(self):
         """(bytes read from the disk file, seconds in reads) of a disk-tier context."""

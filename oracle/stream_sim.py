@@ -169,3 +169,100 @@ def check_reuse_log(logs, schedule, n_bufs: int) -> None:
                 assert layer == schedule[call]
                 assert content.get(buf) == layer, (call, buf, content.get(buf), layer)
                 last_user[buf] = call
+
+
+# ------------------------------------------------------------------ the head slot of a stack step
+SLOT_COPY = 2
+SLOT_WAIT = 3
+
+
+def stack_step_log(n_layers: int, n_bufs: int, dpo: bool = False, embed_from_host: bool = False,
+                   first: bool = True, loads_before: int = 0):
+    """Event log of one step of the streamed stack with its head slot (layer ring as in
+    ``simulate``).  The slot holds embed_tokens at the start of the step and the untied
+    lm_head at the forward/backward turn (the Soup deep dive, "How layer streaming works":
+    embed_tokens and lm_head share one device slot).  Slot schedule of the stack (a reading:
+    the pages only say that they share it):
+
+    * the embedding is loaded whole before the first step; in every backward call one of L
+      parts of the next step's embedding follows that call's layer copies (part 0 waits
+      for the head, the slot's last user);
+    * lm_head is loaded after the last forward call of the (first) forward pass and waited
+      for right after the stream step of the first call past each forward pass (DPO: the
+      reference pass and the policy pass), where the head runs;
+    * ``embed_from_host``: the embedding rows are read from the host table, so the slot
+      only ever holds lm_head, loaded once at the start of the first step.
+
+    A SLOT_COPY event is (SLOT_COPY, call, load index, shard, -1 whole or -1 - part,
+    previous load index for a whole load or part 0, else -1); a SLOT_WAIT event is
+    (SLOT_WAIT, call, last complete load, -1, -1, last complete load).  The shard ids of
+    the slot are ``n_layers`` (embed_tokens) and ``n_layers + 1`` (lm_head); ``loads_before``
+    counts the slot loads completed in earlier steps."""
+    L = n_layers
+    E, LM = L, L + 1
+    sched = dpo_schedule(L) if dpo else sft_schedule(L)
+    ring = simulate(sched, n_bufs)
+    n_fwd = 2 * L if dpo else L
+    n = loads_before
+    log = []
+
+    def whole(call, shard):
+        nonlocal n
+        log.append((SLOT_COPY, call, n, shard, -1, n - 1))
+        n += 1
+
+    def wait(call):
+        log.append((SLOT_WAIT, call, n - 1, -1, -1, n - 1))
+
+    if embed_from_host:
+        if first:
+            whole(0, LM)
+    else:
+        if first:
+            whole(0, E)
+        wait(0)
+    for k in range(len(sched)):
+        log.extend(e for e in ring if e[1] == k)
+        if k == L or k == n_fwd:
+            wait(k + 1)
+        if k < n_fwd:
+            if k == L - 1 and not embed_from_host:
+                whole(L, LM)
+        elif not embed_from_host:
+            p = k - n_fwd
+            log.append((SLOT_COPY, k + 1, n, E, -1 - p, n - 1 if p == 0 else -1))
+            if p == L - 1:
+                n += 1
+    return log
+
+
+def check_slot_log(log, n_layers: int, dpo: bool = False, start=None) -> None:
+    """Replay the slot events of one stack step: at the wait before call 0 the slot holds
+    embed_tokens, at each wait of the turn it holds lm_head, and no load into the slot is
+    issued between the lm_head load and the last wait for it (the head's use).  A load is
+    logged as consecutive parts 0, 1, ... of one shard (buffer -1 - part; a whole load is
+    its own part 0), and a wait can only follow a complete load, so at a wait the slot
+    holds the shard of the last load.  ``start``: what the slot holds when the step begins
+    (None before the first step)."""
+    L = n_layers
+    E, LM = L, L + 1
+    content, loading, lm_waits_left = start, None, (2 if dpo else 1)
+    for kind, call, j, shard, buf, wait in log:
+        if kind == SLOT_COPY:
+            part = -1 - buf
+            if part == 0:
+                assert content != LM or lm_waits_left == 0 or call == 0, \
+                    "slot overwritten while the head still needs lm_head"
+                content, loading = None, (shard, 0)
+            else:
+                assert loading == (shard, part - 1), "parts out of order"
+                loading = (shard, part)
+        elif kind == SLOT_WAIT:
+            if loading is not None:
+                content, loading = loading[0], None
+            if call == 0:
+                assert content == E, "embedding not in the slot at the start of the step"
+            else:
+                assert content == LM, "lm_head not in the slot at the turn"
+                lm_waits_left -= 1
+    assert lm_waits_left == 0

@@ -201,11 +201,14 @@ def _same(a, b):
         assert np.array_equal(a["head"][k], b["head"][k]), k
 
 
-@pytest.mark.parametrize("fmt,dpo,reuse", [("nf4", False, False), ("bf16", False, False), ("nf4", True, False),
-                                           ("nf4", False, True), ("nf4", True, True)])
-def test_streamed_equals_resident_bitwise(fmt, dpo, reuse):
+@pytest.mark.parametrize("fmt,dpo,reuse,efh", [("nf4", False, False, False), ("bf16", False, False, False),
+                                               ("nf4", True, False, False), ("nf4", False, True, False),
+                                               ("nf4", True, True, False), ("nf4", False, False, True),
+                                               ("nf4", True, False, True)])
+def test_streamed_equals_resident_bitwise(fmt, dpo, reuse, efh):
+    """efh: the embedding rows read from the page-locked host table (the slot keeps lm_head)."""
     wl = _small_workload(fmt)
-    stack = StreamedStack(wl, n_bufs=2, seed=3, dpo=dpo, reuse=reuse)
+    stack = StreamedStack(wl, n_bufs=2, seed=3, dpo=dpo, reuse=reuse, embed_from_host=efh)
     try:
         stack.step()
         a = _snapshot(stack)
@@ -356,10 +359,10 @@ def _check_head(stack, dpo):
     check_tol(bf16_f64(_bits(stack.dh)), dh_o, "dh (lm_head input gradient)")
 
 
-@pytest.mark.parametrize("dpo", [False, True])
-def test_stack_step_matches_oracle(dpo):
+@pytest.mark.parametrize("dpo,efh", [(False, False), (True, False), (False, True)])
+def test_stack_step_matches_oracle(dpo, efh):
     wl = _small_workload("nf4", adapted=("q", "k", "v", "o", "gate", "up", "down"), rank=4)
-    stack = StreamedStack(wl, n_bufs=2, seed=5, dpo=dpo)
+    stack = StreamedStack(wl, n_bufs=2, seed=5, dpo=dpo, embed_from_host=efh)
     try:
         stack.step()
         torch.cuda.synchronize()
@@ -530,3 +533,31 @@ def test_disk_tier_reset_in_the_middle_of_a_pass(n_stage, tmp_path):
     finally:
         torch.cuda.synchronize()
         lnf4.stream_destroy(st)
+
+
+@pytest.mark.parametrize("dpo", [False, True])
+@pytest.mark.parametrize("efh", [False, True])
+@pytest.mark.parametrize("nbuf", [2, 3])
+def test_stack_log_matches_the_slot_simulator(dpo, efh, nbuf):
+    """Three steps of a stack with its head slot: each step's event log (layer ring and
+    slot loads and waits) equals the oracle's stack-step simulator, and the bytes copied
+    per step are the layer copies plus the slot loads it lists."""
+    wl = _small_workload()
+    stack = StreamedStack(wl, n_bufs=nbuf, seed=9, dpo=dpo, embed_from_host=efh)
+    stack.keep_log = True
+    L = stack.L
+    try:
+        n = 0
+        for step in range(3):
+            b0 = stack.bytes_copied()
+            stack.step()
+            want = ss.stack_step_log(L, nbuf, dpo, efh, first=(step == 0), loads_before=n)
+            assert stack.last_log == want, step
+            ss.check_slot_log(want, L, dpo, start=None if step == 0 else (L + 1 if efh else L))
+            n += (1 if step == 0 else 0) if efh else (3 if step == 0 else 2)
+            layer_bytes = stack.shard_bytes * len(stack.schedule)
+            slot = (stack.all_shards[L + 1].numel() if step == 0 else 0) if efh else \
+                stack.all_shards[L].numel() * (2 if step == 0 else 1) + stack.all_shards[L + 1].numel()
+            assert stack.bytes_copied() - b0 == layer_bytes + slot, step
+    finally:
+        stack.close()

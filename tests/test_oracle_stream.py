@@ -127,3 +127,69 @@ def test_reuse_check_catches_a_missing_wait_and_a_wrong_buffer():
     bad[step] = (e[0], e[1], e[2], e[3], 1 - e[4], e[5])
     with pytest.raises(AssertionError):
         ss.check_reuse_log([logs[0], bad], sched, 2)
+
+
+# ------------------------------------------------------------------ head slot of a stack step
+@pytest.mark.parametrize("L,nbuf", [(3, 2), (5, 3), (4, 8)])
+@pytest.mark.parametrize("dpo", [False, True])
+@pytest.mark.parametrize("efh", [False, True])
+def test_stack_step_log_ring_part_is_the_ring_simulator(L, nbuf, dpo, efh):
+    lg = ss.stack_step_log(L, nbuf, dpo, efh)
+    sched = ss.dpo_schedule(L) if dpo else ss.sft_schedule(L)
+    assert [e for e in lg if e[0] in (ss.COPY, ss.STEP)] == ss.simulate(sched, nbuf)
+    calls = [e[1] for e in lg]
+    assert calls == sorted(calls)   # events come in call order
+
+
+@pytest.mark.parametrize("L", [2, 3, 6])
+@pytest.mark.parametrize("dpo", [False, True])
+def test_slot_holds_embedding_at_start_and_lm_head_at_each_turn(L, dpo):
+    """Embed_tokens and the untied lm_head share one slot (the deep dive, "How layer
+    streaming works"): replayed over three steps, the slot holds the embedding at each
+    step's start and lm_head at each forward/backward turn (twice for DPO: reference and
+    policy heads)."""
+    n = 0
+    start = None
+    for step in range(3):
+        lg = ss.stack_step_log(L, 2, dpo, first=(step == 0), loads_before=n)
+        ss.check_slot_log(lg, L, dpo, start=start)
+        n += 3 if step == 0 else 2      # (first: the whole embedding,) lm_head, the next embedding
+        start = L
+
+
+@pytest.mark.parametrize("dpo", [False, True])
+def test_slot_reads_per_step(dpo):
+    """Per step the shared slot reads one embedding and one lm_head (the embedding of the
+    first step whole, later ones in L parts of the backward); reading the embedding rows
+    from the host table leaves only one lm_head load, in the first step."""
+    L = 4
+    for first in (True, False):
+        lg = ss.stack_step_log(L, 2, dpo, first=first)
+        loads = [e for e in lg if e[0] == ss.SLOT_COPY]
+        emb_parts = [e for e in loads if e[3] == L]
+        lm = [e for e in loads if e[3] == L + 1]
+        assert len(lm) == 1 and lm[0][4] == -1
+        # the embedding: whole before the first step, and L parts (one per backward call)
+        # for the next step
+        assert [e[4] for e in emb_parts] == ([-1] if first else []) + [-1 - p for p in range(L)]
+        assert [e[1] for e in emb_parts[-L:]] == [k + 1 for k in range((2 * L if dpo else L), (3 if dpo else 2) * L)]
+        efh = ss.stack_step_log(L, 2, dpo, embed_from_host=True, first=first)
+        assert [e[3] for e in efh if e[0] == ss.SLOT_COPY] == ([L + 1] if first else [])
+        assert sum(1 for e in efh if e[0] == ss.SLOT_WAIT) == (2 if dpo else 1)
+
+
+def test_slot_check_catches_a_late_lm_head_and_an_early_embedding_part():
+    L = 3
+    good = ss.stack_step_log(L, 2, first=False, loads_before=2)
+    ss.check_slot_log(good, L, start=L)
+    # lm_head loaded after the turn's wait: the head would read the embedding
+    i = next(i for i, e in enumerate(good) if e[0] == ss.SLOT_COPY and e[3] == L + 1)
+    w = next(i for i, e in enumerate(good) if e[0] == ss.SLOT_WAIT and e[1] > 0)
+    late = good[:i] + good[i + 1:w] + [good[w], good[i]] + good[w + 1:]
+    with pytest.raises(AssertionError):
+        ss.check_slot_log(late, L, start=L)
+    # part 0 of the next embedding moved before the turn's wait
+    p0 = next(i for i, e in enumerate(good) if e[0] == ss.SLOT_COPY and e[3] == L and e[4] == -1)
+    early = good[:w] + [good[p0]] + good[w:p0] + good[p0 + 1:]
+    with pytest.raises(AssertionError):
+        ss.check_slot_log(early, L, start=L)
