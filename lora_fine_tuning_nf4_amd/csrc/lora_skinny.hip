@@ -5,7 +5,8 @@
 //   dA = s v^T x  [r, in]  (reduction over T)
 //   dB = s dy^T u [out, r] (reduction over T)
 //
-// u and v (k_rank_proj): one launch serves several jobs (blockIdx.y).  A job is one
+// u and v (k_rank_tile, below; k_rank_proj is the earlier form, kept behind
+// LNF4_RANK_TILE = 0 for comparison): one launch serves several jobs (blockIdx.y).  A job is one
 // activation matrix src [T, K] and the weights that multiply it; weights that share src
 // (q and v both read x) are one job with their ranks concatenated (R = sum r_p <= 64), so
 // src is read from HBM once.  A workgroup owns RB rows of src and all of K: its waves (as
@@ -174,6 +175,182 @@ __global__ __launch_bounds__(512) void k_rank_proj(const RankArgs args) {
   }
 }
 
+// ---------------------------------------------------------------- tiled u / v (LDS-staged)
+// The same products with the weights staged in LDS and reused across rows: a workgroup owns
+// 8 rows of src and all ranks of its job and walks K in chunks; the chunk of src and the
+// chunk of the job's weights (transposed to [rank][K] for layout 1) are staged in LDS as
+// fp32, and each lane accumulates an OT x OK block of (row, rank) dot products over its
+// wave's quarter of the chunk with 16-byte LDS reads.  The four waves' partial sums are
+// added in a fixed order at the end.  The next chunk's loads are in flight while the
+// current chunk is multiplied.
+template <int RMAX>
+struct TileCfg {
+  static constexpr int OK = RMAX >= 16 ? 2 : 1;    // ranks per lane
+  static constexpr int KP = RMAX / OK;             // lanes along ranks
+  static constexpr int TP = 64 / KP;               // lanes along rows
+  static constexpr int OT = 8 / TP;                // rows per lane
+  static constexpr int TB = 8;                     // rows per workgroup
+  static constexpr int KC = 8192 / RMAX;           // K per chunk (32 KB of fp32 weights)
+  static constexpr int STR = KC + 4;               // LDS row stride (floats): rows start 16 B apart in the banks
+  static constexpr int AL = RMAX * KC / 8 / 256;   // layout 0: 16-byte weight loads per thread and chunk
+  static constexpr int XL = (TB * KC / 8 + 255) / 256;  // 16-byte src loads per thread and chunk
+  static constexpr int BL = RMAX * KC / 256;       // layout 1: weight elements per thread and chunk
+};
+
+template <int RMAX, int LAYOUT>
+__global__ __launch_bounds__(256) void k_rank_tile(const RankArgs args) {
+  using C = TileCfg<RMAX>;
+  constexpr int OT = C::OT, OK = C::OK, TB = C::TB, KC = C::KC, STR = C::STR;
+  static_assert(C::TP * OT == TB && C::KP * OK == RMAX, "lane layout");
+  __shared__ __attribute__((aligned(16))) float ws_[RMAX * STR];   // weights [rank][K chunk]
+  __shared__ __attribute__((aligned(16))) float xs_[TB * STR];     // src rows [row][K chunk]
+  __shared__ const uint16_t* wrow[RMAX];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const RankJob& J = args.job[blockIdx.y];
+  const int T = args.T, K = J.K, R = J.R, n = J.n;
+  const int t0 = blockIdx.x * TB;
+  if (t0 >= T) return;  // whole workgroup
+  if (LAYOUT == 0 && tid < RMAX) {
+    int off;
+    const int p = rank_owner(J.r, n, tid, off);
+    wrow[tid] = (tid < R) ? J.W[p] + (size_t)(tid - off) * K : nullptr;
+  }
+  // ranks past R stay zero in every chunk
+  for (int e = tid; e < (RMAX - R) * STR; e += 256) ws_[R * STR + e] = 0.f;
+  __syncthreads();
+
+  // ---- chunk loads into registers (zeros past K or T)
+  u32x4 xr[C::XL];
+  u32x4 ar[LAYOUT == 0 ? C::AL : 1];
+  uint32_t br[LAYOUT == 1 ? C::BL : 1];
+  u32x4 bv[LAYOUT == 1 ? C::BL / 8 : 1];
+  // layout 1 with whole 16-byte pieces of B rows (R a multiple of 8, B 16-byte aligned)
+  const bool bvec = LAYOUT == 1 && (R & 7) == 0 && (((uintptr_t)J.W[0]) & 15) == 0;
+  auto load = [&](int kc) {
+#pragma unroll
+    for (int q = 0; q < C::XL; ++q) {
+      const int e = 256 * q + tid, row = e / (KC / 8), c8 = e % (KC / 8);
+      const int t = t0 + row < T ? t0 + row : T - 1, i = kc + 8 * c8;
+      xr[q] = (row < TB && i < K) ? *(const u32x4*)(J.src + (size_t)t * K + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (LAYOUT == 0) {
+#pragma unroll
+      for (int q = 0; q < C::AL; ++q) {
+        const int e = 256 * q + tid, k = e / (KC / 8), c8 = e % (KC / 8), i = kc + 8 * c8;
+        ar[q] = (k < R && i < K) ? *(const u32x4*)(wrow[k] + i) : u32x4{0u, 0u, 0u, 0u};
+      }
+    } else if (bvec) {
+      // B [K][R] row-major, 16-byte rows pieces: 8 ranks of one K row per load
+#pragma unroll
+      for (int q = 0; q < C::BL / 8; ++q) {
+        const int e = 256 * q + tid, i = e / (RMAX / 8), k8 = 8 * (e % (RMAX / 8));
+        bv[q] = (k8 < R && kc + i < K) ? *(const u32x4*)(J.W[0] + (size_t)(kc + i) * R + k8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      // B [K][R] row-major: consecutive threads read consecutive elements
+#pragma unroll
+      for (int q = 0; q < C::BL; ++q) {
+        const int e = 256 * q + tid, i = e / RMAX, k = e % RMAX;
+        br[q] = (k < R && kc + i < K) ? (uint32_t)J.W[0][(size_t)(kc + i) * R + k] : 0u;
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < C::XL; ++q) {
+      const int e = 256 * q + tid, row = e / (KC / 8), c8 = e % (KC / 8);
+      if (row < TB) {
+        float f[8];
+        unpack8(xr[q], f);
+        *(float4*)&xs_[row * STR + 8 * c8] = make_float4(f[0], f[1], f[2], f[3]);
+        *(float4*)&xs_[row * STR + 8 * c8 + 4] = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    }
+    if (LAYOUT == 0) {
+#pragma unroll
+      for (int q = 0; q < C::AL; ++q) {
+        const int e = 256 * q + tid, k = e / (KC / 8), c8 = e % (KC / 8);
+        if (k < R) {
+          float f[8];
+          unpack8(ar[q], f);
+          *(float4*)&ws_[k * STR + 8 * c8] = make_float4(f[0], f[1], f[2], f[3]);
+          *(float4*)&ws_[k * STR + 8 * c8 + 4] = make_float4(f[4], f[5], f[6], f[7]);
+        }
+      }
+    } else if (bvec) {
+#pragma unroll
+      for (int q = 0; q < C::BL / 8; ++q) {
+        const int e = 256 * q + tid, i = e / (RMAX / 8), k8 = 8 * (e % (RMAX / 8));
+        if (k8 < R) {
+          float f[8];
+          unpack8(bv[q], f);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ws_[(k8 + j) * STR + i] = f[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::BL; ++q) {
+        const int e = 256 * q + tid, i = e / RMAX, k = e % RMAX;
+        if (k < R) ws_[k * STR + i] = bf16_to_f32((uint16_t)br[q]);
+      }
+    }
+  };
+
+  const int tp = lane / C::KP, kp = lane % C::KP;
+  float acc[OT][OK];
+#pragma unroll
+  for (int a = 0; a < OT; ++a)
+#pragma unroll
+    for (int b = 0; b < OK; ++b) acc[a][b] = 0.f;
+  const int nchunk = (K + KC - 1) / KC;
+  load(0);
+  for (int c = 0; c < nchunk; ++c) {
+    __syncthreads();  // every wave is done with the previous chunk
+    store();
+    __syncthreads();
+    if (c + 1 < nchunk) load((c + 1) * KC);
+    // this wave's quarter of the chunk, 4 K per step
+#pragma unroll 4
+    for (int i = wave * (KC / 4); i < (wave + 1) * (KC / 4); i += 4) {
+      float4 xv[OT], wv[OK];
+#pragma unroll
+      for (int a = 0; a < OT; ++a) xv[a] = *(const float4*)&xs_[(tp * OT + a) * STR + i];
+#pragma unroll
+      for (int b = 0; b < OK; ++b) wv[b] = *(const float4*)&ws_[(kp * OK + b) * STR + i];
+#pragma unroll
+      for (int a = 0; a < OT; ++a)
+#pragma unroll
+        for (int b = 0; b < OK; ++b) {
+          float s_ = acc[a][b];
+          s_ += xv[a].x * wv[b].x;
+          s_ += xv[a].y * wv[b].y;
+          s_ += xv[a].z * wv[b].z;
+          s_ += xv[a].w * wv[b].w;
+          acc[a][b] = s_;
+        }
+    }
+  }
+  // fixed-order sum of the four waves' partials
+  __syncthreads();
+  float* red = ws_;  // [4 waves][64 lanes][OT*OK]
+#pragma unroll
+  for (int a = 0; a < OT; ++a)
+#pragma unroll
+    for (int b = 0; b < OK; ++b) red[(wave * 64 + lane) * (OT * OK) + a * OK + b] = acc[a][b];
+  __syncthreads();
+  for (int o = tid; o < 64 * OT * OK; o += 256) {
+    const float s_ = red[o] + red[64 * OT * OK + o] + red[2 * 64 * OT * OK + o] + red[3 * 64 * OT * OK + o];
+    const int l = o / (OT * OK), a = (o % (OT * OK)) / OK, b = o % OK;
+    const int t = t0 + (l / C::KP) * OT + a, kk = (l % C::KP) * OK + b;
+    if (t < T && kk < R) {
+      int off;
+      const int p = rank_owner(J.r, n, kk, off);
+      J.dst[p][(size_t)t * J.dst_stride[p] + (kk - off)] = s_;
+    }
+  }
+}
+
 // ==================================================================== dA, dB partials
 template <int RMAX>
 struct GradCfg {
@@ -315,8 +492,24 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef LNF4_RANK_TILE
+#define LNF4_RANK_TILE 1
+#endif
+template <int LAYOUT>
+static hipError_t launch_rank_tile(const RankArgs& a, int rmax, hipStream_t s) {
+  const dim3 grid((a.T + 7) / 8, a.n_jobs), blk(256);
+  switch (rmax) {
+    case 8: hipLaunchKernelGGL((k_rank_tile<8, LAYOUT>), grid, blk, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_rank_tile<16, LAYOUT>), grid, blk, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_rank_tile<32, LAYOUT>), grid, blk, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_rank_tile<64, LAYOUT>), grid, blk, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int LAYOUT>
 static hipError_t launch_rank_layout(const RankArgs& a, int rmax, hipStream_t s) {
+  if (LNF4_RANK_TILE) return launch_rank_tile<LAYOUT>(a, rmax, s);
   // one lane per 8 K of the widest job, 1 to 8 waves: small K does not leave most lanes idle
   int kmax = 8;
   for (int j = 0; j < a.n_jobs; ++j) kmax = a.job[j].K > kmax ? a.job[j].K : kmax;

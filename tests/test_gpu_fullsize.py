@@ -1,8 +1,9 @@
 """Parity at the full layer shapes of the benchmark configurations, in the launch
 configuration the benchmark times (grouped q|k|v, gate|up and down calls at the
 configuration's T), on sampled outputs the oracle computes one by one: whole rows of y and
-dx, whole columns of dA, whole rows of dB.  Llama-3.1-8B NF4 (T = 2048, and the DPO step's
-T = 4096), Qwen2.5-0.5B NF4 with rank 16 on every projection, Qwen2.5-3B bf16 weights."""
+dx, whole columns of dA, whole rows of dB.  Llama-3.1-8B NF4 (every group at T = 2048, and
+the DPO step's T = 4096), Qwen2.5-0.5B NF4 with rank 16 on every projection, Qwen2.5-3B bf16
+weights."""
 import numpy as np
 import pytest
 
@@ -17,7 +18,8 @@ from lora_fine_tuning_nf4_amd import lnf4  # noqa: E402
 from oracle import nf4 as onf4  # noqa: E402
 from helpers import bf16_f64, check_tol, dev_f32, dev_u16, dev_u8, host_f32, host_u16  # noqa: E402
 
-CASES = [("llama8b", ("q", "k", "v")), ("llama8b", ("gate", "up")), ("llama8b_dpo", ("gate", "up")),
+CASES = [("llama8b", ("q", "k", "v")), ("llama8b", ("o",)), ("llama8b", ("gate", "up")), ("llama8b", ("down",)),
+         ("llama8b_dpo", ("gate", "up")),
          ("qwen05b", ("q", "k", "v")), ("qwen05b", ("gate", "up")), ("qwen05b", ("down",)),
          ("qwen3b_bf16", ("q", "k", "v")), ("qwen3b_bf16", ("gate", "up"))]
 
@@ -72,7 +74,8 @@ def _dev(WL, names, x, P):
 def test_full_size_group_sampled(wl_name, names):
     WL = synthgen.WORKLOADS[wl_name]
     T = WL.tokens
-    ROWS = [0, 1, 777, T // 2 + 3, T - 1]
+    # sampled rows: both ends, one in each 256-row tile of the first half, a few inside tiles
+    ROWS = sorted(set([0, 1, 255, 256, 511, 777, T // 2 + 3, T - 129, T - 1]))
     x, P = _group(WL, names)
     dev, projs = _dev(WL, names, x, P)
     in_f = WL.shapes[names[0]][1]
