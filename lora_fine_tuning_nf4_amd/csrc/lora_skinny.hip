@@ -5,8 +5,8 @@
 //   dA = s v^T x  [r, in]  (reduction over T)
 //   dB = s dy^T u [out, r] (reduction over T)
 //
-// u and v (k_rank_tile, below; k_rank_proj is the earlier form, kept behind
-// LNF4_RANK_TILE = 0 for comparison): one launch serves several jobs (blockIdx.y).  A job is one
+// u and v (k_rank_proj; from 16 concatenated ranks on, k_rank_tile below): one launch
+// serves several jobs (blockIdx.y).  A job is one
 // activation matrix src [T, K] and the weights that multiply it; weights that share src
 // (q and v both read x) are one job with their ranks concatenated (R = sum r_p <= 64), so
 // src is read from HBM once.  A workgroup owns RB rows of src and all of K: its waves (as
@@ -492,9 +492,6 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef LNF4_RANK_TILE
-#define LNF4_RANK_TILE 1
-#endif
 template <int LAYOUT>
 static hipError_t launch_rank_tile(const RankArgs& a, int rmax, hipStream_t s) {
   const dim3 grid((a.T + 7) / 8, a.n_jobs), blk(256);
@@ -509,7 +506,10 @@ static hipError_t launch_rank_tile(const RankArgs& a, int rmax, hipStream_t s) {
 
 template <int LAYOUT>
 static hipError_t launch_rank_layout(const RankArgs& a, int rmax, hipStream_t s) {
-  if (LNF4_RANK_TILE) return launch_rank_tile<LAYOUT>(a, rmax, s);
+  // staged weights pay off from 16 concatenated ranks on; with 8 ranks the per-row kernel
+  // below is faster (8B shapes: v of q and v in 17 us against 23 us; u of q|v, 16 ranks, in
+  // 24.6 us against 25.2 us, and 12-17 us against 19-40 us for the 0.5B shapes' 16-64)
+  if (rmax >= 16) return launch_rank_tile<LAYOUT>(a, rmax, s);
   // one lane per 8 K of the widest job, 1 to 8 waves: small K does not leave most lanes idle
   int kmax = 8;
   for (int j = 0; j < a.n_jobs; ++j) kmax = a.job[j].K > kmax ? a.job[j].K : kmax;
