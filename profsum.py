@@ -20,9 +20,10 @@ bytes per launch of the dominant kernel and of the NF4 input-gradient launch of 
 group.  The printed ``kernel_source_sha256`` ties the figures to the kernel sources they
 were taken on.
 
-``pmc`` prints, for every counter of a ``--pmc`` run, its per-dispatch average over the
-dominant launches and over the calibration copy, plus the derived MFMA-busy, busy and
-clock figures where the counters for them are present.
+``pmc`` prints, for every counter of a ``--kernel-trace --pmc`` run, its per-dispatch
+average over the dominant launches, plus the derived clock (one XCD's GUI-active cycles
+over the dispatch's duration) and the MFMA-busy, LDS and wait fractions where the counters
+for them are present.
 
 The dominant kernel is named by ``bench.DOM_KERNEL`` / ``bench.DOM_GRID``; this script
 sits beside bench.py and reads those definitions from it.
@@ -148,22 +149,47 @@ def traffic(fetch_dir: str, write_dir: str, command: str) -> str:
 
 
 def pmc(pmc_dir: str, _unused: str, command: str) -> str:
+    """Per-dispatch averages of every counter over the dominant launches, and the derived
+    clock and busy fractions.  rocprofv3 sums a counter over its instances: GRBM_GUI_ACTIVE
+    over the 8 XCDs (so one XCD's cycles are a 1/8 of it), SQ counters over every shader
+    engine; the chip has 256 compute units and 1024 SIMDs."""
     rows = _rows(pmc_dir)
-    counters = sorted({r["Counter_Name"] for r in rows})
-    out = [f"# rocprofv3 counters: {command}",
-           f"kernel_source_sha256: {bench.kernel_source_hash()}"]
-    dom = {}
-    for c in counters:
-        v, n = _avg(rows, c, bench.DOM_KERNEL, bench.DOM_GRID)
-        cal, _ = _avg(rows, c, CAL_NAME)
-        dom[c] = v
-        out.append(f"{c}: dominant {('%.1f' % v) if v is not None else '-'} per dispatch ({n} dispatches); "
-                   f"calibration copy {('%.1f' % cal) if cal is not None else '-'}")
-    # derived figures (counters summed over the chip's XCDs / SEs by rocprofv3)
-    if dom.get("SQ_BUSY_CYCLES") and dom.get("SQ_VALU_MFMA_BUSY_CYCLES"):
-        out.append(f"mfma_busy_over_sq_busy: {dom['SQ_VALU_MFMA_BUSY_CYCLES'] / dom['SQ_BUSY_CYCLES']:.4f}")
-    if dom.get("GRBM_GUI_ACTIVE") and dom.get("GRBM_COUNT"):
-        out.append(f"gui_active_over_count: {dom['GRBM_GUI_ACTIVE'] / dom['GRBM_COUNT']:.4f}")
+    per = {}
+    for r in rows:
+        if bench.DOM_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == bench.DOM_GRID:
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+    if not per:
+        raise SystemExit("dominant kernel not in this run")
+    names = sorted({k for d in per.values() for k in d})
+    avg = {k: sum(d[k] for d in per.values() if k in d) / sum(1 for d in per.values() if k in d) for k in names}
+    out = [f"# rocprofv3 counters of {bench.DOM_KERNEL} grid {bench.DOM_GRID} (gate|up forward, M=2048 N=28672 K=4096)",
+           f"# command: {command}",
+           f"kernel_source_sha256: {bench.kernel_source_hash()}",
+           f"dispatches: {len(per)}"]
+    for k in names:
+        out.append(f"{k}: {avg[k]:.6g}" if k != "dur_s" else f"duration_ms: {avg[k] * 1e3:.4f}")
+    if "GRBM_GUI_ACTIVE" in avg:
+        gui = avg["GRBM_GUI_ACTIVE"] / 8.0
+        out.append(f"cycles_per_xcd: {gui:.0f}")
+        out.append(f"clock_GHz (cycles / duration): {gui / avg['dur_s'] / 1e9:.3f}")
+        flops = 2.0 * 2048 * 28672 * 4096
+        out.append(f"achieved_TFLOPs: {flops / avg['dur_s'] / 1e12:.1f} ({flops / avg['dur_s'] / 1e12 / bench.PEAK_BF16_TFLOPS:.4f} of "
+                   f"{bench.PEAK_BF16_TFLOPS:.0f}, a peak taken at 2.4 GHz)")
+        derived = (("SQ_VALU_MFMA_BUSY_CYCLES", 1024, "mfma_busy_fraction (per SIMD)"),
+                   ("SQ_LDS_IDX_ACTIVE", 256, "lds_active_fraction (per CU)"),
+                   ("SQ_LDS_BANK_CONFLICT", 256, "lds_bank_conflict_fraction (per CU)"),
+                   ("SQ_ACTIVE_INST_VALU", 1024, "valu_issue_fraction (per SIMD)"))
+        for k, units, label in derived:
+            if k in avg:
+                out.append(f"{label}: {avg[k] / (gui * units):.4f}")
+    if "SQ_WAVE_CYCLES" in avg:
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"):
+            if k in avg:
+                out.append(f"{k} / SQ_WAVE_CYCLES: {avg[k] / avg['SQ_WAVE_CYCLES']:.4f}")
+    if "SQ_INSTS_MFMA" in avg:
+        out.append(f"mfma_instructions: {avg['SQ_INSTS_MFMA']:.0f} (2 M N K / 32768 = {2.0 * 2048 * 28672 * 4096 / 32768:.0f})")
     return "\n".join(out) + "\n"
 
 
