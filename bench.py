@@ -367,7 +367,7 @@ def t_sweep(wl, seed: int, nbuf: int, steps: int, tokens=(2048, 4096, 8192)):
         finally:
             stack.close()
             del stack
-            torch.cuda.empty_cache()
+            _release_memory()
         out.append({"tokens": T, **res, "exposed_copy_ms": round(res["streamed"]["ms_per_step"] -
                                                                   res["resident"]["ms_per_step"], 2)})
         log(f"T={T}: {out[-1]}")
@@ -406,7 +406,7 @@ def stream_variants(wl, args, L):
         finally:
             stack.close()
             del stack
-            torch.cuda.empty_cache()
+            _release_memory()
         log(f"variant {name}: {out[name]}")
     try:
         out["disk"] = disk_variant(wl, args, L)
@@ -449,8 +449,19 @@ def disk_variant(wl, args, L):
     finally:
         stack.close()
         del stack
-        torch.cuda.empty_cache()
+        _release_memory()
         shutil.rmtree(d, ignore_errors=True)
+
+
+def _release_memory():
+    """Give cached device memory and cached page-locked host memory back: a later run's
+    pinned shards are then allocated afresh instead of landing beside a previous run's
+    cached blocks (later runs on a host full of cached pinned blocks streamed slower)."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if hasattr(torch._C, "_host_emptyCache"):
+        torch._C._host_emptyCache()
 
 
 def _timed_steps(stack, steps: int, warmup: int, resident: bool = False):
@@ -532,7 +543,7 @@ def other_configs(args):
         finally:
             stack.close()
             del stack
-            torch.cuda.empty_cache()
+            _release_memory()
         out[name] = rec
         log(f"config {name}: {rec}")
     return out
@@ -590,7 +601,7 @@ def decoder_model_run(args):
     finally:
         m.close()
         del m
-        torch.cuda.empty_cache()
+        _release_memory()
     log(f"decoder model: {out}")
     return out
 
@@ -825,19 +836,21 @@ def main():
 
     stack.close()
     del stack
-    torch.cuda.empty_cache()
+    _release_memory()
 
     if not args.no_variants:
         result["stream_variants"] = stream_variants(wl, args, L)
-    if not args.no_configs and wl.name == "llama8b" and L == wl.layers:
-        result["other_configs"] = other_configs(args)
+        _release_memory()
     if not args.no_model and L == wl.layers:
         result["decoder_model"] = decoder_model_run(args)
+        _release_memory()
+    if not args.no_configs and wl.name == "llama8b" and L == wl.layers:
+        result["other_configs"] = other_configs(args)
 
     if args.study:
         log("study: dequant share ...")
         result["study"] = {"dequant_share": dequant_share(wl, args.seed)}
-        torch.cuda.empty_cache()
+        _release_memory()
         log("study: T sweep ...")
         result["study"]["t_sweep"] = t_sweep(wl, args.seed, args.nbuf, max(2, args.steps // 2))
 
