@@ -16,6 +16,37 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // (arrays of the HIP uint4 wrapper struct can stay in private memory)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Raw buffer resource over [p, p + bytes) for the direct-to-LDS buffer loads: a 32-bit
+// per-lane offset plus a wave-uniform offset address the data with no per-lane 64-bit
+// arithmetic, and a load whose per-lane offset reaches past `bytes` returns zeros.
+// (dword 3 = 0x00020000: the untyped 32-bit format of gfx9-class buffer descriptors)
+// The host pass of hipcc only parses kernel bodies; it has no buffer-resource type, and a
+// kernel it cannot parse gets no launch stub, so it sees an inert stand-in.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+#define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_, (lds_ptr)(lds_), size_, voff_, soff_, 0, 0)
+#else
+typedef const void* rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* p, int64_t) { return p; }
+#define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) ((void)(rsrc_), (void)(lds_), (void)(voff_), (void)(soff_))
+#endif
+
+// Buffer loads into registers.  The host pass gets inert stand-ins, as for the
+// direct-to-LDS loads.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define LNF4_BUF_LD128(rsrc_, voff_, soff_) __builtin_amdgcn_raw_buffer_load_b128(rsrc_, voff_, soff_, 0)
+#define LNF4_BUF_LD32(rsrc_, voff_, soff_) __builtin_amdgcn_raw_buffer_load_b32(rsrc_, voff_, soff_, 0)
+#else
+#define LNF4_BUF_LD128(rsrc_, voff_, soff_) ((void)(rsrc_), (void)(voff_), (void)(soff_), u32x4{0u, 0u, 0u, 0u})
+#define LNF4_BUF_LD32(rsrc_, voff_, soff_) ((void)(rsrc_), (void)(voff_), (void)(soff_), 0u)
+#endif
+
 // Two fp32 -> packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 // `lo` lands in bits 0..15 (the lower address), `hi` in bits 16..31.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
