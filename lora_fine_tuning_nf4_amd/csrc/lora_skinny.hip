@@ -78,9 +78,9 @@ __device__ __forceinline__ const uint16_t* rank_row(const RankJob& J, int kk, in
 }
 
 // A workgroup owns 16 rows of src and every rank of its job (RT tiles of 16).  Its 8 waves
-// take the job's K in super-steps of 64 (wave w: steps w, w + 8, ...); lane l of a wave
-// reads 32 consecutive bytes (16 K) of its row at 16 (l >> 4) in each super-step, the two
-// 8-K halves feeding two MFMAs, so the 4 lanes of a row cover 128 contiguous bytes.
+// take the job's K in super-steps of 64 (wave w: steps w, w + 8, ...).  Half h of a
+// super-step (K 32h .. 32h+31) feeds one MFMA; lane l reads the 8 K at 8 (l >> 4) of it
+// from its row, so one load instruction reads 64 contiguous bytes of each of 16 rows.
 // src is read through a buffer resource: a step past K reads zeros without touching
 // memory.  Weights in layout 0 (A [r][K], K contiguous) load straight into the B operand
 // the same way (a step past K re-reads the last one; never used).  In layout 1 (B [K][r],
@@ -92,7 +92,8 @@ __device__ __forceinline__ const uint16_t* rank_row(const RankJob& J, int kk, in
 // depends on K alone, so a result does not depend on the other ranks of its job or on PD.
 template <int RT, int LAYOUT, int PD_>
 __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
-  constexpr int PD = (LAYOUT == 1 && RT == 4 && PD_ > 2) ? 2 : PD_;  // register budget
+  // register budget: 8 steps in flight for the 1-2 tile shapes, at most 2 for the widest
+  constexpr int PD = (LAYOUT == 1 && RT == 4 && PD_ > 2) ? 2 : ((RT > 2 || (LAYOUT == 1 && RT > 1)) && PD_ > 4 ? 4 : PD_);
   constexpr int NW = 8, BT = 16, R16 = 16 * RT;
   constexpr int SL = LAYOUT == 1 ? 64 * R16 : 8;  // staging slice per wave (bf16 elements)
   constexpr int PL = 2 * RT;                       // layout 1: 16-byte weight pieces per lane
@@ -110,11 +111,11 @@ __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
   // A operand: row t0 + l16 (rows past T repeat row T - 1; their sums are not stored)
   const rsrc_t srs = make_rsrc(J.src, (int64_t)T * K * 2);
   const int trow = t0 + l16 < T ? t0 + l16 : T - 1;
-  const uint32_t aoff = 2u * ((uint32_t)trow * (uint32_t)K + 16u * g);
+  const uint32_t aoff = 2u * ((uint32_t)trow * (uint32_t)K + 8u * g);
   // layout 0: weight row of concatenated rank 16 rt + l16
   const uint16_t* wrow[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) wrow[rt] = LAYOUT == 0 ? rank_row(J, 16 * rt + l16, K) + 16 * g : J.W[0];
+  for (int rt = 0; rt < RT; ++rt) wrow[rt] = LAYOUT == 0 ? rank_row(J, 16 * rt + l16, K) + 8 * g : J.W[0];
   // layout 1: one projection, r = R; 16-byte pieces when r % 8 == 0 and B is 16-byte
   // aligned, single elements otherwise
   const uint16_t* Bw = J.W[0];
@@ -140,10 +141,10 @@ __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
   const auto load = [&](Frag& f, int s) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int k = 64 * s + 16 * g + 8 * h;  // K % 8 == 0: a half is all in or all out
-      f.a[h] = LNF4_BUF_LD128(srs, k < K ? aoff + 128u * s + 16u * h : OOB, 0);
+      const int k = 64 * s + 32 * h + 8 * g;  // K % 8 == 0: a half is all in or all out
+      f.a[h] = LNF4_BUF_LD128(srs, k < K ? aoff + 128u * s + 64u * h : OOB, 0);
       if (LAYOUT == 0) {
-        const int kc = (k < K ? 64 * s + 8 * h : K - 8 - 16 * g);  // clamped into the row
+        const int kc = (k < K ? 64 * s + 32 * h : K - 8 - 8 * g);  // clamped into the row
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) f.b[rt][h] = *(const u32x4*)(wrow[rt] + kc);
       }
@@ -184,12 +185,12 @@ __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
         }
       }
       __builtin_amdgcn_wave_barrier();
-      const int rr = 16 * g + (l16 >> 2), cc = 4 * (l16 & 3);
+      const int rr = 8 * g + (l16 >> 2), cc = 4 * (l16 & 3);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint16_t* p = slice + (rr + 8 * h) * R16 + 16 * rt + cc;
+          const uint16_t* p = slice + (rr + 32 * h) * R16 + 16 * rt + cc;
           bop[rt][h] = join8(lds_tr16(p), lds_tr16(p + 4 * R16));
         }
     }
@@ -271,6 +272,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const GradArgs args) {
   constexpr int R16 = 16 * RT;
   constexpr int QS = 32 * 64, PS = 32 * R16;  // bf16 elements per stage
   constexpr int PQ = (8 * R16 + 255) / 256;   // 4-element P pieces per thread and step
+  constexpr uint32_t OOB = 0x80000000u;       // buffer offset past any resource
   __shared__ __attribute__((aligned(16))) uint16_t qs[2][QS];
   __shared__ __attribute__((aligned(16))) uint16_t ph[2][PS];
   __shared__ __attribute__((aligned(16))) uint16_t pl[2][PS];
@@ -284,29 +286,35 @@ __global__ __launch_bounds__(256) void k_lora_grad(const GradArgs args) {
   const int nsteps = te > tb ? (te - tb + 31) / 32 : 0;  // an empty split writes zeros
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  // staging roles: Q chunk (row tq, 8 columns at 8 cq); P pieces (row, 4 ranks)
+  // staging roles: Q chunk (row tq, 8 columns at 8 cq); P pieces (row, 4 ranks).  Loads go
+  // through buffer resources: rows past the split, columns past C and ranks past R read
+  // zeros without touching memory, so every load is issued unconditionally.
+  const rsrc_t qrs = make_rsrc(J.Q, (int64_t)T * C * 2);
+  const rsrc_t prs = make_rsrc(J.P, (int64_t)T * J.pstride * 4);
   const int tq = tid >> 3, cq = tid & 7;
   const bool cq_ok = cb + 8 * cq < C;  // C % 8 == 0: a chunk is all in or all out
-  const uint16_t* qsrc = J.Q + (size_t)cb + 8 * cq;
   const int qdst = tq * 64 + 8 * (cq ^ grad_swz(tq));
-  u32x4 qr;
-  float pr[PQ][4];
-  const auto load = [&](int st) {
+  struct Set {
+    u32x4 q;
+    float p[PQ][4];
+  };
+  const auto load = [&](Set& S, int st) {
     const int t = tb + 32 * st + tq;
-    qr = (cq_ok && t < te) ? *(const u32x4*)(qsrc + (size_t)t * C) : zero;
+    S.q = LNF4_BUF_LD128(qrs, (cq_ok && t < te) ? 2u * ((uint32_t)t * (uint32_t)C + (uint32_t)(cb + 8 * cq)) : OOB, 0);
+    // P ranks past R read whatever follows (they only reach result columns that are
+    // never stored); rows past the split read zeros
 #pragma unroll
     for (int q = 0; q < PQ; ++q) {
       const int e = tid + 256 * q, row = e / (R16 / 4), k0 = 4 * (e - row * (R16 / 4));
       const int tp = tb + 32 * st + row;
-      const bool ok = e < 8 * R16 && tp < te;
+      const uint32_t off = (e < 8 * R16 && tp < te) ? 4u * ((uint32_t)tp * (uint32_t)J.pstride + (uint32_t)k0) : OOB;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pr[q][j] = (ok && k0 + j < R) ? J.P[(size_t)tp * J.pstride + k0 + j] : 0.f;
+      for (int j = 0; j < 4; ++j) S.p[q][j] = __uint_as_float(LNF4_BUF_LD32(prs, off, 4 * j));
     }
   };
-  const auto store = [&](int buf) {
-    *(u32x4*)&qs[buf][qdst] = qr;
+  const auto store = [&](const Set& S, int buf) {
+    *(u32x4*)&qs[buf][qdst] = S.q;
 #pragma unroll
     for (int q = 0; q < PQ; ++q) {
       const int e = tid + 256 * q, row = e / (R16 / 4), k0 = 4 * (e - row * (R16 / 4));
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const GradArgs args) {
         uint32_t hw[2], lw[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const float a = pr[q][2 * j], b = pr[q][2 * j + 1];
+          const float a = S.p[q][2 * j], b = S.p[q][2 * j + 1];
           hw[j] = pack_bf16x2(a, b);
           lw[j] = pack_bf16x2(a - bf16_lo(hw[j]), b - bf16_hi(hw[j]));
         }
@@ -333,15 +341,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const GradArgs args) {
   const int qa0 = rr * 64 + 8 * ((qc >> 3) ^ grad_swz(rr)) + (qc & 7);
   const int qa1 = (rr + 4) * 64 + 8 * ((qc >> 3) ^ grad_swz(rr + 4)) + (qc & 7);
   const int pa = rr * R16 + 4 * (l16 & 3);
-
-  if (nsteps > 0) {
-    load(0);
-    store(0);
-  }
-  if (nsteps > 1) load(1);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
+  const auto compute = [&](int buf) {
     const bf16x8 a = join8(lds_tr16(&qs[buf][qa0]), lds_tr16(&qs[buf][qa1]));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -354,10 +354,27 @@ __global__ __launch_bounds__(256) void k_lora_grad(const GradArgs args) {
         acc[rt] = mfma16(a, bl, acc[rt]);
       }
     }
-    if (st + 1 < nsteps) {
-      store(buf ^ 1);
-      if (st + 2 < nsteps) load(st + 2);
-    }
+  };
+
+  // Step st is staged in LDS buffer st & 1 from register set st & 1; the set of step st + 2
+  // is loaded as soon as step st is staged, so two steps' loads are in flight behind the
+  // MFMAs.  Steps past the split load and stage zeros that no MFMA reads; loads and stores
+  // are unconditional, so the compiler's waits before a store leave the newer set's loads
+  // outstanding.
+  Set s0, s1;
+  load(s0, 0);
+  load(s1, 1);
+  store(s0, 0);
+  load(s0, 2);
+  __syncthreads();
+  for (int st = 0; st < nsteps; st += 2) {
+    compute(0);
+    store(s1, 1);
+    load(s1, st + 3);
+    __syncthreads();
+    if (st + 1 < nsteps) compute(1);
+    store(s0, 0);
+    load(s0, st + 4);
     __syncthreads();
   }
 
@@ -420,10 +437,12 @@ static void launch_proj_pd(const RankArgs& a, int rt, hipStream_t s) {
 
 template <int LAYOUT>
 static void launch_proj_layout(const RankArgs& a, int rt, int spw, hipStream_t s) {
-  // ring depth: the steps of the wave with the most, up to 4 (2 for 2-3 steps)
+  // ring depth: the steps of the wave with the most (1, 2, 4 or 8; the kernel caps it by
+  // its register budget)
   if (spw <= 1) launch_proj_pd<LAYOUT, 1>(a, rt, s);
   else if (spw <= 3) launch_proj_pd<LAYOUT, 2>(a, rt, s);
-  else launch_proj_pd<LAYOUT, 4>(a, rt, s);
+  else if (spw <= 7) launch_proj_pd<LAYOUT, 4>(a, rt, s);
+  else launch_proj_pd<LAYOUT, 8>(a, rt, s);
 }
 
 // every job of one launch must have the same layout
