@@ -408,12 +408,18 @@ def stream_variants(wl, args, L):
             del stack
             _release_memory()
         log(f"variant {name}: {out[name]}")
-    try:
-        out["disk"] = disk_variant(wl, args, L)
-    except (OSError, RuntimeError) as e:  # e.g. no room for the 3.9 GB shard file: report, do not fail the bench
-        out["disk"] = {"error": f"{type(e).__name__}: {e}"}
-    log(f"variant disk: {out['disk']}")
     return out
+
+
+def disk_run(wl, args, L):
+    """The disk variant, reported with the stream variants; run after every other
+    streamed measurement so that its file and page-cache traffic precede none of them."""
+    try:
+        rec = disk_variant(wl, args, L)
+    except (OSError, RuntimeError) as e:  # e.g. no room for the 3.9 GB shard file: report, do not fail the bench
+        rec = {"error": f"{type(e).__name__}: {e}"}
+    log(f"variant disk: {rec}")
+    return rec
 
 
 def disk_variant(wl, args, L):
@@ -846,6 +852,9 @@ def main():
         _release_memory()
     if not args.no_configs and wl.name == "llama8b" and L == wl.layers:
         result["other_configs"] = other_configs(args)
+    if not args.no_variants:
+        result["stream_variants"]["disk"] = disk_run(wl, args, L)
+        _release_memory()
 
     if args.study:
         log("study: dequant share ...")

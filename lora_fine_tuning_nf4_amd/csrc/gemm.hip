@@ -1327,11 +1327,15 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
   __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(           \
       (SM_) + X_BYTES + (row_) * 512 + ((((col_) >> 3) ^ (4 * ((row_) & 3))) << 4) + (((col_) & 7) << 1)))
   // B fragment of step s (K = 32h + 8s .. +7) for the 32-column block starting at cb
+  const int tbo0 = (32 * h + tr_c) * 512 + (((8 * wave + 0 + (tr_col >> 3)) ^ (4 * tr_c)) << 4) + ((tr_col & 7) << 1);
+  const int tbo1 = (32 * h + tr_c) * 512 + (((8 * wave + 4 + (tr_col >> 3)) ^ (4 * tr_c)) << 4) + ((tr_col & 7) << 1);
+#define LNF4_TRO(SM_, off_) \
+  __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)((SM_) + X_BYTES + (off_)))
 #define LNF4_DXB_FRAG(SM_, s_, cb_)                                                              \
   ({                                                                                             \
-    const int r0_ = 32 * h + 8 * (s_) + tr_c;                                                    \
-    const v4s_t lo_ = LNF4_TRB(SM_, r0_, (cb_) + tr_col);                                        \
-    const v4s_t hi_ = LNF4_TRB(SM_, r0_ + 4, (cb_) + tr_col);                                    \
+    const int o_ = ((cb_) == 64 * wave ? tbo0 : tbo1) + 4096 * (s_);                              \
+    const v4s_t lo_ = LNF4_TRO(SM_, o_);                                                         \
+    const v4s_t hi_ = LNF4_TRO(SM_, o_ + 2048);                                                  \
     __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7));      \
   })
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))

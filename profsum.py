@@ -3,7 +3,7 @@
     python profsum.py trace   TRACE_DIR BENCH_OUT  "<command>"
     python profsum.py stats   TRACE_DIR -          "<command>"
     python profsum.py traffic FETCH_DIR WRITE_DIR  "<command>"
-    python profsum.py pmc     PMC_DIR   -          "<command>"
+    python profsum.py pmc     PMC_DIR   KERNEL     "<command>"
 
 ``trace`` reads ``*_kernel_stats.csv`` and ``*_kernel_trace.csv`` of a ``--kernel-trace
 --stats -f csv`` run of bench.py and prints the per-kernel table plus the average
@@ -21,7 +21,8 @@ group.  The printed ``kernel_source_sha256`` ties the figures to the kernel sour
 were taken on.
 
 ``pmc`` prints, for every counter of a ``--kernel-trace --pmc`` run, its per-dispatch
-average over the dominant launches, plus the derived clock (one XCD's GUI-active cycles
+average over the dominant launches (KERNEL "-") or over every launch whose name contains
+KERNEL, plus the derived clock (one XCD's GUI-active cycles
 over the dispatch's duration) and the MFMA-busy, LDS and wait fractions where the counters
 for them are present.
 
@@ -148,15 +149,17 @@ def traffic(fetch_dir: str, write_dir: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def pmc(pmc_dir: str, _unused: str, command: str) -> str:
-    """Per-dispatch averages of every counter over the dominant launches, and the derived
-    clock and busy fractions.  rocprofv3 sums a counter over its instances: GRBM_GUI_ACTIVE
-    over the 8 XCDs (so one XCD's cycles are a 1/8 of it), SQ counters over every shader
-    engine; the chip has 256 compute units and 1024 SIMDs."""
+def pmc(pmc_dir: str, kernel: str, command: str) -> str:
+    """Per-dispatch averages of every counter over the dominant launches (KERNEL "-"), or
+    over every launch whose name contains KERNEL, and the derived clock and busy fractions.
+    rocprofv3 sums a counter over its instances: GRBM_GUI_ACTIVE over the 8 XCDs (so one
+    XCD's cycles are a 1/8 of it), SQ counters over every shader engine; the chip has 256
+    compute units and 1024 SIMDs."""
     rows = _rows(pmc_dir)
+    dom = kernel == "-"
     per = {}
     for r in rows:
-        if bench.DOM_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == bench.DOM_GRID:
+        if (bench.DOM_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == bench.DOM_GRID) if dom else kernel in r["Kernel_Name"]:
             d = per.setdefault(r["Dispatch_Id"], {})
             d[r["Counter_Name"]] = float(r["Counter_Value"])
             d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
@@ -164,7 +167,9 @@ def pmc(pmc_dir: str, _unused: str, command: str) -> str:
         raise SystemExit("dominant kernel not in this run")
     names = sorted({k for d in per.values() for k in d})
     avg = {k: sum(d[k] for d in per.values() if k in d) / sum(1 for d in per.values() if k in d) for k in names}
-    out = [f"# rocprofv3 counters of {bench.DOM_KERNEL} grid {bench.DOM_GRID} (gate|up forward, M=2048 N=28672 K=4096)",
+    what = (f"{bench.DOM_KERNEL} grid {bench.DOM_GRID} (gate|up forward, M=2048 N=28672 K=4096)" if dom
+            else f"every launch of {kernel}")
+    out = [f"# rocprofv3 counters of {what}",
            f"# command: {command}",
            f"kernel_source_sha256: {bench.kernel_source_hash()}",
            f"dispatches: {len(per)}"]
@@ -174,9 +179,10 @@ def pmc(pmc_dir: str, _unused: str, command: str) -> str:
         gui = avg["GRBM_GUI_ACTIVE"] / 8.0
         out.append(f"cycles_per_xcd: {gui:.0f}")
         out.append(f"clock_GHz (cycles / duration): {gui / avg['dur_s'] / 1e9:.3f}")
-        flops = 2.0 * 2048 * 28672 * 4096
-        out.append(f"achieved_TFLOPs: {flops / avg['dur_s'] / 1e12:.1f} ({flops / avg['dur_s'] / 1e12 / bench.PEAK_BF16_TFLOPS:.4f} of "
-                   f"{bench.PEAK_BF16_TFLOPS:.0f}, a peak taken at 2.4 GHz)")
+        if dom:
+            flops = 2.0 * 2048 * 28672 * 4096
+            out.append(f"achieved_TFLOPs: {flops / avg['dur_s'] / 1e12:.1f} ({flops / avg['dur_s'] / 1e12 / bench.PEAK_BF16_TFLOPS:.4f} of "
+                       f"{bench.PEAK_BF16_TFLOPS:.0f}, a peak taken at 2.4 GHz)")
         derived = (("SQ_VALU_MFMA_BUSY_CYCLES", 1024, "mfma_busy_fraction (per SIMD)"),
                    ("SQ_LDS_IDX_ACTIVE", 256, "lds_active_fraction (per CU)"),
                    ("SQ_LDS_BANK_CONFLICT", 256, "lds_bank_conflict_fraction (per CU)"),
@@ -188,7 +194,7 @@ def pmc(pmc_dir: str, _unused: str, command: str) -> str:
         for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"):
             if k in avg:
                 out.append(f"{k} / SQ_WAVE_CYCLES: {avg[k] / avg['SQ_WAVE_CYCLES']:.4f}")
-    if "SQ_INSTS_MFMA" in avg:
+    if "SQ_INSTS_MFMA" in avg and dom:
         out.append(f"mfma_instructions: {avg['SQ_INSTS_MFMA']:.0f} (2 M N K / 32768 = {2.0 * 2048 * 28672 * 4096 / 32768:.0f})")
     return "\n".join(out) + "\n"
 
