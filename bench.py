@@ -785,6 +785,18 @@ def main():
             "exposed_copy_ms_per_step": round(ms_per_step - r_ms, 3),
         }
 
+    # the same stream calls (layer copies, slot loads, event waits) without any kernel: the
+    # time the copy schedule of the ring takes by itself
+    for _ in range(max(1, args.warmup)):
+        stack.step(compute=False)
+    torch.cuda.synchronize()
+    s0 = time.perf_counter()
+    n_sched = max(2, min(args.steps, 5))
+    for _ in range(n_sched):
+        stack.step(compute=False)
+    torch.cuda.synchronize()
+    result["h2d"]["schedule_only_ms_per_step"] = round((time.perf_counter() - s0) * 1000.0 / n_sched, 3)
+
     # copy-only rate of the link (the same copies, no compute)
     hb = stack.host[0]
     db = stack.bufs[0]
@@ -798,6 +810,8 @@ def main():
         e1.record(cs)
     torch.cuda.synchronize()
     result["h2d"]["copy_only_GBps"] = round(8 * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
+    # the step's bytes at that rate: the floor of any schedule on this link
+    result["h2d"]["link_floor_ms_per_step"] = round(result["h2d"]["bytes_per_step"] / (result["h2d"]["copy_only_GBps"] * 1e6), 3)
     # every shard once (host placement can differ between shards)
     rates = []
     for h in stack.host:
