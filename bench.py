@@ -482,6 +482,20 @@ def _timed_steps(stack, steps: int, warmup: int, resident: bool = False):
     return (time.perf_counter() - t0) * 1000.0 / steps
 
 
+def _timed_graph(stack, steps: int, warmup: int):
+    """ms per resident step replayed from its captured HIP graph (capture not timed)."""
+    import torch
+    stack.resident_graph()
+    for _ in range(warmup):
+        stack.step_graph()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack.step_graph()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1000.0 / steps
+
+
 def _gemm_rate(stack, wl, resident: bool = False):
     """TFLOP/s of the grouped GEMM calls (skinny LoRA kernels included) over one step, HIP
     events around every call."""
@@ -546,6 +560,8 @@ def other_configs(args):
             ms = _timed_steps(stack, steps, warm, resident=True)
             rec["resident"] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(stack.T / (ms / 1000.0), 1),
                                **_gemm_rate(stack, wl, resident=True)}
+            gms = _timed_graph(stack, max(steps, 5), warm)
+            rec["resident_graph"] = {"ms_per_step": round(gms, 3), "tokens_per_s": round(stack.T / (gms / 1000.0), 1)}
         finally:
             stack.close()
             del stack
@@ -784,6 +800,9 @@ def main():
             "ms_per_step": round(r_ms, 3), "tokens_per_s": round(tokens / (r_ms / 1000.0), 2),
             "exposed_copy_ms_per_step": round(ms_per_step - r_ms, 3),
         }
+        g_ms = _timed_graph(stack, args.steps, max(1, args.warmup))
+        result["resident_h2d_removed"]["graph_replay_ms_per_step"] = round(g_ms, 3)
+        result["resident_h2d_removed"]["graph_replay_tokens_per_s"] = round(tokens / (g_ms / 1000.0), 2)
 
     # the same stream calls (layer copies, slot loads, event waits) without any kernel: the
     # time the copy schedule of the ring takes by itself

@@ -464,7 +464,11 @@ int stream_create(const void* const* host_shards, const size_t* shard_bytes, int
  * streaming works").  Records the release of call k-1's
  * buffer on `compute`, issues the copies the ring rule allows, makes `compute` wait
  * for layer k's copy and returns its device address in *dev_ptr_out.  Every kernel
- * that reads layer k must be enqueued on `compute` before call k+1.
+ * that reads layer k must be enqueued on `compute` before call k+1.  Resident mode: each
+ * layer is copied once, and once that copy has been seen complete (a host-side event
+ * query) the call enqueues nothing on `compute`: after one resident pass has finished,
+ * the calls of a resident pass issue no stream work, so the caller may capture that
+ * pass's kernel launches as a graph.
  * Errors: ESTATE (k out of order, pass finished, destroyed), EINVAL, EHIP.
  */
 int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** dev_ptr_out);

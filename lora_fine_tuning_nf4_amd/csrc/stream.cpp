@@ -96,6 +96,7 @@ struct lnf4_stream {
   int issued = 0;
   int pass = 0;
   bool resident_copied = false;
+  std::vector<char> resident_ready;  // resident mode: buffer b's one copy was seen complete
   int slot_loads = 0;
   int64_t bytes_copied = 0;
   std::vector<lnf4_stream_event> log;
@@ -562,7 +563,21 @@ int stream_layer_step(lnf4_stream* st, int32_t k, hipStream_t compute, void** de
       st->resident_copied = true;
     }
     const int s = st->sched[k];
-    if ((e = hipStreamWaitEvent(compute, st->copy_done[s], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(copy_done)");
+    // each buffer is written once: after its copy has been seen complete no wait is
+    // enqueued (the call then issues no stream work at all, so a caller may capture the
+    // resident step's launches in a graph)
+    if ((int)st->resident_ready.size() != (int)st->host.size()) st->resident_ready.assign(st->host.size(), 0);
+    if (!st->resident_ready[s]) {
+      e = hipEventQuery(st->copy_done[s]);
+      if (e == hipSuccess) {
+        st->resident_ready[s] = 1;
+      } else if (e == hipErrorNotReady) {
+        (void)hipGetLastError();  // a pending copy is not an error
+        if ((e = hipStreamWaitEvent(compute, st->copy_done[s], 0)) != hipSuccess) return hip_fail(e, "stream: hipStreamWaitEvent(copy_done)");
+      } else {
+        return hip_fail(e, "stream: hipEventQuery(copy_done)");
+      }
+    }
     log_ev(st, LNF4_EV_STEP, k, s, s, s, s);
     st->next_call = k + 1;
     *dev_ptr_out = st->bufs[s];

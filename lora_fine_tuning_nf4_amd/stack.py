@@ -153,6 +153,7 @@ class StreamedStack:
         self._embed_in_slot = False   # the next step's embed_tokens was loaded during the last backward
         self._lm_head_in_slot = False  # embed_from_host: the lm_head was loaded into the slot
         self.st_res = None
+        self._graph = None            # the resident step captured as a HIP graph (resident_graph)
         self.res_bufs = None
 
     def _init_output_side(self, loss_chunk):
@@ -471,7 +472,37 @@ class StreamedStack:
     def bytes_copied(self) -> int:
         return lnf4.stream_bytes_copied(self.st)
 
+    def resident_graph(self):
+        """The resident step captured as one HIP graph: the same kernel launches, in the same
+        order and on the same buffers, recorded once on a capture stream, so a replay costs
+        one launch from the host instead of about 40 per layer.  Built on first use, after
+        an eager resident step has finished (the resident stream calls then issue no stream
+        work; see stream_layer_step).  A step reads its inputs and writes its outputs in
+        place, so every replay gives the eager step's results."""
+        if self._graph is None:
+            if self.timers is not None or self.wait_events is not None:
+                raise RuntimeError("resident_graph: timing instrumentation is on")
+            self.step(resident=True)
+            torch.cuda.synchronize(self.dev)
+            graph = torch.cuda.CUDAGraph()
+            prev = self.compute
+            try:
+                with torch.cuda.graph(graph, stream=torch.cuda.Stream(self.dev)):
+                    self.compute = torch.cuda.current_stream(self.dev)
+                    self.step(resident=True)
+            finally:
+                self.compute = prev
+            self._graph = graph
+        return self._graph
+
+    def step_graph(self):
+        """One resident step by replaying the captured graph on the compute stream."""
+        g = self.resident_graph()
+        with torch.cuda.stream(self.compute):
+            g.replay()
+
     def close(self):
+        self._graph = None
         if self.st is not None or self.st_res is not None:
             torch.cuda.synchronize(self.dev)
         if self.st is not None:

@@ -201,6 +201,31 @@ def _same(a, b):
         assert np.array_equal(a["head"][k], b["head"][k]), k
 
 
+@pytest.mark.parametrize("dpo", [False, True])
+def test_resident_graph_replays_equal_eager(dpo):
+    """The resident step captured as a HIP graph: every replay gives the eager resident
+    step's outputs bitwise, with eager work between the replays (the outputs overwritten,
+    then a streamed step, which writes the same outputs)."""
+    wl = _small_workload("nf4")
+    stack = StreamedStack(wl, n_bufs=2, seed=3, dpo=dpo)
+    try:
+        stack.step(resident=True)
+        ref = _snapshot(stack)
+        for rep in range(3):
+            for t in list(stack.y.values()) + list(stack.dx) + [stack.dh, stack.logp]:
+                t.fill_(7)
+            for ls in stack.layers:
+                for p in ls.dA:
+                    ls.dA[p].fill_(-1.0)
+                    ls.dB[p].fill_(-1.0)
+            stack.step_graph()
+            _same(ref, _snapshot(stack))
+            stack.step()
+            _same(ref, _snapshot(stack))
+    finally:
+        stack.close()
+
+
 @pytest.mark.parametrize("fmt,dpo,reuse,efh", [("nf4", False, False, False), ("bf16", False, False, False),
                                                ("nf4", True, False, False), ("nf4", False, True, False),
                                                ("nf4", True, True, False), ("nf4", False, False, True),
