@@ -29,11 +29,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
   const int n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
 }
+// the same with a byte count already in [0, 2^31)
+__device__ __forceinline__ rsrc_t make_rsrc_n(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
 #define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_, (lds_ptr)(lds_), size_, voff_, soff_, 0, 0)
 #else
 typedef const void* rsrc_t;
 __device__ inline rsrc_t make_rsrc(const void* p, int64_t) { return p; }
+__device__ inline rsrc_t make_rsrc_n(const void* p, int) { return p; }
 #define LNF4_BUF_LDS(rsrc_, lds_, size_, voff_, soff_) ((void)(rsrc_), (void)(lds_), (void)(voff_), (void)(soff_))
 #endif
 

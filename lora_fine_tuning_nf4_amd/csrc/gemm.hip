@@ -779,6 +779,69 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16(const FwdArgs args) {
 }
 
 // =====================================================================================
+// Prefetch cursor over the K space of an input-gradient launch
+// =====================================================================================
+// The K-blocks a split loads run through the group's projections in order, so the
+// projection that holds the next block to load (its pointers and out_f, read from the
+// kernel arguments) changes at most n_proj - 1 times per split.  The cursor keeps that
+// projection in scalar registers and otherwise only moves its row offset by one block.
+// (Looking the projection up afresh for every block, a compare chain over the group and
+// scalar loads of its fields with a wait on them, held up the wave's MFMA issue once per
+// block.)  KS is the kernel's block height; the projections' kb0 count 64-row blocks.
+struct DxCursor {
+  int kb;    // next block to load
+  int pi;    // its projection
+  int next;  // first block of projection pi + 1 (INT_MAX after the last)
+  int k0;    // its first row within the projection
+  int Kp;    // the projection's out_f
+  const uint16_t* dy;
+  const void* w;
+  const float* absmax;
+};
+
+template <int KS>
+__device__ __forceinline__ void dx_cursor_load(DxCursor& c, const DxArgs& a) {
+  const DxProj& P = a.p[c.pi];
+  c.dy = P.dy;
+  c.w = P.w;
+  c.absmax = P.absmax;
+  c.Kp = P.out_f;
+  const int nx = c.pi + 1 < kMaxGroup ? c.pi + 1 : kMaxGroup - 1;
+  c.next = c.pi + 1 < a.n_proj ? (64 / KS) * a.p[nx].kb0 : 0x7fffffff;
+}
+
+template <int KS>
+__device__ __forceinline__ DxCursor dx_cursor_init(const DxArgs& a, int kb) {
+  DxCursor c;
+  int pi = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxGroup; ++q)
+    if (q < a.n_proj && kb >= (64 / KS) * a.p[q].kb0) pi = q;
+  c.pi = __builtin_amdgcn_readfirstlane(pi);
+  c.kb = kb;
+  dx_cursor_load<KS>(c, a);
+  c.k0 = (kb - (64 / KS) * a.p[c.pi].kb0) * KS;
+  return c;
+}
+
+// move to the next block; true when it starts the next projection
+template <int KS>
+__device__ __forceinline__ bool dx_cursor_next(DxCursor& c, const DxArgs& a) {
+  ++c.kb;
+  c.k0 += KS;
+  if (c.kb != c.next) return false;
+  ++c.pi;
+  dx_cursor_load<KS>(c, a);
+  c.k0 = 0;
+  return true;
+}
+
+// a byte count for a buffer resource, clamped to 2^31 - 1 with scalar operations
+__device__ __forceinline__ int clamp31(uint64_t b) {
+  return (uint32_t)(b >> 31) != 0u ? 0x7fffffff : (int)(uint32_t)b;
+}
+
+// =====================================================================================
 // Input gradient, NF4 weights: direct-to-LDS ring with transposing code reads
 // =====================================================================================
 // dx [T][N] = sum over the group's K space (the projections' out rows) of dy . W'.
@@ -1179,6 +1242,93 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   }
 }
 
+// Rank-R LoRA term of the bf16-weight input gradient (ranks of the group concatenated),
+// folded into the accumulators: hi and lo halves of s_p v_p staged in Uh / Ul [BM][RP],
+// the adapter columns of the tile in V [256][RP] (three LDS slabs of BM x 64 and 256 x 64
+// bf16), then the rank update on the MFMA units.  Accumulators are not transposed.
+template <int MI>
+__device__ __forceinline__ void dx_bf16_rank_init(floatx16 (&acc)[MI][2], const DxArgs& args, int m0, int n0,
+                                                  uint8_t* s_uh, uint8_t* s_ul, uint8_t* s_v, int tid, int l32,
+                                                  int h, int nc0, int nc1) {
+  constexpr int BM = 32 * MI;
+  const int M = args.M, N = args.N;
+  int R = 0;
+  for (int pi = 0; pi < args.n_proj; ++pi) {
+    const DxProj P = select_dx(args, pi);
+    if (P.v != nullptr && P.r > 0) R += P.r;
+  }
+  if (R <= 0) return;
+  const int RP = (R + 15) & ~15;
+  uint16_t* Uh = (uint16_t*)s_uh;
+  uint16_t* Ul = (uint16_t*)s_ul;
+  uint16_t* V = (uint16_t*)s_v;
+  for (int idx = tid; idx < BM * RP; idx += NTHR) Uh[idx] = Ul[idx] = 0;
+  for (int idx = tid; idx < BN * RP; idx += NTHR) V[idx] = 0;
+  __syncthreads();
+  int off = 0;
+  for (int pi = 0; pi < args.n_proj; ++pi) {
+    const DxProj P = select_dx(args, pi);
+    if (P.v == nullptr || P.r <= 0) continue;
+    const int r = P.r;
+    for (int idx = tid; idx < BM * r; idx += NTHR) {
+      const int mm = idx / r, kk = idx - mm * r, gm = m0 + mm;
+      if (gm < M) split_bf16(P.scale * P.v[(size_t)gm * P.v_stride + kk], Uh[mm * RP + off + kk], Ul[mm * RP + off + kk]);
+    }
+    for (int idx = tid; idx < BN * r; idx += NTHR) {
+      const int kk = idx / BN, nn = idx - kk * BN, n = n0 + nn;
+      if (n < N) V[nn * RP + off + kk] = P.A[(size_t)kk * N + n];
+    }
+    off += r;
+  }
+  __syncthreads();
+  rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+  __syncthreads();
+}
+
+// Output of a bf16-weight input-gradient tile: this split's fp32 sums into the split-K
+// workspace, or bf16 dx (optionally added to the existing dx).  Lane (l32, h) holds columns
+// nc0 / nc1 and, for q = 0..15, row 32i + 8(q / 4) + 4h + q % 4 of the tile.
+template <int MI>
+__device__ __forceinline__ void dx_bf16_store(const floatx16 (&acc)[MI][2], const DxArgs& args, int split, int m0,
+                                              int n0, int nc0, int nc1, int h) {
+  const int M = args.M, N = args.N;
+  const int n0g = n0 + nc0, n1g = n0 + nc1;
+  const bool c0ok = n0g < N, c1ok = n1g < N;
+  if (args.part != nullptr) {  // split-K: this split's fp32 sums, added up by k_dx_split_sum
+    float* pp = args.part + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (gm >= M) continue;
+        if (c0ok) pp[(size_t)gm * N + n0g] = acc[i][0][q];
+        if (c1ok) pp[(size_t)gm * N + n1g] = acc[i][1][q];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      if (gm >= M) continue;
+      uint16_t* dr = args.dx + (size_t)gm * N;
+      float v0 = acc[i][0][q], v1 = acc[i][1][q];
+      if (args.accumulate) {
+        if (c0ok) v0 += bf16_to_f32(dr[n0g]);
+        if (c1ok) v1 += bf16_to_f32(dr[n1g]);
+      }
+      if (c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
+      if (c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
+    }
+  }
+}
+
+
 // =====================================================================================
 // Input gradient, bf16 weights: direct-to-LDS ring with transposing 16-bit reads
 // =====================================================================================
@@ -1229,38 +1379,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-  int R = 0;
-  for (int pi = 0; pi < args.n_proj; ++pi) {
-    const DxProj P = select_dx(args, pi);
-    if (P.v != nullptr && P.r > 0) R += P.r;
-  }
-  if (R > 0 && split == 0) {  // the rank-R term once, in split 0
-    const int RP = (R + 15) & ~15;
-    uint16_t* Uh = (uint16_t*)sm0;
-    uint16_t* Ul = (uint16_t*)sm1;
-    uint16_t* V = (uint16_t*)sm2;
-    for (int idx = tid; idx < BM * RP; idx += NTHR) Uh[idx] = Ul[idx] = 0;
-    for (int idx = tid; idx < BN * RP; idx += NTHR) V[idx] = 0;
-    __syncthreads();
-    int off = 0;
-    for (int pi = 0; pi < args.n_proj; ++pi) {
-      const DxProj P = select_dx(args, pi);
-      if (P.v == nullptr || P.r <= 0) continue;
-      const int r = P.r;
-      for (int idx = tid; idx < BM * r; idx += NTHR) {
-        const int mm = idx / r, kk = idx - mm * r, gm = m0 + mm;
-        if (gm < M) split_bf16(P.scale * P.v[(size_t)gm * P.v_stride + kk], Uh[mm * RP + off + kk], Ul[mm * RP + off + kk]);
-      }
-      for (int idx = tid; idx < BN * r; idx += NTHR) {
-        const int kk = idx / BN, nn = idx - kk * BN, n = n0 + nn;
-        if (n < N) V[nn * RP + off + kk] = P.A[(size_t)kk * N + n];
-      }
-      off += r;
-    }
-    __syncthreads();
-    rank_update<MI>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
-    __syncthreads();
-  }
+  if (split == 0) dx_bf16_rank_init<MI>(acc, args, m0, n0, sm0, sm1, sm2, tid, l32, h, nc0, nc1);
 
   // ---- direct global -> LDS loads of one K-block (64 rows of one projection)
   //  * dy: load q of wave w fills tile rows (w*XQ+q)*8 .. +7 (as the forward's x)
@@ -1414,41 +1533,226 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
 #undef LNF4_DXB_FRAG
 #undef LNF4_XS
 
-  // ---- store bf16 (optionally accumulating into the existing dx)
-  const int n0g = n0 + nc0, n1g = n0 + nc1;
-  const bool c0ok = n0g < N, c1ok = n1g < N;
-  if (args.part != nullptr) {  // split-K: this split's fp32 sums, added up by k_dx_split_sum
-    float* pp = args.part + (size_t)split * M * N;
+  dx_bf16_store<MI>(acc, args, split, m0, n0, nc0, nc1, h);
+}
+
+// Input gradient, bf16 weights, 256-row tiles: 32-wide K-blocks in a 5-stage ring.
+// A 256 x 256 tile loads 32 KB per 32 K (dy [256][32] and W [32][256]), 1.5x fewer bytes per
+// MFMA than the 128-row tile, but with 64-wide blocks only two 64 KB stages fit LDS and a
+// block's loads then have one block of MFMAs (about 2,000 cycles) to land, less than the
+// latency of the streamed operands of a long-K launch such as the lm_head input gradient.
+// With 32-wide blocks five 32 KB stages fit (160 KB): a block's loads are issued right
+// after the barrier that frees its stage, four blocks (128 MFMAs per wave) before they are
+// read.
+//  * K order inside a block: lane (n, h) of the MFMA supplies K = 16h + 8s .. +7 at step s
+//    (two steps per block); the dy tile's 64-byte rows hold four 16-byte chunks, chunk c of
+//    row r at slot c ^ ((r >> 2) & 3), so the 16 rows one read phase serves cover all 16
+//    bank groups.
+//  * Weight rows (K) are 512 bytes, stored and read back transposed as in the 128-row
+//    kernel; a step's B fragment is rows 16h + 8s .. +7 of the block.
+//  * Wave w owns the 64 columns [64w, 64w+64) and all 256 rows.
+__global__ __launch_bounds__(NTHR, 1) void k_dx_bf16_deep(const DxArgs args) {
+  constexpr int BM = 256, MI = 8, NM = 16;
+  constexpr int KS = 32;                    // K-block width
+  constexpr int X_BYTES = BM * KS * 2;      // dy tile [256][32] bf16
+  constexpr int W_BYTES = KS * BN * 2;      // weight tile [32][256] bf16
+  constexpr int STAGE = X_BYTES + W_BYTES;  // 32 KB
+  static_assert(BM * LNF4_EPI_RANK * 2 <= STAGE && BN * LNF4_EPI_RANK * 2 <= STAGE, "LoRA slabs fit a stage");
+  static_assert(5 * STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm3[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm4[STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  int tm, tn;
+  const int n_tiles = args.n_tiles_m * args.n_tiles_n;
+  const int split = (int)blockIdx.x / n_tiles;
+  tile_coords((int)blockIdx.x - split * n_tiles, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  const int M = args.M, N = args.N;
+  const int m0 = tm * BM, n0 = tn * BN;
+  // the split's 64-row blocks, counted in 32-row blocks
+  const int kb64_end = split * args.kb_per_split + args.kb_per_split < args.total_kb
+                           ? split * args.kb_per_split + args.kb_per_split : args.total_kb;
+  const int kb_beg = 2 * split * args.kb_per_split;
+  const int kb_end = 2 * kb64_end;
+  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;
+
+  floatx16 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (gm >= M) continue;
-        if (c0ok) pp[(size_t)gm * N + n0g] = acc[i][0][q];
-        if (c1ok) pp[(size_t)gm * N + n1g] = acc[i][1][q];
-      }
-    }
-    return;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  if (split == 0) dx_bf16_rank_init<MI>(acc, args, m0, n0, sm0, sm1, sm2, tid, l32, h, nc0, nc1);
+
+  // ---- direct global -> LDS loads of one K-block (32 rows of one projection)
+  //  * dy: load q of wave w fills tile rows (w*XQ+q)*16 .. +15; lane L -> row +L/4, slot L%4,
+  //    which holds chunk (L%4) ^ ((row >> 2) & 3) of the row
+  //  * weights: load q of wave w fills rows 2g, 2g+1 (g = w*WQ+q); lane L -> row 2g + L/32,
+  //    stored chunk L%32, which holds global chunk (L%32) ^ 4(row & 3) of the row
+  //  Rows past the projection's out_f load zeros (the block's resources end there); a block
+  //  wholly past it has empty resources.  Columns past N belong to outputs that are dropped.
+  constexpr int XQ = X_BYTES / 1024 / 4;
+  constexpr int WQ = W_BYTES / 1024 / 4;
+  constexpr int NLD = XQ + WQ;
+  uint32_t dyr2[XQ], dyc[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int row = (wave * XQ + q) * 16 + (lane >> 2);
+    dyr2[q] = 2u * (uint32_t)(m0 + row < M ? m0 + row : M - 1);
+    dyc[q] = 16u * (uint32_t)((lane & 3) ^ ((row >> 2) & 3));
   }
+  uint32_t woff[WQ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int gm = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-      if (gm >= M) continue;
-      uint16_t* dr = args.dx + (size_t)gm * N;
-      float v0 = acc[i][0][q], v1 = acc[i][1][q];
-      if (args.accumulate) {
-        if (c0ok) v0 += bf16_to_f32(dr[n0g]);
-        if (c1ok) v1 += bf16_to_f32(dr[n1g]);
-      }
-      if (c0ok) dr[n0g] = __builtin_bit_cast(uint16_t, (__bf16)v0);
-      if (c1ok) dr[n1g] = __builtin_bit_cast(uint16_t, (__bf16)v1);
-    }
+  for (int q = 0; q < WQ; ++q) {
+    const int row = 2 * (wave * WQ + q) + (lane >> 5);
+    const int cg = (lane & 31) ^ (4 * (row & 3));
+    woff[q] = 2u * ((uint32_t)row * (uint32_t)N + (uint32_t)(n0 + 8 * cg));
   }
+
+  // the next block to load: its resources end at the projection's last row (rows past
+  // out_f load as zeros); blocks past the split, or wholly past out_f, have empty ones
+  DxCursor cur = dx_cursor_init<KS>(args, kb_beg);
+  rsrc_t wrs_next;  // weight resource of the block whose dy rows went out last
+  uint32_t dyo[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) dyo[q] = dyr2[q] * (uint32_t)cur.Kp + dyc[q];
+  // A block's loads go out in two parts: its dy rows right after the barrier that frees its
+  // stage (step 1 of the block five before it), its weight rows at step 0 of the next
+  // block (a burst of all of them at once held up the wave's MFMA issue).  Branch-free: a
+  // branch would split the step that issues them, and the interleaving of its MFMAs with
+  // its LDS reads is only kept within one basic block.
+#define LNF4_DXD_ISSUE_X(SM_)                                                                    \
+  {                                                                                              \
+    const int live_ = -(int)((cur.kb < kb_end) & (cur.k0 < cur.Kp));                             \
+    const int dyn_ = clamp31(((uint64_t)(uint32_t)M * (uint32_t)cur.Kp - (uint32_t)cur.k0) * 2u) & live_; \
+    const int wn_ = clamp31((uint64_t)(uint32_t)(cur.Kp - cur.k0) * (2u * (uint32_t)N)) & live_; \
+    const rsrc_t dyrs_ = make_rsrc_n(cur.dy + cur.k0, dyn_);                                      \
+    wrs_next = make_rsrc_n((const uint16_t*)cur.w + (size_t)cur.k0 * N, wn_);                     \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                               \
+      LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + q) * 1024, 16, dyo[q], 0);                       \
+  }
+#define LNF4_DXD_ISSUE_W(SM_)                                                                    \
+  {                                                                                              \
+    _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                               \
+      LNF4_BUF_LDS(wrs_next, (SM_) + X_BYTES + (wave_u * WQ + q) * 1024, 16, woff[q], 0);       \
+  }
+  // the cursor moves after the step's MFMAs, outside its interleaved region
+#define LNF4_DXD_ADVANCE()                                                                       \
+  {                                                                                              \
+    if (dx_cursor_next<KS>(cur, args)) {                                                         \
+      _Pragma("unroll") for (int q = 0; q < XQ; ++q) dyo[q] = dyr2[q] * (uint32_t)cur.Kp + dyc[q]; \
+    }                                                                                            \
+  }
+
+  typedef short v4s_t __attribute__((ext_vector_type(4)));
+  const int tr_c = (lane & 15) >> 2, tr_col = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
+  const int tbo0 = (16 * h + tr_c) * 512 + (((8 * wave + 0 + (tr_col >> 3)) ^ (4 * tr_c)) << 4) + ((tr_col & 7) << 1);
+  const int tbo1 = (16 * h + tr_c) * 512 + (((8 * wave + 4 + (tr_col >> 3)) ^ (4 * tr_c)) << 4) + ((tr_col & 7) << 1);
+#define LNF4_DXD_TR(SM_, off_) \
+  __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)((SM_) + X_BYTES + (off_)))
+#define LNF4_DXD_BFRAG(SM_, s_, o_)                                                              \
+  ({                                                                                             \
+    const v4s_t lo_ = LNF4_DXD_TR(SM_, (o_) + 4096 * (s_));                                      \
+    const v4s_t hi_ = LNF4_DXD_TR(SM_, (o_) + 4096 * (s_) + 2048);                               \
+    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7));      \
+  })
+#define LNF4_DXD_AFRAG(SM_, i_, c_)                                                              \
+  (*(const bf16x8*)((const uint16_t*)(SM_) + (32 * (i_) + l32) * KS +                           \
+                    ((((c_) ^ (((32 * (i_) + l32) >> 2) & 3))) << 3)))
+
+  // prologue: blocks 0 .. 3 and the dy rows of block 4 in flight (its weight rows go out at
+  // step 0 of block 0); block 0 visible
+  LNF4_DXD_ISSUE_X(sm0);
+  LNF4_DXD_ISSUE_W(sm0);
+  LNF4_DXD_ADVANCE();
+  LNF4_DXD_ISSUE_X(sm1);
+  LNF4_DXD_ISSUE_W(sm1);
+  LNF4_DXD_ADVANCE();
+  LNF4_DXD_ISSUE_X(sm2);
+  LNF4_DXD_ISSUE_W(sm2);
+  LNF4_DXD_ADVANCE();
+  LNF4_DXD_ISSUE_X(sm3);
+  LNF4_DXD_ISSUE_W(sm3);
+  LNF4_DXD_ADVANCE();
+  LNF4_DXD_ISSUE_X(sm4);
+  LNF4_DXD_ADVANCE();
+  LNF4_WAIT_VM(3 * NLD + XQ);
+  __syncthreads();
+
+  bf16x8 ac[MI], an_[MI];
+  bf16x8 bc0, bc1, bn0, bn1;
+  bc0 = LNF4_DXD_BFRAG(sm0, 0, tbo0);
+  bc1 = LNF4_DXD_BFRAG(sm0, 0, tbo1);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) ac[i] = LNF4_DXD_AFRAG(sm0, i, 2 * h);
+
+  // One 32-row block KB on stage SC; SN holds block KB+1, SP (the stage of KB-1) receives
+  // the weight rows of block KB+4 at step 0.  Step 1: every wave's loads of block KB+1 have
+  // landed (those of KB+2 .. KB+4 may still be in flight: 3 NLD loads issued after them),
+  // the barrier makes KB+1 visible and SC free, and the dy rows of block KB+5 go into SC.
+#define LNF4_DXD_BLOCK(KB, SC, SN, SP)                                                             \
+  {                                                                                            \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 1) {                                                                            \
+        LNF4_WAIT_VM_LGKM0(3 * NLD);                                                           \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        bn0 = LNF4_DXD_BFRAG(SN, 0, tbo0);                                                     \
+        bn1 = LNF4_DXD_BFRAG(SN, 0, tbo1);                                                     \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] = LNF4_DXD_AFRAG(SN, i, 2 * h);  \
+        LNF4_DXD_ISSUE_X(SC);                                                          \
+      } else {                                                                                 \
+        bn0 = LNF4_DXD_BFRAG(SC, 1, tbo0);                                                     \
+        bn1 = LNF4_DXD_BFRAG(SC, 1, tbo1);                                                     \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] = LNF4_DXD_AFRAG(SC, i, 2 * h + 1); \
+        LNF4_DXD_ISSUE_W(SP);                                                                  \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
+        acc[i][0] = mfma32(ac[i], bc0, acc[i][0]);                                             \
+        acc[i][1] = mfma32(ac[i], bc1, acc[i][1]);                                             \
+      }                                                                                        \
+      _Pragma("unroll") for (int g = 0; g < NM; ++g) {                                         \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) ac[i] = an_[i];                           \
+      bc0 = bn0;                                                                               \
+      bc1 = bn1;                                                                               \
+      if (s == 1) {                                                                            \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        LNF4_DXD_ADVANCE();                                                                    \
+      }                                                                                        \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+  }
+
+  // whole turns of the ring, one exit test per turn (blocks past the last add zeros)
+  for (int kb = kb_beg; kb < kb_end; kb += 5) {
+    LNF4_DXD_BLOCK(kb + 0, sm0, sm1, sm4);
+    LNF4_DXD_BLOCK(kb + 1, sm1, sm2, sm0);
+    LNF4_DXD_BLOCK(kb + 2, sm2, sm3, sm1);
+    LNF4_DXD_BLOCK(kb + 3, sm3, sm4, sm2);
+    LNF4_DXD_BLOCK(kb + 4, sm4, sm0, sm3);
+  }
+#undef LNF4_DXD_BLOCK
+#undef LNF4_DXD_ISSUE_X
+#undef LNF4_DXD_ISSUE_W
+#undef LNF4_DXD_ADVANCE
+#undef LNF4_DXD_TR
+#undef LNF4_DXD_BFRAG
+#undef LNF4_DXD_AFRAG
+
+  dx_bf16_store<MI>(acc, args, split, m0, n0, nc0, nc1, h);
 }
 
 // Split-K input gradient: dx = bf16(sum of the splits' fp32 sums in split order, plus the
@@ -1573,16 +1877,19 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
 // often per MFMA as 128-row tiles; when they are too few to fill the compute units, K splits
 // make up the count (dx_split_count).  Kept only where every split still runs at least 64
 // K-blocks: shorter splits lose more to the fp32 partials and the per-tile start than the
-// decode saves (measured: gate|up of the 8B shape, K = 28672, 2 splits: 17 % faster;
-// K = 4096 or 9728 in 2 or 8 splits: slower).  bf16 weight tiles only fit LDS with 128 rows.
+// decode (NF4) or the deeper load ring (bf16) saves (measured: gate|up of the 8B shape,
+// K = 28672, 2 splits: 17 % faster; K = 4096 or 9728 in 2 or 8 splits: slower).
+// bf16 weights take 256-row tiles (k_dx_bf16_deep) only where they need at most two
+// splits: with four (the 3B gate|up shape, K = 22016) the extra fp32 partials cost more
+// than the tile saves (0.270 against 0.234 ms for 128-row tiles in two splits).
 static int dx_bm(int M, int N, int total_kb, int fmt) {
-  if (fmt != 0) return 128;
   const int tn = (N + BN - 1) / BN;
-  if (pick_bm(M, tn) == 256) return 256;
+  if (fmt == 0 && pick_bm(M, tn) == 256) return 256;
   if (M <= 128) return 128;
   const int tiles = ((M + 255) / 256) * tn;
   int ns = (256 + tiles - 1) / tiles;
   ns = ns > 8 ? 8 : ns;
+  if (fmt != 0 && ns > 2) return 128;
   return total_kb / ns >= 64 ? 256 : 128;
 }
 
@@ -1621,7 +1928,8 @@ hipError_t launch_dx(const DxArgs& a0, int fmt, hipStream_t s) {
     if (bm == 256) hipLaunchKernelGGL((k_dxq<256>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_dxq<128>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_dx_bf16<128>), grid, block, 0, s, a);
+    if (bm == 256) hipLaunchKernelGGL(k_dx_bf16_deep, grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dx_bf16<128>), grid, block, 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;

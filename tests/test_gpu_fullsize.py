@@ -113,3 +113,38 @@ def test_full_size_group_sampled(wl_name, names):
         check_tol(bf16_f64(host_u16(d["y"])[ROWS]), y_ref, f"y {p}")
         del Wd
     check_tol(bf16_f64(host_u16(dx)[ROWS]), dx_ref, "dx")
+
+
+@pytest.mark.parametrize("T", [2048, 4096])
+def test_lm_head_gemms_full_size_sampled_rows(T):
+    """The untied lm_head of the 8B head at the loss turn (T = 2048 SFT, 4096 DPO), in one
+    launch each: logits = h W^T (K = 4096, N = 128256) and dh = dlogits W (K = 128256 in
+    256-row tiles with 32-row K-blocks: two splits at T = 2048, none at 4096), adapter
+    off; sampled rows of both against the fp64 oracle, summed over vocabulary chunks of W."""
+    V, H = 128256, 4096
+    W = synthgen.device_normal((V, H), 0.02, 12, "lm_head_full", dtype=torch.bfloat16)
+    h = synthgen.device_normal((T, H), 1.0, 12, "h_full", dtype=torch.bfloat16)
+    dl = synthgen.device_normal((T, V), 1e-3, 12, "dlogits_full", dtype=torch.bfloat16)
+    Wd = lnf4.make_weight(lnf4.FMT_BF16, W, None, V, H, 64)
+    logits = torch.empty((T, V), dtype=torch.bfloat16, device="cuda")
+    dh = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = lnf4.lora_linear_bwd_workspace(T, V, H, 0)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    lnf4.lora_linear_fwd(Wd, h, T, None, None, 0, 0.0, logits, None)
+    lnf4.lora_linear_bwd(Wd, h, dl, T, None, None, 0, 0.0, None, dh, None, None, 0, ws, ws_bytes)
+    torch.cuda.synchronize()
+    ROWS = [0, 1, 255, 256, 777, T // 2 + 3, T - 129, T - 1]
+    ridx = torch.tensor(ROWS, dtype=torch.int64, device="cuda")
+    hs = bf16_f64(host_u16(h.index_select(0, ridx).view(torch.int16)))
+    dls = bf16_f64(host_u16(dl.index_select(0, ridx).view(torch.int16)))
+    logits_ref = np.zeros((len(ROWS), V))
+    dh_ref = np.zeros((len(ROWS), H))
+    step = 16384
+    for v0 in range(0, V, step):
+        v1 = min(V, v0 + step)
+        Wc = bf16_f64(host_u16(W[v0:v1].view(torch.int16)))
+        logits_ref[:, v0:v1] = hs @ Wc.T
+        dh_ref += dls[:, v0:v1] @ Wc
+        del Wc
+    check_tol(bf16_f64(host_u16(logits.index_select(0, ridx).view(torch.int16))), logits_ref, "logits")
+    check_tol(bf16_f64(host_u16(dh.index_select(0, ridx).view(torch.int16))), dh_ref, "dh")

@@ -155,11 +155,11 @@ def test_accumulate_adds_to_existing():
     check_tol(host_f32(d.dB)[:, :8], dB1[:, :8] + dB_ref, "dB accumulated")
 
 
-@pytest.mark.parametrize("fmt,out_f", [(0, 2048), (1, 2048), (0, 32768)])
+@pytest.mark.parametrize("fmt,out_f", [(0, 2048), (1, 2048), (0, 32768), (1, 32768)])
 def test_backward_split_k(fmt, out_f):
     # few output tiles and a long K space: the dx GEMM splits K (fp32 sums per split, then a
     # fixed-order sum); checked alone and accumulating into the existing dx.  K = 2048: 128-row
-    # tiles; NF4 with K = 32768: 256-row tiles in 8 splits of 64 K-blocks
+    # tiles; K = 32768: NF4 in 256-row tiles, bf16 in 128-row tiles, 8 splits each
     c = make_case(19, 256, out_f, 256, 8, 16.0, fmt, tag=f"split-k-{out_f}")
     d = DevCase(c)
     _run_bwd(d)
