@@ -950,11 +950,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
   const int cbyte_max = halfN - 16;
   const int ablk = (n0 / 64 + wave) < nblk ? n0 / 64 + wave : nblk - 1;
 
-#define LNF4_DXQ_PROJ(kb_, P_)                                                   \
-  int pi_ = 0;                                                                   \
-  _Pragma("unroll") for (int q = 1; q < kMaxGroup; ++q) if (q < args.n_proj && (kb_) >= args.p[q].kb0) pi_ = q; \
-  pi_ = __builtin_amdgcn_readfirstlane(pi_);                                     \
-  const DxProj& P_ = args.p[pi_];
 
   // per-lane constant parts of the buffer-load offsets (as in the forward kernels); the projection and the
   // K offset go into each block's resources, whose ranges end at the projection's last
@@ -977,35 +972,48 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 
   // The loads of one K-block go out in three parts, one per step of the block before the
   // ring wraps: dy rows of the first half, of the second half, then codes and absmax.
-  // Blocks past the last (the loop runs whole trips) belong to no projection's row range:
-  // their resources are empty and every load returns zeros (zero dy, zero absmax).
-#define LNF4_DXQ_RSRC(kb_)                                                                       \
-    LNF4_DXQ_PROJ(kb_, Pi_)                                                                      \
-    const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
-    const int64_t lv_ = (kb_) < kb_end ? 1 : 0; /* blocks past the split: empty ranges */       \
-    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, lv_ * ((int64_t)M * Kp_ - k0_) * 2);            \
-    const rsrc_t wrs_ =                                                                          \
-        make_rsrc((const uint8_t*)Pi_.w + (size_t)k0_ * halfN, lv_ * (int64_t)(Kp_ - k0_) * halfN); \
-    const rsrc_t ars_ =                                                                          \
-        make_rsrc(Pi_.absmax + (size_t)k0_ * nblk, lv_ * (int64_t)(Kp_ - k0_) * nblk * 4);
+  // The block is the prefetch cursor's; its resources end at the projection's last row.
+  // Blocks past the split (the loop runs whole trips) get empty resources, and every load
+  // returns zeros (zero dy, zero absmax).  Branch-free: a branch would split the step.
+  DxCursor cur = dx_cursor_init<BK>(args, kb_beg);
+  uint32_t dyo[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) dyo[q] = dyr2[q] * (uint32_t)cur.Kp + dyc[q];
+#define LNF4_DXQ_RSRC()                                                                          \
+    const int live_ = -(int)((cur.kb < kb_end) & (cur.k0 < cur.Kp));                             \
+    const uint32_t rows_ = (uint32_t)((cur.Kp - cur.k0) & live_);                                \
+    const rsrc_t dyrs_ = make_rsrc_n(                                                            \
+        cur.dy + cur.k0, clamp31(((uint64_t)(uint32_t)M * (uint32_t)cur.Kp - (uint32_t)cur.k0) * 2u) & live_); \
+    const rsrc_t wrs_ = make_rsrc_n((const uint8_t*)cur.w + (size_t)cur.k0 * halfN,               \
+                                    clamp31((uint64_t)rows_ * (uint32_t)halfN));                  \
+    const rsrc_t ars_ = make_rsrc_n(cur.absmax + (size_t)cur.k0 * nblk,                          \
+                                    clamp31((uint64_t)rows_ * (uint32_t)(4 * nblk)));
+  // the cursor moves after the block's last step, outside its interleaved regions
+#define LNF4_DXQ_ADVANCE()                                                                       \
+  {                                                                                              \
+    if (dx_cursor_next<BK>(cur, args)) {                                                         \
+      _Pragma("unroll") for (int q = 0; q < XQ; ++q) dyo[q] = dyr2[q] * (uint32_t)cur.Kp + dyc[q]; \
+    }                                                                                            \
+  }
 #define LNF4_DXQ_ISSUE_PART(SM_, part_)                                                          \
   {                                                                                              \
     if ((part_) < 2) {                                                                           \
       _Pragma("unroll") for (int q = (part_) * (XQ / 2); q < ((part_) + 1) * (XQ / 2); ++q)      \
-          LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + q) * 1024, 16, dyr2[q] * (uint32_t)Kp_ + dyc[q], 0); \
+          LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + q) * 1024, 16, dyo[q], 0);                 \
     } else {                                                                                     \
       _Pragma("unroll") for (int q = 0; q < 2; ++q)                                              \
           LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * 2 + q) * 1024, 16, cwoff[q], 0);        \
       LNF4_BUF_LDS(ars_, (SM_) + X_BYTES + W_BYTES + wave_u * 256, 4, caoff, 0);                  \
     }                                                                                            \
   }
-#define LNF4_DXQ_ISSUE(kb_, SM_)                                                                 \
+#define LNF4_DXQ_ISSUE(SM_)                                                                      \
   {                                                                                              \
-    LNF4_DXQ_RSRC(kb_)                                                                           \
+    LNF4_DXQ_RSRC()                                                                              \
     LNF4_DXQ_ISSUE_PART(SM_, 0)                                                                  \
     LNF4_DXQ_ISSUE_PART(SM_, 1)                                                                  \
     LNF4_DXQ_ISSUE_PART(SM_, 2)                                                                  \
-  }
+  }                                                                                              \
+  LNF4_DXQ_ADVANCE()
 
   typedef int v2i_t __attribute__((ext_vector_type(2)));
   // transposed code reads of one stage: cw[s] = 8 codes (rows 32h+8s .. +7) of the column
@@ -1047,9 +1055,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))
 
   // prologue: blocks 0 .. NSTG-2 in flight; block 0 visible
-  LNF4_DXQ_ISSUE(kb_beg, sm0);
-  LNF4_DXQ_ISSUE(kb_beg + 1, sm1);
-  if (NSTG == 4) LNF4_DXQ_ISSUE(kb_beg + 2, sm2);
+  LNF4_DXQ_ISSUE(sm0);
+  LNF4_DXQ_ISSUE(sm1);
+  if (NSTG == 4) { LNF4_DXQ_ISSUE(sm2); }
   LNF4_WAIT_VM((NSTG - 2) * NLD);
   __syncthreads();
 
@@ -1073,7 +1081,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
 #define LNF4_DXQ_BLOCK(KB, SC, SN, SP)                                                         \
   {                                                                                            \
     u32x4 nw0, nw1;                                                                            \
-    LNF4_DXQ_RSRC((KB) + NSTG - 1)                                                             \
+    LNF4_DXQ_RSRC()                                                                            \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
       __builtin_amdgcn_sched_barrier(0);                                                       \
       if (s == 3) {                                                                            \
@@ -1129,6 +1137,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     asm volatile("" ::"v"(bc0), "v"(bc1)); /* decoded before the exit test */            \
     cw0 = nw0;                                                                                 \
     cw1 = nw1;                                                                                 \
+    LNF4_DXQ_ADVANCE();                                                                        \
   }
 
   // whole trips of two turns of the ring, one exit test per trip (blocks past the last
@@ -1155,7 +1164,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dxq(const DxArgs args) {
     }
   }
 #undef LNF4_DXQ_BLOCK
-#undef LNF4_DXQ_PROJ
+#undef LNF4_DXQ_ADVANCE
 #undef LNF4_DXQ_ISSUE
 #undef LNF4_DXQ_ISSUE_PART
 #undef LNF4_DXQ_RSRC
@@ -1406,36 +1415,45 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
     woff[q] = 2u * ((uint32_t)row * (uint32_t)N + (uint32_t)(n0 + 8 * cg));
   }
 
-#define LNF4_DXB_PROJ(kb_, P_)                                                   \
-  int pi_ = 0;                                                                   \
-  _Pragma("unroll") for (int q = 1; q < kMaxGroup; ++q) if (q < args.n_proj && (kb_) >= args.p[q].kb0) pi_ = q; \
-  pi_ = __builtin_amdgcn_readfirstlane(pi_);                                     \
-  const DxProj& P_ = args.p[pi_];
-  // Blocks past the last (the loop runs whole trips) belong to no projection's row range:
-  // their resources are empty and every load returns zeros.
-#define LNF4_DXB_RSRC(kb_)                                                                       \
-    LNF4_DXB_PROJ(kb_, Pi_)                                                                      \
-    const int k0_ = ((kb_) - Pi_.kb0) * BK, Kp_ = Pi_.out_f;                                     \
-    const int64_t lv_ = (kb_) < kb_end ? 1 : 0; /* blocks past the split: empty ranges */       \
-    const rsrc_t dyrs_ = make_rsrc(Pi_.dy + k0_, lv_ * ((int64_t)M * Kp_ - k0_) * 2);            \
-    const rsrc_t wrs_ = make_rsrc((const uint16_t*)Pi_.w + (size_t)k0_ * N, lv_ * (int64_t)(Kp_ - k0_) * N * 2);
+  // The block is the prefetch cursor's; its resources end at the projection's last row
+  // (rows past out_f load zeros).  Blocks past the split (the loop runs whole trips) get
+  // empty resources and every load returns zeros.  Branch-free: a branch would split the
+  // step.
+  DxCursor cur = dx_cursor_init<BK>(args, kb_beg);
+  uint32_t dyo[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) dyo[q] = dyr2[q] * (uint32_t)cur.Kp + dyc[q];
+#define LNF4_DXB_RSRC()                                                                          \
+    const int live_ = -(int)((cur.kb < kb_end) & (cur.k0 < cur.Kp));                             \
+    const rsrc_t dyrs_ = make_rsrc_n(                                                            \
+        cur.dy + cur.k0, clamp31(((uint64_t)(uint32_t)M * (uint32_t)cur.Kp - (uint32_t)cur.k0) * 2u) & live_); \
+    const rsrc_t wrs_ = make_rsrc_n((const uint16_t*)cur.w + (size_t)cur.k0 * N,                 \
+        clamp31((uint64_t)(uint32_t)((cur.Kp - cur.k0) & live_) * (2u * (uint32_t)N)));
+  // the cursor moves after the block's last step, outside its interleaved regions
+#define LNF4_DXB_ADVANCE()                                                                       \
+  {                                                                                              \
+    if (dx_cursor_next<BK>(cur, args)) {                                                         \
+      _Pragma("unroll") for (int q = 0; q < XQ; ++q) dyo[q] = dyr2[q] * (uint32_t)cur.Kp + dyc[q]; \
+    }                                                                                            \
+  }
   // load i of a block (0 .. NLD-1): dy loads first, then weight loads
 #define LNF4_DXB_LOAD1(SM_, i_)                                                                  \
   {                                                                                              \
     if ((i_) < XQ)                                                                               \
-      LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + (i_)) * 1024, 16, dyr2[(i_) < XQ ? (i_) : 0] * (uint32_t)Kp_ + dyc[(i_) < XQ ? (i_) : 0], 0); \
+      LNF4_BUF_LDS(dyrs_, (SM_) + (wave_u * XQ + (i_)) * 1024, 16, dyo[(i_) < XQ ? (i_) : 0], 0); \
     else                                                                                         \
       LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * WQ + (i_) - XQ) * 1024, 16, woff[(i_) < XQ ? 0 : (i_) - XQ], 0); \
   }
 #define LNF4_DXB_ISSUE_PART(SM_, part_)                                                          \
   { _Pragma("unroll") for (int i = (part_) * (NLD / 3); i < ((part_) + 1) * (NLD / 3); ++i) LNF4_DXB_LOAD1(SM_, i) }
-#define LNF4_DXB_ISSUE(kb_, SM_)                                                                 \
+#define LNF4_DXB_ISSUE(SM_)                                                                      \
   {                                                                                              \
-    LNF4_DXB_RSRC(kb_)                                                                           \
+    LNF4_DXB_RSRC()                                                                              \
     LNF4_DXB_ISSUE_PART(SM_, 0)                                                                  \
     LNF4_DXB_ISSUE_PART(SM_, 1)                                                                  \
     LNF4_DXB_ISSUE_PART(SM_, 2)                                                                  \
-  }
+  }                                                                                              \
+  LNF4_DXB_ADVANCE()
 
   typedef short v4s_t __attribute__((ext_vector_type(4)));
   // transposing reads: lane j = a + 4c of its 16-lane group (j = lane % 16) names row
@@ -1460,8 +1478,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
 #define LNF4_XS(SM_) ((const uint16_t*)(SM_))
 
   // prologue: blocks 0 and 1 in flight; block 0 visible
-  LNF4_DXB_ISSUE(kb_beg, sm0);
-  LNF4_DXB_ISSUE(kb_beg + 1, sm1);
+  LNF4_DXB_ISSUE(sm0);
+  LNF4_DXB_ISSUE(sm1);
   LNF4_WAIT_VM(NLD);
   __syncthreads();
 
@@ -1476,7 +1494,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
   // parts over steps 0..2, each after the step's LDS reads).
 #define LNF4_DXB_BLOCK(KB, SC, SN, SP)                                                         \
   {                                                                                            \
-    LNF4_DXB_RSRC((KB) + 2)                                                                    \
+    LNF4_DXB_RSRC()                                                                            \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                            \
       __builtin_amdgcn_sched_barrier(0);                                                       \
       if (s == 3) {                                                                            \
@@ -1511,6 +1529,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
       bc1 = bn1;                                                                               \
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                         \
+    LNF4_DXB_ADVANCE();                                                                        \
   }
 
   // whole trips of two turns of the 3-stage ring, one exit test per trip (blocks past the
@@ -1524,7 +1543,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_dx_bf16(const DxArgs args) {
     LNF4_DXB_BLOCK(kb + 5, sm2, sm0, sm1);
   }
 #undef LNF4_DXB_BLOCK
-#undef LNF4_DXB_PROJ
+#undef LNF4_DXB_ADVANCE
 #undef LNF4_DXB_RSRC
 #undef LNF4_DXB_LOAD1
 #undef LNF4_DXB_ISSUE_PART
