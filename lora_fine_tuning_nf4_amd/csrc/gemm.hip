@@ -778,6 +778,252 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16(const FwdArgs args) {
   }
 }
 
+// Forward, bf16 weights, 256-row tiles: 32-wide K-blocks in a 5-stage ring, as the
+// 256-row input gradient.  Both operands are K-contiguous, so the activation tile [256][32]
+// and the weight tile [256 columns][32] share one layout: 64-byte rows, 16-byte chunk c of
+// row r at slot c ^ ((r >> 2) & 3) (the 16 rows one read phase serves cover all 16 bank
+// groups).  Lane (n, h) of the MFMA supplies K = 16h + 8s .. +7 at step s.  The weights are
+// the MFMA's A operand, so the accumulators hold the tile transposed, as in the 128-row
+// kernel.  A block's activation rows are issued right after the barrier that frees its
+// stage, its weight rows one step later.  Blocks past the last read the last block's
+// activations against an empty weight range (zeros), so the loop runs whole turns of the
+// ring.
+__global__ __launch_bounds__(NTHR, 1) void k_fwd_bf16_deep(const FwdArgs args) {
+  constexpr int BM = 256, MI = 8, NM = 16;
+  constexpr int KS = 32;                    // K-block width
+  constexpr int X_BYTES = BM * KS * 2;      // activation tile [256][32] bf16
+  constexpr int W_BYTES = BN * KS * 2;      // weight tile [256][32] bf16
+  constexpr int STAGE = X_BYTES + W_BYTES;  // 32 KB
+  static_assert(BM * LNF4_EPI_RANK * 2 <= STAGE && BN * LNF4_EPI_RANK * 2 <= STAGE, "LoRA slabs fit a stage");
+  static_assert(BM * 128 <= STAGE, "a wave's output rows fit a stage");
+  static_assert(5 * STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm3[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sm4[STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  int tm, tn;
+  tile_coords(blockIdx.x, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+  tn += args.tn_base;
+  int pi = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxGroup; ++q)
+    if (q < args.n_proj && tn >= args.p[q].tile_n0) pi = q;
+  const FwdProj P = select_fwd(args, pi);
+
+  const int M = args.M, K = args.K, out_f = P.out_f;
+  const int m0 = tm * BM;
+  const int nloc0 = (tn - P.tile_n0) * BN;
+  const int nk = K / KS;
+  const int nc0 = 64 * wave + l32, nc1 = nc0 + 32;
+
+  floatx16 acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  if (P.u != nullptr && P.r > 0) {
+    const int r = P.r, RP = (r + 15) & ~15;
+    uint16_t* Uh = (uint16_t*)sm0;
+    uint16_t* Ul = (uint16_t*)sm1;
+    uint16_t* V = (uint16_t*)sm2;
+    for (int idx = tid; idx < BM * RP; idx += NTHR) {
+      const int mm = idx / RP, kk = idx - mm * RP, gm = m0 + mm;
+      const float uv = (gm < M && kk < r) ? P.scale * P.u[(size_t)gm * r + kk] : 0.0f;
+      split_bf16(uv, Uh[idx], Ul[idx]);
+    }
+    for (int idx = tid; idx < BN * RP; idx += NTHR) {
+      const int nn = idx / RP, kk = idx - nn * RP, n = nloc0 + nn;
+      V[idx] = (n < out_f && kk < r) ? P.B[(size_t)n * r + kk] : (uint16_t)0;
+    }
+    __syncthreads();
+    rank_update<MI, true>(acc, Uh, Ul, V, RP, l32, h, nc0, nc1);
+    __syncthreads();
+  }
+
+  // global -> LDS streams (lane L of a direct load writes slot L): load q of wave w fills
+  // rows (w*4+q)*16 .. +15 of its tile, lane L -> row + L/4, slot L%4 holding chunk
+  // (L%4) ^ ((row >> 2) & 3).  Activation rows >= M read row M-1 and weight columns >=
+  // out_f read column out_f-1 (their outputs are discarded).  The K-block advance is the
+  // wave-uniform offset.
+  constexpr int XQ = X_BYTES / 1024 / 4;
+  constexpr int WQ = W_BYTES / 1024 / 4;
+  constexpr int NLD = XQ + WQ;
+  const rsrc_t xrs = make_rsrc(args.x + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+  uint32_t xoff[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int row = (wave * XQ + q) * 16 + (lane >> 2);
+    const int lr = (m0 + row < M) ? row : (M - 1 - m0);
+    xoff[q] = 2u * ((uint32_t)lr * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) * 8));
+  }
+  const int64_t wbytes = (int64_t)out_f * K * 2;
+  uint32_t woff[WQ];
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int col = (wave * WQ + q) * 16 + (lane >> 2);
+    int n = nloc0 + col;
+    n = n < out_f ? n : out_f - 1;
+    woff[q] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)(((lane & 3) ^ ((col >> 2) & 3)) * 16);
+  }
+#define LNF4_FD_ISSUE_X(kb_, SM_)                                                                \
+  {                                                                                              \
+    const int kx_ = (kb_) < nk ? (kb_) : nk - 1;                                                 \
+    _Pragma("unroll") for (int q = 0; q < XQ; ++q)                                               \
+      LNF4_BUF_LDS(xrs, (SM_) + (wave_u * XQ + q) * 1024, 16, xoff[q], kx_ * (KS * 2));          \
+  }
+#define LNF4_FD_ISSUE_W(kb_, SM_)                                                                \
+  {                                                                                              \
+    const int kw_ = (kb_) < nk ? (kb_) : nk - 1;                                                 \
+    const rsrc_t wrs_ = make_rsrc(P.w, (kb_) < nk ? wbytes : 0);                                 \
+    _Pragma("unroll") for (int q = 0; q < WQ; ++q)                                               \
+      LNF4_BUF_LDS(wrs_, (SM_) + X_BYTES + (wave_u * WQ + q) * 1024, 16, woff[q], kw_ * (KS * 2)); \
+  }
+  // fragments of step s: weight column col (MFMA A) and activation row block i (MFMA B)
+#define LNF4_FD_WFRAG(SM_, s_, col_) \
+  (*(const bf16x8*)((SM_) + X_BYTES + (col_) * 64 + ((((2 * h + (s_)) ^ (((col_) >> 2) & 3))) << 4)))
+#define LNF4_FD_XFRAG(SM_, i_, s_)                                                               \
+  (*(const bf16x8*)((SM_) + (32 * (i_) + l32) * 64 +                                             \
+                    ((((2 * h + (s_)) ^ (((32 * (i_) + l32) >> 2) & 3))) << 4)))
+
+  // prologue: blocks 0 .. 3 and the activation rows of block 4 in flight; block 0 visible
+  LNF4_FD_ISSUE_X(0, sm0);
+  LNF4_FD_ISSUE_W(0, sm0);
+  LNF4_FD_ISSUE_X(1, sm1);
+  LNF4_FD_ISSUE_W(1, sm1);
+  LNF4_FD_ISSUE_X(2, sm2);
+  LNF4_FD_ISSUE_W(2, sm2);
+  LNF4_FD_ISSUE_X(3, sm3);
+  LNF4_FD_ISSUE_W(3, sm3);
+  LNF4_FD_ISSUE_X(4, sm4);
+  LNF4_WAIT_VM(3 * NLD + XQ);
+  __syncthreads();
+
+  bf16x8 ac[MI], an_[MI];
+  bf16x8 bc0, bc1, bn0, bn1;
+  bc0 = LNF4_FD_WFRAG(sm0, 0, nc0);
+  bc1 = LNF4_FD_WFRAG(sm0, 0, nc1);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) ac[i] = LNF4_FD_XFRAG(sm0, i, 0);
+
+  // One 32-wide block KB on stage SC; SN holds block KB+1, SP (the stage of KB-1) receives
+  // the weight rows of block KB+4 at step 0.  Step 1: every wave's loads of block KB+1 have
+  // landed (3 NLD loads issued after them may be in flight), the barrier makes KB+1 visible
+  // and SC free, and the activation rows of block KB+5 go into SC.
+#define LNF4_FD_BLOCK(KB, SC, SN, SP)                                                          \
+  {                                                                                            \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      if (s == 1) {                                                                            \
+        LNF4_WAIT_VM_LGKM0(3 * NLD);                                                           \
+        __builtin_amdgcn_s_barrier();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        bn0 = LNF4_FD_WFRAG(SN, 0, nc0);                                                       \
+        bn1 = LNF4_FD_WFRAG(SN, 0, nc1);                                                       \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] = LNF4_FD_XFRAG(SN, i, 0);       \
+        LNF4_FD_ISSUE_X((KB) + 5, SC);                                                         \
+      } else {                                                                                 \
+        bn0 = LNF4_FD_WFRAG(SC, 1, nc0);                                                       \
+        bn1 = LNF4_FD_WFRAG(SC, 1, nc1);                                                       \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) an_[i] = LNF4_FD_XFRAG(SC, i, 1);       \
+        LNF4_FD_ISSUE_W((KB) + 4, SP);                                                         \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
+        acc[i][0] = mfma32(bc0, ac[i], acc[i][0]);                                             \
+        acc[i][1] = mfma32(bc1, ac[i], acc[i][1]);                                             \
+      }                                                                                        \
+      _Pragma("unroll") for (int g = 0; g < NM; ++g) {                                         \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                     \
+      }                                                                                        \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) ac[i] = an_[i];                           \
+      bc0 = bn0;                                                                               \
+      bc1 = bn1;                                                                               \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+  }
+
+  for (int kb = 0; kb < nk; kb += 5) {
+    LNF4_FD_BLOCK(kb + 0, sm0, sm1, sm4);
+    LNF4_FD_BLOCK(kb + 1, sm1, sm2, sm0);
+    LNF4_FD_BLOCK(kb + 2, sm2, sm3, sm1);
+    LNF4_FD_BLOCK(kb + 3, sm3, sm4, sm2);
+    LNF4_FD_BLOCK(kb + 4, sm4, sm0, sm3);
+  }
+#undef LNF4_FD_BLOCK
+#undef LNF4_FD_ISSUE_X
+#undef LNF4_FD_ISSUE_W
+#undef LNF4_FD_WFRAG
+#undef LNF4_FD_XFRAG
+
+  // ---- store bf16 (the 128-row kernel's scheme): lane (l32, h) has token 32i + l32 and,
+  // for q = 4g..4g+3, the outputs 64 wave + 32j + 8g + 4h + 0..3.  With out_f % 8 == 0 and
+  // y 16-byte aligned each wave stages its 256 rows in its own ring stage and stores whole
+  // 128-byte lines; else 8-byte groups or single elements.
+  if ((out_f & 7) == 0 && (((uintptr_t)P.y) & 15) == 0) {
+    LNF4_WAIT_VM_LGKM0(0);  // the ring's last (past-the-end) loads have landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* const rg = wave == 0 ? sm0 : (wave == 1 ? sm1 : (wave == 2 ? sm2 : sm3));
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = 32 * i + l32;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int pc = (4 * j + g) ^ ((row >> 1) & 7);
+          *(uint2*)(rg + row * 128 + pc * 16 + 8 * h) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                         pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_sched_barrier(0);
+    const int c = lane & 7;
+    const int n = nloc0 + 64 * wave + 8 * c;
+#pragma unroll
+    for (int k = 0; k < BM / 8; ++k) {
+      const int row = 8 * k + (lane >> 3);
+      const u32x4 v = *(const u32x4*)(rg + row * 128 + ((c ^ ((row >> 1) & 7)) * 16));
+      const int gm = m0 + row;
+      if (gm < M && n < out_f) *(u32x4*)(P.y + (size_t)gm * out_f + n) = v;
+    }
+    return;
+  }
+  const bool vec4 = (out_f & 3) == 0 && (((uintptr_t)P.y) & 7) == 0;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int gm = m0 + 32 * i + l32;
+    if (gm >= M) continue;
+    uint16_t* yr = P.y + (size_t)gm * out_f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nloc0 + 64 * wave + 32 * j + 8 * g + 4 * h;
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if (vec4 && n < out_f) {
+          *(uint2*)(yr + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < out_f) yr[n + e] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+        }
+      }
+  }
+}
+
 // =====================================================================================
 // Prefetch cursor over the K space of an input-gradient launch
 // =====================================================================================
@@ -1829,13 +2075,21 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   a.tn_base = 0;
   a.split_block = 0x7fffffff;
   a.tail_m = a.tail_n = a.xcd_f = a.xcd_h = 0;
+  const int cus = n_cus();
   if (fmt != 0) {
-    // bf16 weight tiles are 4x the NF4 bytes: their 3-stage ring only fits LDS with 128 rows
+    // bf16 weights: 256-row tiles with 32-wide K-blocks (a 5-stage ring) where they make
+    // at least two rounds over the compute units (the lm_head: 4008 tiles at T = 2048),
+    // else 128-row tiles in a 3-stage ring of 64-wide blocks, which keep more units busy
+    const int t256 = ((a.M + 255) / 256) * a.n_tiles_n;
+    if (t256 >= 2 * cus) {
+      a.n_tiles_m = (a.M + 255) / 256;
+      hipLaunchKernelGGL(k_fwd_bf16_deep, dim3(t256), dim3(NTHR), 0, s, a);
+      return hipGetLastError();
+    }
     a.n_tiles_m = (a.M + 127) / 128;
     hipLaunchKernelGGL((k_fwd_bf16<128>), dim3(a.n_tiles_m * a.n_tiles_n), dim3(NTHR), 0, s, a);
     return hipGetLastError();
   }
-  const int cus = n_cus();
   const int tn_all = a.n_tiles_n;
   const int tm256 = (a.M + 255) / 256;
   const int t256 = tm256 * tn_all;

@@ -31,6 +31,9 @@ CASES = [
     # the dx GEMM's 5-stage ring of 32-row K-blocks; the first projection's last 32-row block
     # holds 8 rows, the second's is wholly past out_f
     (300, 16320, [(4136, 8), (4112, 4)], 1),
+    # bf16, 2 x 258 tiles of 256 x 256: the forward's 5-stage ring of 32-wide K-blocks (the
+    # second projection's last column tile ragged)
+    (300, 320, [(32808, 8), (32800, 4)], 1),
 ]
 
 

@@ -186,12 +186,13 @@ def test_backward_split_k(fmt, out_f):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("out_f", [333, 1100, 1096])
+@pytest.mark.parametrize("out_f", [333, 1100, 1096, 65283, 65284])
 def test_forward_store_paths_and_unaligned_y(out_f, fmt):
     # The forward (NF4 and bf16 weights) writes y in whole lines through LDS (out_f % 8 == 0,
     # y 16-byte aligned), in 8-byte groups (out_f % 4 == 0, y 8-byte aligned) or element by
     # element; y need only be 2-byte aligned.  Every path gives the same bits; checked
-    # against the oracle once.
+    # against the oracle once.  out_f = 65283 / 65284 at T = 300: 2 x 256 tiles of 256 x 256,
+    # the bf16 forward's 5-stage ring.
     T, in_f, r = 300, 256, 8
     c = make_case(29, T, out_f, in_f, r, 16.0, fmt, tag=f"store-{out_f}-{fmt}")
     d = DevCase(c)
