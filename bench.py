@@ -103,6 +103,32 @@ def head_summary(wl, stack, head_ms):
     return out
 
 
+def library_bf16_same_shape(M: int, N: int, K: int, reps: int = 20):
+    """Context for the dominant kernel's fraction of peak: torch's bf16 GEMM (hipBLASLt) on
+    plain bf16 weights of the same shape, y = x W^T, timed with events on this GPU.  It does
+    no NF4 decode and no LoRA term; it is reported beside the roofline, not used by the path."""
+    import torch
+    import torch.nn.functional as F
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    for _ in range(3):
+        F.linear(x, w)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        F.linear(x, w)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * M * N * K / (ms / 1000.0) / 1e12
+    del x, w
+    return {"what": "torch.nn.functional.linear in bf16 (hipBLASLt), plain bf16 weights, no decode, no LoRA",
+            "M": M, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tflops, 2),
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
@@ -786,6 +812,11 @@ def main():
             "compute_blocked_share_of_step": round(blocked_ms / ms_per_step, 4),
         },
     }
+
+    # the library's bf16 GEMM at the dominant launch's shape, as context for its fraction of peak
+    result["roofline"]["library_bf16_same_shape"] = library_bf16_same_shape(
+        stack.T, sum(wl.shapes[p][0] for p in GROUPS[2]), wl.shapes[GROUPS[2][0]][1])
+    log(f"[bench] library bf16 GEMM at the dominant shape: {result['roofline']['library_bf16_same_shape']}")
 
     if not args.no_resident:
         for _ in range(max(1, args.warmup)):
