@@ -426,9 +426,12 @@ def stream_variants(wl, args, L):
                 stack.step()
             torch.cuda.synchronize()
             ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+            h2d = (stack.bytes_copied() - b0) // args.steps
+            gbps = _copy_only_gbps(stack)
             out[name] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(stack.T / (ms / 1000.0), 2),
-                         "h2d_bytes_per_step": (stack.bytes_copied() - b0) // args.steps,
-                         "compute_blocked_on_copies_ms": round(_blocked_on_copies(stack), 3)}
+                         "h2d_bytes_per_step": h2d,
+                         "compute_blocked_on_copies_ms": round(_blocked_on_copies(stack), 3),
+                         "copy_only_GBps": round(gbps, 2), "link_floor_ms_per_step": round(h2d / (gbps * 1e6), 3)}
         finally:
             stack.close()
             del stack
@@ -542,6 +545,23 @@ def _gemm_rate(stack, wl, resident: bool = False):
             "gemm_frac_of_peak": round(flops / (ms / 1000.0) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def _copy_only_gbps(stack, reps: int = 4) -> float:
+    """The link's copy-only rate right now: the stack's first shard copied into its first
+    device buffer `reps` times on the copy stream, nothing else running.  Taken beside each
+    streamed measurement, so a slow stretch of the host link shows in the record."""
+    import torch
+    hb, db, cs = stack.host[0], stack.bufs[0], stack.copy
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        e0.record(cs)
+        for _ in range(reps):
+            db[:hb.numel()].copy_(hb, non_blocking=True)
+        e1.record(cs)
+    torch.cuda.synchronize()
+    return reps * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9
+
+
 def _blocked_on_copies(stack, steps: int = 1):
     """Compute-stream time per step blocked on copies (layer copies and slot loads): HIP
     events on the compute stream right before and after every call that enqueues such a
@@ -579,10 +599,13 @@ def other_configs(args):
                 b0 = stack.bytes_copied()
                 ms = _timed_steps(stack, steps, warm)
                 h2d = (stack.bytes_copied() - b0) // (steps + warm)
+                gbps = _copy_only_gbps(stack)
                 rec[f"streamed_nbuf{nb}"] = {"ms_per_step": round(ms, 3),
                                              "tokens_per_s": round(stack.T / (ms / 1000.0), 1),
                                              "h2d_bytes_per_step": h2d,
-                                             "compute_blocked_on_copies_ms": round(_blocked_on_copies(stack), 3)}
+                                             "compute_blocked_on_copies_ms": round(_blocked_on_copies(stack), 3),
+                                             "copy_only_GBps": round(gbps, 2),
+                                             "link_floor_ms_per_step": round(h2d / (gbps * 1e6), 3)}
             ms = _timed_steps(stack, steps, warm, resident=True)
             rec["resident"] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(stack.T / (ms / 1000.0), 1),
                                **_gemm_rate(stack, wl, resident=True)}
@@ -625,6 +648,8 @@ def decoder_model_run(args):
             ms = (time.perf_counter() - t0) * 1000.0 / args.steps
             out[f"{mode}_ms_per_step"] = round(ms, 3)
             out[f"{mode}_tokens_per_s"] = round(m.T / (ms / 1000.0), 2)
+            if not res:
+                out["streamed_copy_only_GBps"] = round(_copy_only_gbps(m), 2)
         # attention alone, on the model's own buffers (the last layer's q, k, v, o)
         T, nh, nkv, D, S = m.T, m.nh, m.nkv, m.D, m.S
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
