@@ -170,9 +170,10 @@ struct CodeSet {
 // ring.  Each 16-wide K step is split into two halves of MFMAs: the first half issues the
 // next step's code-table and activation reads (and a third of the loads for the block
 // three ahead), the second half the next fragments' fp32 products and bf16 packs.
-// NW = 4: each wave owns 64 columns x all BM rows (one wave per SIMD).  NW = 8: two waves
-// per column group, each on half of the rows (two waves per SIMD: more latency hiding for
-// grids of less than one tile per compute unit; each code is decoded by both waves).
+// NW = 4: each wave owns 64 columns x all BM rows (one wave per SIMD).  The tile also
+// compiles for NW = 8 (two waves per column group, each on half of the rows, two waves
+// per SIMD, each code decoded by both); the launcher no longer uses it, since it measured
+// slower than NW = 4 even for grids of under one tile per compute unit.
 // LDS bytes of one ring stage: an activation tile, or (LoRA staging before the K loop,
 // spread over three stages: hi, lo, adapter rows) a 64-rank slab
 constexpr int fwd_stage_bytes(int BM) {
@@ -2107,9 +2108,10 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
     return hipGetLastError();
   }
   if (t256 <= cus) {
-    // one partial wave of tiles: two waves per SIMD hide more latency per tile
+    // one partial round of tiles, one wave per SIMD (the two-wave form, NW = 8, decodes
+    // every code twice: 8B q|k|v, 192 tiles, 0.144 -> 0.134 ms with NW = 4, same bits)
     a.n_tiles_m = tm256;
-    hipLaunchKernelGGL((k_fwd_nf4<256, 8>), dim3(t256), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(t256), dim3(NTHR), 0, s, a);
     return hipGetLastError();
   }
   // Several rounds of 256-row tiles whose last round leaves many compute units idle: the
