@@ -27,10 +27,11 @@ CASES = [
     (130, 256, [(256, 8), (72, 5), (512, 16)], 1),   # bf16 weights
     (300, 320, [(264, 64)], 0),                       # one projection at the rank limit
     (45, 64, [(8, 7), (16, 1)], 0),                   # out_f = 8 (one K group of v = dy B), r = 1
-    # bf16, 2 x 64 tiles of 256 x 256 (the last column tile ragged) in 2 splits of 65 K-blocks:
-    # the dx GEMM's 5-stage ring of 32-row K-blocks; the first projection's last 32-row block
-    # holds 8 rows, the second's is wholly past out_f
-    (300, 16320, [(4136, 8), (4112, 4)], 1),
+    # bf16, 2 x 64 tiles of 256 x 256 (the last column tile ragged) in 2 splits of 66 of the
+    # 131 K-blocks: the dx GEMM's 5-stage ring of 32-row K-blocks, each split crossing from
+    # one projection into the next; the first projection's last 32-row block holds 8 rows,
+    # the other two's are wholly past out_f
+    (300, 16320, [(4136, 8), (2064, 4), (2072, 4)], 1),
     # bf16, 2 x 258 tiles of 256 x 256: the forward's 5-stage ring of 32-wide K-blocks (the
     # second projection's last column tile ragged)
     (300, 320, [(32808, 8), (32800, 4)], 1),
