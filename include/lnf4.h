@@ -60,10 +60,14 @@ typedef struct ihipStream_t* hipStream_t; /* same declaration as the HIP runtime
 #define LNF4_MAX_RANK 64
 #define LNF4_MAX_GROUP 8
 
-/* Message of the last failing call on this thread ("" if none). */
+/* Message of the last failing call on this thread ("" if none).  Every call checks its
+ * arguments and fails loudly rather than running a silently different computation, as
+ * the Soup deep dive describes the settings schema rejecting what it cannot apply
+ * ("Structure: a CLI whose settings schema is the product"). */
 const char* lnf4_last_error(void);
 
-/* Library version string. */
+/* Library version string (measurements are tied to a release, as the Soup deep dive ties
+ * its numbers to versions: "What the published numbers say and don't say"). */
 const char* lnf4_version(void);
 
 /*
@@ -92,7 +96,8 @@ int nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n_elems, int3
                 uint16_t* out_bf16, hipStream_t stream);
 
 /*
- * Quantize fp32 weights to NF4 (set-up, off the hot path: shards are built once).
+ * Quantize fp32 weights to NF4 (set-up, off the hot path: shards are built once; the
+ * frozen base is stored 4-bit NF4, Soup 4 GB article, "Configuration and training").
  * Blocks of `blocksize` consecutive elements; absmax = max|w| (fp32); code = nearest
  * level to w/absmax (fp32 division and comparison, ties to the lower index); an
  * all-zero block gets code 7.  Packing as in nf4_dequant.
@@ -208,16 +213,21 @@ typedef struct lnf4_proj {
   float* dB;           /* bwd: device fp32 [out, r] or NULL */
 } lnf4_proj;
 
-/* Grouped forward: n (1..8) projections with the same in_f share x. */
+/* Grouped forward: n (1..8) projections with the same in_f share x (the adapted projections
+ * of the pages' configs, q and v, read the same attention input: 20B RLHF article,
+ * "Low-rank adaptation via PEFT"). */
 int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
                    hipStream_t stream);
 
-/* Workspace bytes for lora_group_bwd with these projs and T: which gradients are asked
+/* Workspace bytes for lora_group_bwd (the grouped backward below) with these projs and T:
+ * which gradients are asked
  * for (dA, dB non-NULL) and whether u is saved decide the buffers, so query with the
  * same descriptors as the call.  Host-only. */
 size_t lora_group_bwd_workspace(const lnf4_proj* projs, int32_t n, int64_t T);
 
-/* Grouped backward: dx [T, in] = sum over the group (NULL to skip), per-projection dA/dB.
+/* Grouped backward: dx [T, in] = sum over the group (NULL to skip), per-projection dA/dB
+ * (the frozen weights are read again in the backward because dx = W^T dy: Soup deep dive,
+ * "Core feature: how layer streaming works").
  * Errors: as lora_linear_bwd (every projection's out_f a multiple of 8). */
 int lora_group_bwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, uint16_t* dx,
                    int32_t accumulate, void* workspace, size_t ws_bytes, hipStream_t stream);
@@ -284,7 +294,8 @@ int lnf4_cross_entropy(const uint16_t* logits, int64_t T, int64_t vocab, const i
                        hipStream_t stream);
 
 /*
- * Per-sequence sums of token values (log-probs): sums[i] = sum_{j < seq_len} x[i*seq_len + j],
+ * Per-sequence sums of token values (log-probs, the sequence scores of the preference
+ * losses: Soup 4 GB article, "Preference optimization"): sums[i] = sum_{j < seq_len} x[i*seq_len + j],
  * fp32 in a fixed order.  x device fp32 [n_seq * seq_len]; sums device fp32 [n_seq].
  * Errors: EINVAL, EALIGN, EHIP.
  */
@@ -484,7 +495,9 @@ int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute);
 /*
  * The same copy issued in n_parts pieces (part = 0, 1, ..., n_parts-1, in order, on
  * successive calls), so a large slot shard can trickle over the copy stream between
- * layer copies instead of holding it for one long transfer.  Part p copies bytes
+ * layer copies instead of holding it for one long transfer (the prefetch stream the Soup
+ * deep dive describes carries layers and the slot alike, "Core feature: how layer
+ * streaming works").  Part p copies bytes
  * [p*c, min((p+1)*c, size)) with c = ceil(size/n_parts) rounded up to 4 KiB.  Part 0
  * waits for the work enqueued so far on `compute` (the slot's previous user); the load
  * counts as issued after the last part, and only then may stream_slot_wait be called.
@@ -494,11 +507,13 @@ int stream_slot_load(lnf4_stream* st, int32_t shard, hipStream_t compute);
  */
 int stream_slot_load_part(lnf4_stream* st, int32_t shard, int32_t part, int32_t n_parts, hipStream_t compute);
 
-/* Make `compute` wait for the last complete slot load; *slot_ptr_out = the slot.
+/* Make `compute` wait for the last complete slot load; *slot_ptr_out = the slot (the
+ * shared embed_tokens / lm_head slot: Soup deep dive, "Core feature: how layer streaming works").
  * Errors: EINVAL (no slot), ESTATE (no complete load issued, destroyed), EHIP. */
 int stream_slot_wait(lnf4_stream* st, hipStream_t compute, void** slot_ptr_out);
 
-/* Rewind a finished (or unfinished) pass so the same schedule runs again (next step).
+/* Rewind a finished (or unfinished) pass so the same schedule runs again (next step: every
+ * step streams the layers anew, Soup deep dive, "Core feature: how layer streaming works").
  * The first copies of the new pass wait for the release of the old pass's buffers.  On a
  * disk-tier context whose pass did not issue all its copies (a step abandoned, e.g. after
  * a failed call), the reader thread is stopped, the copies out of the staging buffers
@@ -514,7 +529,9 @@ int stream_reset(lnf4_stream* st, hipStream_t compute);
  * Errors: ESTATE (NULL or destroyed context), EINVAL (n NULL, cap < 0, ev NULL with cap > 0). */
 int stream_log(const lnf4_stream* st, lnf4_stream_event* ev, int32_t cap, int32_t* n);
 
-/* Bytes copied host-to-device by this context since creation (layers + slot).
+/* Bytes copied host-to-device by this context since creation (layers + slot): the transfer
+ * whose cost the Soup deep dive measures by removing it ("Core feature: how layer streaming
+ * works").
  * Errors: ESTATE (NULL or destroyed), EINVAL (bytes NULL). */
 int stream_bytes_copied(const lnf4_stream* st, int64_t* bytes);
 
@@ -551,8 +568,9 @@ int stream_create_disk(const char* path, const int64_t* file_offsets, int32_t dr
                        const int32_t* schedule, int32_t sched_len, hipStream_t copy_stream, void* slot_buf,
                        size_t slot_bytes, lnf4_stream** out);
 
-/* Disk tier only: bytes read from the file so far and the reader's time inside the reads
- * (seconds), for the disk's achieved rate.  Errors: EINVAL (no disk tier), ESTATE. */
+/* Disk tier only (stream_source: disk, Soup deep dive, "Streaming config keys"): bytes read
+ * from the file so far and the reader's time inside the reads (seconds), for the disk's
+ * achieved rate.  Errors: EINVAL (no disk tier), ESTATE. */
 int stream_disk_stats(const lnf4_stream* st, int64_t* bytes_read, double* read_seconds);
 
 /*
