@@ -431,6 +431,27 @@ typedef struct lnf4_stream_event {
 } lnf4_stream_event;
 
 /*
+ * The stream a streamed step's kernels run on, with a hardware queue of its own, so the
+ * layer copies overlap the compute (the 4 GB-laptop article, "Layer streaming: technical
+ * implementation and memory efficiency": the next layer loads while the current one
+ * computes; the Soup deep dive, "Core feature: how layer streaming works").  The HIP
+ * runtime maps ordinary streams onto a few hardware queues shared in turn (4 by default);
+ * a copy stream that lands on the compute stream's queue loses all overlap, since the
+ * event wait or event record of one stream then holds back every later packet of the
+ * other in that in-order queue.  This stream is created with a compute-unit mask of every
+ * CU of the device, which gives it a queue no other stream uses; its kernels run on all
+ * CUs at default priority.  It follows the default-flag stream rules: it orders itself
+ * with the null stream (work on either waits for earlier work on the other) and not with
+ * other streams.
+ *   device  HIP device index
+ *   out     receives the stream: created on the device's first call, the same handle on
+ *           every later call, owned by the library and kept until the process ends (never
+ *           destroy it)
+ * Errors: EINVAL (device out of range, NULL out), EHIP.
+ */
+int stream_compute_stream(int32_t device, hipStream_t* out);
+
+/*
  * Create a layer stream over one pass of `schedule` (shard indices, e.g. layers
  * 0..L-1 then L-1..0 for an SFT step: forward, then recompute + backward).  The frozen
  * layers stay in page-locked host RAM and a separate stream copies them into a few

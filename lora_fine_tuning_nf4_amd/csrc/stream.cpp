@@ -444,7 +444,47 @@ static int create_impl(const char* who, const void* const* host_shards, bool hos
   return LNF4_OK;
 }
 
+// The compute stream of each device: created on first use with a compute-unit mask of every
+// CU, which gives it a hardware queue of its own (ordinary streams share a few queues in
+// turn, and a copy stream on the compute stream's queue would serialise with it).  Never
+// destroyed, so a handle once given out stays valid for the process.
+static std::mutex g_compute_mu;
+static std::vector<hipStream_t> g_compute;
+
 extern "C" {
+
+int stream_compute_stream(int32_t device, hipStream_t* out) {
+  const char* who = "stream_compute_stream";
+  if (!out) return fail(LNF4_EINVAL, "%s: out is NULL", who);
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_fail(e, "stream_compute_stream: hipGetDeviceCount");
+  if (device < 0 || device >= n) return fail(LNF4_EINVAL, "%s: device %d outside 0..%d", who, (int)device, n - 1);
+  std::lock_guard<std::mutex> lk(g_compute_mu);
+  if ((int)g_compute.size() < n) g_compute.resize(n, nullptr);
+  if (!g_compute[device]) {
+    int cus = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device)) != hipSuccess)
+      return hip_fail(e, "stream_compute_stream: hipDeviceGetAttribute(multiprocessor count)");
+    if (cus <= 0) return fail(LNF4_EHIP, "%s: device %d reports %d compute units", who, (int)device, cus);
+    std::vector<uint32_t> mask((cus + 31) / 32, 0xffffffffu);
+    if (cus % 32) mask.back() = (1u << (cus % 32)) - 1u;
+    int prev = 0;
+    if ((e = hipGetDevice(&prev)) != hipSuccess) return hip_fail(e, "stream_compute_stream: hipGetDevice");
+    if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "stream_compute_stream: hipSetDevice");
+    hipStream_t s = nullptr;
+    e = hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data());
+    const hipError_t e_restore = hipSetDevice(prev);
+    if (e != hipSuccess) return hip_fail(e, "stream_compute_stream: hipExtStreamCreateWithCUMask");
+    if (e_restore != hipSuccess) {
+      (void)hipStreamDestroy(s);
+      return hip_fail(e_restore, "stream_compute_stream: hipSetDevice(restore)");
+    }
+    g_compute[device] = s;
+  }
+  *out = g_compute[device];
+  return LNF4_OK;
+}
 
 int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards, void* const* dev_bufs,
                   size_t buf_bytes, int32_t n_bufs, const int32_t* schedule, int32_t sched_len, int32_t mode,

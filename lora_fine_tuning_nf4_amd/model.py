@@ -20,7 +20,7 @@ import torch
 
 import synthgen
 from . import lnf4
-from .stack import PROJ_ORDER, dpo_schedule, sft_schedule
+from .stack import PROJ_ORDER, dpo_schedule, on_stream, sft_schedule
 
 QKV, O, GU, DOWN = ("q", "k", "v"), ("o",), ("gate", "up"), ("down",)
 
@@ -47,7 +47,7 @@ class StreamedDecoder:
         self.dpo = ("ref" in wl.passes) if dpo is None else dpo
         self.seed, self.n_bufs = seed, n_bufs
         dev = self.dev = torch.device(device)
-        self.compute = torch.cuda.current_stream(dev)
+        self.compute = lnf4.stream_compute_stream(dev)   # a hardware queue of its own
         self.copy = torch.cuda.Stream(dev)
         bf16, f32 = torch.bfloat16, torch.float32
         if T % self.S:
@@ -289,6 +289,12 @@ class StreamedDecoder:
 
     # ------------------------------------------------------------------ one step
     def step(self, resident: bool = False):
+        """One training step of the decoder (asynchronous on the compute stream, ordered after
+        the caller's stream's earlier work; the caller's later work waits for it)."""
+        with on_stream(self.compute):
+            self._step(resident)
+
+    def _step(self, resident: bool):
         L, cs = self.L, self.compute
         st = self.enable_resident() if resident else self.st
         if not resident:

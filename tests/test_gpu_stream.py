@@ -226,6 +226,74 @@ def test_resident_graph_replays_equal_eager(dpo):
         stack.close()
 
 
+def test_resident_graph_on_a_fresh_stack():
+    """The graph captured on a stack that has run no resident step: the eager steps ahead
+    of the capture copy the layers in and see every copy complete, so the capture issues
+    no stream work, and the replay gives the eager resident step's outputs."""
+    stack = StreamedStack(_small_workload("nf4"), n_bufs=2, seed=3)
+    try:
+        stack.step_graph()
+        got = _snapshot(stack)
+        stack.step(resident=True)
+        _same(_snapshot(stack), got)
+    finally:
+        stack.close()
+
+
+def test_compute_stream_one_per_device():
+    """The library hands out one compute stream per device (the same handle on every call)
+    and rejects a device that does not exist; the stacks run their kernels on it."""
+    import ctypes
+    h1, h2 = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lnf4.lib().stream_compute_stream(0, ctypes.byref(h1)) == 0
+    assert lnf4.lib().stream_compute_stream(0, ctypes.byref(h2)) == 0
+    assert h1.value and h1.value == h2.value
+    assert lnf4.stream_compute_stream(0).cuda_stream == h1.value
+    for bad in (-1, torch.cuda.device_count()):
+        with pytest.raises(lnf4.LNF4Error, match="EINVAL|device"):
+            lnf4.stream_compute_stream(bad)
+    stack = StreamedStack(_small_workload("nf4"), n_bufs=2, seed=3)
+    try:
+        assert stack.compute.cuda_stream == h1.value
+        assert stack.copy.cuda_stream != h1.value
+    finally:
+        stack.close()
+
+
+@pytest.mark.parametrize("caller", ["null", "side"])
+def test_step_is_ordered_with_the_callers_stream(caller):
+    """A step called with the null stream or a side stream current runs after that stream's
+    earlier work (a few milliseconds of products, then fills of every output) and that
+    stream's later work (clones of the outputs) runs after the step: the clones and the
+    outputs equal a plain step's, bitwise.  The null stream is ordered with the compute
+    stream by the default-flag stream rules, a side stream by explicit event waits."""
+    stack = StreamedStack(_small_workload("nf4"), n_bufs=2, seed=3)
+    try:
+        stack.step()
+        ref = _snapshot(stack)
+        outs = list(stack.y.values()) + list(stack.dx) + [stack.dh, stack.logp]
+        grads = [t for ls in stack.layers for p in ls.dA for t in (ls.dA[p], ls.dB[p])]
+        side = torch.cuda.Stream() if caller == "side" else torch.cuda.default_stream()
+        assert (side.cuda_stream == 0) == (caller == "null")
+        m = torch.randn(4096, 4096, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            for _ in range(30):
+                m = (m @ m) * 1e-3
+            for t in outs:
+                t.fill_(7)
+            for t in grads:
+                t.fill_(-1.0)
+            stack.step()
+            clones = [t.clone() for t in outs + grads]
+        torch.cuda.synchronize()
+        _same(ref, _snapshot(stack))
+        for t, c in zip(outs + grads, clones):
+            assert torch.equal(t, c)
+    finally:
+        stack.close()
+
+
 @pytest.mark.parametrize("fmt,dpo,reuse,efh", [("nf4", False, False, False), ("bf16", False, False, False),
                                                ("nf4", True, False, False), ("nf4", False, True, False),
                                                ("nf4", True, True, False), ("nf4", False, False, True),
