@@ -562,6 +562,54 @@ def _copy_only_gbps(stack, reps: int = 4) -> float:
     return reps * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9
 
 
+def _copy_rate_under_load(stack, reps: int = 8):
+    """The link's rate while the compute stream is busy: the stack's first shard copied into
+    its first device buffer `reps` times on the copy stream while the compute stream runs,
+    back to back, (a) nothing, (b) the gate|up forward GEMM of the layer held in the second
+    buffer, (c) a bf16 8192^3 library GEMM (matrix cores, little HBM traffic), (d) a 1 GiB
+    device-to-device copy (HBM traffic, no matrix work).  The load is enqueued first and
+    outlasts the copies."""
+    import torch
+    hb, db, cs, comp = stack.host[0], stack.bufs[0], stack.copy, stack.compute
+    projs = stack._projs(0, 2, stack.bufs[1].data_ptr(), adapters=False)
+    x = stack.layers[0].x[2]
+    a = torch.randn(8192, 8192, device=stack.dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=stack.dev).to(torch.bfloat16)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=stack.dev)
+    dst = torch.empty_like(src)
+    copy_ms = reps * hb.numel() / 50e9 * 1000.0
+
+    def load(kind):
+        if kind == "nf4_gate_up_fwd":
+            for _ in range(int(copy_ms / 0.4) + 10):
+                lnf4.lora_group_fwd(projs, x, stack.T, 0, comp)
+        elif kind == "bf16_gemm_8192":
+            with torch.cuda.stream(comp):
+                for _ in range(int(copy_ms / 0.6) + 10):
+                    torch.matmul(a, b)
+        elif kind == "hbm_copy_1GiB":
+            with torch.cuda.stream(comp):
+                for _ in range(int(copy_ms / 0.25) + 10):
+                    dst.copy_(src)
+
+    from lora_fine_tuning_nf4_amd import lnf4
+    out = {}
+    for kind in ("none", "nf4_gate_up_fwd", "bf16_gemm_8192", "hbm_copy_1GiB", "none"):
+        torch.cuda.synchronize()
+        load(kind)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(cs):
+            e0.record(cs)
+            for _ in range(reps):
+                db[:hb.numel()].copy_(hb, non_blocking=True)
+            e1.record(cs)
+        torch.cuda.synchronize()
+        key = kind if kind not in out else kind + "_again"
+        out[key] = round(reps * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
+    del a, b, src, dst
+    return out
+
+
 def _blocked_on_copies(stack, steps: int = 1):
     """Compute-stream time per step blocked on copies (layer copies and slot loads): HIP
     events on the compute stream right before and after every call that enqueues such a
@@ -573,6 +621,69 @@ def _blocked_on_copies(stack, steps: int = 1):
     torch.cuda.synchronize()
     we, stack.wait_events = stack.wait_events, None
     return sum(a.elapsed_time(b) for a, b in we) / steps
+
+
+def _copy_timeline(stack):
+    """Where the link's time goes in one streamed step.  Every stream call that may issue
+    copies is bracketed by an event on the compute stream just before it (where the call
+    records the release that its copies wait for) and one on the copy stream just after it
+    (reached when its copies are done).  A call's copies start at the later of the copy
+    stream's previous mark and that release (the first call of a pass and the later parts
+    of a slot load wait for nothing recorded at the call), so the link is idle before them
+    for the difference, and busy for the rest of the interval."""
+    import torch
+    torch.cuda.synchronize()
+    ref_c = torch.cuda.Event(enable_timing=True)
+    ref_x = torch.cuda.Event(enable_timing=True)
+    ref_c.record(stack.compute)
+    ref_x.record(stack.copy)
+    stack.copy_marks = []
+    stack.step()
+    end = torch.cuda.Event(enable_timing=True)
+    end.record(stack.compute)
+    torch.cuda.synchronize()
+    marks, stack.copy_marks = stack.copy_marks, None
+    t = lambda ev: ref_c.elapsed_time(ev)
+    prev = t(ref_x)
+    L = stack.L
+    n_fwd = 2 * L if stack.dpo else L
+    first_part = min([k for tag, k, *_ in marks if tag == "part"], default=None)
+    groups = {"fwd_layer": [], "bwd_layer": [], "slot": []}
+    idle = {"forward": 0.0, "backward": 0.0}
+    busy_total = idle_total = 0.0
+    bytes_total = 0
+    for tag, k, e0, e1, nbytes in marks:
+        t1 = t(e1)
+        if nbytes <= 0:
+            prev = max(prev, t1)
+            continue
+        waits = (tag == "layer" and k > 0) or tag == "slot" or (tag == "part" and k == first_part)
+        start = max(prev, t(e0)) if waits else prev
+        gap, busy = start - prev, max(t1 - start, 1e-6)
+        phase = "forward" if (0 <= k < n_fwd) else "backward"
+        if tag == "slot" and k < 0:
+            phase = "forward"
+        idle[phase] += gap
+        idle_total += gap
+        busy_total += busy
+        bytes_total += nbytes
+        key = "slot" if tag in ("slot", "part") else ("fwd_layer" if k < n_fwd else "bwd_layer")
+        groups[key].append((busy, nbytes))
+        prev = t1
+
+    def summary(v):
+        if not v:
+            return None
+        ms = [b for b, _ in v]
+        return {"n": len(v), "mean_ms": round(sum(ms) / len(ms), 3), "min_ms": round(min(ms), 3),
+                "max_ms": round(max(ms), 3), "GBps": round(sum(n for _, n in v) / (sum(ms) / 1000.0) / 1e9, 2)}
+
+    return {"step_ms": round(t(end), 3), "link_busy_ms": round(busy_total, 3), "link_idle_ms": round(idle_total, 3),
+            "link_idle_ms_by_pass": {k: round(v, 3) for k, v in idle.items()},
+            "GBps_while_busy": round(bytes_total / (busy_total / 1000.0) / 1e9, 2),
+            "copy_stream_done_ms": round(prev, 3), "bytes": bytes_total,
+            "forward_layer_copies": summary(groups["fwd_layer"]), "backward_layer_copies": summary(groups["bwd_layer"]),
+            "slot_copies": summary(groups["slot"])}
 
 
 def other_configs(args):
@@ -774,6 +885,8 @@ def main():
         else:
             call_ms[k] = ms
     blocked_ms = _blocked_on_copies(stack, n_bd)
+    timeline = _copy_timeline(stack)
+    log(f"[bench] copy timeline of one streamed step: {timeline}")
     gemm_time_ms = sum(sum(v) for v in call_ms.values()) / n_bd
     gemm_flops_step = 0.0
     for (kind, gi, _on), ts in call_ms.items():
@@ -835,6 +948,7 @@ def main():
             "avg_GBps_over_step": round((b1 - b0) / args.steps / (ms_per_step / 1000.0) / 1e9, 2),
             "compute_blocked_on_copies_ms_per_step": round(blocked_ms, 3),
             "compute_blocked_share_of_step": round(blocked_ms / ms_per_step, 4),
+            "copy_timeline": timeline,
         },
     }
 
@@ -887,6 +1001,8 @@ def main():
     result["h2d"]["copy_only_GBps"] = round(8 * hb.numel() / (e0.elapsed_time(e1) / 1000.0) / 1e9, 2)
     # the step's bytes at that rate: the floor of any schedule on this link
     result["h2d"]["link_floor_ms_per_step"] = round(result["h2d"]["bytes_per_step"] / (result["h2d"]["copy_only_GBps"] * 1e6), 3)
+    result["h2d"]["copy_GBps_under_load"] = _copy_rate_under_load(stack)
+    log(f"[bench] link rate under compute load: {result['h2d']['copy_GBps_under_load']}")
     # every shard once (host placement can differ between shards)
     rates = []
     for h in stack.host:

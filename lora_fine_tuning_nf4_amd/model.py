@@ -20,7 +20,7 @@ import torch
 
 import synthgen
 from . import lnf4
-from .stack import PROJ_ORDER, dpo_schedule, on_stream, sft_schedule
+from .stack import PROJ_ORDER, StepPacer, dpo_schedule, on_stream, sft_schedule
 
 QKV, O, GU, DOWN = ("q", "k", "v"), ("o",), ("gate", "up"), ("down",)
 
@@ -48,6 +48,7 @@ class StreamedDecoder:
         self.seed, self.n_bufs = seed, n_bufs
         dev = self.dev = torch.device(device)
         self.compute = lnf4.stream_compute_stream(dev)   # a hardware queue of its own
+        self.pacer = StepPacer()   # streamed steps wait for the previous streamed step
         self.copy = torch.cuda.Stream(dev)
         bf16, f32 = torch.bfloat16, torch.float32
         if T % self.S:
@@ -290,9 +291,15 @@ class StreamedDecoder:
     # ------------------------------------------------------------------ one step
     def step(self, resident: bool = False):
         """One training step of the decoder (asynchronous on the compute stream, ordered after
-        the caller's stream's earlier work; the caller's later work waits for it)."""
+        the caller's stream's earlier work; the caller's later work waits for it).  A streamed
+        step first waits on the host for the previous streamed step to finish (StepPacer)."""
+        pace = not resident and self.pacer is not None
+        if pace:
+            self.pacer.wait()
         with on_stream(self.compute):
             self._step(resident)
+            if pace:
+                self.pacer.mark(self.compute)
 
     def _step(self, resident: bool):
         L, cs = self.L, self.compute

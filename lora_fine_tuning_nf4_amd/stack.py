@@ -79,6 +79,29 @@ def on_stream(stream):
     cur.wait_stream(stream)
 
 
+class StepPacer:
+    """Keeps the host at most one streamed step ahead of the GPU: before a step is
+    enqueued, the host sleeps on a blocking-sync event recorded at the end of the previous
+    one.  Left to run ahead, the host fills HIP's command queue and then sits blocked inside
+    kernel launches, and in that state the layer copies of the Llama-8B-shaped stack ran at
+    49.5 instead of 56.2 GB/s (197 against 180.5 ms per step; the link was idle for the same
+    3.5-4 ms of each step either way).  Paced, the GPU loses only the time the host takes to
+    enqueue a step's first calls, which the step's first layer copy covers."""
+
+    def __init__(self):
+        self.ev = None
+
+    def wait(self):
+        if self.ev is not None:
+            self.ev.synchronize()
+            self.ev = None
+
+    def mark(self, stream):
+        ev = torch.cuda.Event(blocking=True)
+        ev.record(stream)
+        self.ev = ev
+
+
 class StreamedStack:
     def __init__(self, wl: synthgen.Workload, n_bufs: int = 2, seed: int = 0,
                  layers: int | None = None, tokens: int | None = None, head_slot: bool = True,
@@ -174,6 +197,13 @@ class StreamedStack:
         # makes compute wait for a copy (layer steps and slot waits); between the two events
         # the stream runs no kernel, so their distance is the time compute was blocked
         self.wait_events = None
+        # when a list: per stream call that may issue copies, (tag, call, event on the compute
+        # stream just before it, event on the copy stream just after it, bytes the call
+        # issued); the call's copies wait for nothing later than the first event, and are
+        # done when the copy stream reaches the second
+        self.copy_marks = None
+        # streamed steps wait for the previous streamed step before they are enqueued
+        self.pacer = StepPacer()
         self.keep_log = False        # True: step() keeps the pass's event log in last_log
         self.last_log = None
         self._embed_in_slot = False   # the next step's embed_tokens was loaded during the last backward
@@ -293,6 +323,20 @@ class StreamedStack:
         we.append((e0, e1))
         return out
 
+    def _copying(self, st, tag, k, fn):
+        """Run a stream call of context st that may issue copies, bracketed by copy_marks
+        events when set."""
+        cm = self.copy_marks
+        if cm is None:
+            return fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0 = lnf4.stream_bytes_copied(st)
+        e0.record(self.compute)
+        out = fn()
+        e1.record(self.copy)
+        cm.append((tag, k, e0, e1, lnf4.stream_bytes_copied(st) - b0))
+        return out
+
     def _lm_head(self, ptr):
         return lnf4.make_weight(lnf4.FMT_BF16, ptr, None, self.wl.vocab, self.wl.hidden, 64)
 
@@ -374,9 +418,15 @@ class StreamedStack:
         it).  resident=True runs the same step from the resident context (no layer copies;
         the head matrices sit in buffers of their own).  compute=False issues the same
         stream calls (copies, waits, slot loads) without the kernels: the time of the
-        stream schedule alone."""
+        stream schedule alone.  A streamed step first waits on the host for the previous
+        streamed step to finish (StepPacer); a resident step, which copies nothing, does not."""
+        pace = not resident and self.pacer is not None
+        if pace:
+            self.pacer.wait()
         with on_stream(self.compute):
             self._step(resident, compute)
+            if pace:
+                self.pacer.mark(self.compute)
 
     def _step(self, resident: bool, compute: bool):
         L = self.L
@@ -385,13 +435,13 @@ class StreamedStack:
         head = self.head and compute
         if slot and self.embed_from_host:
             if not self._lm_head_in_slot:   # loaded once; the embedding never enters the slot
-                lnf4.stream_slot_load(st, self.head_ids[1], self.compute)
+                self._copying(st, "slot", -1, lambda: lnf4.stream_slot_load(st, self.head_ids[1], self.compute))
                 self._lm_head_in_slot = True
             if head:
                 self._embed(self.all_shards[self.head_ids[0]])   # T rows over the host link
         elif slot:
             if not self._embed_in_slot:   # first step: nothing trickled in yet
-                lnf4.stream_slot_load(st, self.head_ids[0], self.compute)   # embed_tokens
+                self._copying(st, "slot", -1, lambda: lnf4.stream_slot_load(st, self.head_ids[0], self.compute))
             ptr = self._waited(lambda: lnf4.stream_slot_wait(st, self.compute))
             self._embed_in_slot = False
             if head:
@@ -400,7 +450,7 @@ class StreamedStack:
             self._embed(self.res_head[0])
         n_fwd = 2 * L if self.dpo else L
         for k, layer in enumerate(self.schedule):
-            base = self._waited(lambda: lnf4.stream_layer_step(st, k, self.compute))
+            base = self._waited(lambda: self._copying(st, "layer", k, lambda: lnf4.stream_layer_step(st, k, self.compute)))
             if k == L or k == n_fwd:
                 # the output head of the forward pass that just ended.  It runs after this
                 # call's stream step, which released the last forward layer's buffer, so the
@@ -423,12 +473,13 @@ class StreamedStack:
                 if slot and k == L - 1 and not self.embed_from_host:
                     # the untied lm_head takes the slot at the end of the first forward pass
                     # and stays there for the second (DPO)
-                    lnf4.stream_slot_load(st, self.head_ids[1], self.compute)
+                    self._copying(st, "slot", k, lambda: lnf4.stream_slot_load(st, self.head_ids[1], self.compute))
             else:
                 if slot and not self.embed_from_host:
                     # the backward is compute-bound: the next step's embed_tokens trickles into
                     # the slot in one piece per layer, between the layer copies
-                    lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L, self.compute)
+                    self._copying(st, "part", k, lambda: lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L,
+                                                                                 self.compute))
                 for gi in range(len(GROUPS) if compute and self.recompute else 0):
                     self._group_fwd(layer, gi, base, adapters=True)   # recompute from the checkpointed inputs
                 for gi in reversed(range(len(GROUPS) if compute else 0)):
