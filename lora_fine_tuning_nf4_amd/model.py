@@ -292,16 +292,15 @@ class StreamedDecoder:
     def step(self, resident: bool = False):
         """One training step of the decoder (asynchronous on the compute stream, ordered after
         the caller's stream's earlier work; the caller's later work waits for it).  A streamed
-        step first waits on the host for the previous streamed step to finish (StepPacer)."""
+        step waits on the host, after its first layer call, for the previous streamed step to
+        finish (StepPacer)."""
         pace = not resident and self.pacer is not None
-        if pace:
-            self.pacer.wait()
         with on_stream(self.compute):
-            self._step(resident)
+            self._step(resident, pace)
             if pace:
                 self.pacer.mark(self.compute)
 
-    def _step(self, resident: bool):
+    def _step(self, resident: bool, pace: bool = False):
         L, cs = self.L, self.compute
         st = self.enable_resident() if resident else self.st
         if not resident:
@@ -317,6 +316,8 @@ class StreamedDecoder:
         dout_i = 0
         for k, layer in enumerate(self.schedule):
             base = lnf4.stream_layer_step(st, k, cs)
+            if pace and k == 0:
+                self.pacer.wait()
             if k == L or k == n_fwd:
                 # the output head of the forward pass that just ended (after this call's
                 # stream step, so the next layer copy overlaps it)

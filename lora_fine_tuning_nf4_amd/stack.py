@@ -80,13 +80,13 @@ def on_stream(stream):
 
 
 class StepPacer:
-    """Keeps the host at most one streamed step ahead of the GPU: before a step is
-    enqueued, the host sleeps on a blocking-sync event recorded at the end of the previous
-    one.  Left to run ahead, the host fills HIP's command queue and then sits blocked inside
-    kernel launches, and in that state the layer copies of the Llama-8B-shaped stack ran at
-    49.5 instead of 56.2 GB/s (197 against 180.5 ms per step; the link was idle for the same
-    3.5-4 ms of each step either way).  Paced, the GPU loses only the time the host takes to
-    enqueue a step's first calls, which the step's first layer copy covers."""
+    """Keeps the host about one streamed step ahead of the GPU: once a step has enqueued its
+    first layer call (and with it the copies of its first layers, which wait only for the
+    buffers' last users), the host sleeps on a blocking-sync event recorded at the end of
+    the previous step before it enqueues the rest.  Left to run ahead, the host fills HIP's
+    command queue and then sits blocked inside kernel launches, and in that state the layer
+    copies of the Llama-8B-shaped stack ran at 49.5 instead of 56.2 GB/s (197 against
+    180.5 ms per step; the link was idle for the same 3.5-4 ms of each step either way)."""
 
     def __init__(self):
         self.ev = None
@@ -418,17 +418,16 @@ class StreamedStack:
         it).  resident=True runs the same step from the resident context (no layer copies;
         the head matrices sit in buffers of their own).  compute=False issues the same
         stream calls (copies, waits, slot loads) without the kernels: the time of the
-        stream schedule alone.  A streamed step first waits on the host for the previous
-        streamed step to finish (StepPacer); a resident step, which copies nothing, does not."""
+        stream schedule alone.  A streamed step waits on the host, after its first layer
+        call, for the previous streamed step to finish (StepPacer); a resident step, which
+        copies nothing, does not."""
         pace = not resident and self.pacer is not None
-        if pace:
-            self.pacer.wait()
         with on_stream(self.compute):
-            self._step(resident, compute)
+            self._step(resident, compute, pace)
             if pace:
                 self.pacer.mark(self.compute)
 
-    def _step(self, resident: bool, compute: bool):
+    def _step(self, resident: bool, compute: bool, pace: bool = False):
         L = self.L
         st = self.enable_resident() if resident else self.st
         slot = self.slot is not None and not resident
@@ -451,6 +450,8 @@ class StreamedStack:
         n_fwd = 2 * L if self.dpo else L
         for k, layer in enumerate(self.schedule):
             base = self._waited(lambda: self._copying(st, "layer", k, lambda: lnf4.stream_layer_step(st, k, self.compute)))
+            if pace and k == 0:
+                self.pacer.wait()
             if k == L or k == n_fwd:
                 # the output head of the forward pass that just ended.  It runs after this
                 # call's stream step, which released the last forward layer's buffer, so the
