@@ -219,6 +219,24 @@ typedef struct lnf4_proj {
 int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
                    hipStream_t stream);
 
+/* The same grouped forward with a caller-owned workspace, which lets a launch of few output
+ * tiles over a long K (the SwiGLU down projection of a small model: 896 outputs over 4864
+ * inputs at T = 2048) run as K splits whose fp32 sums a second launch adds in split order.
+ * The operation and its results' definition are those of lora_group_fwd (20B RLHF
+ * article, "Low-rank adaptation via PEFT"); a split launch sums K in another order, so y
+ * may differ from lora_group_fwd's in the last bits, and it is the same for every call with
+ * the same shapes (no atomics).
+ *   lora_group_fwd_workspace: bytes needed for these descriptors and T (host-only; 0 when
+ *   the launch is not split: bf16 weights, enough output tiles, a short K, or an out_f that
+ *   is not a multiple of 4).
+ *   workspace: device memory of at least that many bytes, 256-byte aligned, used only
+ *   during the call (stream-ordered).  NULL with ws_bytes 0 runs the unsplit launch.
+ * Errors: as lora_group_fwd; EINVAL for a NULL workspace with ws_bytes > 0 when one is
+ * needed, ESHAPE for a workspace smaller than needed, EALIGN for a misaligned one. */
+size_t lora_group_fwd_workspace(const lnf4_proj* projs, int32_t n, int64_t T);
+int lora_group_fwd_ws(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
+                      void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes for lora_group_bwd (the grouped backward below) with these projs and T:
  * which gradients are asked
  * for (dA, dB non-NULL) and whether u is saved decide the buffers, so query with the

@@ -84,8 +84,21 @@ static int adapter_state(const uint16_t* A, const uint16_t* B, int32_t r, const 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // --------------------------------------------------------------------------- group fwd
+// Workspace bytes of a grouped forward with a workspace (0: the launch is not split)
+static size_t group_fwd_ws(const lnf4_proj* projs, int32_t n, int64_t T) {
+  if (!projs || n < 1 || n > LNF4_MAX_GROUP || T < 1 || T > 0x7fffffff) return 0;
+  int32_t of[LNF4_MAX_GROUP];
+  for (int p = 0; p < n; ++p) {
+    if (projs[p].W.fmt != projs[0].W.fmt || projs[p].W.in_f != projs[0].W.in_f || projs[p].W.out_f < 1 ||
+        projs[p].W.out_f > 0x7fffffff || projs[0].W.in_f < 1 || projs[0].W.in_f > 0x7fffffff)
+      return 0;
+    of[p] = (int32_t)projs[p].W.out_f;
+  }
+  return fwd_split_bytes((int)T, of, n, (int)projs[0].W.in_f, projs[0].W.fmt);
+}
+
 int group_fwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t enabled,
-                   hipStream_t s, const char* who) {
+                   void* ws, size_t ws_bytes, hipStream_t s, const char* who) {
   if (!projs) return fail(LNF4_EINVAL, "%s: projs is NULL", who);
   if (n < 1 || n > LNF4_MAX_GROUP) return fail(LNF4_EINVAL, "%s: n=%d outside 1..%d", who, (int)n, LNF4_MAX_GROUP);
   int rc = check_tokens(T, who);
@@ -111,10 +124,18 @@ int group_fwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
   if (T == 0) return LNF4_OK;
   if (!x) return fail(LNF4_EINVAL, "%s: x is NULL", who);
   if (!aligned(x, 16)) return fail(LNF4_EALIGN, "%s: x not 16-byte aligned", who);
+  // K splits need the workspace the caller sized with lora_group_fwd_workspace
+  const size_t need = ws_bytes || ws ? group_fwd_ws(projs, n, T) : 0;
+  if (need > 0) {
+    if (!ws) return fail(LNF4_EINVAL, "%s: workspace is NULL (%zu bytes needed)", who, need);
+    if (ws_bytes < need) return fail(LNF4_ESHAPE, "%s: workspace %zu bytes < %zu needed", who, ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(LNF4_EALIGN, "%s: workspace not 256-byte aligned", who);
+  }
 
   const int K = (int)projs[0].W.in_f;
   FwdArgs a;
   std::memset(&a, 0, sizeof a);
+  a.part = need > 0 ? (float*)ws : nullptr;
   a.x = x;
   a.M = (int)T;
   a.K = K;
@@ -572,7 +593,7 @@ int lora_linear_fwd(const lnf4_weight* W, const uint16_t* x, int64_t T, const ui
   p.scale = scale;
   p.y = y;
   p.u = u;
-  return group_fwd_impl(&p, 1, x, T, 1, stream, "lora_linear_fwd");
+  return group_fwd_impl(&p, 1, x, T, 1, nullptr, 0, stream, "lora_linear_fwd");
 }
 
 size_t lora_linear_bwd_workspace(int64_t T, int64_t out_f, int64_t in_f, int32_t r) {
@@ -628,7 +649,14 @@ int lora_linear_bwd_noalloc(const lnf4_weight* W, const uint16_t* x, const uint1
 
 int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
                    hipStream_t stream) {
-  return group_fwd_impl(projs, n, x, T, adapters_enabled, stream, "lora_group_fwd");
+  return group_fwd_impl(projs, n, x, T, adapters_enabled, nullptr, 0, stream, "lora_group_fwd");
+}
+
+size_t lora_group_fwd_workspace(const lnf4_proj* projs, int32_t n, int64_t T) { return group_fwd_ws(projs, n, T); }
+
+int lora_group_fwd_ws(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
+                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return group_fwd_impl(projs, n, x, T, adapters_enabled, workspace, ws_bytes, stream, "lora_group_fwd_ws");
 }
 
 size_t lora_group_bwd_workspace(const lnf4_proj* projs, int32_t n, int64_t T) { return group_bwd_ws(projs, n, T); }

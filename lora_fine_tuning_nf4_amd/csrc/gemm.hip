@@ -85,6 +85,7 @@ __device__ __forceinline__ FwdProj select_fwd(const FwdArgs& a, int idx) {
   LNF4_SEL(P, a.p, idx, r);
   LNF4_SEL(P, a.p, idx, scale);
   LNF4_SEL(P, a.p, idx, tile_n0);
+  LNF4_SEL(P, a.p, idx, part_off);
   return P;
 }
 
@@ -184,7 +185,7 @@ constexpr int fwd_stage_bytes(int BM) {
 // each), lut2 the byte-pair code table, filled by the caller.
 template <int BM, int NW>
 __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn, uint8_t* sm0, uint8_t* sm1,
-                                             uint8_t* sm2, uint8_t* sm3, const float2* lut2) {
+                                             uint8_t* sm2, uint8_t* sm3, const float2* lut2, int split = 0) {
   constexpr int NT = 64 * NW;
   constexpr int WM = NW / 4;          // waves sharing a column group
   constexpr int MI = BM / 32 / WM;    // 32-row MFMA tiles per wave
@@ -208,7 +209,12 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
   const int M = args.M, K = args.K, out_f = P.out_f;
   const int m0 = tm * BM;
   const int nloc0 = (tn - P.tile_n0) * BN;
-  const int nk = K / BK;
+  // K range of this split (the whole K when the launch is not split): the activation, code
+  // and absmax resources start at its first K-block, so the loop below runs over nk blocks
+  // as for an unsplit tile
+  const bool splitk = args.ksplit > 1;
+  const int kbs = splitk ? split * args.kb_per_split : 0;
+  const int nk = splitk ? min(args.kb_per_split, K / BK - kbs) : K / BK;
   const int nc0 = 64 * wn + l32, nc1 = nc0 + 32;   // this lane's two tile columns
 
   // ---- accumulators start at the rank-r LoRA term s * u[m, :] . B[n, :]
@@ -219,7 +225,7 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-  if (P.u != nullptr && P.r > 0) {
+  if (P.u != nullptr && P.r > 0 && kbs == 0) {  // the first split carries the LoRA term
     const int r = P.r, RP = (r + 15) & ~15;
     uint16_t* Uh = (uint16_t*)sm0;
     uint16_t* Ul = (uint16_t*)sm1;
@@ -246,7 +252,7 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
   constexpr int XQ = X_BYTES / 1024 / NW;
   static_assert(XQ % 2 == 0, "activation loads split over two steps");
   constexpr int NLD = XQ + 4;  // vector-memory ops per wave per K-block
-  const rsrc_t xrs = make_rsrc(args.x + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+  const rsrc_t xrs = make_rsrc(args.x + (size_t)m0 * K + (size_t)kbs * BK, (int64_t)(M - m0) * K * 2 - (int64_t)kbs * BK * 2);
   uint32_t xoff[XQ];
 #pragma unroll
   for (int q = 0; q < XQ; ++q) {
@@ -256,8 +262,8 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
   }
   // ---- weight words (registers): codes of columns nc0 / nc1, K half h; columns >= out_f
   // read column out_f - 1 (their outputs are discarded)
-  const rsrc_t wrs = make_rsrc(P.w, (int64_t)out_f * K / 2);
-  const rsrc_t ars = make_rsrc(P.absmax, (int64_t)out_f * (K / 64) * 4);
+  const rsrc_t wrs = make_rsrc((const uint8_t*)P.w + (size_t)kbs * 32, (int64_t)out_f * K / 2 - (int64_t)kbs * 32);
+  const rsrc_t ars = make_rsrc(P.absmax + kbs, ((int64_t)out_f * (K / 64) - kbs) * 4);
   const int g0 = nloc0 + nc0 < out_f ? nloc0 + nc0 : out_f - 1;
   const int g1 = nloc0 + nc1 < out_f ? nloc0 + nc1 : out_f - 1;
   const uint32_t woff0 = (uint32_t)g0 * (uint32_t)(K / 2) + 16u * h;
@@ -415,6 +421,44 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
 #undef LNF4_XS
 #undef LNF4_AFRAG
 
+  // ---- K split: this split's fp32 sums, added up by a second launch in split order.  As for
+  // the bf16 output below, each wave stages its 64 columns of its rows in its column group's
+  // ring stage (a row is 256 bytes: 16-byte chunk c at c ^ (row & 15), so the 32 rows one
+  // staging write covers spread over all banks) and then stores whole 256-byte row pieces,
+  // 16 lanes to a row.
+  if constexpr (BM / WM * 256 <= fwd_stage_bytes(BM)) {  // 128- and 64-row tiles (the split launches)
+  if (splitk) {
+    LNF4_WAIT_VM_LGKM0(0);  // the ring's last (past-the-end) loads have landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* const stg = wn == 0 ? sm0 : (wn == 1 ? sm1 : (wn == 2 ? sm2 : sm3));
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = 32 * i + l32;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = 8 * j + 2 * g + h;
+          *(floatx4*)(stg + row * 256 + ((c ^ (row & 15)) * 16)) =
+              floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_sched_barrier(0);
+    float* const pp = args.part + P.part_off + (size_t)split * M * out_f;
+    const int c = lane & 15;
+    const int n = nloc0 + 64 * wn + 4 * c;
+#pragma unroll
+    for (int k = 0; k < BM / WM / 4; ++k) {
+      const int row = 4 * k + (lane >> 4);
+      const floatx4 v = *(const floatx4*)(stg + row * 256 + ((c ^ (row & 15)) * 16));
+      const int gm = m0 + rbase + row;
+      if (gm < M && n < out_f) *(floatx4*)(pp + (size_t)gm * out_f + n) = v;
+    }
+    return;
+  }
+  }
   // ---- store bf16.  The accumulators hold the transposed tile: lane (l32, h) has token
   // rbase + 32i + l32 and, for q = 4g..4g+3, the four adjacent outputs 32j + 8g + 4h + 0..3
   // of its column group.  Each wave's 64 columns of a row are one 128-byte line of y, so the
@@ -504,6 +548,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
 
   int tm, tn;
   const int b = blockIdx.x;
+  if constexpr (BM != 256) {
+    if (args.ksplit > 1) {
+      // K splits: blocks [s T, (s+1) T) run split s of the T = n_tiles_m x n_tiles_n tiles
+      const int nt = args.n_tiles_m * args.n_tiles_n, sp = b / nt;
+      tile_coords(b - sp * nt, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+      fwd_nf4_tile<BM, NW>(args, tm, tn + args.tn_base, sm0, sm1, sm2, sm3, lut2, sp);
+      return;
+    }
+  }
   if constexpr (BM == 256 && NW == 4) {
     if (args.xcd_f > 0) {
       // XCD x = b mod 8 runs its blocks i = b / 8 in order; its tiles are the contiguous
@@ -2070,6 +2123,33 @@ static int n_cus() {
   return cus;
 }
 
+int fwd_split_count(int M, const int32_t* out_f, int n_proj, int K, int fmt) {
+  // NF4 weights only, when 128-row tiles would fill under half of the compute units and
+  // K holds at least 32 blocks of 64: up to 4 splits of at least 8 blocks each, as many
+  // as bring the launch to about one round over the compute units
+  if (fmt != 0 || M <= 0 || n_proj < 1) return 1;
+  int tn = 0;
+  for (int p = 0; p < n_proj; ++p) {
+    if (out_f[p] % 4 != 0) return 1;  // the fp32 sums are stored 16 bytes at a time
+    tn += (out_f[p] + 255) / 256;
+  }
+  if (pick_bm(M, tn) != 128) return 1;
+  const int tiles = ((M + 127) / 128) * tn, nk = K / 64, cus = n_cus();
+  if (2 * tiles > cus || nk < 32) return 1;
+  int ks = cus / tiles;
+  if (ks > 4) ks = 4;
+  if (ks > nk / 8) ks = nk / 8;
+  return ks < 2 ? 1 : ks;
+}
+
+size_t fwd_split_bytes(int M, const int32_t* out_f, int n_proj, int K, int fmt) {
+  const int ks = fwd_split_count(M, out_f, n_proj, K, fmt);
+  if (ks < 2) return 0;
+  size_t b = 0;
+  for (int p = 0; p < n_proj; ++p) b += (size_t)ks * (size_t)M * (size_t)out_f[p] * 4;
+  return b;
+}
+
 hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   FwdArgs a = a0;
   if (a.M <= 0 || a.n_tiles_n <= 0) return hipSuccess;
@@ -2094,6 +2174,34 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   const int tn_all = a.n_tiles_n;
   const int tm256 = (a.M + 255) / 256;
   const int t256 = tm256 * tn_all;
+  a.ksplit = 1;
+  if (a.part != nullptr) {
+    int32_t of[kMaxGroup];
+    for (int p = 0; p < a.n_proj; ++p) of[p] = a.p[p].out_f;
+    const int ks = fwd_split_count(a.M, of, a.n_proj, a.K, fmt);
+    if (ks > 1) {
+      // few 128-row tiles over a long K: each tile runs as ks K splits, and a second launch
+      // per projection adds the splits' fp32 sums in split order
+      a.ksplit = ks;
+      a.kb_per_split = (a.K / BK + ks - 1) / ks;
+      int64_t off = 0;
+      for (int p = 0; p < a.n_proj; ++p) {
+        a.p[p].part_off = off;
+        off += (int64_t)ks * a.M * a.p[p].out_f;
+      }
+      a.n_tiles_m = (a.M + 127) / 128;
+      hipLaunchKernelGGL((k_fwd_nf4<128, 4>), dim3(a.n_tiles_m * a.n_tiles_n * ks), dim3(NTHR), 0, s, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      for (int p = 0; p < a.n_proj; ++p) {
+        const int64_t n = (int64_t)a.M * a.p[p].out_f;
+        hipLaunchKernelGGL(k_dx_split_sum, dim3((unsigned)(((n + 3) / 4 + 255) / 256)), dim3(256), 0, s,
+                           (const float*)(a.part + a.p[p].part_off), ks, n, 0, a.p[p].y);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  }
   if (pick_bm(a.M, tn_all) == 128) {
     a.n_tiles_m = (a.M + 127) / 128;
     if (a.n_tiles_m * a.n_tiles_n < cus) {

@@ -22,6 +22,7 @@ struct FwdProj {
   int32_t r;
   float scale;
   int32_t tile_n0;      // first N-tile of this projection in the group's tile space
+  int64_t part_off;     // K-split launches: this projection's fp32 sums [ksplit][T][out] at part + part_off
 };
 struct FwdArgs {
   const uint16_t* x;
@@ -40,8 +41,18 @@ struct FwdArgs {
   int32_t tail_n;
   int32_t xcd_f;
   int32_t xcd_h;
+  // K splits (NF4, 128- and 64-row tiles; set by launch_fwd): ksplit > 1 runs every tile
+  // ksplit times, split s over K-blocks [s kb_per_split, (s+1) kb_per_split), each writing
+  // its fp32 sums to part; a second launch adds the splits in order into y
+  int32_t ksplit;
+  int32_t kb_per_split;
+  float* part;
   FwdProj p[kMaxGroup];
 };
+// K splits of the forward: split count and workspace bytes (0: not split) for (T, the
+// projections' out_f, in, fmt)
+int fwd_split_count(int M, const int32_t* out_f, int n_proj, int K, int fmt);
+size_t fwd_split_bytes(int M, const int32_t* out_f, int n_proj, int K, int fmt);
 
 // ---------------------------------------------------------------- fused dx GEMM
 // dx[T, in] = bf16( sum_p dy_p W'_p + scale_p v_p A_p  (+ dx if accumulate) )

@@ -76,6 +76,8 @@ def _declare(L):
         "lora_linear_bwd_noalloc": (i32, [POINTER(lnf4_weight), vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, i32,
                                           vp]),
         "lora_group_fwd": (i32, [POINTER(lnf4_proj), i32, vp, i64, i32, vp]),
+        "lora_group_fwd_workspace": (sz, [POINTER(lnf4_proj), i32, i64]),
+        "lora_group_fwd_ws": (i32, [POINTER(lnf4_proj), i32, vp, i64, i32, vp, sz, vp]),
         "lora_group_bwd_workspace": (sz, [POINTER(lnf4_proj), i32, i64]),
         "lora_group_bwd": (i32, [POINTER(lnf4_proj), i32, vp, i64, vp, i32, vp, sz, vp]),
         "lnf4_shard_layout": (i32, [i32, POINTER(c_int64), POINTER(c_int64), i32, POINTER(c_int64),
@@ -226,6 +228,17 @@ def _proj_array(projs):
 def lora_group_fwd(projs, x, T: int, adapters_enabled: int = 1, stream=None):
     arr, n = _proj_array(projs)
     _check(lib().lora_group_fwd(arr, n, _ptr(x), T, adapters_enabled, _stream(stream)))
+
+
+def lora_group_fwd_workspace(projs, T: int) -> int:
+    arr, n = _proj_array(projs)
+    return int(lib().lora_group_fwd_workspace(arr, n, T))
+
+
+def lora_group_fwd_ws(projs, x, T: int, adapters_enabled: int, workspace, ws_bytes: int, stream=None):
+    arr, n = _proj_array(projs)
+    _check(lib().lora_group_fwd_ws(arr, n, _ptr(x), T, adapters_enabled, _ptr(workspace), ws_bytes,
+                                   _stream(stream)))
 
 
 def lora_group_bwd_workspace(projs, T: int) -> int:

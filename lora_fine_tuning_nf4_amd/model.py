@@ -140,7 +140,8 @@ class StreamedDecoder:
         self.head_ws = torch.empty(self.head_ws_bytes, dtype=torch.uint8, device=dev)
         ws = 256
         for grp in (QKV, O, GU, DOWN):
-            ws = max(ws, lnf4.lora_group_bwd_workspace(self._projs(0, grp, 256, bwd=True), T))
+            ws = max(ws, lnf4.lora_group_bwd_workspace(self._projs(0, grp, 256, bwd=True), T),
+                     lnf4.lora_group_fwd_workspace(self._projs(0, grp, 256), T))
         self.ws_bytes = ws
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
 
@@ -210,16 +211,20 @@ class StreamedDecoder:
         T, H, cs = self.T, self.H, self.compute
         on = 1 if adapters else 0
         lnf4.lnf4_rmsnorm_fwd(x_in, T, H, base + self.g1_off, self.eps, self.a, self.rstd1, cs)
-        lnf4.lora_group_fwd(self._projs(layer, QKV, base, adapters, ys=(self.q, self.k, self.v)), self.a, T, on, cs)
+        lnf4.lora_group_fwd_ws(self._projs(layer, QKV, base, adapters, ys=(self.q, self.k, self.v)), self.a, T, on,
+                               self.ws, self.ws_bytes, cs)
         lnf4.lnf4_rope(self.q, T, self.nh, self.D, self.S, self.rope, 0, cs)
         lnf4.lnf4_rope(self.k, T, self.nkv, self.D, self.S, self.rope, 0, cs)
         lnf4.lnf4_attn_fwd(self.q, self.k, self.v, T, self.nh, self.nkv, self.D, self.S, self.o, self.lse, cs)
-        lnf4.lora_group_fwd(self._projs(layer, O, base, adapters, ys=(self.po,)), self.o, T, on, cs)
+        lnf4.lora_group_fwd_ws(self._projs(layer, O, base, adapters, ys=(self.po,)), self.o, T, on,
+                               self.ws, self.ws_bytes, cs)
         lnf4.lnf4_add(x_in, self.po, T * H, self.h, cs)
         lnf4.lnf4_rmsnorm_fwd(self.h, T, H, base + self.g2_off, self.eps, self.m, self.rstd2, cs)
-        lnf4.lora_group_fwd(self._projs(layer, GU, base, adapters, ys=(self.g, self.up)), self.m, T, on, cs)
+        lnf4.lora_group_fwd_ws(self._projs(layer, GU, base, adapters, ys=(self.g, self.up)), self.m, T, on,
+                               self.ws, self.ws_bytes, cs)
         lnf4.lnf4_swiglu_fwd(self.g, self.up, self.g.numel(), self.s, cs)
-        lnf4.lora_group_fwd(self._projs(layer, DOWN, base, adapters, ys=(self.dn,)), self.s, T, on, cs)
+        lnf4.lora_group_fwd_ws(self._projs(layer, DOWN, base, adapters, ys=(self.dn,)), self.s, T, on,
+                               self.ws, self.ws_bytes, cs)
         if x_out is not None:
             lnf4.lnf4_add(self.h, self.dn, T * H, x_out, cs)
 

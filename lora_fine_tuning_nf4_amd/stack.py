@@ -181,7 +181,8 @@ class StreamedStack:
         self.dx = [torch.empty((T, wl.shapes[g[0]][1]), dtype=torch.bfloat16, device=dev) for g in GROUPS]
         ws = 0
         for gi, g in enumerate(GROUPS):
-            ws = max(ws, lnf4.lora_group_bwd_workspace(self._projs(0, gi, 256, bwd=True), T))
+            ws = max(ws, lnf4.lora_group_bwd_workspace(self._projs(0, gi, 256, bwd=True), T),
+                     lnf4.lora_group_fwd_workspace(self._projs(0, gi, 256), T))
         self.ws_bytes = max(ws, 256)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
 
@@ -401,8 +402,8 @@ class StreamedStack:
     def _group_fwd(self, layer, gi, base, adapters):
         key = ("fwd", gi, adapters)
         self._mark(key, 0)
-        lnf4.lora_group_fwd(self._projs(layer, gi, base, adapters=adapters), self.layers[layer].x[gi], self.T,
-                            1 if adapters else 0, self.compute)
+        lnf4.lora_group_fwd_ws(self._projs(layer, gi, base, adapters=adapters), self.layers[layer].x[gi], self.T,
+                               1 if adapters else 0, self.ws, self.ws_bytes, self.compute)
         self._mark(key, 1)
 
     def _group_bwd(self, layer, gi, base):

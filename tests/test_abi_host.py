@@ -231,3 +231,25 @@ def test_decoder_glue_validation(L):
     assert L.lnf4_attn_bwd_workspace(128, 4, 4, 64) == 4 * 128 * 4                        # no grouping: no shares
     assert L.lnf4_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 4, 2, 64, 64, FAKE, FAKE, FAKE, FAKE, need - 1,
                            None) == E.LNF4_ESHAPE
+
+
+def test_group_fwd_workspace_and_validation(L):
+    """The K-split forward's workspace query (host-only; a host with no GPU counts 256
+    compute units) and its workspace checks, which come before any launch."""
+    def projs(fmt, out_f, in_f, n=1):
+        return [lnf4.make_proj(_weight(fmt=fmt, out_f=out_f, in_f=in_f), y=FAKE) for _ in range(n)]
+
+    # the SwiGLU down projection of a Qwen2.5-0.5B layer at T = 2048: 16 x 4 tiles of 128 x 256
+    # over 76 K-blocks run as 4 splits, one fp32 [T, 896] array of sums per split
+    assert lnf4.lora_group_fwd_workspace(projs(0, 896, 4864), 2048) == 4 * 2048 * 896 * 4
+    assert lnf4.lora_group_fwd_workspace(projs(1, 896, 4864), 2048) == 0        # bf16 weights
+    assert lnf4.lora_group_fwd_workspace(projs(0, 4096, 14336), 2048) == 0      # 256 tiles: not split
+    assert lnf4.lora_group_fwd_workspace(projs(0, 896, 896), 2048) == 0         # 14 K-blocks: too short
+    assert lnf4.lora_group_fwd_workspace(projs(0, 904, 2112, 2), 200) == 4 * 200 * 904 * 4 * 2
+    assert lnf4.lora_group_fwd_workspace(projs(0, 896, 4864), 0) == 0
+    need = lnf4.lora_group_fwd_workspace(projs(0, 896, 4864), 2048)
+    arr, n = lnf4._proj_array(projs(0, 896, 4864))
+    ws = L.lora_group_fwd_ws
+    assert ws(arr, n, FAKE, 2048, 1, None, need, None) == lnf4.LNF4_EINVAL
+    assert ws(arr, n, FAKE, 2048, 1, FAKE, need - 1, None) == lnf4.LNF4_ESHAPE
+    assert ws(arr, n, FAKE, 2048, 1, FAKE + 16, need, None) == lnf4.LNF4_EALIGN

@@ -1,0 +1,102 @@
+"""The grouped forward with a workspace, where a launch of few 128-row tiles over a long K
+runs as K splits whose fp32 sums a second launch adds in split order: y against the fp64
+oracle per projection, u bitwise equal to the unsplit call's (the same skinny launch), y
+within the bar of the unsplit call's and bitwise the same from call to call.  Cases: the
+Qwen2.5-0.5B down projection shape at T = 256 (4 splits of 19 K-blocks), a two-projection
+group at ragged T whose 33 K-blocks split 9, 9, 9, 6 and whose column tiles end ragged, an
+adapter-off projection with 4 valid columns in its last tile, and one token."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import synthgen  # noqa: E402
+from lora_fine_tuning_nf4_amd import lnf4  # noqa: E402
+from oracle import lora as olora  # noqa: E402
+from oracle import nf4 as onf4  # noqa: E402
+from helpers import bf16_f64, check_tol, dev_f32, dev_u16, dev_u8, host_f32, host_u16  # noqa: E402
+
+# T, in_f, [(out_f, r), ...]
+CASES = [
+    (256, 4864, [(896, 16)]),
+    (200, 2112, [(904, 8), (452, 4)]),
+    (130, 4096, [(260, 0)]),
+    (1, 2048, [(64, 4)]),
+]
+
+
+def _build(T, in_f, spec, seed):
+    x = synthgen.act_bits(T, in_f, seed, "split-x", in_f)
+    host, dev = [], []
+    for p, (o, r) in enumerate(spec):
+        w = synthgen.weight_f32(o, in_f, seed, "split-w", p)
+        codes, absmax = onf4.quantize(w)
+        d = dict(codes=dev_u8(codes), absmax=dev_f32(absmax), o=o, r=r)
+        h = dict(Wd=onf4.decode_f64(codes, absmax), r=r, scale=16.0 / max(r, 1))
+        if r:
+            A = synthgen.adapter_a_bits(r, in_f, seed, "split", p)
+            B = synthgen.adapter_b_bits(o, r, seed, "split", p, std=0.05)
+            d.update(A=dev_u16(A), B=dev_u16(B))
+            h.update(A=bf16_f64(A), B=bf16_f64(B))
+        host.append(h)
+        dev.append(d)
+    return x, host, dev
+
+
+def _run(x_dev, T, in_f, dev, host, ws=None, ws_bytes=0):
+    projs, outs = [], []
+    for d, h in zip(dev, host):
+        y = torch.empty((T, d["o"]), dtype=torch.int16, device="cuda")
+        u = torch.empty((T, d["r"]), dtype=torch.float32, device="cuda") if d["r"] else None
+        W = lnf4.make_weight(lnf4.FMT_NF4, d["codes"], d["absmax"], d["o"], in_f, 64)
+        projs.append(lnf4.make_proj(W, A=d.get("A"), B=d.get("B"), r=d["r"], scale=h["scale"] if d["r"] else 0.0,
+                                    y=y, u=u))
+        outs.append((y, u))
+    if ws is None:
+        lnf4.lora_group_fwd(projs, x_dev, T, 1)
+    else:
+        lnf4.lora_group_fwd_ws(projs, x_dev, T, 1, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return projs, [(host_u16(y), host_f32(u) if u is not None else None) for y, u in outs]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}_in{c[1]}_out{'-'.join(str(o) for o, _ in c[2])}" for c in CASES])
+def test_split_forward_matches_oracle(case):
+    T, in_f, spec = case
+    x, host, dev = _build(T, in_f, spec, seed=33)
+    xd = dev_u16(x)
+    projs, plain = _run(xd, T, in_f, dev, host)
+    ws_bytes = lnf4.lora_group_fwd_workspace(projs, T)
+    assert ws_bytes > 0, "the case is meant to take the K-split launch"
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    _, split = _run(xd, T, in_f, dev, host, ws, ws_bytes)
+    _, again = _run(xd, T, in_f, dev, host, ws, ws_bytes)
+    xf = bf16_f64(x)
+    for p, h in enumerate(host):
+        if h["r"]:
+            y_ref, u_ref = olora.linear_fwd(xf, h["Wd"], h["A"], h["B"], h["scale"])
+            check_tol(split[p][1], u_ref, f"u {p}")
+            assert np.array_equal(split[p][1].view(np.uint32), plain[p][1].view(np.uint32)), f"u {p}"
+        else:
+            y_ref = xf @ h["Wd"].T
+        check_tol(bf16_f64(split[p][0]), y_ref, f"y {p}")
+        check_tol(bf16_f64(split[p][0]), bf16_f64(plain[p][0]), f"y {p} against the unsplit launch")
+        assert np.array_equal(split[p][0], again[p][0]), f"y {p} differs between two calls"
+
+
+def test_split_forward_workspace_errors():
+    T, in_f, spec = 256, 4864, [(896, 16)]
+    x, host, dev = _build(T, in_f, spec, seed=34)
+    xd = dev_u16(x)
+    projs, _ = _run(xd, T, in_f, dev, host)
+    need = lnf4.lora_group_fwd_workspace(projs, T)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    for args, code in (((None, need), lnf4.LNF4_EINVAL), ((ws, need - 4), lnf4.LNF4_ESHAPE),
+                       ((ws.data_ptr() + 16, need), lnf4.LNF4_EALIGN)):
+        with pytest.raises(lnf4.LNF4Error) as ei:
+            lnf4.lora_group_fwd_ws(projs, xd, T, 1, *args)
+        assert ei.value.code == code
