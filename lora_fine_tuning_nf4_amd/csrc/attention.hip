@@ -382,17 +382,25 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
   Staged<D, NT> pq, po;
   pq.load(q, t0 + (int64_t)qb_first * BQ, ldq, (int64_t)hq0 * D);
   po.load(dO, t0 + (int64_t)qb_first * BQ, ldq, (int64_t)hq0 * D);
+  // the block's per-query statistics travel with its rows: loaded one block ahead into
+  // registers of the first BQ threads (a load issued just before the barrier that
+  // publishes them would expose its latency once per block)
+  float lse_n = 0.0f, dsum_n = 0.0f;
+  if (threadIdx.x < BQ) {
+    const int64_t r = (int64_t)hq0 * T + t0 + (int64_t)qb_first * BQ + threadIdx.x;
+    lse_n = lse[r];
+    dsum_n = dsum[r];
+  }
   for (int hq = hq0; hq < hq1; ++hq)
     for (int qb = qb_first; qb < nqb; ++qb) {
       __syncthreads();
-      const int64_t r0 = t0 + (int64_t)qb * BQ;
       pq.template rows<QS>(Qs);
       pq.rows_swz(Qr);
       po.template rows<QS>(Os);
       po.rows_swz(Or);
       if (threadIdx.x < BQ) {
-        lse_s[threadIdx.x] = lse[(int64_t)hq * T + r0 + threadIdx.x] * 1.44269504088896341f;
-        dsum_s[threadIdx.x] = dsum[(int64_t)hq * T + r0 + threadIdx.x];
+        lse_s[threadIdx.x] = lse_n * 1.44269504088896341f;
+        dsum_s[threadIdx.x] = dsum_n;
       }
       __syncthreads();
       {  // the next block (the next query block, or the next head's first) while this computes
@@ -401,6 +409,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
           const int nq = last_qb ? qb_first : qb + 1, nhq = last_qb ? hq + 1 : hq;
           pq.load(q, t0 + (int64_t)nq * BQ, ldq, (int64_t)nhq * D);
           po.load(dO, t0 + (int64_t)nq * BQ, ldq, (int64_t)nhq * D);
+          if (threadIdx.x < BQ) {
+            const int64_t r = (int64_t)nhq * T + t0 + (int64_t)nq * BQ + threadIdx.x;
+            lse_n = lse[r];
+            dsum_n = dsum[r];
+          }
         }
       }
 #pragma unroll
