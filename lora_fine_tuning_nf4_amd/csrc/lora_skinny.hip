@@ -77,7 +77,9 @@ __device__ __forceinline__ const uint16_t* rank_row(const RankJob& J, int kk, in
   return w;
 }
 
-// A workgroup owns 16 rows of src and every rank of its job (RT tiles of 16).  Its 8 waves
+// A workgroup owns BT (16, or 8 when 16-row workgroups would leave compute units idle)
+// rows of src and every rank of its job (RT tiles of 16); with 8 rows the MFMA's other 8
+// A rows read zeros.  Its 8 waves
 // take the job's K in super-steps of 64 (wave w: steps w, w + 8, ...).  Half h of a
 // super-step (K 32h .. 32h+31) feeds one MFMA; lane l reads the 8 K at 8 (l >> 4) of it
 // from its row, so one load instruction reads 64 contiguous bytes of each of 16 rows.
@@ -90,15 +92,16 @@ __device__ __forceinline__ const uint16_t* rank_row(const RankJob& J, int kk, in
 // branches, so the compiler's wait before a step's MFMAs leaves the later steps' loads
 // outstanding.  The waves' partial sums add through LDS in wave order; the K split
 // depends on K alone, so a result does not depend on the other ranks of its job or on PD.
-template <int RT, int LAYOUT, int PD_>
+template <int RT, int LAYOUT, int PD_, int BT = 16>
 __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
   // register budget: 8 steps in flight for the 1-2 tile shapes, at most 2 for the widest
   constexpr int PD = (LAYOUT == 1 && RT == 4 && PD_ > 2) ? 2 : ((RT > 2 || (LAYOUT == 1 && RT > 1)) && PD_ > 4 ? 4 : PD_);
-  constexpr int NW = 8, BT = 16, R16 = 16 * RT;
+  constexpr int NW = 8, BTM = 16, R16 = 16 * RT;  // BTM: rows of the MFMA tile
+  static_assert(BT == 16 || BT == 8, "workgroup rows");
   constexpr int SL = LAYOUT == 1 ? 64 * R16 : 8;  // staging slice per wave (bf16 elements)
   constexpr int PL = 2 * RT;                       // layout 1: 16-byte weight pieces per lane
   constexpr uint32_t OOB = 0x80000000u;            // buffer offset past any resource
-  __shared__ float red[NW * BT * R16];
+  __shared__ float red[NW * BTM * R16];
   __shared__ __attribute__((aligned(16))) uint16_t bst[NW * SL];
   const RankJob& J = args.job[blockIdx.y];
   const int T = args.T, K = J.K, R = J.R;
@@ -108,9 +111,11 @@ __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
   const int nss = (K + 63) >> 6;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  // A operand: row t0 + l16 (rows past T repeat row T - 1; their sums are not stored)
+  // A operand: row t0 + l16 (rows past T repeat row T - 1; their sums are not stored;
+  // lanes past the workgroup's BT rows read zeros)
   const rsrc_t srs = make_rsrc(J.src, (int64_t)T * K * 2);
   const int trow = t0 + l16 < T ? t0 + l16 : T - 1;
+  const bool arow = l16 < BT;
   const uint32_t aoff = 2u * ((uint32_t)trow * (uint32_t)K + 8u * g);
   // layout 0: weight row of concatenated rank 16 rt + l16
   const uint16_t* wrow[RT];
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = 64 * s + 32 * h + 8 * g;  // K % 8 == 0: a half is all in or all out
-      f.a[h] = LNF4_BUF_LD128(srs, k < K ? aoff + 128u * s + 64u * h : OOB, 0);
+      f.a[h] = LNF4_BUF_LD128(srs, (k < K && arow) ? aoff + 128u * s + 64u * h : OOB, 0);
       if (LAYOUT == 0) {
         const int kc = (k < K ? 64 * s + 32 * h : K - 8 - 8 * g);  // clamped into the row
 #pragma unroll
@@ -234,14 +239,14 @@ __global__ __launch_bounds__(512) void k_lora_proj(const RankArgs args) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wave * BT + 4 * g + i) * R16 + 16 * rt + l16] = acc[rt][i];
+    for (int i = 0; i < 4; ++i) red[(wave * BTM + 4 * g + i) * R16 + 16 * rt + l16] = acc[rt][i];
   __syncthreads();
   for (int idx = tid; idx < BT * R; idx += 64 * NW) {
     const int row = idx / R, kk = idx - row * R, t = t0 + row;
     if (t >= T) continue;
     float sum = red[row * R16 + kk];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) sum += red[(w * BT + row) * R16 + kk];
+    for (int w = 1; w < NW; ++w) sum += red[(w * BTM + row) * R16 + kk];
     float* d = J.dst[0];
     int off = 0;
 #pragma unroll
@@ -424,15 +429,35 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int LAYOUT, int PD, int BT>
+static void launch_proj_bt(const RankArgs& a, int rt, hipStream_t s) {
+  const dim3 grid((a.T + BT - 1) / BT, a.n_jobs), blk(512);
+  switch (rt) {
+    case 1: hipLaunchKernelGGL((k_lora_proj<1, LAYOUT, PD, BT>), grid, blk, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_lora_proj<2, LAYOUT, PD, BT>), grid, blk, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_lora_proj<3, LAYOUT, PD, BT>), grid, blk, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_lora_proj<4, LAYOUT, PD, BT>), grid, blk, 0, s, a); break;
+  }
+}
+
+static int proj_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+           prop.multiProcessorCount > 0) ? prop.multiProcessorCount : 256;
+  }
+  return cus;
+}
+
 template <int LAYOUT, int PD>
 static void launch_proj_pd(const RankArgs& a, int rt, hipStream_t s) {
-  const dim3 grid((a.T + 15) / 16, a.n_jobs), blk(512);
-  switch (rt) {
-    case 1: hipLaunchKernelGGL((k_lora_proj<1, LAYOUT, PD>), grid, blk, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_lora_proj<2, LAYOUT, PD>), grid, blk, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_lora_proj<3, LAYOUT, PD>), grid, blk, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_lora_proj<4, LAYOUT, PD>), grid, blk, 0, s, a); break;
-  }
+  // 8-row workgroups when 16-row ones would fill under one round of the compute units:
+  // the launch reads src at the rate of the units it runs on (Llama-8B u of q|v at
+  // T = 2048: 128 workgroups of 16 rows)
+  if ((int64_t)((a.T + 15) / 16) * a.n_jobs < proj_cus()) launch_proj_bt<LAYOUT, PD, 8>(a, rt, s);
+  else launch_proj_bt<LAYOUT, PD, 16>(a, rt, s);
 }
 
 template <int LAYOUT>
