@@ -647,17 +647,17 @@ def _copy_timeline(stack):
     prev = t(ref_x)
     L = stack.L
     n_fwd = 2 * L if stack.dpo else L
-    first_part = min([k for tag, k, *_ in marks if tag == "part"], default=None)
+    first_part = next((i for i, m in enumerate(marks) if m[0] == "part"), None)  # part 0 waits for the head
     groups = {"fwd_layer": [], "bwd_layer": [], "slot": []}
     idle = {"forward": 0.0, "backward": 0.0}
     busy_total = idle_total = 0.0
     bytes_total = 0
-    for tag, k, e0, e1, nbytes in marks:
+    for mi, (tag, k, e0, e1, nbytes) in enumerate(marks):
         t1 = t(e1)
         if nbytes <= 0:
             prev = max(prev, t1)
             continue
-        waits = (tag == "layer" and k > 0) or tag == "slot" or (tag == "part" and k == first_part)
+        waits = (tag == "layer" and k > 0) or tag == "slot" or (tag == "part" and mi == first_part)
         start = max(prev, t(e0)) if waits else prev
         gap, busy = start - prev, max(t1 - start, 1e-6)
         phase = "forward" if (0 <= k < n_fwd) else "backward"

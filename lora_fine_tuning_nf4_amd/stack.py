@@ -205,6 +205,13 @@ class StreamedStack:
         self.copy_marks = None
         # streamed steps wait for the previous streamed step before they are enqueued
         self.pacer = StepPacer()
+        # head-slot schedule: lm_head is loaded after forward call lm_head_call, so that it is
+        # in the slot when the forward ends and the head runs while the first backward layers
+        # copy; the first backward call issues lead_parts parts of the next embedding (the
+        # link would otherwise wait for the first backward layer's compute there), every
+        # later one a single part
+        self.lm_head_call = self.L - 2 if self.L >= 2 else self.L - 1
+        self.lead_parts = min(3, self.L)
         self.keep_log = False        # True: step() keeps the pass's event log in last_log
         self.last_log = None
         self._embed_in_slot = False   # the next step's embed_tokens was loaded during the last backward
@@ -472,16 +479,20 @@ class StreamedStack:
                 ref_pass = self.dpo and k < L
                 for gi in range(len(GROUPS) if compute else 0):
                     self._group_fwd(layer, gi, base, adapters=not ref_pass)
-                if slot and k == L - 1 and not self.embed_from_host:
-                    # the untied lm_head takes the slot at the end of the first forward pass
-                    # and stays there for the second (DPO)
+                if slot and k == self.lm_head_call and not self.embed_from_host:
+                    # the untied lm_head takes the slot before the end of the first forward
+                    # pass and stays there for the second (DPO)
                     self._copying(st, "slot", k, lambda: lnf4.stream_slot_load(st, self.head_ids[1], self.compute))
             else:
                 if slot and not self.embed_from_host:
-                    # the backward is compute-bound: the next step's embed_tokens trickles into
-                    # the slot in one piece per layer, between the layer copies
-                    self._copying(st, "part", k, lambda: lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L,
-                                                                                 self.compute))
+                    # the next step's embed_tokens trickles into the slot in L parts between
+                    # the layer copies: lead_parts at the first backward call, then one per call
+                    i = k - n_fwd
+                    p0 = 0 if i == 0 else self.lead_parts + i - 1
+                    p1 = self.lead_parts - 1 if i == 0 else p0
+                    for p in range(p0, min(p1, L - 1) + 1):
+                        self._copying(st, "part", k, lambda: lnf4.stream_slot_load_part(st, self.head_ids[0], p, L,
+                                                                                     self.compute))
                 for gi in range(len(GROUPS) if compute and self.recompute else 0):
                     self._group_fwd(layer, gi, base, adapters=True)   # recompute from the checkpointed inputs
                 for gi in reversed(range(len(GROUPS) if compute else 0)):

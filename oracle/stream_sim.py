@@ -177,7 +177,8 @@ SLOT_WAIT = 3
 
 
 def stack_step_log(n_layers: int, n_bufs: int, dpo: bool = False, embed_from_host: bool = False,
-                   first: bool = True, loads_before: int = 0):
+                   first: bool = True, loads_before: int = 0, lm_head_call: int | None = None,
+                   lead_parts: int = 1):
     """Event log of one step of the streamed stack with its head slot (layer ring as in
     ``simulate``).  The slot holds embed_tokens at the start of the step and the untied
     lm_head at the forward/backward turn (the Soup deep dive, "How layer streaming works":
@@ -187,9 +188,13 @@ def stack_step_log(n_layers: int, n_bufs: int, dpo: bool = False, embed_from_hos
     * the embedding is loaded whole before the first step; in every backward call one of L
       parts of the next step's embedding follows that call's layer copies (part 0 waits
       for the head, the slot's last user);
-    * lm_head is loaded after the last forward call of the (first) forward pass and waited
-      for right after the stream step of the first call past each forward pass (DPO: the
-      reference pass and the policy pass), where the head runs;
+    * lm_head is loaded after forward call ``lm_head_call`` of the (first) forward pass (by
+      default the last one, L - 1) and waited for right after the stream step of the first
+      call past each forward pass (DPO: the reference pass and the policy pass), where the
+      head runs;
+    * the first backward call issues ``lead_parts`` parts of the next embedding (part 0
+      first, waiting for the head), every later backward call one more, until all L are
+      issued;
     * ``embed_from_host``: the embedding rows are read from the host table, so the slot
       only ever holds lm_head, loaded once at the start of the first step.
 
@@ -203,6 +208,8 @@ def stack_step_log(n_layers: int, n_bufs: int, dpo: bool = False, embed_from_hos
     sched = dpo_schedule(L) if dpo else sft_schedule(L)
     ring = simulate(sched, n_bufs)
     n_fwd = 2 * L if dpo else L
+    lm_at = L - 1 if lm_head_call is None else lm_head_call
+    assert 0 <= lm_at < L and 1 <= lead_parts <= L
     n = loads_before
     log = []
 
@@ -226,13 +233,16 @@ def stack_step_log(n_layers: int, n_bufs: int, dpo: bool = False, embed_from_hos
         if k == L or k == n_fwd:
             wait(k + 1)
         if k < n_fwd:
-            if k == L - 1 and not embed_from_host:
-                whole(L, LM)
+            if k == lm_at and not embed_from_host:
+                whole(k + 1, LM)
         elif not embed_from_host:
-            p = k - n_fwd
-            log.append((SLOT_COPY, k + 1, n, E, -1 - p, n - 1 if p == 0 else -1))
-            if p == L - 1:
-                n += 1
+            i = k - n_fwd
+            first_p = 0 if i == 0 else lead_parts + i - 1
+            last_p = lead_parts - 1 if i == 0 else first_p
+            for p in range(first_p, min(last_p, L - 1) + 1):
+                log.append((SLOT_COPY, k + 1, n, E, -1 - p, n - 1 if p == 0 else -1))
+                if p == L - 1:
+                    n += 1
     return log
 
 

@@ -644,7 +644,8 @@ def test_stack_log_matches_the_slot_simulator(dpo, efh, nbuf):
         for step in range(3):
             b0 = stack.bytes_copied()
             stack.step()
-            want = ss.stack_step_log(L, nbuf, dpo, efh, first=(step == 0), loads_before=n)
+            want = ss.stack_step_log(L, nbuf, dpo, efh, first=(step == 0), loads_before=n,
+                                     lm_head_call=stack.lm_head_call, lead_parts=stack.lead_parts)
             assert stack.last_log == want, step
             ss.check_slot_log(want, L, dpo, start=None if step == 0 else (L + 1 if efh else L))
             n += (1 if step == 0 else 0) if efh else (3 if step == 0 else 2)

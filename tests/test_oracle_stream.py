@@ -193,3 +193,43 @@ def test_slot_check_catches_a_late_lm_head_and_an_early_embedding_part():
     early = good[:w] + [good[p0]] + good[w:p0] + good[p0 + 1:]
     with pytest.raises(AssertionError):
         ss.check_slot_log(early, L, start=L)
+
+
+@pytest.mark.parametrize("L", [2, 3, 5, 8])
+@pytest.mark.parametrize("dpo", [False, True])
+@pytest.mark.parametrize("lead", [1, 2, 3])
+def test_early_lm_head_and_lead_parts_keep_the_slot_valid(L, dpo, lead):
+    """lm_head loaded one forward call before the last and several embedding parts issued at
+    the first backward call: over three steps the slot still holds the embedding at each
+    step's start and lm_head at each turn, every part is issued once and in order, and the
+    layer ring's events are unchanged."""
+    lead = min(lead, L)
+    n, start = 0, None
+    sched = ss.dpo_schedule(L) if dpo else ss.sft_schedule(L)
+    for step in range(3):
+        lg = ss.stack_step_log(L, 2, dpo, first=(step == 0), loads_before=n, lm_head_call=max(L - 2, 0),
+                               lead_parts=lead)
+        ss.check_slot_log(lg, L, dpo, start=start)
+        assert [e for e in lg if e[0] in (ss.COPY, ss.STEP)] == ss.simulate(sched, 2)
+        parts = [e for e in lg if e[0] == ss.SLOT_COPY and e[3] == L and e[4] <= -1 and not (step == 0 and e[1] == 0)]
+        assert [-1 - e[4] for e in parts] == list(range(L))
+        n_fwd = 2 * L if dpo else L
+        assert [e[1] for e in parts[:lead]] == [n_fwd + 1] * lead
+        assert [e[1] for e in parts[lead:]] == [n_fwd + 1 + i for i in range(1, L - lead + 1)]
+        lm = [e for e in lg if e[0] == ss.SLOT_COPY and e[3] == L + 1]
+        assert len(lm) == 1 and lm[0][1] == max(L - 2, 0) + 1
+        n += 3 if step == 0 else 2
+        start = L
+
+
+def test_slot_check_catches_lm_head_before_the_embedding_is_used():
+    """A negative control for the early lm_head: loaded before the first call's wait, it
+    would overwrite the embedding the step starts from."""
+    L = 4
+    lg = ss.stack_step_log(L, 2, first=False, loads_before=2, lm_head_call=L - 2)
+    i = next(i for i, e in enumerate(lg) if e[0] == ss.SLOT_COPY and e[3] == L + 1)
+    w0 = next(i for i, e in enumerate(lg) if e[0] == ss.SLOT_WAIT and e[1] == 0)
+    bad = [lg[i]] + lg[:i] + lg[i + 1:]
+    assert bad.index(lg[i]) < w0 + 1
+    with pytest.raises(AssertionError):
+        ss.check_slot_log(bad, L, start=L)
