@@ -49,6 +49,10 @@ class StreamedDecoder:
         dev = self.dev = torch.device(device)
         self.compute = lnf4.stream_compute_stream(dev)   # a hardware queue of its own
         self.pacer = StepPacer()   # streamed steps wait for the previous streamed step
+        # head-slot schedule, as in StreamedStack: lm_head loaded after forward call
+        # lm_head_call, lead_parts embedding parts at the first backward call
+        self.lm_head_call = self.L - 2 if self.L >= 2 else self.L - 1
+        self.lead_parts = min(3, self.L)
         self.copy = torch.cuda.Stream(dev)
         bf16, f32 = torch.bfloat16, torch.float32
         if T % self.S:
@@ -342,11 +346,15 @@ class StreamedDecoder:
                     self._layer_fwd(layer, base, x_in, ref_x[layer % 2], adapters=False)
                 else:
                     self._layer_fwd(layer, base, self.xs[layer], self.xs[layer + 1], adapters=True)
-                if k == L - 1 and not resident:
+                if k == self.lm_head_call and not resident:
                     lnf4.stream_slot_load(st, self.head_ids[1], cs)   # lm_head takes the slot
             else:
                 if not resident:
-                    lnf4.stream_slot_load_part(st, self.head_ids[0], k - n_fwd, L, cs)
+                    i = k - n_fwd
+                    p0 = 0 if i == 0 else self.lead_parts + i - 1
+                    p1 = self.lead_parts - 1 if i == 0 else p0
+                    for p in range(p0, min(p1, L - 1) + 1):
+                        lnf4.stream_slot_load_part(st, self.head_ids[0], p, L, cs)
                 self._layer_bwd(layer, base, self.xs[layer], self.dx[dout_i], self.dx[1 - dout_i])
                 dout_i = 1 - dout_i
         lnf4.stream_reset(st, cs)
