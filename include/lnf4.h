@@ -470,6 +470,20 @@ typedef struct lnf4_stream_event {
 int stream_compute_stream(int32_t device, hipStream_t* out);
 
 /*
+ * The stream the layer copies run on, made the same way as the compute stream (a queue of
+ * its own; the 4 GB-laptop article, "Layer streaming: technical implementation and memory
+ * efficiency": the prefetch runs on a dedicated stream).  An ordinary stream shares one of
+ * the runtime's few hardware queues with other streams, and where their packets sit in
+ * front of the copies' event waits and records the ring loses overlap: a Llama-8B-shaped
+ * decoder model whose copy stream was drawn from a process's stream pool after other
+ * streams had been used ran its streamed step in 201 ms, against 182 ms on this stream.
+ * It follows the default-flag stream rules (ordered with the null stream).
+ *   device, out  as for stream_compute_stream (a second, distinct stream; never destroy it)
+ * Errors: EINVAL (device out of range, NULL out), EHIP.
+ */
+int stream_copy_stream(int32_t device, hipStream_t* out);
+
+/*
  * Create a layer stream over one pass of `schedule` (shard indices, e.g. layers
  * 0..L-1 then L-1..0 for an SFT step: forward, then recompute + backward).  The frozen
  * layers stay in page-locked host RAM and a separate stream copies them into a few

@@ -449,41 +449,50 @@ static int create_impl(const char* who, const void* const* host_shards, bool hos
 // turn, and a copy stream on the compute stream's queue would serialise with it).  Never
 // destroyed, so a handle once given out stays valid for the process.
 static std::mutex g_compute_mu;
-static std::vector<hipStream_t> g_compute;
+static std::vector<hipStream_t> g_compute, g_copy;
 
 extern "C" {
 
-int stream_compute_stream(int32_t device, hipStream_t* out) {
-  const char* who = "stream_compute_stream";
+// A stream with a compute-unit mask of every CU of `device`: the runtime gives such a
+// stream a hardware queue of its own.  Created once per device and slot, kept for good.
+static int dedicated_stream(std::vector<hipStream_t>& tab, int32_t device, hipStream_t* out, const char* who) {
   if (!out) return fail(LNF4_EINVAL, "%s: out is NULL", who);
   int n = 0;
   hipError_t e = hipGetDeviceCount(&n);
-  if (e != hipSuccess) return hip_fail(e, "stream_compute_stream: hipGetDeviceCount");
+  if (e != hipSuccess) return hip_fail(e, "dedicated stream: hipGetDeviceCount");
   if (device < 0 || device >= n) return fail(LNF4_EINVAL, "%s: device %d outside 0..%d", who, (int)device, n - 1);
   std::lock_guard<std::mutex> lk(g_compute_mu);
-  if ((int)g_compute.size() < n) g_compute.resize(n, nullptr);
-  if (!g_compute[device]) {
+  if ((int)tab.size() < n) tab.resize(n, nullptr);
+  if (!tab[device]) {
     int cus = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device)) != hipSuccess)
-      return hip_fail(e, "stream_compute_stream: hipDeviceGetAttribute(multiprocessor count)");
+      return hip_fail(e, "dedicated stream: hipDeviceGetAttribute(multiprocessor count)");
     if (cus <= 0) return fail(LNF4_EHIP, "%s: device %d reports %d compute units", who, (int)device, cus);
     std::vector<uint32_t> mask((cus + 31) / 32, 0xffffffffu);
     if (cus % 32) mask.back() = (1u << (cus % 32)) - 1u;
     int prev = 0;
-    if ((e = hipGetDevice(&prev)) != hipSuccess) return hip_fail(e, "stream_compute_stream: hipGetDevice");
-    if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "stream_compute_stream: hipSetDevice");
-    hipStream_t s = nullptr;
-    e = hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data());
+    if ((e = hipGetDevice(&prev)) != hipSuccess) return hip_fail(e, "dedicated stream: hipGetDevice");
+    if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "dedicated stream: hipSetDevice");
+    hipStream_t st = nullptr;
+    e = hipExtStreamCreateWithCUMask(&st, (uint32_t)mask.size(), mask.data());
     const hipError_t e_restore = hipSetDevice(prev);
-    if (e != hipSuccess) return hip_fail(e, "stream_compute_stream: hipExtStreamCreateWithCUMask");
+    if (e != hipSuccess) return hip_fail(e, "dedicated stream: hipExtStreamCreateWithCUMask");
     if (e_restore != hipSuccess) {
-      (void)hipStreamDestroy(s);
-      return hip_fail(e_restore, "stream_compute_stream: hipSetDevice(restore)");
+      (void)hipStreamDestroy(st);
+      return hip_fail(e_restore, "dedicated stream: hipSetDevice(restore)");
     }
-    g_compute[device] = s;
+    tab[device] = st;
   }
-  *out = g_compute[device];
+  *out = tab[device];
   return LNF4_OK;
+}
+
+int stream_compute_stream(int32_t device, hipStream_t* out) {
+  return dedicated_stream(g_compute, device, out, "stream_compute_stream");
+}
+
+int stream_copy_stream(int32_t device, hipStream_t* out) {
+  return dedicated_stream(g_copy, device, out, "stream_copy_stream");
 }
 
 int stream_create(const void* const* host_shards, const size_t* shard_bytes, int32_t n_shards, void* const* dev_bufs,

@@ -97,6 +97,7 @@ def _declare(L):
         "lnf4_attn_bwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp]),
         "lnf4_attn_bwd_workspace": (sz, [i64, i32, i32, i32]),
         "stream_compute_stream": (i32, [i32, POINTER(c_void_p)]),
+        "stream_copy_stream": (i32, [i32, POINTER(c_void_p)]),
         "stream_create": (i32, [POINTER(c_void_p), POINTER(c_size_t), i32, POINTER(c_void_p), sz, i32,
                                 POINTER(c_int32), i32, i32, vp, vp, sz, POINTER(c_void_p)]),
         "stream_layer_step": (i32, [vp, i32, vp, POINTER(c_void_p)]),
@@ -330,6 +331,7 @@ def lnf4_attn_bwd(q, k, v, o, lse, dout, T: int, n_heads: int, n_kv: int, head_d
 
 # ------------------------------------------------------------------ layer stream
 _compute_streams = {}
+_copy_streams = {}
 
 
 def stream_compute_stream(device=None):
@@ -348,6 +350,24 @@ def stream_compute_stream(device=None):
         _check(lib().stream_compute_stream(idx, ctypes.byref(h)))
         s = torch.cuda.ExternalStream(h.value, device=torch.device("cuda", idx))
         _compute_streams[idx] = s
+    return s
+
+
+def stream_copy_stream(device=None):
+    """The library's copy stream of `device` as a torch stream: like the compute stream, a
+    hardware queue of its own, ordered with the null stream.  The same stream on every call."""
+    import torch
+    if isinstance(device, int):
+        idx = device
+    else:
+        d = torch.device(device or "cuda")
+        idx = d.index if d.index is not None else torch.cuda.current_device()
+    s = _copy_streams.get(idx)
+    if s is None:
+        h = c_void_p()
+        _check(lib().stream_copy_stream(idx, ctypes.byref(h)))
+        s = torch.cuda.ExternalStream(h.value, device=torch.device("cuda", idx))
+        _copy_streams[idx] = s
     return s
 
 

@@ -53,7 +53,7 @@ class StreamedDecoder:
         # lm_head_call, lead_parts embedding parts at the first backward call
         self.lm_head_call = self.L - 2 if self.L >= 2 else self.L - 1
         self.lead_parts = min(3, self.L)
-        self.copy = torch.cuda.Stream(dev)
+        self.copy = lnf4.stream_copy_stream(dev)   # a hardware queue of its own
         bf16, f32 = torch.bfloat16, torch.float32
         if T % self.S:
             raise ValueError(f"T={T} is not a whole number of sequences of {self.S}")

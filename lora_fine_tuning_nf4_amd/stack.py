@@ -128,7 +128,7 @@ class StreamedStack:
         # the kernels run on the library's compute stream, which has a hardware queue of its
         # own: a copy stream that shared the compute stream's queue would serialise with it
         self.compute = lnf4.stream_compute_stream(dev)
-        self.copy = torch.cuda.Stream(dev)
+        self.copy = lnf4.stream_copy_stream(dev)   # a hardware queue of its own
 
         # ---- pinned host shards (one contiguous blob per layer), built on the device
         self.host = []

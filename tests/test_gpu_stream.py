@@ -240,6 +240,26 @@ def test_resident_graph_on_a_fresh_stack():
         stack.close()
 
 
+def test_copy_stream_one_per_device_and_not_the_compute_stream():
+    """The library's copy stream: one per device, the same handle on every call, distinct from
+    the compute stream; the stacks issue their layer copies on it."""
+    import ctypes
+    c1, c2, k = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+    assert lnf4.lib().stream_copy_stream(0, ctypes.byref(c1)) == 0
+    assert lnf4.lib().stream_copy_stream(0, ctypes.byref(c2)) == 0
+    assert lnf4.lib().stream_compute_stream(0, ctypes.byref(k)) == 0
+    assert c1.value and c1.value == c2.value and c1.value != k.value
+    assert lnf4.stream_copy_stream(0).cuda_stream == c1.value
+    for bad in (-1, torch.cuda.device_count()):
+        with pytest.raises(lnf4.LNF4Error, match="EINVAL|device"):
+            lnf4.stream_copy_stream(bad)
+    stack = StreamedStack(_small_workload("nf4"), n_bufs=2, seed=3)
+    try:
+        assert stack.copy.cuda_stream == c1.value
+    finally:
+        stack.close()
+
+
 def test_compute_stream_one_per_device():
     """The library hands out one compute stream per device (the same handle on every call)
     and rejects a device that does not exist; the stacks run their kernels on it."""
