@@ -319,7 +319,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_bwd_dq(const 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb * BK + 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float p = key > qpos ? 0.0f : exp2f(st[i] * sl2e - lse2);
+        const float e = exp2f(st[i] * sl2e - lse2);  // masked by a select, not a branch
+        const float p = key > qpos ? 0.0f : e;
         st[i] = p * (dp[i] - dd);  // dS^T
       }
 #pragma unroll
@@ -428,7 +429,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qr = 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);  // query row in the block
-          const float p = kpos > qb * BQ + qr ? 0.0f : exp2f(sa[i] * sl2e - lse_s[qr]);
+          // the exponential for every element, masked afterwards by a select: a branch
+          // around it would split the wave's instruction stream 16 times per half block
+          const float e = exp2f(sa[i] * sl2e - lse_s[qr]);
+          const float p = kpos > qb * BQ + qr ? 0.0f : e;
           sa[i] = p;
           ds[i] = p * (dp[i] - dsum_s[qr]);
         }
