@@ -353,7 +353,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t Os[BQ * QS];   // dO rows
   __shared__ __attribute__((aligned(16))) uint16_t Qr[BQ * D];  // row-major, swizzled
   __shared__ __attribute__((aligned(16))) uint16_t Or[BQ * D];  // dO rows, row-major, swizzled
-  __shared__ float lse_s[BQ], dsum_s[BQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[BQ];
+  __shared__ __attribute__((aligned(16))) float dsum_s[BQ];
   const int nqb = (int)(S / BQ), n_seq = (int)(T / S);
   const int seq = blockIdx.x % n_seq, kb = (int)(blockIdx.x / n_seq);  // early key blocks have the most work
   // part == nullptr: blockIdx.y is a kv head and the workgroup sums its query heads;
@@ -426,15 +427,23 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
           dp = mma(ld16(&Os[(32 * t + l32) * QS + 16 * s + 8 * h]), vf[s], dp);
         }
         floatx16 ds;
+        // a lane's 16 query rows come in 4 runs of 4 consecutive ones: one 16-byte read of
+        // each statistic per run
+        floatx4 lse4[4], dsum4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lse4[j] = *(const floatx4*)&lse_s[32 * t + 8 * j + 4 * h];
+          dsum4[j] = *(const floatx4*)&dsum_s[32 * t + 8 * j + 4 * h];
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qr = 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);  // query row in the block
           // the exponential for every element, masked afterwards by a select: a branch
           // around it would split the wave's instruction stream 16 times per half block
-          const float e = exp2f(sa[i] * sl2e - lse_s[qr]);
+          const float e = exp2f(sa[i] * sl2e - lse4[i >> 2][i & 3]);
           const float p = kpos > qb * BQ + qr ? 0.0f : e;
           sa[i] = p;
-          ds[i] = p * (dp[i] - dsum_s[qr]);
+          ds[i] = p * (dp[i] - dsum4[i >> 2][i & 3]);
         }
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
