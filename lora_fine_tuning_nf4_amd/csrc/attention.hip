@@ -208,13 +208,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_fwd(const uin
       }
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float mn = fmaxf(m, bm);
-    const float alpha = exp2f(m - mn);
+    // the hardware exponential (v_exp_f32): exp2f adds a rescale for results below 2^-126,
+    // which the forward's VALU-bound loop pays for on every element; such probabilities
+    // flush to zero here, beside the row maximum's probability 1 they change no sum
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     float rs = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(st[t][i] - mn);
+        const float p = __builtin_amdgcn_exp2f(st[t][i] - mn);
         st[t][i] = p;
         rs += p;
       }
