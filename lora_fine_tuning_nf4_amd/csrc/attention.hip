@@ -166,6 +166,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_fwd(const uin
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, h = lane >> 5;
   const int64_t ldq = (int64_t)nh * D, ldk = (int64_t)nkv * D, t0 = (int64_t)seq * S;
   const int qpos = qb * BR + wave * 32 + l32;  // this lane's query, position in its sequence
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int kb_last = (qb * BR + BR - 1) / BK;
 
   bf16x8 qf[D / 16];
@@ -197,15 +198,28 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_fwd(const uin
       for (int s = 0; s < D / 16; ++s) st[t] = mma(ld16(&Ks[(32 * t + l32) * KS + 16 * s + 8 * h]), qf[s], st[t]);
     }
     float bm = -INFINITY;
+    // the causal mask only touches the key blocks that reach past this wave's first query
+    // (a wave-uniform test); elsewhere every score is kept
+    if (kb * BK + BK - 1 > qb * BR + wave_u * 32) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * BK + 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float x = key > qpos ? -INFINITY : st[t][i] * sl2e;
-        st[t][i] = x;
-        bm = fmaxf(bm, x);
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * BK + 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
+          const float x = key > qpos ? -INFINITY : st[t][i] * sl2e;
+          st[t][i] = x;
+          bm = fmaxf(bm, x);
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = st[t][i] * sl2e;
+          st[t][i] = x;
+          bm = fmaxf(bm, x);
+        }
+    }
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float mn = fmaxf(m, bm);
     // the hardware exponential (v_exp_f32): exp2f adds a rescale for results below 2^-126,
@@ -224,10 +238,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_fwd(const uin
     rs += __shfl_xor(rs, 32);
     l = l * alpha + rs;
     m = mn;
+    if (__ballot(alpha != 1.0f)) {  // a factor of exactly 1 for every lane changes nothing
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
