@@ -338,7 +338,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_bwd_dq(const 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb * BK + 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float e = exp2f(st[i] * sl2e - lse2);  // masked by a select, not a branch
+        // masked by a select, not a branch; the hardware exponential, as in the forward
+        const float e = __builtin_amdgcn_exp2f(st[i] * sl2e - lse2);
         const float p = key > qpos ? 0.0f : e;
         st[i] = p * (dp[i] - dd);  // dS^T
       }
