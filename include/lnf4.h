@@ -215,7 +215,14 @@ typedef struct lnf4_proj {
 
 /* Grouped forward: n (1..8) projections with the same in_f share x (the adapted projections
  * of the pages' configs, q and v, read the same attention input: 20B RLHF article,
- * "Low-rank adaptation via PEFT"). */
+ * "Low-rank adaptation via PEFT").
+ *   adapters_enabled  0: base only (y = x W'^T; A, B, u ignored).  1: adapters on, u = x A^T
+ *                     computed and written.  2: adapters on, u read as given: it must hold
+ *                     x A^T from an earlier call with the same x and A, as in the checkpoint
+ *                     recompute of the backward, which re-reads a layer for its forward on
+ *                     the saved input (Soup deep dive, "Core feature: how layer streaming
+ *                     works"); y is then bitwise the y of that earlier call.
+ * Errors: as lora_linear_fwd; EINVAL for adapters_enabled outside 0..2. */
 int lora_group_fwd(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t T, int32_t adapters_enabled,
                    hipStream_t stream);
 

@@ -103,6 +103,8 @@ int group_fwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
   if (n < 1 || n > LNF4_MAX_GROUP) return fail(LNF4_EINVAL, "%s: n=%d outside 1..%d", who, (int)n, LNF4_MAX_GROUP);
   int rc = check_tokens(T, who);
   if (rc) return rc;
+  if (enabled < 0 || enabled > 2)
+    return fail(LNF4_EINVAL, "%s: adapters_enabled=%d (0 off, 1 on, 2 on with u already computed)", who, (int)enabled);
   int on[LNF4_MAX_GROUP];
   for (int p = 0; p < n; ++p) {
     const lnf4_proj& P = projs[p];
@@ -147,7 +149,7 @@ int group_fwd_impl(const lnf4_proj* projs, int32_t n, const uint16_t* x, int64_t
     std::memset(&ra, 0, sizeof ra);
     ra.T = (int)T;
     for (int p = 0; p < n; ++p) {
-      if (!on[p]) continue;
+      if (!on[p] || enabled == 2) continue;  // 2: u holds x A^T from an earlier call on this x
       const lnf4_proj& P = projs[p];
       RankJob* J = ra.n_jobs > 0 ? &ra.job[ra.n_jobs - 1] : nullptr;
       if (!J || J->R + P.r > LNF4_MAX_RANK || J->n == kMaxGroup) {

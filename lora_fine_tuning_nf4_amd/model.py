@@ -211,9 +211,11 @@ class StreamedDecoder:
         return out
 
     # ------------------------------------------------------------------ one layer
-    def _layer_fwd(self, layer, base, x_in, x_out, adapters=True):
+    def _layer_fwd(self, layer, base, x_in, x_out, adapters=True, u_saved=False):
+        """u_saved: the recompute of a layer whose forward already wrote every u = x A^T from
+        the same checkpointed input (the calls read them instead of recomputing them)."""
         T, H, cs = self.T, self.H, self.compute
-        on = 1 if adapters else 0
+        on = (2 if u_saved else 1) if adapters else 0
         lnf4.lnf4_rmsnorm_fwd(x_in, T, H, base + self.g1_off, self.eps, self.a, self.rstd1, cs)
         lnf4.lora_group_fwd_ws(self._projs(layer, QKV, base, adapters, ys=(self.q, self.k, self.v)), self.a, T, on,
                                self.ws, self.ws_bytes, cs)
@@ -235,7 +237,7 @@ class StreamedDecoder:
     def _layer_bwd(self, layer, base, x_in, dout, dx_out):
         """Recompute the layer from its checkpointed input, then its backward."""
         T, H, cs = self.T, self.H, self.compute
-        self._layer_fwd(layer, base, x_in, None, True)
+        self._layer_fwd(layer, base, x_in, None, True, u_saved=True)
         gb = lambda grp, x, dys, dx: lnf4.lora_group_bwd(self._projs(layer, grp, base, True, True, dys=dys), x, T, dx,
                                                           0, self.ws, self.ws_bytes, cs)
         gb(DOWN, self.s, (dout,), self.ds)

@@ -406,11 +406,14 @@ class StreamedStack:
             self._head_dx(W, c0, n)
         self._mark(("head", "pol"), 1)
 
-    def _group_fwd(self, layer, gi, base, adapters):
+    def _group_fwd(self, layer, gi, base, adapters, u_saved=False):
+        """u_saved: the recompute, whose u = x A^T the forward of the same layer already wrote
+        (same checkpointed x, same adapters), so the call reads it instead of recomputing it."""
         key = ("fwd", gi, adapters)
         self._mark(key, 0)
+        on = (2 if u_saved else 1) if adapters else 0
         lnf4.lora_group_fwd_ws(self._projs(layer, gi, base, adapters=adapters), self.layers[layer].x[gi], self.T,
-                               1 if adapters else 0, self.ws, self.ws_bytes, self.compute)
+                               on, self.ws, self.ws_bytes, self.compute)
         self._mark(key, 1)
 
     def _group_bwd(self, layer, gi, base):
@@ -494,7 +497,7 @@ class StreamedStack:
                         self._copying(st, "part", k, lambda: lnf4.stream_slot_load_part(st, self.head_ids[0], p, L,
                                                                                      self.compute))
                 for gi in range(len(GROUPS) if compute and self.recompute else 0):
-                    self._group_fwd(layer, gi, base, adapters=True)   # recompute from the checkpointed inputs
+                    self._group_fwd(layer, gi, base, adapters=True, u_saved=True)   # recompute from the checkpoints
                 for gi in reversed(range(len(GROUPS) if compute else 0)):
                     self._group_bwd(layer, gi, base)
         if self.keep_log:

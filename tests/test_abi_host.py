@@ -92,6 +92,9 @@ def test_group_validation(L):
     assert L.lora_group_fwd(arr, 2, FAKE, 4, 1, None) == lnf4.LNF4_ESHAPE   # different in_f
     assert L.lora_group_fwd(arr, 9, FAKE, 4, 1, None) == lnf4.LNF4_EINVAL
     assert L.lora_group_fwd(arr, 0, FAKE, 4, 1, None) == lnf4.LNF4_EINVAL
+    one = (lnf4.lnf4_proj * 1)(p)
+    for bad in (-1, 3):   # adapters_enabled: 0 off, 1 on, 2 on with u given
+        assert L.lora_group_fwd(one, 1, FAKE, 4, bad, None) == lnf4.LNF4_EINVAL
 
 
 def test_shard_layout():

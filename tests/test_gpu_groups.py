@@ -121,3 +121,38 @@ def test_group_u_independent_of_rank_neighbours():
         torch.cuda.synchronize()
         outs.append({p: host_f32(u) for p, u, _ in us})
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
+def test_forward_with_u_given_reads_u():
+    """adapters_enabled = 2 (the checkpoint recompute): the call reads u instead of computing
+    it. With the u of an earlier call on the same x, y is bitwise that call's y; with u
+    changed, y changes (so u was read, not recomputed), and u itself is left as given."""
+    T, in_f, seed = 200, 320, 8
+    x = dev_u16(synthgen.act_bits(T, in_f, seed, "ug-x"))
+    projs, outs = [], []
+    for p, (o, r) in enumerate([(264, 8), (136, 16)]):
+        codes, absmax = onf4.quantize(synthgen.weight_f32(o, in_f, seed, "ug-w", p))
+        dc, da = dev_u8(codes), dev_f32(absmax)
+        A = dev_u16(synthgen.adapter_a_bits(r, in_f, seed, "ug", p))
+        B = dev_u16(synthgen.adapter_b_bits(o, r, seed, "ug", p, std=0.05))
+        y = torch.empty((T, o), dtype=torch.int16, device="cuda")
+        u = torch.empty((T, r), dtype=torch.float32, device="cuda")
+        projs.append(lnf4.make_proj(lnf4.make_weight(lnf4.FMT_NF4, dc, da, o, in_f, 64), A=A, B=B, r=r,
+                                    scale=16.0 / r, y=y, u=u))
+        outs.append((y, u, dc, da, A, B))
+    lnf4.lora_group_fwd(projs, x, T, 1)
+    torch.cuda.synchronize()
+    first = [(host_u16(y).copy(), host_f32(u).copy()) for y, u, *_ in outs]
+    for y, *_ in outs:
+        y.zero_()
+    lnf4.lora_group_fwd(projs, x, T, 2)
+    torch.cuda.synchronize()
+    for (y, u, *_), (y1, u1) in zip(outs, first):
+        assert np.array_equal(host_u16(y), y1)
+        assert np.array_equal(host_f32(u).view(np.uint32), u1.view(np.uint32))
+    outs[0][1].mul_(2.0)
+    lnf4.lora_group_fwd(projs, x, T, 2)
+    torch.cuda.synchronize()
+    assert not np.array_equal(host_u16(outs[0][0]), first[0][0])
+    assert np.array_equal(host_f32(outs[0][1]).view(np.uint32), (2.0 * first[0][1]).view(np.uint32))
+    assert np.array_equal(host_u16(outs[1][0]), first[1][0])
