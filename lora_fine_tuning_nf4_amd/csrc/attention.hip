@@ -194,8 +194,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_fwd(const uin
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       st[t] = zero16();
+      bf16x8 kfr[D / 16];
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) st[t] = mma(ld16(&Ks[(32 * t + l32) * KS + 16 * s + 8 * h]), qf[s], st[t]);
+      for (int s = 0; s < D / 16; ++s) kfr[s] = ld16(&Ks[(32 * t + l32) * KS + 16 * s + 8 * h]);
+      __builtin_amdgcn_sched_barrier(0);  // every fragment read in flight before the products
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) st[t] = mma(kfr[s], qf[s], st[t]);
     }
     float bm = -INFINITY;
     // the causal mask only touches the key blocks that reach past this wave's first query
@@ -441,10 +445,19 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_dkdv(const uint16_t* __res
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         floatx16 sa = zero16(), dp = zero16();
+        // the half block's Q and dO fragments are read into registers of their own before
+        // the products (reused registers made every read wait for the MFMA before it)
+        bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          sa = mma(ld16(&Qs[(32 * t + l32) * QS + 16 * s + 8 * h]), kf[s], sa);
-          dp = mma(ld16(&Os[(32 * t + l32) * QS + 16 * s + 8 * h]), vf[s], dp);
+          qa[s] = ld16(&Qs[(32 * t + l32) * QS + 16 * s + 8 * h]);
+          oa[s] = ld16(&Os[(32 * t + l32) * QS + 16 * s + 8 * h]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          sa = mma(qa[s], kf[s], sa);
+          dp = mma(oa[s], vf[s], dp);
         }
         floatx16 ds;
         // a lane's 16 query rows come in 4 runs of 4 consecutive ones: one 16-byte read of
