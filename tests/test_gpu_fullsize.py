@@ -1,6 +1,7 @@
 """Parity at the full layer shapes of the benchmark configurations, in the launch
 configuration the benchmark times (grouped q|k|v, gate|up and down calls at the
-configuration's T), on sampled outputs the oracle computes one by one: whole rows of y and
+configuration's T, the forward through the workspace form the stack calls, so the Qwen2.5-0.5B
+down projection runs its K-split launch), on sampled outputs the oracle computes one by one: whole rows of y and
 dx, whole columns of dA, whole rows of dB.  Llama-3.1-8B NF4 (every group at T = 2048, and
 the DPO step's T = 4096), Qwen2.5-0.5B NF4 with rank 16 on every projection, Qwen2.5-3B bf16
 weights."""
@@ -79,10 +80,14 @@ def test_full_size_group_sampled(wl_name, names):
     x, P = _group(WL, names)
     dev, projs = _dev(WL, names, x, P)
     in_f = WL.shapes[names[0]][1]
-    lnf4.lora_group_fwd(projs, dev["x"], T, 1)
     dx = torch.empty((T, in_f), dtype=torch.int16, device="cuda")
-    ws_bytes = lnf4.lora_group_bwd_workspace(projs, T)
+    # one workspace for both directions, as the stack sizes it: the forward takes its K-split
+    # launch where it has one (the Qwen2.5-0.5B down projection)
+    fwd_ws = lnf4.lora_group_fwd_workspace(projs, T)
+    assert (fwd_ws > 0) == (wl_name == "qwen05b" and names == ("down",)), "which launches take K splits"
+    ws_bytes = max(lnf4.lora_group_bwd_workspace(projs, T), fwd_ws)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    lnf4.lora_group_fwd_ws(projs, dev["x"], T, 1, ws, ws_bytes)
     lnf4.lora_group_bwd(projs, dev["x"], T, dx, 0, ws, ws_bytes)
     torch.cuda.synchronize()
 
