@@ -425,39 +425,45 @@ __device__ __forceinline__ void fwd_nf4_tile(const FwdArgs& args, int tm, int tn
   // the bf16 output below, each wave stages its 64 columns of its rows in its column group's
   // ring stage (a row is 256 bytes: 16-byte chunk c at c ^ (row & 15), so the 32 rows one
   // staging write covers spread over all banks) and then stores whole 256-byte row pieces,
-  // 16 lanes to a row.
-  if constexpr (BM / WM * 256 <= fwd_stage_bytes(BM)) {  // 128- and 64-row tiles (the split launches)
+  // 16 lanes to a row; rows that do not fit the stage at once (256-row tiles) go in passes.
   if (splitk) {
     LNF4_WAIT_VM_LGKM0(0);  // the ring's last (past-the-end) loads have landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* const stg = wn == 0 ? sm0 : (wn == 1 ? sm1 : (wn == 2 ? sm2 : sm3));
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int row = 32 * i + l32;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = 8 * j + 2 * g + h;
-          *(floatx4*)(stg + row * 256 + ((c ^ (row & 15)) * 16)) =
-              floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
-    __builtin_amdgcn_sched_barrier(0);
+    constexpr int RPW = BM / WM;                                   // rows of this wave
+    constexpr int RPP = RPW < fwd_stage_bytes(BM) / 256 ? RPW : fwd_stage_bytes(BM) / 256;  // per pass
+    static_assert(RPW % RPP == 0 && RPP % 32 == 0, "whole MFMA row blocks per pass");
     float* const pp = args.part + P.part_off + (size_t)split * M * out_f;
-    const int c = lane & 15;
-    const int n = nloc0 + 64 * wn + 4 * c;
+    const int cl = lane & 15;
+    const int n = nloc0 + 64 * wn + 4 * cl;
 #pragma unroll
-    for (int k = 0; k < BM / WM / 4; ++k) {
-      const int row = 4 * k + (lane >> 4);
-      const floatx4 v = *(const floatx4*)(stg + row * 256 + ((c ^ (row & 15)) * 16));
-      const int gm = m0 + rbase + row;
-      if (gm < M && n < out_f) *(floatx4*)(pp + (size_t)gm * out_f + n) = v;
+    for (int pass = 0; pass < RPW / RPP; ++pass) {
+#pragma unroll
+      for (int i = pass * (RPP / 32); i < (pass + 1) * (RPP / 32); ++i) {
+        const int row = 32 * i + l32 - pass * RPP;  // row within the pass
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = 8 * j + 2 * g + h;
+            *(floatx4*)(stg + row * 256 + ((c ^ (row & 15)) * 16)) =
+                floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < RPP / 4; ++k) {
+        const int row = 4 * k + (lane >> 4);
+        const floatx4 v = *(const floatx4*)(stg + row * 256 + ((cl ^ (row & 15)) * 16));
+        const int gm = m0 + rbase + pass * RPP + row;
+        if (gm < M && n < out_f) *(floatx4*)(pp + (size_t)gm * out_f + n) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // the pass's reads are done before the next overwrites
+      __builtin_amdgcn_sched_barrier(0);
     }
     return;
-  }
   }
   // ---- store bf16.  The accumulators hold the transposed tile: lane (l32, h) has token
   // rbase + 32i + l32 and, for q = 4g..4g+3, the four adjacent outputs 32j + 8g + 4h + 0..3
@@ -548,14 +554,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_nf4(const FwdArgs args) {
 
   int tm, tn;
   const int b = blockIdx.x;
-  if constexpr (BM != 256) {
-    if (args.ksplit > 1) {
-      // K splits: blocks [s T, (s+1) T) run split s of the T = n_tiles_m x n_tiles_n tiles
-      const int nt = args.n_tiles_m * args.n_tiles_n, sp = b / nt;
-      tile_coords(b - sp * nt, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
-      fwd_nf4_tile<BM, NW>(args, tm, tn + args.tn_base, sm0, sm1, sm2, sm3, lut2, sp);
-      return;
-    }
+  if (args.ksplit > 1) {
+    // K splits: blocks [s T, (s+1) T) run split s of the T = n_tiles_m x n_tiles_n tiles
+    const int nt = args.n_tiles_m * args.n_tiles_n, sp = b / nt;
+    tile_coords(b - sp * nt, args.n_tiles_m, args.n_tiles_n, kGroupM, tm, tn);
+    fwd_nf4_tile<BM, NW>(args, tm, tn + args.tn_base, sm0, sm1, sm2, sm3, lut2, sp);
+    return;
   }
   if constexpr (BM == 256 && NW == 4) {
     if (args.xcd_f > 0) {
@@ -2123,23 +2127,43 @@ static int n_cus() {
   return cus;
 }
 
-int fwd_split_count(int M, const int32_t* out_f, int n_proj, int K, int fmt) {
-  // NF4 weights only, when 128-row tiles would fill under half of the compute units and
-  // K holds at least 32 blocks of 64: up to 4 splits of at least 8 blocks each, as many
-  // as bring the launch to about one round over the compute units
+// K-split plan of an NF4 forward: split count (1: none) and tile height.  128-row tiles when
+// they would fill under half of the compute units and K holds at least 32 blocks of 64 (up
+// to 4 splits of at least 8 blocks); else 256-row tiles when those fill under half of the
+// units and K holds at least 128 blocks (up to 4 splits of at least 64 blocks: a long K
+// whose 256-row tiles run more efficiently than twice as many 128-row ones, the Llama-8B
+// down projection); in each case as many splits as bring the launch to about one round
+static int fwd_split_plan(int M, const int32_t* out_f, int n_proj, int K, int fmt, int& bm) {
+  bm = 128;
   if (fmt != 0 || M <= 0 || n_proj < 1) return 1;
   int tn = 0;
   for (int p = 0; p < n_proj; ++p) {
     if (out_f[p] % 4 != 0) return 1;  // the fp32 sums are stored 16 bytes at a time
     tn += (out_f[p] + 255) / 256;
   }
-  if (pick_bm(M, tn) != 128) return 1;
-  const int tiles = ((M + 127) / 128) * tn, nk = K / 64, cus = n_cus();
-  if (2 * tiles > cus || nk < 32) return 1;
-  int ks = cus / tiles;
-  if (ks > 4) ks = 4;
-  if (ks > nk / 8) ks = nk / 8;
-  return ks < 2 ? 1 : ks;
+  const int nk = K / 64, cus = n_cus();
+  const auto fit = [&](int tiles, int min_blocks) {
+    int ks = cus / tiles;
+    if (ks > 4) ks = 4;
+    if (ks > nk / min_blocks) ks = nk / min_blocks;
+    return ks < 2 ? 1 : ks;
+  };
+  if (pick_bm(M, tn) == 128) {
+    const int t128 = ((M + 127) / 128) * tn;
+    if (2 * t128 <= cus && nk >= 32) return fit(t128, 8);
+  }
+  const int t256 = ((M + 255) / 256) * tn;
+  if (M > 128 && 2 * t256 <= cus && nk >= 128) {
+    const int ks = fit(t256, 64);
+    if (ks > 1) bm = 256;
+    return ks;
+  }
+  return 1;
+}
+
+int fwd_split_count(int M, const int32_t* out_f, int n_proj, int K, int fmt) {
+  int bm;
+  return fwd_split_plan(M, out_f, n_proj, K, fmt, bm);
 }
 
 size_t fwd_split_bytes(int M, const int32_t* out_f, int n_proj, int K, int fmt) {
@@ -2178,7 +2202,8 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
   if (a.part != nullptr) {
     int32_t of[kMaxGroup];
     for (int p = 0; p < a.n_proj; ++p) of[p] = a.p[p].out_f;
-    const int ks = fwd_split_count(a.M, of, a.n_proj, a.K, fmt);
+    int bm = 128;
+    const int ks = fwd_split_plan(a.M, of, a.n_proj, a.K, fmt, bm);
     if (ks > 1) {
       // few 128-row tiles over a long K: each tile runs as ks K splits, and a second launch
       // per projection adds the splits' fp32 sums in split order
@@ -2189,8 +2214,9 @@ hipError_t launch_fwd(const FwdArgs& a0, int fmt, hipStream_t s) {
         a.p[p].part_off = off;
         off += (int64_t)ks * a.M * a.p[p].out_f;
       }
-      a.n_tiles_m = (a.M + 127) / 128;
-      hipLaunchKernelGGL((k_fwd_nf4<128, 4>), dim3(a.n_tiles_m * a.n_tiles_n * ks), dim3(NTHR), 0, s, a);
+      a.n_tiles_m = (a.M + bm - 1) / bm;
+      if (bm == 256) hipLaunchKernelGGL((k_fwd_nf4<256, 4>), dim3(a.n_tiles_m * a.n_tiles_n * ks), dim3(NTHR), 0, s, a);
+      else hipLaunchKernelGGL((k_fwd_nf4<128, 4>), dim3(a.n_tiles_m * a.n_tiles_n * ks), dim3(NTHR), 0, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       for (int p = 0; p < a.n_proj; ++p) {

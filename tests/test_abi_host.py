@@ -246,7 +246,11 @@ def test_group_fwd_workspace_and_validation(L):
     # over 76 K-blocks run as 4 splits, one fp32 [T, 896] array of sums per split
     assert lnf4.lora_group_fwd_workspace(projs(0, 896, 4864), 2048) == 4 * 2048 * 896 * 4
     assert lnf4.lora_group_fwd_workspace(projs(1, 896, 4864), 2048) == 0        # bf16 weights
-    assert lnf4.lora_group_fwd_workspace(projs(0, 4096, 14336), 2048) == 0      # 256 tiles: not split
+    # the Llama-8B down projection: 8 x 16 tiles of 256 x 256 over 224 K-blocks run as 2 splits
+    assert lnf4.lora_group_fwd_workspace(projs(0, 4096, 14336), 2048) == 2 * 2048 * 4096 * 4
+    assert lnf4.lora_group_fwd_workspace(projs(0, 4096, 4096), 2048) == 0       # 64 K-blocks: too short
+    assert lnf4.lora_group_fwd_workspace(projs(0, 4300, 8192), 1000) == 2 * 1000 * 4300 * 4  # 256-row, 2 splits
+    assert lnf4.lora_group_fwd_workspace(projs(0, 28672, 4096), 2048) == 0      # 896 tiles: not split
     assert lnf4.lora_group_fwd_workspace(projs(0, 896, 896), 2048) == 0         # 14 K-blocks: too short
     assert lnf4.lora_group_fwd_workspace(projs(0, 904, 2112, 2), 200) == 4 * 200 * 904 * 4 * 2
     assert lnf4.lora_group_fwd_workspace(projs(0, 896, 4864), 0) == 0

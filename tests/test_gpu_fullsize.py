@@ -1,7 +1,7 @@
 """Parity at the full layer shapes of the benchmark configurations, in the launch
 configuration the benchmark times (grouped q|k|v, gate|up and down calls at the
 configuration's T, the forward through the workspace form the stack calls, so the Qwen2.5-0.5B
-down projection runs its K-split launch), on sampled outputs the oracle computes one by one: whole rows of y and
+and Llama-8B down projections run their K-split launches), on sampled outputs the oracle computes one by one: whole rows of y and
 dx, whole columns of dA, whole rows of dB.  Llama-3.1-8B NF4 (every group at T = 2048, and
 the DPO step's T = 4096), Qwen2.5-0.5B NF4 with rank 16 on every projection, Qwen2.5-3B bf16
 weights."""
@@ -84,7 +84,7 @@ def test_full_size_group_sampled(wl_name, names):
     # one workspace for both directions, as the stack sizes it: the forward takes its K-split
     # launch where it has one (the Qwen2.5-0.5B down projection)
     fwd_ws = lnf4.lora_group_fwd_workspace(projs, T)
-    assert (fwd_ws > 0) == (wl_name == "qwen05b" and names == ("down",)), "which launches take K splits"
+    assert (fwd_ws > 0) == (names == ("down",) and wl_name in ("qwen05b", "llama8b")), "which launches take K splits"
     ws_bytes = max(lnf4.lora_group_bwd_workspace(projs, T), fwd_ws)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     lnf4.lora_group_fwd_ws(projs, dev["x"], T, 1, ws, ws_bytes)
