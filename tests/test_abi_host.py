@@ -251,6 +251,9 @@ def test_group_fwd_workspace_and_validation(L):
     assert lnf4.lora_group_fwd_workspace(projs(0, 4096, 4096), 2048) == 0       # 64 K-blocks: too short
     assert lnf4.lora_group_fwd_workspace(projs(0, 4300, 8192), 1000) == 2 * 1000 * 4300 * 4  # 256-row, 2 splits
     assert lnf4.lora_group_fwd_workspace(projs(0, 28672, 4096), 2048) == 0      # 896 tiles: not split
+    # two projections, 4 x 18 tiles of 256 rows over 256 K-blocks: 3 splits (3 x 72 tiles)
+    assert lnf4.lora_group_fwd_workspace(projs(0, 2200, 16384) + projs(0, 2100, 16384), 1000) == \
+        3 * 1000 * (2200 + 2100) * 4
     assert lnf4.lora_group_fwd_workspace(projs(0, 896, 896), 2048) == 0         # 14 K-blocks: too short
     assert lnf4.lora_group_fwd_workspace(projs(0, 904, 2112, 2), 200) == 4 * 200 * 904 * 4 * 2
     assert lnf4.lora_group_fwd_workspace(projs(0, 896, 4864), 0) == 0

@@ -3,7 +3,8 @@ runs as K splits whose fp32 sums a second launch adds in split order: y against 
 oracle per projection, u bitwise equal to the unsplit call's (the same skinny launch), y
 within the bar of the unsplit call's and bitwise the same from call to call.  Cases: the
 Qwen2.5-0.5B down projection shape at T = 256 (4 splits of 19 K-blocks), 256-row tiles over
-128 K-blocks in 2 splits with ragged last row and column tiles, a two-projection
+128 K-blocks in 2 splits with ragged last row and column tiles, the same over 256 K-blocks in
+3 splits for a two-projection group, a two-projection
 group at ragged T whose 33 K-blocks split 9, 9, 9, 6 and whose column tiles end ragged, an
 adapter-off projection with 4 valid columns in its last tile, and one token."""
 import numpy as np
@@ -27,6 +28,9 @@ CASES = [
     # 256-row tiles (136 tiles of 128 rows would fill over half of the compute units): 4 x 17
     # tiles over 128 K-blocks in 2 splits of 64, the last row and column tiles ragged
     (1000, 8192, [(4300, 8)]),
+    # two projections on 256-row tiles, 4 x 18 of them over 256 K-blocks in 3 splits (86, 86,
+    # 84 blocks), each projection's last column tile ragged
+    (1000, 16384, [(2200, 8), (2100, 4)]),
     (200, 2112, [(904, 8), (452, 4)]),
     (130, 4096, [(260, 0)]),
     (1, 2048, [(64, 4)]),
