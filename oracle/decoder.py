@@ -2,10 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
-The configs name Llama/Qwen decoder layers by their parts: RMSNorm, grouped-query
-attention with 32 query and 8 KV heads of dim 128 (or 14 / 2 of dim 64), a SwiGLU MLP,
-residual connections (the BASELINE configs; the Soup deep dive, "Core feature: how
-layer streaming works", names the per-layer checkpoint recompute).  The pages give no
+The Llama-3.1-8B and Qwen2.5 workloads are decoder layers made of RMSNorm, grouped-query
+attention with 32 query and 8 KV heads of dim 128 (or 14 / 2 of dim 64), a SwiGLU MLP and
+residual connections (the Soup deep dive, "Core feature: how layer streaming works", names
+the per-layer checkpoint recompute).  The pages give no
 formulas for them; the readings are the standard Llama definitions:
 
   RMSNorm   y = x / sqrt(mean(x^2) + eps) * g                         (g frozen)
